@@ -1,0 +1,169 @@
+"""CPU oracle for the W4A16 symmetric-INT4 GPTQ linear (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product path never imports this
+package, and this package never imports the product.
+
+The arithmetic lives in ``w4a16_oracle.c`` (plain C, fp64 accumulation); this
+file only compiles it with gcc and marshals numpy arrays.  See the C file's
+header for the definition it follows and the passages of the pages it cites.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC_PATH = os.path.join(_HERE, "w4a16_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libw4a16_oracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+             "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one oracle source file to a shared library with the oracle's flags."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *GCC_FLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no FP contraction, no fast-math)."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    return compile_source(SRC_PATH, LIB_PATH)
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid arguments (rc={rc})")
+
+
+class Oracle:
+    """One loaded build of the oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_unpack.argtypes = [p, i64, i64, p]
+        lib.oracle_pack.argtypes = [p, i64, i64, p]
+        lib.oracle_dequant.argtypes = [p, p, i64, i64, i64, p]
+        lib.oracle_linear.argtypes = [p, p, p, i64, i64, i64, i64, p]
+        lib.oracle_linear_at.argtypes = [p, p, p, i64, i64, i64, i64, p, p, i64, p]
+        for f in (lib.oracle_unpack, lib.oracle_pack, lib.oracle_dequant,
+                  lib.oracle_linear, lib.oracle_linear_at):
+            f.restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def pack(self, codes: np.ndarray) -> np.ndarray:
+        """uint8 codes [K, N] -> int32 qweight [K/8, N]."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        K, N = codes.shape
+        out = np.empty((K // 8, N), dtype=np.int32)
+        _check(self.lib.oracle_pack(_ptr(codes), K, N, _ptr(out)), "pack")
+        return out
+
+    def unpack(self, qweight: np.ndarray) -> np.ndarray:
+        """int32 qweight [K/8, N] -> uint8 codes [K, N]."""
+        qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+        R, N = qweight.shape
+        out = np.empty((8 * R, N), dtype=np.uint8)
+        _check(self.lib.oracle_unpack(_ptr(qweight), 8 * R, N, _ptr(out)), "unpack")
+        return out
+
+    def dequant(self, qweight: np.ndarray, scales: np.ndarray, group_size: int) -> np.ndarray:
+        """Dense fp32 weight [K, N] = (q - 8) * s."""
+        qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+        scales = np.ascontiguousarray(scales, dtype=np.float16)
+        K, N = 8 * qweight.shape[0], qweight.shape[1]
+        out = np.empty((K, N), dtype=np.float32)
+        _check(self.lib.oracle_dequant(_ptr(qweight), _ptr(scales.view(np.uint16)), K, N,
+                                       group_size, _ptr(out)), "dequant")
+        return out
+
+    def linear(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+               group_size: int) -> np.ndarray:
+        """y [M, N] float64 = x [M, K] fp16 . dequant(qweight, scales)."""
+        x = np.ascontiguousarray(x, dtype=np.float16)
+        qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+        scales = np.ascontiguousarray(scales, dtype=np.float16)
+        M, K = x.shape
+        N = qweight.shape[1]
+        if qweight.shape[0] * 8 != K:
+            raise ValueError("qweight rows must be K/8")
+        y = np.empty((M, N), dtype=np.float64)
+        _check(self.lib.oracle_linear(_ptr(x.view(np.uint16)), _ptr(qweight),
+                                      _ptr(scales.view(np.uint16)), M, K, N, group_size,
+                                      _ptr(y)), "linear")
+        return y
+
+    def linear_at(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+                  group_size: int, ms: np.ndarray, ns: np.ndarray) -> np.ndarray:
+        """y[ms[i], ns[i]] for sampled outputs, each computed from the definition."""
+        x = np.ascontiguousarray(x, dtype=np.float16)
+        qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+        scales = np.ascontiguousarray(scales, dtype=np.float16)
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        M, K = x.shape
+        N = qweight.shape[1]
+        out = np.empty(ms.shape[0], dtype=np.float64)
+        _check(self.lib.oracle_linear_at(_ptr(x.view(np.uint16)), _ptr(qweight),
+                                         _ptr(scales.view(np.uint16)), M, K, N, group_size,
+                                         _ptr(ms), _ptr(ns), ms.shape[0], _ptr(out)),
+               "linear_at")
+        return out
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``w4a16_oracle.c`` (compiled on first use if missing)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _default = Oracle(LIB_PATH)
+    return _default
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def pack(codes):
+    return default().pack(codes)
+
+
+def unpack(qweight):
+    return default().unpack(qweight)
+
+
+def dequant(qweight, scales, group_size):
+    return default().dequant(qweight, scales, group_size)
+
+
+def linear(x, qweight, scales, group_size):
+    return default().linear(x, qweight, scales, group_size)
+
+
+def linear_at(x, qweight, scales, group_size, ms, ns):
+    return default().linear_at(x, qweight, scales, group_size, ms, ns)

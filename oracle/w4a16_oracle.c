@@ -1,0 +1,193 @@
+/*
+ * CPU oracle for the W4A16 symmetric-INT4 GPTQ linear.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously-correct
+ * definition that the HIP path is checked against.  Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load it.  It shares no
+ * code, header, table or helper with the product library, and it never calls
+ * into it.
+ *
+ * What it computes (the plain definition, written out):
+ *
+ *   q[k,n]  = (uint32(qweight[k/8][n]) >> (4*(k mod 8))) & 0xF
+ *   gidx(k) = (g == -1) ? 0 : floor(k / g)
+ *   w[k,n]  = float(q[k,n] - 8) * float(scales[gidx(k)][n])        (exact in fp32)
+ *   y[m,n]  = sum_{k=0..K-1} double(x[m,k]) * double(w[k,n])        (k ascending,
+ *                                                                    fp64 accumulator)
+ *
+ * Sources on the pages:
+ *  - symmetric GPTQ INT4, FP16 activations, desc_act=False only (so the group
+ *    of k is floor(k/g), no g_idx), native int32 qweight, group sizes
+ *    {-1,16,32,64,128,256,512,1024}, input features divisible by 16 and output
+ *    features by 8: "GPTQ-Pro" README, "Runtime contract" table;
+ *  - int32 is only the pack container, not the weight width: "Installation and
+ *    Quickstart", "Defaults and compatibility decisions" table (pack_dtype);
+ *  - g = -1 is per-output-channel (one group over all of K): "Installation and
+ *    Quickstart", "Troubleshooting and edge cases" table;
+ *  - the dequantise-then-matmul semantics of the portable GPTQ Torch backend:
+ *    "Installation and Quickstart", "End-to-end quickstart: GPTQ W4A16".
+ * The pages print neither the nibble order inside a word nor the zero point;
+ * this file takes nibble j of row r = K index 8r+j, low bits first, and an
+ * implicit zero point of 8 (the GPTQ_V2 layout of the benchmark spec).
+ *
+ * The result y is returned in float64 and is never rounded to fp16.
+ * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math).  OpenMP only
+ * splits rows m and column blocks of n, never the sum over k.
+ */
+
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_OK 0
+#define OR_ERR_ARG 1
+
+/* IEEE 754 binary16 bits -> double, decoded field by field. */
+static double half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int exp = (h >> 10) & 0x1F;
+    int man = h & 0x3FF;
+    double v;
+    if (exp == 0) {
+        v = ldexp((double)man, -24);                 /* subnormal or zero */
+    } else if (exp == 31) {
+        v = man ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(man | 0x400), exp - 25);  /* (1.man) * 2^(exp-15) */
+    }
+    return sign ? -v : v;
+}
+
+static int group_ok(int64_t K, int64_t g) {
+    (void)K;
+    return g == -1 || g == 16 || g == 32 || g == 64 || g == 128 || g == 256 ||
+           g == 512 || g == 1024;
+}
+
+static int shape_ok(int64_t M, int64_t K, int64_t N) {
+    return M >= 0 && K > 0 && N > 0 && K % 16 == 0 && N % 8 == 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Code of weight (k, n): nibble (k mod 8) of word qweight[k/8][n], read as
+ * unsigned so that words whose top nibble is >= 8 (negative int32) unpack
+ * the same way as the others. */
+static inline unsigned code_at(const int32_t *qweight, int64_t N, int64_t k, int64_t n) {
+    uint32_t word = (uint32_t)qweight[(k / 8) * N + n];
+    return (word >> (4 * (unsigned)(k % 8))) & 0xFu;
+}
+
+static inline int64_t group_of(int64_t k, int64_t g) {
+    return g == -1 ? 0 : k / g;
+}
+
+/* Dequantised weight as the pages' symmetric scheme defines it:
+ * (q - 8) * s, computed in fp32 (exact: at most 4 + 11 significant bits). */
+static inline float weight_at(const int32_t *qweight, const uint16_t *scales, int64_t N,
+                              int64_t g, int64_t k, int64_t n) {
+    int q = (int)code_at(qweight, N, k, n);
+    float s = (float)half_to_double(scales[group_of(k, g) * N + n]);
+    return (float)(q - 8) * s;
+}
+
+/* codes[k*N + n] <- q[k, n]. */
+int oracle_unpack(const int32_t *qweight, int64_t K, int64_t N, uint8_t *codes) {
+    if (!qweight || !codes || K <= 0 || N <= 0 || K % 8 != 0) return OR_ERR_ARG;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            codes[k * N + n] = (uint8_t)code_at(qweight, N, k, n);
+    return OR_OK;
+}
+
+/* qweight[r][n] <- sum_j codes[8r+j][n] << 4j, as a 32-bit pattern. */
+int oracle_pack(const uint8_t *codes, int64_t K, int64_t N, int32_t *qweight) {
+    if (!qweight || !codes || K <= 0 || N <= 0 || K % 8 != 0) return OR_ERR_ARG;
+    for (int64_t r = 0; r < K / 8; ++r) {
+        for (int64_t n = 0; n < N; ++n) {
+            uint32_t word = 0;
+            for (int j = 0; j < 8; ++j) {
+                uint8_t c = codes[(8 * r + j) * N + n];
+                if (c > 15) return OR_ERR_ARG;
+                word |= (uint32_t)c << (4 * j);
+            }
+            memcpy(&qweight[r * N + n], &word, sizeof word);
+        }
+    }
+    return OR_OK;
+}
+
+/* W[k*N + n] <- w[k, n] in fp32. */
+int oracle_dequant(const int32_t *qweight, const uint16_t *scales, int64_t K, int64_t N,
+                   int64_t g, float *W) {
+    if (!qweight || !scales || !W || !shape_ok(0, K, N) || !group_ok(K, g)) return OR_ERR_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            W[k * N + n] = weight_at(qweight, scales, N, g, k, n);
+    return OR_OK;
+}
+
+/* y[m*N + n] <- sum_k x[m,k] * w[k,n] in fp64, k ascending.  x and scales are
+ * fp16 bit patterns.  The dequantised weight is built once as fp32 and reused
+ * for every row; the loop runs m -> k -> n with a row of fp64 accumulators, so
+ * every output still adds its K products in ascending k. */
+int oracle_linear(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                  int64_t M, int64_t K, int64_t N, int64_t g, double *y) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g)) return OR_ERR_ARG;
+    if (M == 0) return OR_OK;
+    if (!x || !qweight || !scales || !y) return OR_ERR_ARG;
+    float *W = (float *)malloc((size_t)K * (size_t)N * sizeof(float));
+    if (!W) return OR_ERR_ARG;
+    oracle_dequant(qweight, scales, K, N, g, W);
+    const int64_t NB = 256;                      /* column block per task */
+    const int64_t nblocks = (N + NB - 1) / NB;
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < nblocks; ++b) {
+            int64_t n0 = b * NB, n1 = n0 + NB < N ? n0 + NB : N;
+            double acc[256];
+            for (int64_t n = n0; n < n1; ++n) acc[n - n0] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double xk = half_to_double(x[m * K + k]);
+                const float *wrow = W + k * N;
+                for (int64_t n = n0; n < n1; ++n) acc[n - n0] += xk * (double)wrow[n];
+            }
+            for (int64_t n = n0; n < n1; ++n) y[m * N + n] = acc[n - n0];
+        }
+    }
+    free(W);
+    return OR_OK;
+}
+
+/* out[i] <- y[ms[i], ns[i]] for sampled outputs, each from the definition
+ * directly (no dequantised matrix): used at sizes where the full product is
+ * too slow for a test. */
+int oracle_linear_at(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                     int64_t M, int64_t K, int64_t N, int64_t g,
+                     const int64_t *ms, const int64_t *ns, int64_t count, double *out) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || count < 0) return OR_ERR_ARG;
+    if (count == 0) return OR_OK;
+    if (!x || !qweight || !scales || !ms || !ns || !out) return OR_ERR_ARG;
+    for (int64_t i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return OR_ERR_ARG;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += half_to_double(x[m * K + k]) * (double)weight_at(qweight, scales, N, g, k, n);
+        out[i] = acc;
+    }
+    return OR_OK;
+}

@@ -1,0 +1,251 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes a loaded oracle build and raises AssertionError
+when it disagrees with:
+  - hand-derived worked words and a hand-derived worked example
+    (``tests/golden/``), which follow from the layout and the definition;
+  - closed forms (q=0 -> -8s, q=8 -> 0, q=15 -> 7s; all-8 codes -> y == 0);
+  - numpy's own fp16 decoding, over every fp16 bit pattern;
+  - a textbook int64 GEMM (g = -1 with integer activations is an exact
+    integer matrix product followed by a per-column scale);
+  - brute force on tiny inputs with W built from the codes, never from the
+    packed words;
+  - exact rational arithmetic on an adversarial cancellation case;
+  - metamorphic relations (scale doubling, column permutation, linearity).
+``tests/test_oracle_mutants.py`` plants plausible mistakes in copies of the
+oracle source and checks that every one of them trips at least one pin.
+"""
+
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+GROUPS = (-1, 16, 32, 64, 128, 256, 512, 1024)
+
+
+def read_pack_words():
+    rows = []
+    with open(os.path.join(GOLDEN, "pack_words.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            fields = line.split()
+            rows.append((list(map(int, fields[:8])), int(fields[8], 16), int(fields[9])))
+    return rows
+
+
+def read_worked_example():
+    rows = []
+    with open(os.path.join(GOLDEN, "worked_example.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            fields = line.split()
+            rows.append((int(fields[0]), fields[1], [float(v) for v in fields[2:]]))
+    return rows
+
+
+def _worked_inputs(g: int, xname: str):
+    K, N = 32, 8
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    codes = ((k + n) % 16).astype(np.uint8)
+    if g == 16:
+        scales = np.stack([np.ones(N), np.arange(1, N + 1)]).astype(np.float16)
+    else:
+        scales = np.ones((1, N), dtype=np.float16)
+    x = np.zeros((1, K))
+    if xname == "ones":
+        x[:] = 1.0
+    elif xname == "mix":
+        x[0, 0], x[0, 31] = 0.5, 2.0
+    else:
+        x[0, int(xname[1:])] = 1.0
+    return codes, scales, x.astype(np.float16)
+
+
+def _brute(codes: np.ndarray, scales: np.ndarray, x: np.ndarray, g: int) -> np.ndarray:
+    """Dense fp64 product with W built from the unpacked codes."""
+    K = codes.shape[0]
+    gidx = np.zeros(K, dtype=np.int64) if g == -1 else np.arange(K) // g
+    W = (codes.astype(np.float64) - 8.0) * scales.astype(np.float64)[gidx]
+    return x.astype(np.float64) @ W
+
+
+# --- pins ----------------------------------------------------------------------
+
+def pin_pack_words(o):
+    for codes, word, as_i32 in read_pack_words():
+        c = np.array(codes, dtype=np.uint8).reshape(8, 1)
+        q = o.pack(c)
+        assert q.shape == (1, 1)
+        assert int(q[0, 0]) == as_i32, (codes, hex(word), int(q[0, 0]))
+        back = o.unpack(np.array([[as_i32]], dtype=np.int32))
+        assert back[:, 0].tolist() == codes, (hex(word), back[:, 0].tolist())
+
+
+def pin_pack_roundtrip(o):
+    rng = np.random.default_rng(11)
+    for K, N in ((8, 8), (64, 24), (48, 40), (16, 1000)):
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        q = o.pack(codes)
+        assert q.shape == (K // 8, N)
+        assert np.array_equal(o.unpack(q), codes)
+    # a column of the words depends only on the same column of the codes
+    codes = np.zeros((16, 8), dtype=np.uint8)
+    codes[:, 3] = np.arange(16)
+    q = o.pack(codes)
+    assert np.count_nonzero(q[:, [0, 1, 2, 4, 5, 6, 7]]) == 0
+    assert q[0, 3] == 0x76543210 and q[1, 3] == np.int32(-19088744)
+
+
+def pin_dequant_closed_form(o):
+    rng = np.random.default_rng(12)
+    svals = np.concatenate([
+        np.array([1.0, 0.5, 2.0 ** -14, 2.0 ** -24, 65504.0, 1e-3, 2e-2, 0.0078125]),
+        rng.uniform(1e-4, 5e-2, size=56)]).astype(np.float16)
+    N = svals.size
+    s32 = svals.astype(np.float32)
+    scales = svals.reshape(1, N)
+    for code, factor in ((0, -8.0), (8, 0.0), (15, 7.0), (9, 1.0), (1, -7.0)):
+        codes = np.full((16, N), code, dtype=np.uint8)
+        W = o.dequant(o.pack(codes), scales, -1)
+        expect = (np.float32(factor) * s32)[None, :].repeat(16, axis=0)
+        assert np.array_equal(W, expect), (code, W[0, :4], expect[0, :4])
+
+
+def pin_half_decode_all_patterns(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    svals = bits.view(np.float16)
+    scales = svals.reshape(1, 65536)
+    codes = np.full((16, 65536), 9, dtype=np.uint8)      # q - 8 = 1 -> w = s
+    W = o.dequant(o.pack(codes), scales, -1)[0]
+    ref = svals.astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(W), nan)
+    assert np.array_equal(W[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(W[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_worked_example(o):
+    for g, xname, expect in read_worked_example():
+        codes, scales, x = _worked_inputs(g, xname)
+        y = o.linear(x, o.pack(codes), scales, g)
+        assert y.shape == (1, 8)
+        assert y[0].tolist() == expect, (g, xname, y[0].tolist(), expect)
+
+
+def pin_all_eights_zero(o):
+    rng = np.random.default_rng(13)
+    for g in GROUPS:
+        K, N, M = 128, 48, 3
+        G = 1 if g == -1 else -(-K // g)
+        codes = np.full((K, N), 8, dtype=np.uint8)
+        scales = rng.uniform(1e-3, 1.0, size=(G, N)).astype(np.float16)
+        x = rng.standard_normal((M, K)).astype(np.float16)
+        y = o.linear(x, o.pack(codes), scales, g)
+        assert np.all(y == 0.0), g
+
+
+def pin_per_channel_integer_gemm(o):
+    """g = -1 with integer x is an int64 GEMM then a per-column scale, exactly."""
+    rng = np.random.default_rng(14)
+    for M, K, N in ((3, 96, 40), (5, 256, 16), (1, 2048, 8)):
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        scales = rng.normal(0.0, 0.05, size=(1, N)).astype(np.float16)
+        xi = rng.integers(-8, 9, size=(M, K)).astype(np.int64)
+        x = xi.astype(np.float16)
+        exact_int = xi @ (codes.astype(np.int64) - 8)            # textbook integer GEMM
+        expect = exact_int.astype(np.float64) * scales.astype(np.float64)
+        y = o.linear(x, o.pack(codes), scales, -1)
+        assert np.array_equal(y, expect), (M, K, N)
+
+
+def pin_group_equivalences(o):
+    """g=-1, g=K and any g whose group rows carry equal scales give identical y."""
+    rng = np.random.default_rng(15)
+    K, N, M = 256, 24, 4
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    q = o.pack(codes)
+    s1 = rng.uniform(1e-3, 2e-2, size=(1, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    base = o.linear(x, q, s1, -1)
+    assert np.array_equal(o.linear(x, q, s1, 256), base)
+    assert np.array_equal(o.linear(x, q, s1, 512), base)      # g > K: one group
+    for g in (16, 32, 64, 128):
+        assert np.array_equal(o.linear(x, q, np.repeat(s1, K // g, axis=0), g), base), g
+
+
+def pin_brute_force_tiny(o):
+    rng = np.random.default_rng(16)
+    shapes = ((1, 16, 8), (2, 32, 16), (4, 48, 24), (3, 64, 8), (4, 256, 64), (2, 80, 40))
+    for M, K, N in shapes:
+        for g in GROUPS:
+            G = 1 if g == -1 else -(-K // g)
+            codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+            scales = rng.uniform(1e-3, 2e-2, size=(G, N)).astype(np.float16)
+            x = rng.standard_normal((M, K)).astype(np.float16)
+            y = o.linear(x, o.pack(codes), scales, g)
+            ref = _brute(codes, scales, x, g)
+            tol = 1e-12 * max(1.0, float(np.abs(ref).max()))
+            assert np.abs(y - ref).max() <= tol, (M, K, N, g)
+
+
+def pin_exact_rational(o):
+    """fp64 accumulation: an adversarial cancellation case vs exact rationals."""
+    K, N = 32, 8
+    codes = np.full((K, N), 15, dtype=np.uint8)                 # w = 7 s
+    codes[1:K - 1, :] = (np.arange(1, K - 1)[:, None] + np.arange(N)[None, :]) % 16
+    scales = np.ones((1, N), dtype=np.float16)
+    x = np.full((1, K), 0.0010004, dtype=np.float64)
+    x[0, 0], x[0, K - 1] = 16384.0, -16384.0                   # big terms cancel last
+    x = x.astype(np.float16)
+    y = o.linear(x, o.pack(codes), scales, -1)
+    for n in range(N):
+        exact = sum(Fraction(float(x[0, k])) * Fraction(int(codes[k, n]) - 8)
+                    for k in range(K))
+        mag = sum(abs(float(x[0, k]) * (int(codes[k, n]) - 8)) for k in range(K))
+        assert abs(Fraction(y[0, n]) - exact) <= Fraction(K * mag) * Fraction(2) ** -53, n
+
+
+def pin_metamorphic(o):
+    rng = np.random.default_rng(17)
+    M, K, N, g = 3, 128, 32, 32
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    q = o.pack(codes)
+    scales = rng.uniform(1e-3, 2e-2, size=(K // g, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    y = o.linear(x, q, scales, g)
+    # doubling every scale doubles y exactly (no fp16 overflow/underflow here)
+    assert np.array_equal(o.linear(x, q, (scales.astype(np.float32) * 2).astype(np.float16), g), 2 * y)
+    # permuting output columns (with their weight and scale columns) permutes y
+    perm = rng.permutation(N)
+    assert np.array_equal(o.linear(x, o.pack(codes[:, perm]), scales[:, perm], g), y[:, perm])
+    # permuting rows of x permutes rows of y
+    assert np.array_equal(o.linear(x[::-1].copy(), q, scales, g), y[::-1])
+    # linearity over disjoint supports (the fp16 sum is exact there)
+    xa, xb = x.copy(), x.copy()
+    xa[:, 1::2] = 0
+    xb[:, 0::2] = 0
+    ya, yb = o.linear(xa, q, scales, g), o.linear(xb, q, scales, g)
+    assert np.abs(ya + yb - y).max() <= 1e-12 * np.abs(y).max()
+
+
+def pin_sampled_matches_full(o):
+    rng = np.random.default_rng(18)
+    M, K, N, g = 5, 512, 64, 64
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    q = o.pack(codes)
+    scales = rng.uniform(1e-3, 2e-2, size=(K // g, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    y = o.linear(x, q, scales, g)
+    ms = rng.integers(0, M, size=40)
+    ns = rng.integers(0, N, size=40)
+    assert np.array_equal(o.linear_at(x, q, scales, g, ms, ns), y[ms, ns])
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,47 @@
+"""Plant plausible mistakes in copies of the oracle source (on the CPU) and check
+that each one trips at least one pin.  The planted copies live in a temporary
+directory; the oracle itself is never modified."""
+
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "nibble_order_reversed": ("(4 * (unsigned)(k % 8))", "(4 * (unsigned)(7 - k % 8))"),
+    "pack_order_reversed": ("<< (4 * j)", "<< (4 * (7 - j))"),
+    "zero_point_7": ("(float)(q - 8)", "(float)(q - 7)"),
+    "group_of_packed_row": ("return g == -1 ? 0 : k / g;", "return g == -1 ? 0 : (k / 8) / g;"),
+    "per_channel_as_k_groups": ("return g == -1 ? 0 : k / g;", "return g == -1 ? k / 16 : k / g;"),
+    "dropped_last_k": ("for (int64_t k = 0; k < K; ++k) {\n                double xk",
+                       "for (int64_t k = 0; k < K - 1; ++k) {\n                double xk"),
+    "fp32_accumulator": ("double acc[256];", "float acc[256];"),
+    "x_transposed": ("half_to_double(x[m * K + k]);", "half_to_double(x[k * M + m]);"),
+    "half_exponent_bias": ("exp - 25", "exp - 24"),
+    "half_subnormal_scale": ("ldexp((double)man, -24)", "ldexp((double)man, -23)"),
+    "half_sign_dropped": ("return sign ? -v : v;", "return v;"),
+    "scale_column_offset": ("scales[group_of(k, g) * N + n]", "scales[group_of(k, g) * N + (n ^ 1)]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(oracle.SRC_PATH) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    src_m = src.replace(old, new)
+    path = os.path.join(tmp_path, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src_m)
+    lib = oracle.compile_source(path, os.path.join(tmp_path, f"lib{name}.so"))
+    mutant = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
