@@ -1,0 +1,111 @@
+/*
+ * w4a16.h - C ABI of the MI355X (gfx950) W4A16 symmetric-INT4 GPTQ linear.
+ *
+ * The operation is the GPTQ weight-only linear layer described by the
+ * "GPTQ-Pro" README ("Runtime contract" table and "Ampere kernel
+ * architecture" section): FP16 activations, symmetric INT4 weights stored as
+ * native int32 qweight, one FP16 scale per (group, output column), group
+ * sizes {-1, 16, 32, 64, 128, 256, 512, 1024}, input features divisible by
+ * 16 and output features divisible by 8, desc_act=False only.  For every
+ * row m < M and column n < N:
+ *
+ *     q[k,n] = (uint32(qweight[k/8][n]) >> 4*(k mod 8)) & 0xF
+ *     w[k,n] = (q[k,n] - 8) * scales[gidx(k)][n],   gidx(k) = (g == -1) ? 0 : k / g
+ *     y[m,n] = sum_k x[m,k] * w[k,n]                (fp32 accumulation, fp16 result)
+ *
+ * g = -1 is one group over all of K (per output channel): "Installation and
+ * Quickstart" page, "Troubleshooting and edge cases" table.  int32 is only
+ * the container of eight 4-bit codes: same page, "Defaults and compatibility
+ * decisions" table (pack_dtype).  The nibble order (nibble j of row r holds K
+ * index 8r+j, low bits first) and the zero point 8 are the GPTQ_V2 layout
+ * this library implements; the pages print neither.
+ *
+ * Layouts (all row-major, contiguous, caller-owned):
+ *   x        fp16  [M, K]
+ *   qweight  int32 [K/8, N]
+ *   scales   fp16  [G, N]   with G = 1 for g = -1, else ceil(K/g); a partial
+ *                           last group (K % g != 0) and g > K are allowed
+ *   y        fp16  [M, N]   must not overlap the inputs
+ *
+ * Common rules:
+ *   - Every argument is validated before any HIP call.  On error nothing is
+ *     launched, y is untouched and a nonzero w4a16_status is returned.
+ *   - The library allocates no device memory, keeps no copy of the weights
+ *     (dense, dequantised or repacked) and holds no state beyond a per-device
+ *     cache of the device's architecture.  It is thread-safe and reentrant.
+ *   - Device calls are asynchronous on the given stream (a hipStream_t; 0 is
+ *     the null stream); results are valid once the stream is synchronised.
+ *     No call synchronises the device and nothing is printed.
+ *   - Results are deterministic: the same inputs give bit-identical y.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = 1,    /* a required pointer is null (M > 0) */
+    W4A16_ERR_SHAPE = 2,   /* M < 0, K <= 0, N <= 0, K % 16 != 0, N % 8 != 0, or a
+                              buffer reaches 2^31 bytes */
+    W4A16_ERR_GROUP = 3,   /* group_size not in {-1,16,32,64,128,256,512,1024} */
+    W4A16_ERR_ALIGN = 4,   /* a device pointer is not 16-byte aligned */
+    W4A16_ERR_CODE = 5,    /* pack_gptq_v2: a code above 15 */
+    W4A16_ERR_DEVICE = 6,  /* no usable HIP device, or the current one is not gfx950 */
+    W4A16_ERR_LAUNCH = 7,  /* the kernel launch reported an error */
+    W4A16_ERR_KERNEL = 8   /* w4a16_linear_ex: the requested kernel cannot take this M */
+} w4a16_status;
+
+/* Largest M the small-batch (decode) kernel takes; larger M runs the MFMA
+ * GEMM (prefill) kernel.  The split follows the pages' separate fused-decode
+ * and Tensor-Core prefill paths ("GPTQ-Pro" README, "Ampere kernel
+ * architecture"). */
+#define W4A16_DECODE_MAX_M 16
+
+/* y = x . dequant(qweight, scales) on the current HIP device.
+ *   x, qweight, scales, y : device pointers, each 16-byte aligned
+ *   M >= 0 rows of x (M == 0 returns W4A16_OK and does nothing);
+ *   K > 0, K % 16 == 0 input features; N > 0, N % 8 == 0 output features;
+ *   group_size in {-1, 16, 32, 64, 128, 256, 512, 1024};
+ *   stream : hipStream_t to enqueue on (0 = null stream).
+ * Dispatch: M <= W4A16_DECODE_MAX_M runs the decode kernel, larger M the
+ * prefill kernel.  Returns a w4a16_status. */
+int w4a16_linear(const void *x, const int32_t *qweight, const void *scales, void *y,
+                 int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream);
+
+/* Kernel selectors for w4a16_linear_ex. */
+#define W4A16_KERNEL_AUTO 0     /* same choice as w4a16_linear */
+#define W4A16_KERNEL_DECODE 1   /* small-batch kernel; requires M <= W4A16_DECODE_MAX_M */
+#define W4A16_KERNEL_PREFILL 2  /* MFMA GEMM kernel; any M */
+
+/* As w4a16_linear, with the kernel chosen by the caller (tests and crossover
+ * measurements).  Same arguments, layouts and errors, plus W4A16_ERR_KERNEL
+ * when `kernel` is unknown or cannot take M. */
+int w4a16_linear_ex(const void *x, const int32_t *qweight, const void *scales, void *y,
+                    int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
+                    int kernel);
+
+/* Host-side packing into the GPTQ_V2 layout (native int32 qweight, "GPTQ-Pro"
+ * README, "Runtime contract"):
+ *   qweight[r][n] = sum_{j=0..7} codes[8r+j][n] << 4j   (as a 32-bit pattern)
+ *   codes   : host uint8 [K, N], every value in 0..15
+ *   qweight : host int32 [K/8, N]
+ * Requires K > 0, K % 8 == 0, N > 0.  Returns W4A16_ERR_CODE (and leaves
+ * qweight unspecified) when a code exceeds 15. */
+int pack_gptq_v2(const uint8_t *codes, int32_t *qweight, int64_t K, int64_t N);
+
+/* Exact inverse of pack_gptq_v2: host int32 [K/8, N] -> host uint8 [K, N]. */
+int unpack_gptq_v2(const int32_t *qweight, uint8_t *codes, int64_t K, int64_t N);
+
+/* Static, human-readable name of a status code (never null). */
+const char *w4a16_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,158 @@
+"""MI355X-native W4A16 symmetric-INT4 GPTQ linear: Python binding of libw4a16.so.
+
+The binding only marshals arguments: every step of the linear runs in the
+gfx950 HIP kernels of ``libw4a16.so``; PyTorch supplies device memory and
+streams.  There is no fallback: if the library is missing or the device is
+not a gfx950, calls raise.
+
+Names match the C ABI in ``include/w4a16.h``:
+  w4a16_linear, w4a16_linear_ex, pack_gptq_v2, unpack_gptq_v2,
+  w4a16_status_string
+plus ``linear`` (allocates y with torch, then calls w4a16_linear_ex).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+
+W4A16_OK = 0
+W4A16_ERR_NULL = 1
+W4A16_ERR_SHAPE = 2
+W4A16_ERR_GROUP = 3
+W4A16_ERR_ALIGN = 4
+W4A16_ERR_CODE = 5
+W4A16_ERR_DEVICE = 6
+W4A16_ERR_LAUNCH = 7
+W4A16_ERR_KERNEL = 8
+
+W4A16_DECODE_MAX_M = 16
+W4A16_KERNEL_AUTO = 0
+W4A16_KERNEL_DECODE = 1
+W4A16_KERNEL_PREFILL = 2
+
+EXPORTS = ("w4a16_linear", "w4a16_linear_ex", "pack_gptq_v2", "unpack_gptq_v2",
+           "w4a16_status_string")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {w4a16_status_string(status)} (status {status})")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libw4a16.so (built in-tree).  torch is imported first so that the
+    library binds to the HIP runtime torch already loaded."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (HIP runtime shared with torch)
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.w4a16_linear.argtypes = [p, p, p, p, i64, i64, i64, i64, p]
+    lib.w4a16_linear.restype = i32
+    lib.w4a16_linear_ex.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i32]
+    lib.w4a16_linear_ex.restype = i32
+    lib.pack_gptq_v2.argtypes = [p, p, i64, i64]
+    lib.pack_gptq_v2.restype = i32
+    lib.unpack_gptq_v2.argtypes = [p, p, i64, i64]
+    lib.unpack_gptq_v2.restype = i32
+    lib.w4a16_status_string.argtypes = [i32]
+    lib.w4a16_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def w4a16_status_string(status: int) -> str:
+    return load_library().w4a16_status_string(int(status)).decode()
+
+
+def _addr(t) -> Optional[int]:
+    """Device address of a torch tensor, or an integer address as given."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def w4a16_linear_ex(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
+                    stream=None, kernel: int = W4A16_KERNEL_AUTO) -> None:
+    """Enqueue y = x . dequant(qweight, scales); raises W4A16Error on a nonzero status.
+
+    Tensors (or raw device addresses) are passed through as pointers; the
+    C library validates shapes, group size and alignment."""
+    st = load_library().w4a16_linear_ex(_addr(x), _addr(qweight), _addr(scales), _addr(y),
+                                        int(M), int(K), int(N), int(group_size),
+                                        _stream_handle(stream), int(kernel))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_linear")
+
+
+def w4a16_linear(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
+                 stream=None) -> None:
+    """Same as the C ``w4a16_linear`` (kernel chosen by M)."""
+    w4a16_linear_ex(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO)
+
+
+def pack_gptq_v2(codes: np.ndarray) -> np.ndarray:
+    """Host uint8 codes [K, N] (0..15) -> int32 qweight [K/8, N]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    K, N = codes.shape
+    out = np.empty((K // 8, N), dtype=np.int32)
+    st = load_library().pack_gptq_v2(codes.ctypes.data, out.ctypes.data, K, N)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "pack_gptq_v2")
+    return out
+
+
+def unpack_gptq_v2(qweight: np.ndarray) -> np.ndarray:
+    """Host int32 qweight [K/8, N] -> uint8 codes [K, N]."""
+    qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+    R, N = qweight.shape
+    out = np.empty((8 * R, N), dtype=np.uint8)
+    st = load_library().unpack_gptq_v2(qweight.ctypes.data, out.ctypes.data, 8 * R, N)
+    if st != W4A16_OK:
+        raise W4A16Error(st, "unpack_gptq_v2")
+    return out
+
+
+def linear(x, qweight, scales, group_size: int, out=None, stream=None,
+           kernel: int = W4A16_KERNEL_AUTO):
+    """Allocate y (fp16 [M, N]) with torch on x's device and run the linear.
+
+    x: fp16 [M, K]; qweight: int32 [K/8, N]; scales: fp16 [G, N]; all CUDA
+    (HIP) tensors, contiguous."""
+    import torch
+    for name, t, dt in (("x", x, torch.float16), ("qweight", qweight, torch.int32),
+                        ("scales", scales, torch.float16)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    M, K = x.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K:
+        raise ValueError("qweight must be [K/8, N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    w4a16_linear_ex(x, qweight, scales, out, M, K, N, group_size, stream, kernel)
+    return out

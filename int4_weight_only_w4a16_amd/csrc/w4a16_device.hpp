@@ -1,0 +1,104 @@
+// Device-side building blocks shared by the gfx950 W4A16 kernels.
+//
+// The operation is the symmetric-INT4 GPTQ linear of the "GPTQ-Pro" README
+// ("Runtime contract" table): y = x . W with W[k,n] = (q[k,n] - 8) * s[k/g, n],
+// FP16 activations, int32-packed codes (nibble j of qweight row r = K index
+// 8r+j, low bits first) and fp32 accumulation ("Ampere kernel architecture":
+// the prefill path accumulates in FP32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// Raw (stride-0) buffer resources, gfx9 family: a load whose byte offset is at
+// or past the record count returns zero, a store there is dropped.  Every
+// buffer handed to the kernels is smaller than 2^31 bytes (the host checks),
+// so kOOB is out of range for all of them.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+__device__ __forceinline__ u4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ u2 load_b64(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+// The eight 4-bit codes of one qweight word as eight fp16 values (q - 8), in
+// the order (q0, q4, q1, q5, q2, q6, q3, q7).  Each pair of nibbles (j, j+4)
+// sits at bits 4j and 4j+16 after a shift by 4j; OR-ing them into the
+// mantissa of fp16 1024.0 (0x6400) makes each half read as 1024 + q, and one
+// packed subtraction of 1032 leaves q - 8, exactly.  The int->fp16 "magic
+// number" conversion is the published one of Kim et al. (2022), "Who Says
+// Elephants Can't Run?".
+__device__ __forceinline__ h8 unpack_codes(uint32_t w) {
+    const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
+    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+    h2 p0 = __builtin_bit_cast(h2, (w & mask) | magic) - bias;
+    h2 p1 = __builtin_bit_cast(h2, ((w >> 4) & mask) | magic) - bias;
+    h2 p2 = __builtin_bit_cast(h2, ((w >> 8) & mask) | magic) - bias;
+    h2 p3 = __builtin_bit_cast(h2, ((w >> 12) & mask) | magic) - bias;
+    u4 r = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+            __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+    return __builtin_bit_cast(h8, r);
+}
+
+// Same, each value multiplied by the fp16 scale s (one rounding: RNE((q-8)*s)).
+__device__ __forceinline__ h8 unpack_codes_scaled(uint32_t w, _Float16 s) {
+    h8 v = unpack_codes(w);
+    const h8 sv = {s, s, s, s, s, s, s, s};
+    return v * sv;
+}
+
+// Eight consecutive fp16 activations k0..k7 (one 16-byte load, dwords
+// (k0,k1),(k2,k3),(k4,k5),(k6,k7)) reordered to (k0,k4,k1,k5,k2,k6,k3,k7),
+// the order unpack_codes gives the weights.  Applying the same permutation
+// to both MFMA operands leaves every dot product unchanged.
+__device__ __forceinline__ u4 perm_x(u4 d) {
+    u4 r;
+    r.x = (d.x & 0xFFFFu) | (d.z << 16);
+    r.y = (d.x >> 16) | (d.z & 0xFFFF0000u);
+    r.z = (d.y & 0xFFFFu) | (d.w << 16);
+    r.w = (d.y >> 16) | (d.w & 0xFFFF0000u);
+    return r;
+}
+
+// Four consecutive fp16 scales (one 8-byte load) as floats / halves.
+__device__ __forceinline__ _Float16 half_lo(uint32_t v) {
+    return __builtin_bit_cast(h2, v).x;
+}
+__device__ __forceinline__ _Float16 half_hi(uint32_t v) {
+    return __builtin_bit_cast(h2, v).y;
+}
+
+// D(16x16, fp32) += A(16x32, fp16) * B(32x16, fp16) on the matrix cores.
+// Lane l supplies A row (l % 16) and B column (l % 16), each as 8 values of
+// K-block (l / 16); it receives D rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ f4 mfma16x16x32(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Four fp32 values -> four fp16 (round to nearest even) packed in 8 bytes.
+__device__ __forceinline__ u2 pack4_f16(float a, float b, float c, float d) {
+    h2 lo = {(_Float16)a, (_Float16)b};
+    h2 hi = {(_Float16)c, (_Float16)d};
+    u2 r = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    return r;
+}
+
+}  // namespace w4a16

@@ -1,0 +1,129 @@
+"""The C ABI on the CPU: the library loads, exports what include/w4a16.h declares,
+rejects every invalid argument before any HIP call, and its host packing is
+bit-exact against the oracle's independent packing."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import int4_weight_only_w4a16_amd as w4
+import oracle
+import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w4.LIB_PATH):
+        from int4_weight_only_w4a16_amd import _build
+        _build.build()
+    return w4.load_library()
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:int|const char \*)\s*\*?\s*(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(w4.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_header_compiles_as_c():
+    import subprocess
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        with open(src, "w") as f:
+            f.write('#include "w4a16.h"\nint main(void){return W4A16_OK;}\n')
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                        src, "-o", os.path.join(d, "t")], check=True)
+
+
+def _call(lib, x=0x1000, q=0x2000, s=0x3000, y=0x4000, M=1, K=32, N=8, g=32, kernel=0):
+    return lib.w4a16_linear_ex(x, q, s, y, M, K, N, g, None, kernel)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=24), w4.W4A16_ERR_SHAPE),           # K % 16
+    (dict(K=0), w4.W4A16_ERR_SHAPE),
+    (dict(K=-16), w4.W4A16_ERR_SHAPE),
+    (dict(N=12), w4.W4A16_ERR_SHAPE),           # N % 8
+    (dict(N=0), w4.W4A16_ERR_SHAPE),
+    (dict(M=-1), w4.W4A16_ERR_SHAPE),
+    (dict(M=1 << 20, K=1 << 20), w4.W4A16_ERR_SHAPE),   # x reaches 2^31 bytes
+    (dict(K=1 << 16, N=1 << 16), w4.W4A16_ERR_SHAPE),   # qweight reaches 2^31 bytes
+    (dict(g=48), w4.W4A16_ERR_GROUP),
+    (dict(g=0), w4.W4A16_ERR_GROUP),
+    (dict(g=2048), w4.W4A16_ERR_GROUP),
+    (dict(g=-2), w4.W4A16_ERR_GROUP),
+    (dict(x=0), w4.W4A16_ERR_NULL),
+    (dict(q=0), w4.W4A16_ERR_NULL),
+    (dict(s=0), w4.W4A16_ERR_NULL),
+    (dict(y=0), w4.W4A16_ERR_NULL),
+    (dict(x=0x1008), w4.W4A16_ERR_ALIGN),
+    (dict(q=0x2004), w4.W4A16_ERR_ALIGN),
+    (dict(s=0x3002), w4.W4A16_ERR_ALIGN),
+    (dict(y=0x4001), w4.W4A16_ERR_ALIGN),
+    (dict(M=17, kernel=1), w4.W4A16_ERR_KERNEL),  # decode kernel takes M <= 16
+    (dict(kernel=3), w4.W4A16_ERR_KERNEL),
+    (dict(kernel=-1), w4.W4A16_ERR_KERNEL),
+])
+def test_invalid_arguments_rejected_before_any_hip_call(lib, kw, status):
+    assert _call(lib, **kw) == status
+
+
+def test_empty_batch_is_a_noop(lib):
+    # M == 0: OK without touching the (null) pointers or the device
+    assert _call(lib, x=0, q=0, s=0, y=0, M=0) == w4.W4A16_OK
+    assert lib.w4a16_linear(0, 0, 0, 0, 0, 5120, 17408, 128, None) == w4.W4A16_OK
+    # ...but an invalid shape is still an error at M == 0
+    assert _call(lib, M=0, K=40) == w4.W4A16_ERR_SHAPE
+
+
+def test_status_strings(lib):
+    for st in range(0, 9):
+        assert w4.w4a16_status_string(st)
+    assert w4.w4a16_status_string(99) == "unknown status"
+
+
+def test_pack_matches_oracle_bit_exact(lib):
+    rng = np.random.default_rng(21)
+    for K, N in ((8, 8), (16, 24), (256, 264), (5120, 64)):
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        q = w4.pack_gptq_v2(codes)
+        assert np.array_equal(q, oracle.pack(codes))
+        assert np.array_equal(w4.unpack_gptq_v2(q), codes)
+        assert np.array_equal(w4.unpack_gptq_v2(q), oracle.unpack(q))
+
+
+def test_pack_worked_words(lib):
+    for codes, word, as_i32 in oracle_pins.read_pack_words():
+        q = w4.pack_gptq_v2(np.array(codes, dtype=np.uint8).reshape(8, 1))
+        assert int(q[0, 0]) == as_i32, hex(word)
+        assert w4.unpack_gptq_v2(q)[:, 0].tolist() == codes
+
+
+def test_pack_rejects_bad_input(lib):
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.pack_gptq_v2(np.full((8, 8), 16, dtype=np.uint8))
+    assert e.value.status == w4.W4A16_ERR_CODE
+    codes = np.zeros((12, 8), dtype=np.uint8)
+    assert lib.pack_gptq_v2(codes.ctypes.data, np.zeros(16, np.int32).ctypes.data, 12, 8) == \
+        w4.W4A16_ERR_SHAPE
+    assert lib.pack_gptq_v2(None, None, 8, 8) == w4.W4A16_ERR_NULL
+    assert lib.unpack_gptq_v2(None, None, 8, 8) == w4.W4A16_ERR_NULL
+    assert lib.unpack_gptq_v2(None, None, 7, 8) == w4.W4A16_ERR_SHAPE

@@ -1,0 +1,294 @@
+"""Parity of the gfx950 HIP path with the CPU oracle, through the C ABI.
+
+Every case draws seeded synthetic inputs (``workloads``), packs them with the
+product's ``pack_gptq_v2`` (checked bit-exact against the oracle's own
+packing), runs ``w4a16_linear`` / ``w4a16_linear_ex`` on cuda:0 and compares
+with the oracle's float64 result to the parity bar of ``gpu_util``.  Cases the
+oracle can finish in seconds are compared element by element; at the full
+model shapes with large M the comparison uses whole rows, whole columns and
+random samples that the oracle computes one by one.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import check_parity, sample_indices
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import int4_weight_only_w4a16_amd as w4  # noqa: E402
+
+DEC, PRE, AUTO = w4.W4A16_KERNEL_DECODE, w4.W4A16_KERNEL_PREFILL, w4.W4A16_KERNEL_AUTO
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    w4.load_library()
+    return torch.device("cuda:0")
+
+
+_WCACHE = {}
+
+
+def _weights(case: workloads.Case, inp, dev):
+    """Packed and uploaded weights, shared by cases that differ only in M."""
+    key = (case.K, case.N, case.group_size, case.seed, case.scales, case.zero_cell_frac)
+    if key not in _WCACHE:
+        _WCACHE.clear()
+        q_p = w4.pack_gptq_v2(inp.codes)
+        q_o = oracle.pack(inp.codes)
+        assert np.array_equal(q_p, q_o), "product packing differs from the oracle's"
+        _WCACHE[key] = (q_o, torch.from_numpy(q_p).to(dev),
+                        torch.from_numpy(inp.scales).to(dev))
+    return _WCACHE[key]
+
+
+def _run(inp, q_dev, s_dev, g, dev, kernel=AUTO):
+    x = torch.from_numpy(inp.x).to(dev)
+    y = w4.linear(x, q_dev, s_dev, g, kernel=kernel)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _full_case(case, dev, kernels=(AUTO,)):
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    y_ref = oracle.linear(inp.x, q_o, inp.scales, case.group_size)
+    for k in kernels:
+        y = _run(inp, q_dev, s_dev, case.group_size, dev, k)
+        check_parity(y, y_ref, f"{case.name} kernel={k}")
+
+
+def _sampled_case(case, dev, count=4096, kernels=(AUTO,)):
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    M, N = case.M, case.N
+    ms, ns = sample_indices(M, N, count, seed=case.seed + 1000)
+    # whole first and last rows and columns as well
+    rows = np.repeat(np.array([0, M - 1]), N)
+    rcols = np.tile(np.arange(N), 2)
+    cols = np.tile(np.array([0, N - 1]), M)
+    crows = np.repeat(np.arange(M), 2)
+    ms = np.concatenate([ms, rows, crows]).astype(np.int64)
+    ns = np.concatenate([ns, rcols, cols]).astype(np.int64)
+    y_ref = oracle.linear_at(inp.x, q_o, inp.scales, case.group_size, ms, ns)
+    for k in kernels:
+        y = _run(inp, q_dev, s_dev, case.group_size, dev, k)
+        check_parity(y[ms, ns], y_ref, f"{case.name} kernel={k} (sampled)")
+
+
+# --- the five workloads ---------------------------------------------------------
+
+def test_tiny_both_kernels(dev):
+    _full_case(workloads.tiny(), dev, kernels=(AUTO, DEC, PRE))
+
+
+def test_decode_up_full(dev):
+    _full_case(workloads.decode_up(), dev, kernels=(AUTO, PRE))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_down_small_batch_full(dev, M):
+    _full_case(workloads.down_small_batch(M), dev, kernels=(AUTO, PRE))
+
+
+def test_prefill_up_sampled(dev):
+    _sampled_case(workloads.prefill_up(), dev)
+
+
+@pytest.mark.parametrize("case", workloads.sweep(), ids=lambda c: c.name)
+def test_sweep(dev, case):
+    if case.M <= 8:
+        _full_case(case, dev)
+    else:
+        _sampled_case(case, dev, count=2048)
+
+
+# --- exact arithmetic: bit-exact against the oracle rounded once to fp16 -------
+
+EXACT_SHAPES = [
+    # M, K, N, g
+    (1, 256, 256, 32),
+    (4, 512, 264, 16),
+    (5, 48, 64, 32),        # K % 32 == 16, partial last group
+    (3, 256, 8, 512),       # g > K
+    (16, 1024, 136, -1),
+    (2, 16, 8, 16),         # smallest legal shape
+    (17, 1024, 136, 64),
+    (64, 2048, 520, 128),
+    (130, 512, 264, 256),
+    (33, 4096, 1032, 1024),
+    (1, 17408, 64, 32),     # the longest K of the workloads
+    (16, 17408, 64, -1),
+]
+
+
+@pytest.mark.parametrize("M,K,N,g", EXACT_SHAPES)
+def test_exact_arithmetic_bitwise(dev, M, K, N, g):
+    case = workloads.exact_case(f"exact_{M}_{K}_{N}_{g}", M, K, N, g, seed=31)
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    y_ref = oracle.linear(inp.x, q_o, inp.scales, g)
+    expect = y_ref.astype(np.float16)               # the exact value, rounded once
+    kernels = (DEC, PRE) if M <= 16 else (PRE,)
+    for k in kernels:
+        y = _run(inp, q_dev, s_dev, g, dev, k)
+        bad = np.flatnonzero(y != expect)
+        assert bad.size == 0, (k, bad[:5], y.ravel()[bad[:5]], expect.ravel()[bad[:5]])
+
+
+# --- special cases ----------------------------------------------------------------
+
+@pytest.mark.parametrize("g", [-1, 16, 128])
+def test_all_codes_eight_give_exact_zero(dev, g):
+    K, N = 512, 264
+    G = 1 if g == -1 else K // g
+    rng = np.random.default_rng(41)
+    codes = np.full((K, N), 8, dtype=np.uint8)
+    q = torch.from_numpy(w4.pack_gptq_v2(codes)).to(dev)
+    s = torch.from_numpy(rng.uniform(1e-3, 1.0, size=(G, N)).astype(np.float16)).to(dev)
+    for M, k in ((1, DEC), (16, DEC), (3, PRE), (200, PRE)):
+        x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float16)).to(dev)
+        y = w4.linear(x, q, s, g, kernel=k)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(y).item() == 0, (M, k)
+
+
+def test_zero_cell_columns_are_exact_zero(dev):
+    """g = -1 with 5% zero cells: whole columns of codes are 8 -> y exactly 0 there."""
+    case = workloads.Case("zero_cols", 8, 5120, 5120, -1, 4, scales="loguniform",
+                          zero_cell_frac=0.05)
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    zero_cols = np.flatnonzero(inp.zero_cells[0])
+    assert zero_cols.size == 256
+    for k in (DEC, PRE):
+        y = _run(inp, q_dev, s_dev, -1, dev, k)
+        assert np.all(y[:, zero_cols] == 0), k
+
+
+@pytest.mark.parametrize("kernel,M", [(DEC, 1), (DEC, 16), (PRE, 64), (PRE, 300)])
+def test_deterministic_bitwise(dev, kernel, M):
+    case = workloads.Case("det", M, 5120, 1032, 64, 7, scales="loguniform")
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    runs = [_run(inp, q_dev, s_dev, 64, dev, kernel) for _ in range(3)]
+    for r in runs[1:]:
+        assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 63, 64, 65, 127, 128, 129, 512])
+def test_dispatch_edges(dev, M):
+    case = workloads.Case(f"edge_M{M}", M, 1024, 520, 128, 9)
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    y_ref = oracle.linear(inp.x, q_o, inp.scales, 128)
+    y_auto = _run(inp, q_dev, s_dev, 128, dev, AUTO)
+    check_parity(y_auto, y_ref, f"M={M} auto")
+    expected_kernel = DEC if M <= w4.W4A16_DECODE_MAX_M else PRE
+    y_explicit = _run(inp, q_dev, s_dev, 128, dev, expected_kernel)
+    assert np.array_equal(y_auto.view(np.uint16), y_explicit.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N,g", [
+    (3, 16, 8, -1), (3, 16, 8, 16), (20, 16, 8, 1024),
+    (2, 48, 24, 32), (33, 48, 24, 32),
+    (4, 272, 5128, 256), (70, 272, 5128, 256),
+    (1, 1040, 8, 1024), (19, 1040, 8, 1024),
+    (16, 5120, 5128, 16), (96, 5120, 5128, 16),
+])
+def test_tails(dev, M, K, N, g):
+    case = workloads.Case(f"tail_{M}_{K}_{N}_{g}", M, K, N, g, 13, scales="loguniform")
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    y_ref = oracle.linear(inp.x, q_o, inp.scales, g)
+    for k in ((DEC, PRE) if M <= 16 else (PRE,)):
+        check_parity(_run(inp, q_dev, s_dev, g, dev, k), y_ref, f"tail {M},{K},{N},{g} k={k}")
+
+
+def test_output_canaries_untouched(dev):
+    M, K, N, g = 5, 256, 264, 32
+    case = workloads.Case("canary", M, K, N, g, 17)
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    x = torch.from_numpy(inp.x).to(dev)
+    y_ref = oracle.linear(inp.x, q_o, inp.scales, g)
+    pad = 4096
+    for k in (DEC, PRE):
+        buf = torch.full((pad + M * N + pad,), 12345.0, dtype=torch.float16, device=dev)
+        y = buf[pad:pad + M * N]
+        w4.w4a16_linear_ex(x, q_dev, s_dev, y, M, K, N, g, None, k)
+        torch.cuda.synchronize()
+        b = buf.cpu().numpy()
+        assert np.all(b[:pad] == 12345.0) and np.all(b[pad + M * N:] == 12345.0), k
+        check_parity(b[pad:pad + M * N].reshape(M, N), y_ref, f"canary k={k}")
+
+
+def test_empty_batch_leaves_output_untouched(dev):
+    q = torch.zeros((32, 8), dtype=torch.int32, device=dev)
+    s = torch.ones((1, 8), dtype=torch.float16, device=dev)
+    x = torch.zeros((1, 256), dtype=torch.float16, device=dev)
+    y = torch.full((1, 8), 7.0, dtype=torch.float16, device=dev)
+    w4.w4a16_linear(x, q, s, y, 0, 256, 8, -1)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0).item()
+
+
+def test_misaligned_pointer_rejected(dev):
+    q = torch.zeros((32, 16), dtype=torch.int32, device=dev)
+    s = torch.ones((1, 16), dtype=torch.float16, device=dev)
+    x = torch.zeros((1, 256 + 8), dtype=torch.float16, device=dev)
+    y = torch.full((1, 16), 3.0, dtype=torch.float16, device=dev)
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_linear(x.data_ptr() + 2, q, s, y, 1, 256, 16, -1)
+    assert e.value.status == w4.W4A16_ERR_ALIGN
+    torch.cuda.synchronize()
+    assert torch.all(y == 3.0).item()
+
+
+def test_two_streams_concurrently(dev):
+    cases = [workloads.Case("s1", 16, 5120, 2048, 128, 21), workloads.Case("s2", 256, 2048, 5120, 32, 22)]
+    prepared = []
+    for c in cases:
+        inp = workloads.generate(c)
+        q_o = oracle.pack(inp.codes)
+        prepared.append((c, inp, q_o, torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev),
+                         torch.from_numpy(inp.scales).to(dev), torch.from_numpy(inp.x).to(dev)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for (c, inp, q_o, q, s, x), st in zip(prepared, streams):
+        y = torch.empty((c.M, c.N), dtype=torch.float16, device=dev)
+        outs.append(y)
+        with torch.cuda.stream(st):
+            for _ in range(3):
+                w4.w4a16_linear(x, q, s, y, c.M, c.K, c.N, c.group_size, st)
+    torch.cuda.synchronize()
+    for (c, inp, q_o, q, s, x), y in zip(prepared, outs):
+        y_ref = oracle.linear(inp.x, q_o, inp.scales, c.group_size)
+        check_parity(y.cpu().numpy(), y_ref, c.name)
+
+
+def test_no_device_allocation(dev):
+    case = workloads.Case("alloc", 64, 5120, 5120, 128, 23)
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    x = torch.from_numpy(inp.x).to(dev)
+    x16 = x[:16].contiguous()
+    y = torch.empty((64, 5120), dtype=torch.float16, device=dev)
+    for k in (PRE, AUTO):
+        w4.w4a16_linear_ex(x, q_dev, s_dev, y, 64, 5120, 5120, 128, None, k)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(5):
+        w4.w4a16_linear_ex(x16, q_dev, s_dev, y, 16, 5120, 5120, 128, None, DEC)
+        w4.w4a16_linear_ex(x, q_dev, s_dev, y, 64, 5120, 5120, 128, None, PRE)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0
