@@ -1,161 +1,534 @@
-// Small-batch (decode) W4A16 kernel for gfx950: M <= 16 rows of x.
+// Small-batch (decode) W4A16 kernels for gfx950: M <= 16 rows of x.
 //
 // What the pages ask of this path ("GPTQ-Pro" README, "Ampere kernel
 // architecture", fused decode): output tiles shared by cooperating warps,
 // reuse of the native qweight across the M rows, scale residency and a
 // deterministic split-K reduction; "Why GPTQ-Pro": no duplicate repacked
-// weight.  The design here is for CDNA4, not a translation:
+// weight.  Decode streams every weight byte once, so the design is about
+// keeping HBM busy on CDNA4:
 //
-//  * One workgroup owns 64 output columns and every row m < M.  Its waves
-//    split K into contiguous ranges of 32-deep steps (split-K inside the
-//    workgroup only, so no atomics and no scratch memory).
-//  * Each lane streams one 128-bit word quad per step: qweight row
-//    4t + lane/16, columns n0 + 4*(lane%16) .. +3.  Sixteen lanes cover 256
-//    contiguous bytes of one packed row, so every fetched line is used whole.
-//  * The four words of a lane are exactly the B operands of four
-//    v_mfma_f32_16x16x32_f16 instructions (one 8-deep K block of one column
-//    each); the activation rows (padded to 16 with zeros) are the A operand.
-//    The matrix cores do the multiply-accumulate for any M <= 16 at the same
+//  * Work unit = (column tile of COLS = 16*NW columns, 32-deep K step).  Per
+//    unit a lane loads NW consecutive qweight words (one 32/64/128-bit load)
+//    of packed row 4t + lane/16; sixteen lanes cover one contiguous row
+//    segment, so fetched lines are used whole.
+//  * Each word is the 8-deep B operand of one v_mfma_f32_16x16x32_f16 (one
+//    column); the activation rows, zero-padded to 16, are the A operand.  The
+//    matrix cores do the multiply-accumulate for any M <= 16 at the same
 //    cost, so the vector ALUs only unpack nibbles.
-//  * For g >= 32 a step lies inside one group: the MFMA sums x*(q-8) over
-//    the group in fp32 and the group's scale is applied once per group and
-//    column (scale-after).  For g = 16 every 8-deep block is scaled before
+//  * Loads run D units ahead of the math through a ring of D register stages
+//    refilled as soon as a stage is consumed.  Every load is issued
+//    unconditionally so the compiler's waits count exactly the loads in
+//    flight; a load that is not needed goes to a zero-length buffer and
+//    moves no data.
+//  * For g >= 32 a step lies inside one group: the MFMA sums x*(q-8) over the
+//    group in fp32 and the group's scale multiplies the sum once per group
+//    and column (scale-after).  For g = 16 each 8-deep block is scaled before
 //    the MFMA (scale-before, one fp16 rounding of (q-8)*s).
-//  * Waves reduce their fp32 partials through LDS in wave order 0..W-1, a
-//    fixed order, then round once to fp16 (8-byte stores of 4 columns).
+//  * A CU can pull only about twice its fair share of HBM bandwidth, so the
+//    work must be spread evenly over all CUs.  The stream-K kernel gives each
+//    of G workgroups (G = CU count) an equal contiguous range of units in
+//    tile-major order; its waves split that range contiguously and keep
+//    their load rings running across tile boundaries.  A tile that lies
+//    wholly inside one workgroup is finished there; a tile split between
+//    workgroups is finished by whichever contributor arrives last, which
+//    adds every contributor's fp32 partial in workgroup order (a fixed
+//    order, so results are bit-reproducible) and resets the tile's counter.
+//  * When there are many more tiles than CUs the tiles kernel (one
+//    workgroup per tile, its waves splitting K) is balanced on its own and
+//    needs no workspace.
+//  * Within a workgroup, wave partials are added through LDS in wave order,
+//    then rounded once to fp16.
+
+#include <algorithm>
 
 #include "w4a16_device.hpp"
 #include "w4a16_launch.h"
 
 namespace w4a16 {
 
-constexpr int kDecodeCols = 64;
+constexpr int kNW = 4;                 // words per lane per unit: one 128-bit load
+constexpr int kCols = 16 * kNW;        // columns per tile
 
-template <int WAVES, int U, bool SCALE_AFTER>
-__global__ __launch_bounds__(WAVES * 64) void decode_kernel(
-    const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
-    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
-    int group_steps) {
-    __shared__ f4 red[WAVES * 4 * 64];
+template <bool XLDS>
+struct Stage {
+    u4 w;     // qweight words of the lane's 4 consecutive columns
+    u4 x;     // 8 activations of this lane's A row / K block (unused when staged in LDS)
+    u2 s;     // the 4 columns' fp16 scales
+};
 
+// Activations staged in LDS: rows m < M of x, each zero-padded to Kp = 32*S
+// halves and already in unpack order (perm_x per 16-byte chunk), followed by
+// one zero chunk that the lanes of rows m >= M read.  Returns this lane's
+// byte address of step 0.
+__device__ __forceinline__ uint32_t stage_x_lds(unsigned char *xs, const __amdgpu_buffer_rsrc_t xr,
+                                                int M, int K, int S) {
+    const int Kp = 32 * S;
+    const int chunks_per_row = Kp / 8;
+    const int total = M * chunks_per_row;
+    for (int c = threadIdx.x; c < total; c += blockDim.x) {
+        const int m = c / chunks_per_row;
+        const int k = 8 * (c - m * chunks_per_row);
+        const u4 v = load_b128(xr, k < K ? ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 2u : kOOB);
+        *reinterpret_cast<u4 *>(xs + ((size_t)m * Kp + k) * 2) = perm_x(v);
+    }
+    if (threadIdx.x == 0) *reinterpret_cast<u4 *>(xs + (size_t)M * Kp * 2) = u4{0u, 0u, 0u, 0u};
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int kb = lane >> 4;        // 8-deep K block of this lane inside a step
-    const int col16 = lane & 15;     // MFMA row (A) / column (B) of this lane
-    const int n = blockIdx.x * kDecodeCols + 4 * col16;
+    const int m = lane & 15, kb = lane >> 4;
+    return m < M ? (uint32_t)(((size_t)m * Kp + 8 * kb) * 2) : (uint32_t)((size_t)M * Kp * 2);
+}
 
-    const int steps = (K + 31) >> 5;
-    const int per = (steps + WAVES - 1) / WAVES;
-    const int t0 = min(steps, wave * per);
-    const int t1 = min(steps, t0 + per);
+__device__ __forceinline__ _Float16 scale_at(const u2 &s, int j) {
+    const uint32_t d = j < 2 ? s.x : s.y;
+    return (j & 1) ? half_hi(d) : half_lo(d);
+}
 
-    const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-    const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
-    const int G = SCALE_AFTER ? (steps + group_steps - 1) / group_steps : (K + 15) >> 4;
-    const auto sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
+__device__ __forceinline__ void store_row4(uint16_t *dst, const float (&v)[4]) {
+    *reinterpret_cast<u2 *>(dst) = pack4_f16(v[0], v[1], v[2], v[3]);
+}
 
-    const uint32_t q_off0 = ((uint32_t)kb * (uint32_t)N + (uint32_t)n) * 4u;
-    const uint32_t q_step = (uint32_t)N * 16u;
-    const uint32_t x_off0 = ((uint32_t)col16 * (uint32_t)K + 8u * kb) * 2u;
+// One wave's pass over a contiguous range [w0, w1) of units (tile-major:
+// unit u = tile u / S, step u % S).  `dump(slot, acc)` receives the wave's
+// fp32 sum for each tile it touches (slot 0 for its first tile, 1 for the
+// next): rows 4*(lane/16)+i, columns 4*(lane%16)+j of the tile.
+//
+// XLDS: activations come from LDS staged by `after_prologue` (called once the
+// first D weight loads are in flight; it returns this lane's LDS byte address
+// of step 0 and must end with a workgroup barrier); otherwise from global.
+template <int D, bool SCALE_AFTER, bool XLDS, typename Dump, typename AfterPrologue>
+__device__ __forceinline__ void decode_units(
+    const __amdgpu_buffer_rsrc_t xr, const __amdgpu_buffer_rsrc_t qr,
+    const __amdgpu_buffer_rsrc_t sr, const __amdgpu_buffer_rsrc_t none, const unsigned char *xs,
+    int M, int K, int N, int S, int group_steps, int w0, int w1, Dump &&dump,
+    AfterPrologue &&after_prologue) {
+    const int xrows = M;
+    const int lane = threadIdx.x & 63;
+    const int kb = lane >> 4;
+    const int c16 = lane & 15;
+    const bool ragged = (K & 31) != 0;   // the last step of a tile is half inside K
 
-    f4 acc[4], accg[4];
+    // per-lane byte offsets of unit (tile 0, step 0); rows or columns past the
+    // tensors fall out of the buffer range and read as zero
+    const uint32_t q_v = ((uint32_t)kb * (uint32_t)N + (uint32_t)(kNW * c16)) * 4u;
+    const uint32_t x_v = ((uint32_t)c16 * (uint32_t)K + 8u * kb) * 2u;
+    const uint32_t x_v_last = (32 * (S - 1) + 8 * kb < K) ? x_v : kOOB;
+    const uint32_t s_v =
+        SCALE_AFTER ? (uint32_t)(kNW * c16) * 2u
+                    : ((uint32_t)(kb >> 1) * (uint32_t)N + (uint32_t)(kNW * c16)) * 2u;
+
+    const UnpackConsts uc = unpack_consts();
+
+    // load cursor (all scalar): unit, tile, step, position in group, group
+    int lu = w0, lb = 0, lt = 0, lpos = 0, lgrp = 0;
+    if (w0 < w1) {
+        lb = w0 / S;
+        lt = w0 - lb * S;
+        if (SCALE_AFTER) {
+            lgrp = lt / group_steps;
+            lpos = lt - lgrp * group_steps;
+        }
+    }
+    auto issue = [&](Stage<XLDS> &st) {
+        const bool live = lu < w1;
+        const uint32_t col_b = (uint32_t)(lb * kCols);
+        st.w = load_b128(live ? qr : none, q_v + ((uint32_t)lt * 4u * (uint32_t)N + col_b) * 4u);
+        if constexpr (!XLDS) {
+            const uint32_t xo = (ragged && lt == S - 1) ? x_v_last : x_v;
+            st.x = load_b128(live ? xr : none, xo + (uint32_t)lt * 64u);
+        }
+        if constexpr (SCALE_AFTER) {
+            // the group's scales are needed only where its sum is flushed
+            const bool flush = live && (lpos == group_steps - 1 || lt == S - 1 || lu == w1 - 1);
+            st.s = load_b64(flush ? sr : none, s_v + ((uint32_t)lgrp * (uint32_t)N + col_b) * 2u);
+        } else {
+            st.s = load_b64(live ? sr : none,
+                            s_v + ((uint32_t)lt * 2u * (uint32_t)N + col_b) * 2u);
+        }
+        ++lu;
+        ++lt;
+        if constexpr (SCALE_AFTER) {
+            if (++lpos == group_steps) {
+                lpos = 0;
+                ++lgrp;
+            }
+        }
+        if (lt == S) {
+            lt = 0;
+            ++lb;
+            lpos = 0;
+            lgrp = 0;
+        }
+    };
+
+    f4 acc[kNW], accg[kNW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kNW; ++j) {
         acc[j] = f4{0.f, 0.f, 0.f, 0.f};
         accg[j] = f4{0.f, 0.f, 0.f, 0.f};
     }
-    int cur_grp = SCALE_AFTER ? t0 / group_steps : 0;
-    u2 cur_s = {0u, 0u};
 
-    for (int t = t0; t < t1; t += U) {
-        u4 wv[U], xv[U];
-        u2 sv[U];
+    Stage<XLDS> ring[D];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int tt = t + u;   // past t1 the loads are in range or return zero; unused
-            wv[u] = load_b128(qr, q_off0 + (uint32_t)tt * q_step);
-            const bool k_ok = 32 * tt + 8 * kb < K;
-            xv[u] = load_b128(xr, k_ok ? x_off0 + (uint32_t)tt * 64u : kOOB);
-            const int srow = SCALE_AFTER ? tt / group_steps : 2 * tt + (kb >> 1);
-            sv[u] = load_b64(sr, ((uint32_t)srow * (uint32_t)N + (uint32_t)n) * 2u);
-        }
+    for (int u = 0; u < D; ++u) issue(ring[u]);
+    const uint32_t xl0 = after_prologue();
+    const bool xl0_moves = XLDS && (lane & 15) < xrows;
+
+    // compute cursor
+    int cu = w0, ct = 0, pos = 0, slot = 0;
+    if (w0 < w1) {
+        ct = w0 % S;
+        if (SCALE_AFTER) pos = ct % group_steps;
+    }
+    while (cu < w1) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int tt = t + u;
-            if (tt >= t1) break;
-            const h8 a = __builtin_bit_cast(h8, perm_x(xv[u]));
-            if constexpr (SCALE_AFTER) {
-                const int grp = tt / group_steps;
-                if (grp != cur_grp) {
-                    const float s[4] = {(float)half_lo(cur_s.x), (float)half_hi(cur_s.x),
-                                        (float)half_lo(cur_s.y), (float)half_hi(cur_s.y)};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[j] += s[j] * accg[j];
-                        accg[j] = f4{0.f, 0.f, 0.f, 0.f};
-                    }
-                    cur_grp = grp;
+        for (int u = 0; u < D; ++u) {
+            if (cu < w1) {
+                Stage<XLDS> &st = ring[u];
+                h8 a;
+                if constexpr (XLDS) {
+                    // lanes of rows >= M sit on the zero chunk and do not advance
+                    const uint32_t off = xl0 + (xl0_moves ? (uint32_t)ct * 64u : 0u);
+                    a = __builtin_bit_cast(h8, *reinterpret_cast<const u4 *>(xs + off));
+                } else {
+                    a = __builtin_bit_cast(h8, perm_x(st.x));
                 }
-                cur_s = sv[u];
+                const bool tile_end = ct == S - 1 || cu == w1 - 1;
+                if constexpr (SCALE_AFTER) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) accg[j] = mfma16x16x32(a, unpack_codes(wv[u][j]), accg[j]);
-            } else {
-                const _Float16 s[4] = {half_lo(sv[u].x), half_hi(sv[u].x), half_lo(sv[u].y),
-                                       half_hi(sv[u].y)};
+                    for (int j = 0; j < kNW; ++j)
+                        accg[j] = mfma16x16x32(a, unpack_codes(st.w[j], uc), accg[j]);
+                    if (pos == group_steps - 1 || tile_end) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[j] = mfma16x16x32(a, unpack_codes_scaled(wv[u][j], s[j]), acc[j]);
+                        for (int j = 0; j < kNW; ++j) {
+                            acc[j] += (float)scale_at(st.s, j) * accg[j];
+                            accg[j] = f4{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
+                    if (++pos == group_steps) pos = 0;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < kNW; ++j)
+                        acc[j] = mfma16x16x32(a, unpack_codes_scaled(st.w[j], uc, scale_at(st.s, j)),
+                                              acc[j]);
+                }
+                if (tile_end) {
+                    dump(slot, acc);
+#pragma unroll
+                    for (int j = 0; j < kNW; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+                    ++slot;
+                    pos = 0;
+                }
+                ++cu;
+                if (++ct == S) ct = 0;
             }
-        }
-    }
-    if constexpr (SCALE_AFTER) {
-        const float s[4] = {(float)half_lo(cur_s.x), (float)half_hi(cur_s.x),
-                            (float)half_lo(cur_s.y), (float)half_hi(cur_s.y)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += s[j] * accg[j];
-    }
-
-    // Fixed-order reduction over the waves, then one fp16 rounding.
-#pragma unroll
-    for (int j = 0; j < 4; ++j) red[(wave * 4 + j) * 64 + lane] = acc[j];
-    __syncthreads();
-    if (threadIdx.x < 256) {
-        const int l = threadIdx.x & 63;
-        const int i = threadIdx.x >> 6;                 // row inside the lane's quad
-        const int m = 4 * (l >> 4) + i;
-        const int nn = blockIdx.x * kDecodeCols + 4 * (l & 15);
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < WAVES; ++w) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] += red[(w * 4 + j) * 64 + l][i];
-        }
-        if (m < M && nn < N) {
-            const u2 out = pack4_f16(v[0], v[1], v[2], v[3]);
-            *reinterpret_cast<u2 *>(y + (size_t)m * N + nn) = out;
+            issue(ring[u]);
         }
     }
 }
 
-template <int WAVES, int U, bool SCALE_AFTER>
-static hipError_t launch(const LinearArgs &a, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// Dynamic LDS: the staged activations (XLDS) follow the static arrays.
+extern __shared__ __attribute__((aligned(16))) unsigned char decode_dyn_lds[];
+
+// Tiles kernel: one workgroup per column tile, its waves split K.
+template <int WAVES, int D, bool SCALE_AFTER, bool XLDS>
+__global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
+    int group_steps) {
+    __shared__ f4 red[WAVES][kNW][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = (K + 31) >> 5;
+    const int tile = blockIdx.x;
+    const int per = (S + WAVES - 1) / WAVES;
+    const int w0 = tile * S + min(S, wave * per);
+    const int w1 = tile * S + min(S, wave * per + per);
+
+    const int G = SCALE_AFTER ? (S + group_steps - 1) / group_steps : (K + 15) >> 4;
+    const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
+    const auto sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
+    const auto none = make_rsrc(qweight, 0u);
+
+#pragma unroll
+    for (int j = 0; j < kNW; ++j) red[wave][j][lane] = f4{0.f, 0.f, 0.f, 0.f};
+    decode_units<D, SCALE_AFTER, XLDS>(
+        xr, qr, sr, none, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
+        [&](int, const f4(&acc)[kNW]) {
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) red[wave][j][lane] = acc[j];
+        },
+        [&]() -> uint32_t {
+            if constexpr (XLDS) {
+                const uint32_t a = stage_x_lds(decode_dyn_lds, xr, M, K, S);
+                __syncthreads();
+                return a;
+            }
+            return 0u;
+        });
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int l = threadIdx.x & 63;
+        const int i = threadIdx.x >> 6;
+        const int m = 4 * (l >> 4) + i;
+        const int n = tile * kCols + kNW * (l & 15);
+        float v[kNW] = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < WAVES; ++w) {
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) v[j] += red[w][j][l][i];
+        }
+        if (m < M && n < N) store_row4(y + (size_t)m * N + n, v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stream-K kernel: gridDim.x workgroups share the units evenly.
+//
+// Workspace for up to `capacity` workgroups (zero-filled once; every launch
+// leaves it zero again).  The layout depends only on the capacity, never on
+// the grid of a launch, so launches of any grid size can share it:
+//   counters: int[capacity], padded to 256 bytes   arrivals at a split tile,
+//                                                  indexed by its last contributor
+//   partials: float[capacity][2][16][kCols]        a workgroup's sums for its
+//                                                  first (0) and last (1) tile
+
+// s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima.
+constexpr unsigned kWaitVmcnt0 = 0x0F70u;
+
+struct StreamK {
+    int U, G;
+    __device__ __forceinline__ int begin(int g) const { return (int)((int64_t)U * g / G); }
+    // workgroup whose range holds unit u
+    __device__ __forceinline__ int owner(int u) const {
+        int g = (int)((int64_t)u * G / U);
+        while (g + 1 < G && begin(g + 1) <= u) ++g;
+        while (g > 0 && begin(g) > u) --g;
+        return g;
+    }
+};
+
+template <int WAVES, int D, bool SCALE_AFTER, bool XLDS>
+__global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
+    int group_steps, int *__restrict__ counters, float *__restrict__ partials) {
+    constexpr int SLOT = 16 * kCols;             // floats per partial slot
+    __shared__ f4 red[2][WAVES][kNW][64];
+    __shared__ int last_arrival[2];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = (K + 31) >> 5;
+    const int T = (N + kCols - 1) / kCols;
+    const StreamK sk{T * S, (int)gridDim.x};
+    const int g = blockIdx.x;
+    const int u0 = sk.begin(g), u1 = sk.begin(g + 1);
+    const int pw = (u1 - u0 + WAVES - 1) / WAVES;   // host keeps pw <= S: <= 2 tiles per wave
+    const int w0 = min(u1, u0 + wave * pw), w1 = min(u1, w0 + pw);
+
+    const int Gs = SCALE_AFTER ? (S + group_steps - 1) / group_steps : (K + 15) >> 4;
+    const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
+    const auto sr = make_rsrc(scales, (uint32_t)Gs * (uint32_t)N * 2u);
+    const auto none = make_rsrc(qweight, 0u);
+
+    decode_units<D, SCALE_AFTER, XLDS>(
+        xr, qr, sr, none, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
+        [&](int slot, const f4(&acc)[kNW]) {
+            if (slot > 1) return;   // cannot happen: ranges hold <= S units
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) red[slot][wave][j][lane] = acc[j];
+        },
+        [&]() -> uint32_t {
+            if constexpr (XLDS) {
+                const uint32_t a = stage_x_lds(decode_dyn_lds, xr, M, K, S);
+                __syncthreads();
+                return a;
+            }
+            return 0u;
+        });
+    __syncthreads();
+    if (u0 >= u1) return;
+
+    const int l = threadIdx.x & 63;
+    const int i = (threadIdx.x >> 6) & 3;
+    const bool worker = threadIdx.x < 256;          // one (lane, row-in-quad) pair each
+    const int m = 4 * (l >> 4) + i;
+    const int c = kNW * (l & 15);
+    const bool row_ok = worker && m < M;
+    const int b0 = u0 / S, b1 = (u1 - 1) / S;
+
+    // Phase 1: fixed-order sum over the waves for every tile of this range;
+    // whole tiles are stored, split tiles (at most the first and the last)
+    // are published.  Each XCD has its own L2 and agent-scope atomics are
+    // performed in the issuing XCD's L2, so the partials and the counters
+    // use system-scope atomics, which are coherent in memory across XCDs.
+    int split_tile[2] = {-1, -1};
+    for (int tau = b0; tau <= b1; ++tau) {
+        const int ta = tau * S, tb = ta + S;
+        float v[kNW] = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < WAVES; ++w) {
+            const int a0 = min(u1, u0 + w * pw), a1 = min(u1, a0 + pw);
+            if (a0 >= a1 || a1 <= ta || a0 >= tb) continue;
+            const int s = tau - a0 / S;
+            if (worker) {
+#pragma unroll
+                for (int j = 0; j < kNW; ++j) v[j] += red[s][w][j][l][i];
+            }
+        }
+        const int n = tau * kCols + c;
+        if (ta >= u0 && tb <= u1) {                 // the whole tile is here
+            if (row_ok && n < N) store_row4(y + (size_t)m * N + n, v);
+            continue;
+        }
+        const int slot = tau == b0 ? 0 : 1;
+        split_tile[slot] = tau;
+        float *mine = partials + ((size_t)g * 2 + slot) * SLOT;
+        if (row_ok) {
+#pragma unroll
+            for (int j = 0; j < kNW; ++j)
+                __hip_atomic_store(mine + m * kCols + c + j, v[j], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+    if (split_tile[0] < 0 && split_tile[1] < 0) return;
+
+    // Phase 2: once every wave's partial stores are complete, count this
+    // workgroup's arrival at each split tile (one round for both).
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (threadIdx.x < 2) {
+        const int tau = split_tile[threadIdx.x];
+        int last = 0;
+        if (tau >= 0) {
+            const int gf = sk.owner(tau * S), gl = sk.owner(tau * S + S - 1);
+            last = __hip_atomic_fetch_add(&counters[gl], 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_SYSTEM) == gl - gf;
+        }
+        last_arrival[threadIdx.x] = last;
+    }
+    __syncthreads();
+
+    // Phase 3: the last contributor of a split tile adds every partial in
+    // workgroup order, stores the tile and resets its counter.
+#pragma unroll
+    for (int slot = 0; slot < 2; ++slot) {
+        const int tau = split_tile[slot];
+        if (tau < 0 || !last_arrival[slot]) continue;
+        const int gf = sk.owner(tau * S), gl = sk.owner(tau * S + S - 1);
+        float r[kNW] = {0.f, 0.f, 0.f, 0.f};
+        for (int h = gf; h <= gl; ++h) {
+            const int hs = tau == sk.begin(h) / S ? 0 : 1;
+            if (row_ok) {
+                const float *q = partials + ((size_t)h * 2 + hs) * SLOT + m * kCols + c;
+#pragma unroll
+                for (int j = 0; j < kNW; ++j)
+                    r[j] += __hip_atomic_load(q + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
+        const int n = tau * kCols + c;
+        if (row_ok && n < N) store_row4(y + (size_t)m * N + n, r);
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&counters[gl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
+// ---------------------------------------------------------------------------
+
+#ifndef W4A16_DECODE_WAVES
+#define W4A16_DECODE_WAVES 8
+#endif
+#ifndef W4A16_DECODE_D
+#define W4A16_DECODE_D 6
+#endif
+
+constexpr int kDecWaves = W4A16_DECODE_WAVES;
+constexpr int kDecD = W4A16_DECODE_D;
+
+static size_t counters_bytes(int capacity) {
+    return ((size_t)capacity * sizeof(int) + 255) & ~(size_t)255;
+}
+
+size_t decode_workspace_bytes(int capacity) {
+    return counters_bytes(capacity) + (size_t)capacity * 2 * 16 * kCols * sizeof(float);
+}
+
+int decode_streamk_grid(const LinearArgs &a, int num_cus) {
+    const int64_t S = (a.K + 31) / 32;
+    const int64_t T = (a.N + kCols - 1) / kCols;
+    // a wave must hold at most S units, so that it meets at most two tiles
+    if (T > (int64_t)kDecWaves * num_cus) return 0;
+    return (int)std::min<int64_t>(num_cus, T * S);
+}
+
+// Activations are staged in LDS when they fit in this many bytes.
+constexpr size_t kXStageMax = 64 * 1024;
+
+// Static LDS of a kernel, read once from its attributes.
+static size_t static_lds(const void *kernel) {
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, kernel) != hipSuccess) return (size_t)-1;
+    return attr.sharedSizeBytes;
+}
+
+template <bool SCALE_AFTER, bool XLDS>
+static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *workspace,
+                            int capacity, int grid) {
     const int K = (int)a.K, N = (int)a.N, M = (int)a.M;
-    const int steps = (K + 31) / 32;
+    const int S = (K + 31) / 32;
     int group_steps = 0;
-    if (SCALE_AFTER) group_steps = a.group_size == -1 ? steps : (int)a.group_size / 32;
+    if (SCALE_AFTER) group_steps = a.group_size == -1 ? S : (int)a.group_size / 32;
     const void *xp = a.x;
     const void *qp = a.qweight;
     const void *sp = a.scales;
     void *yp = a.y;
+    const dim3 block(kDecWaves * 64);
+    const size_t dyn = XLDS ? (size_t)M * 32 * S * 2 + 16 : 0;
+    if (grid > 0) {
+        int *counters = static_cast<int *>(workspace);
+        float *partials =
+            reinterpret_cast<float *>(static_cast<char *>(workspace) + counters_bytes(capacity));
+        void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N,
+                        &group_steps, &counters, &partials};
+        return hipLaunchKernel(
+            reinterpret_cast<const void *>(
+                &decode_streamk_kernel<kDecWaves, kDecD, SCALE_AFTER, XLDS>),
+            dim3(grid), block, args, dyn, stream);
+    }
     void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
-    dim3 grid((unsigned)((N + kDecodeCols - 1) / kDecodeCols));
-    dim3 block(WAVES * 64);
-    return hipLaunchKernel(reinterpret_cast<const void *>(&decode_kernel<WAVES, U, SCALE_AFTER>),
-                           grid, block, args, 0, stream);
+    const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);
+    return hipLaunchKernel(
+        reinterpret_cast<const void *>(
+            &decode_tiles_kernel<kDecWaves, kDecD, SCALE_AFTER, XLDS>),
+        dim3(tiles), block, args, dyn, stream);
 }
 
-hipError_t launch_decode(const LinearArgs &a, hipStream_t stream) {
-    if (a.group_size == 16) return launch<8, 4, false>(a, stream);
-    return launch<8, 4, true>(a, stream);
+// Whether the activations can be staged in LDS: at most kXStageMax bytes,
+// and the kernel's static LDS plus the staging area within the device's
+// per-workgroup LDS limit (a launch beyond it is rejected by the device).
+template <bool SCALE_AFTER>
+static bool stage_fits(const LinearArgs &a, int grid, size_t max_lds) {
+    const size_t dyn = (size_t)a.M * 32 * ((a.K + 31) / 32) * 2 + 16;
+    if (dyn > kXStageMax) return false;
+    static const size_t sk_static = static_lds(reinterpret_cast<const void *>(
+        &decode_streamk_kernel<kDecWaves, kDecD, SCALE_AFTER, true>));
+    static const size_t tiles_static = static_lds(reinterpret_cast<const void *>(
+        &decode_tiles_kernel<kDecWaves, kDecD, SCALE_AFTER, true>));
+    const size_t st = grid > 0 ? sk_static : tiles_static;
+    return st != (size_t)-1 && st + dyn <= max_lds;
+}
+
+hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
+                         int grid, size_t max_lds) {
+    if (grid > capacity) return hipErrorInvalidValue;
+    if (a.group_size == 16)
+        return stage_fits<false>(a, grid, max_lds)
+                   ? launch_sa<false, true>(a, stream, workspace, capacity, grid)
+                   : launch_sa<false, false>(a, stream, workspace, capacity, grid);
+    return stage_fits<true>(a, grid, max_lds)
+               ? launch_sa<true, true>(a, stream, workspace, capacity, grid)
+               : launch_sa<true, false>(a, stream, workspace, capacity, grid);
 }
 
 }  // namespace w4a16

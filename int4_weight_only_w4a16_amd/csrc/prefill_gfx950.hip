@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         }
     };
 
+    const UnpackConsts uc = unpack_consts();
     f4 acc[8][4];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             const _Float16 s4[4] = {half_lo(scur[h].x), half_hi(scur[h].x), half_lo(scur[h].y),
                                     half_hi(scur[h].y)};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = unpack_codes_scaled(wcur[h][j], s4[j]);
+            for (int j = 0; j < 4; ++j) b[j] = unpack_codes_scaled(wcur[h][j], uc, s4[j]);
             const unsigned char *abase =
                 lds + stage * kPreStageBytes + col16 * kPreRowBytes + (h * 4 + kb) * 16;
 #pragma unroll

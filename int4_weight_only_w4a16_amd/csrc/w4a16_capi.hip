@@ -10,6 +10,9 @@
 
 #include <atomic>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "../../include/w4a16.h"
 #include "w4a16_launch.h"
@@ -47,21 +50,60 @@ int validate(const void *x, const int32_t *qweight, const void *scales, void *y,
     return W4A16_OK;
 }
 
-// Per-device answer to "is this a gfx950?" (0 unknown, 1 yes, 2 no).
+// Per-device facts, queried once: is it a gfx950, and its CU count.
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_arch[kMaxDevices];
+std::atomic<int> g_arch[kMaxDevices];      // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cus[kMaxDevices];
+std::atomic<size_t> g_lds[kMaxDevices];    // LDS bytes per workgroup
 
-bool device_ok() {
+// Current device if it is a gfx950 (with its CU count and LDS limit), else -1.
+int usable_device(int *num_cus, size_t *max_lds) {
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
-    int state = dev < kMaxDevices ? g_arch[dev].load(std::memory_order_acquire) : 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    int state = g_arch[dev].load(std::memory_order_acquire);
     if (state == 0) {
         hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
         state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-        if (dev < kMaxDevices) g_arch[dev].store(state, std::memory_order_release);
+        g_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                         std::memory_order_relaxed);
+        g_lds[dev].store(prop.sharedMemPerBlock, std::memory_order_relaxed);
+        g_arch[dev].store(state, std::memory_order_release);
     }
-    return state == 1;
+    *num_cus = g_cus[dev].load(std::memory_order_relaxed);
+    *max_lds = g_lds[dev].load(std::memory_order_relaxed);
+    return state == 1 ? dev : -1;
+}
+
+// Decode workspace, one per (device, stream): calls on one stream run in
+// stream order and calls on different streams use different workspaces, so
+// the kernels never share one concurrently.  Created on the first call on a
+// stream (not while it is being captured into a graph), zero-filled in
+// stream order, kept until the process exits.
+std::mutex g_ws_mu;
+std::map<std::pair<int, uintptr_t>, std::pair<void *, size_t>> g_ws;
+
+void *stream_workspace(int dev, hipStream_t stream, size_t bytes) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    const auto key = std::make_pair(dev, reinterpret_cast<uintptr_t>(stream));
+    auto it = g_ws.find(key);
+    if (it != g_ws.end() && it->second.second >= bytes) return it->second.first;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return nullptr;
+    if (it != g_ws.end()) {                      // grow: the old one may still be in use
+        if (hipStreamSynchronize(stream) != hipSuccess) return nullptr;
+        (void)hipFree(it->second.first);
+        g_ws.erase(it);
+    }
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+    if (hipMemsetAsync(p, 0, bytes, stream) != hipSuccess) {
+        (void)hipFree(p);
+        return nullptr;
+    }
+    g_ws[key] = std::make_pair(p, bytes);
+    return p;
 }
 
 }  // namespace
@@ -79,11 +121,24 @@ extern "C" int w4a16_linear_ex(const void *x, const int32_t *qweight, const void
         return W4A16_ERR_KERNEL;
     }
     if (M == 0) return W4A16_OK;
-    if (!device_ok()) return W4A16_ERR_DEVICE;
+    int num_cus = 0;
+    size_t max_lds = 0;
+    const int dev = usable_device(&num_cus, &max_lds);
+    if (dev < 0) return W4A16_ERR_DEVICE;
     const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const hipError_t e = kernel == W4A16_KERNEL_DECODE ? w4a16::launch_decode(a, s)
-                                                       : w4a16::launch_prefill(a, s);
+    hipError_t e;
+    if (kernel == W4A16_KERNEL_DECODE) {
+        int grid = w4a16::decode_streamk_grid(a, num_cus);
+        void *ws = nullptr;
+        if (grid > 0) {
+            ws = stream_workspace(dev, s, w4a16::decode_workspace_bytes(num_cus));
+            if (!ws) grid = 0;                   // under capture with no workspace yet
+        }
+        e = w4a16::launch_decode(a, s, ws, num_cus, grid, max_lds);
+    } else {
+        e = w4a16::launch_prefill(a, s);
+    }
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 

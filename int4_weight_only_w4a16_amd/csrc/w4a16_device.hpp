@@ -39,28 +39,49 @@ __device__ __forceinline__ u2 load_b64(__amdgpu_buffer_rsrc_t r, uint32_t byte_o
     return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
+// Register-resident constants of the nibble unpack.  gfx9 VOP3 encodings take
+// no literal operands, so the masks and the fp16 bias live in VGPRs; the
+// empty asm makes them opaque so every unpack step stays one v_and_or_b32.
+struct UnpackConsts {
+    uint32_t lo;      // 0x000F000F: nibbles 0 and 4 of a (shifted) word
+    uint32_t hi;      // 0x00F000F0: nibbles 1 and 5
+    uint32_t magic;   // 0x64006400: fp16 1024.0 in both halves
+};
+
+__device__ __forceinline__ UnpackConsts unpack_consts() {
+    UnpackConsts c{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+    asm volatile("" : "+v"(c.lo), "+v"(c.hi), "+v"(c.magic));
+    return c;
+}
+
 // The eight 4-bit codes of one qweight word as eight fp16 values (q - 8), in
-// the order (q0, q4, q1, q5, q2, q6, q3, q7).  Each pair of nibbles (j, j+4)
-// sits at bits 4j and 4j+16 after a shift by 4j; OR-ing them into the
-// mantissa of fp16 1024.0 (0x6400) makes each half read as 1024 + q, and one
-// packed subtraction of 1032 leaves q - 8, exactly.  The int->fp16 "magic
-// number" conversion is the published one of Kim et al. (2022), "Who Says
-// Elephants Can't Run?".
-__device__ __forceinline__ h8 unpack_codes(uint32_t w) {
-    const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
-    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-    h2 p0 = __builtin_bit_cast(h2, (w & mask) | magic) - bias;
-    h2 p1 = __builtin_bit_cast(h2, ((w >> 4) & mask) | magic) - bias;
-    h2 p2 = __builtin_bit_cast(h2, ((w >> 8) & mask) | magic) - bias;
-    h2 p3 = __builtin_bit_cast(h2, ((w >> 12) & mask) | magic) - bias;
-    u4 r = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-            __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+// the order (q0, q4, q1, q5, q2, q6, q3, q7).  OR-ing a nibble into the low
+// mantissa bits of fp16 1024.0 (0x6400) makes the half read as 1024 + q, and
+// subtracting 1032 leaves q - 8 exactly (the int->fp16 "magic number"
+// conversion published by Kim et al. (2022), "Who Says Elephants Can't Run?").
+// Nibbles 1/5 (and 3/7 after one shift) are taken in place at bits 4..7, so
+// they read as 1024 + 16q; one fma by 1/16 with -72 maps them to q - 8, also
+// exactly.  Cost per word: 5 bit operations and 4 packed fp16 operations.
+__device__ __forceinline__ h8 unpack_codes(uint32_t w, const UnpackConsts &c) {
+    const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t w8 = w >> 8;
+    const h2 p0 = __builtin_bit_cast(h2, (w & c.lo) | c.magic) + bias;
+    const h2 p1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w & c.hi) | c.magic),
+                                            sixteenth, bias16);
+    const h2 p2 = __builtin_bit_cast(h2, (w8 & c.lo) | c.magic) + bias;
+    const h2 p3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w8 & c.hi) | c.magic),
+                                            sixteenth, bias16);
+    const u4 r = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                  __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
     return __builtin_bit_cast(h8, r);
 }
 
 // Same, each value multiplied by the fp16 scale s (one rounding: RNE((q-8)*s)).
-__device__ __forceinline__ h8 unpack_codes_scaled(uint32_t w, _Float16 s) {
-    h8 v = unpack_codes(w);
+__device__ __forceinline__ h8 unpack_codes_scaled(uint32_t w, const UnpackConsts &c,
+                                                  _Float16 s) {
+    const h8 v = unpack_codes(w, c);
     const h8 sv = {s, s, s, s, s, s, s, s};
     return v * sv;
 }
@@ -68,13 +89,14 @@ __device__ __forceinline__ h8 unpack_codes_scaled(uint32_t w, _Float16 s) {
 // Eight consecutive fp16 activations k0..k7 (one 16-byte load, dwords
 // (k0,k1),(k2,k3),(k4,k5),(k6,k7)) reordered to (k0,k4,k1,k5,k2,k6,k3,k7),
 // the order unpack_codes gives the weights.  Applying the same permutation
-// to both MFMA operands leaves every dot product unchanged.
+// to both MFMA operands leaves every dot product unchanged.  v_perm_b32
+// picks bytes 0-3 from its second operand and 4-7 from its first.
 __device__ __forceinline__ u4 perm_x(u4 d) {
     u4 r;
-    r.x = (d.x & 0xFFFFu) | (d.z << 16);
-    r.y = (d.x >> 16) | (d.z & 0xFFFF0000u);
-    r.z = (d.y & 0xFFFFu) | (d.w << 16);
-    r.w = (d.y >> 16) | (d.w & 0xFFFF0000u);
+    r.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
+    r.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
+    r.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
+    r.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
     return r;
 }
 

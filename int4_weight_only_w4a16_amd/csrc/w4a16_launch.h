@@ -16,7 +16,17 @@ struct LinearArgs {
     int64_t M, K, N, group_size;
 };
 
-hipError_t launch_decode(const LinearArgs &a, hipStream_t stream);   // M <= 16
+// Decode (M <= 16).  grid > 0 runs the stream-K kernel on `grid` workgroups
+// with `workspace`, a buffer of decode_workspace_bytes(capacity) bytes laid
+// out for up to `capacity` workgroups (grid <= capacity), zero-filled before
+// its first use and left zeroed by every launch; grid == 0 runs the tiles
+// kernel, which needs no workspace.  max_lds is the device's LDS limit per
+// workgroup in bytes.
+size_t decode_workspace_bytes(int capacity);
+int decode_streamk_grid(const LinearArgs &a, int num_cus);   // 0: use the tiles kernel
+hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
+                         int grid, size_t max_lds);
+
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream);  // any M
 
 }  // namespace w4a16

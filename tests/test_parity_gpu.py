@@ -282,6 +282,8 @@ def test_no_device_allocation(dev):
     x = torch.from_numpy(inp.x).to(dev)
     x16 = x[:16].contiguous()
     y = torch.empty((64, 5120), dtype=torch.float16, device=dev)
+    # the first decode call on a stream creates that stream's small workspace
+    w4.w4a16_linear_ex(x16, q_dev, s_dev, y, 16, 5120, 5120, 128, None, DEC)
     for k in (PRE, AUTO):
         w4.w4a16_linear_ex(x, q_dev, s_dev, y, 64, 5120, 5120, 128, None, k)
     torch.cuda.synchronize()
@@ -292,3 +294,72 @@ def test_no_device_allocation(dev):
     torch.cuda.synchronize()
     free1, _ = torch.cuda.mem_get_info()
     assert free1 == free0
+
+
+def test_decode_tiles_kernel_path(dev):
+    """More than 8 column tiles of 64 per CU: the decode runs one workgroup per tile."""
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 8 * 64 * n_cus + 8
+    for M, g in ((1, 32), (5, 16)):
+        case = workloads.Case(f"tiles_{M}_{g}", M, 64, N, g, 27, scales="loguniform")
+        inp = workloads.generate(case)
+        q_o, q_dev, s_dev = _weights(case, inp, dev)
+        y_ref = oracle.linear(inp.x, q_o, inp.scales, g)
+        check_parity(_run(inp, q_dev, s_dev, g, dev, DEC), y_ref, f"tiles path M={M} g={g}")
+
+
+def test_graph_capture_and_replay(dev):
+    """Decode and prefill captured in a HIP graph on a fresh stream, replayed
+    several times with eager work in between; every replay matches eager."""
+    cases = [workloads.Case("g_dec", 4, 5120, 2048, 128, 29),
+             workloads.Case("g_pre", 96, 1024, 1032, 64, 30)]
+    prepared = []
+    for c in cases:
+        inp = workloads.generate(c)
+        prepared.append((c, torch.from_numpy(inp.x).to(dev),
+                         torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev),
+                         torch.from_numpy(inp.scales).to(dev)))
+    eager = [w4.linear(x, q, s, c.group_size) for c, x, q, s in prepared]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(e) for e in eager]
+    st = torch.cuda.Stream()           # no workspace exists for this stream yet
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for (c, x, q, s), y in zip(prepared, outs):
+            w4.w4a16_linear(x, q, s, y, c.M, c.K, c.N, c.group_size, st)
+    for rep in range(4):
+        for y in outs:
+            y.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (c, x, q, s), y, e in zip(prepared, outs, eager):
+            inp = workloads.generate(c)
+            y_ref = oracle.linear(inp.x, oracle.pack(inp.codes), inp.scales, c.group_size)
+            check_parity(y.cpu().numpy(), y_ref, f"{c.name} replay {rep}")
+            if c.M > w4.W4A16_DECODE_MAX_M:
+                assert torch.equal(y, e)
+
+
+def test_decode_launches_of_different_grids_share_a_stream(dev):
+    """Stream-K launches with small and large grids, interleaved on one stream,
+    reuse that stream's workspace; each must be exact (a regression test for a
+    workspace layout that once depended on the grid size)."""
+    shapes = [(1, 256, 256, 32), (4, 512, 264, 16), (1, 17408, 5120, 32), (2, 16, 8, 16),
+              (4, 512, 264, 32), (16, 5120, 5128, 64), (3, 512, 256, -1), (1, 512, 264, 16)]
+    prepared = []
+    for M, K, N, g in shapes:
+        case = workloads.exact_case(f"mix_{M}_{K}_{N}_{g}", M, K, N, g, seed=37)
+        inp = workloads.generate(case)
+        expect = oracle.linear(inp.x, oracle.pack(inp.codes), inp.scales, g).astype(np.float16)
+        prepared.append((case, torch.from_numpy(inp.x).to(dev),
+                         torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev),
+                         torch.from_numpy(inp.scales).to(dev), expect))
+    for rep in range(3):
+        for case, x, q, s, expect in prepared:
+            y = torch.full((case.M, case.N), 777.0, dtype=torch.float16, device=dev)
+            w4.w4a16_linear_ex(x, q, s, y, case.M, case.K, case.N, case.group_size, None, DEC)
+            torch.cuda.synchronize()
+            got = y.cpu().numpy()
+            bad = np.flatnonzero(got != expect)
+            assert bad.size == 0, (rep, case.name, bad[:8])
