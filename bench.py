@@ -251,7 +251,7 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                            "traffic": traffic, "algorithmic_bytes": B,
-                           "kernel": "w4a16::decode_kernel"}
+                           "kernel": "w4a16::decode_streamk_kernel"}
         if not args.no_cpu_baseline:
             cb, y_ref = cpu_baseline_decode(case, inp, args.cpu_seconds)
             out["cpu_baseline"] = cb
