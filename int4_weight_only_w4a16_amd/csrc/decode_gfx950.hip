@@ -18,8 +18,8 @@
 //  * Loads run D units ahead of the math through a ring of D register stages
 //    refilled as soon as a stage is consumed.  Every load is issued
 //    unconditionally so the compiler's waits count exactly the loads in
-//    flight; a load that is not needed goes to a zero-length buffer and
-//    moves no data.
+//    flight; past the wave's last unit the ring reloads that unit (a cache
+//    hit, no HBM traffic).
 //  * For g >= 32 a step lies inside one group: the MFMA sums x*(q-8) over the
 //    group in fp32 and the group's scale multiplies the sum once per group
 //    and column (scale-after).  For g = 16 each 8-deep block is scaled before
@@ -87,76 +87,83 @@ __device__ __forceinline__ void store_row4(uint16_t *dst, const float (&v)[4]) {
 }
 
 // One wave's pass over a contiguous range [w0, w1) of units (tile-major:
-// unit u = tile u / S, step u % S).  `dump(slot, acc)` receives the wave's
-// fp32 sum for each tile it touches (slot 0 for its first tile, 1 for the
-// next): rows 4*(lane/16)+i, columns 4*(lane%16)+j of the tile.
+// unit u = tile u / S, step u % S).  The host keeps w1 - w0 <= S, so the
+// range is at most two tile segments: steps [tA0, S) or [tA0, tA0 + n) of
+// tile bA, then steps [0, n - nA) of tile bA + 1.  `dump(slot, acc)` gets the
+// wave's fp32 sum for each segment (slot 0, then 1): rows 4*(lane/16)+i,
+// columns 4*(lane%16)+j of the tile.
+//
+// Per unit the scalar work is a few compares and selects: every address
+// advances by a precomputed increment (a step, the jump to the next tile, or
+// nothing once past the last unit: the ring's tail reloads the last unit,
+// which hits in cache and moves no HBM data).
 //
 // XLDS: activations come from LDS staged by `after_prologue` (called once the
 // first D weight loads are in flight; it returns this lane's LDS byte address
-// of step 0 and must end with a workgroup barrier); otherwise from global.
+// of step 0 and ends with a workgroup barrier); otherwise from global.
 template <int D, bool SCALE_AFTER, bool XLDS, typename Dump, typename AfterPrologue>
 __device__ __forceinline__ void decode_units(
     const __amdgpu_buffer_rsrc_t xr, const __amdgpu_buffer_rsrc_t qr,
-    const __amdgpu_buffer_rsrc_t sr, const __amdgpu_buffer_rsrc_t none, const unsigned char *xs,
-    int M, int K, int N, int S, int group_steps, int w0, int w1, Dump &&dump,
-    AfterPrologue &&after_prologue) {
-    const int xrows = M;
+    const __amdgpu_buffer_rsrc_t sr, const unsigned char *xs, int M, int K, int N, int S,
+    int group_steps, int w0, int w1, Dump &&dump, AfterPrologue &&after_prologue) {
     const int lane = threadIdx.x & 63;
     const int kb = lane >> 4;
     const int c16 = lane & 15;
-    const bool ragged = (K & 31) != 0;   // the last step of a tile is half inside K
 
-    // per-lane byte offsets of unit (tile 0, step 0); rows or columns past the
-    // tensors fall out of the buffer range and read as zero
-    const uint32_t q_v = ((uint32_t)kb * (uint32_t)N + (uint32_t)(kNW * c16)) * 4u;
-    const uint32_t x_v = ((uint32_t)c16 * (uint32_t)K + 8u * kb) * 2u;
-    const uint32_t x_v_last = (32 * (S - 1) + 8 * kb < K) ? x_v : kOOB;
-    const uint32_t s_v =
-        SCALE_AFTER ? (uint32_t)(kNW * c16) * 2u
-                    : ((uint32_t)(kb >> 1) * (uint32_t)N + (uint32_t)(kNW * c16)) * 2u;
+    // segments (all scalar)
+    const int n = w1 > w0 ? w1 - w0 : 0;
+    const int bA = n ? w0 / S : 0;
+    const int tA0 = n ? w0 - bA * S : 0;
+    const int nA = min(n, S - tA0);
+
+    // per-lane byte offsets of the wave's first unit and their increments
+    const uint32_t q_step = (uint32_t)N * 16u;                       // 4 packed rows
+    const uint32_t q_jump = 256u - (uint32_t)S * q_step;              // to step 0 of the next tile
+    uint32_t q_off = ((uint32_t)(kb + 4 * tA0) * (uint32_t)N + (uint32_t)(bA * kCols + kNW * c16)) * 4u;
+
+    const bool ragged = (K & 31) != 0;        // the last step of a tile is half inside K
+    const uint32_t x_jump = 0u - (uint32_t)S * 64u;
+    uint32_t x_off = ((uint32_t)c16 * (uint32_t)K + 8u * kb) * 2u + 64u * (uint32_t)tA0;
+    const bool x_tail_ok = 32 * (S - 1) + 8 * kb < K;
+
+    // scale rows: scale-after reads the group's row (advances at group ends);
+    // scale-before reads row 2t + kb/2 (advances by two rows per step)
+    int lpos = SCALE_AFTER ? tA0 % group_steps : 0;
+    const uint32_t s_row = (uint32_t)N * 2u;
+    uint32_t s_off;
+    if constexpr (SCALE_AFTER)
+        s_off = ((uint32_t)(tA0 / group_steps) * (uint32_t)N + (uint32_t)(bA * kCols + kNW * c16)) * 2u;
+    else
+        s_off = ((uint32_t)(2 * tA0 + (kb >> 1)) * (uint32_t)N + (uint32_t)(bA * kCols + kNW * c16)) * 2u;
+    const uint32_t s_tile0 = ((uint32_t)(SCALE_AFTER ? 0 : (kb >> 1)) * (uint32_t)N +
+                              (uint32_t)((bA + 1) * kCols + kNW * c16)) * 2u;
 
     const UnpackConsts uc = unpack_consts();
 
-    // load cursor (all scalar): unit, tile, step, position in group, group
-    int lu = w0, lb = 0, lt = 0, lpos = 0, lgrp = 0;
-    if (w0 < w1) {
-        lb = w0 / S;
-        lt = w0 - lb * S;
-        if (SCALE_AFTER) {
-            lgrp = lt / group_steps;
-            lpos = lt - lgrp * group_steps;
-        }
-    }
+    // issue side: unit index li of this wave (loads beyond n - 1 repeat the last unit)
+    int li = 0;
     auto issue = [&](Stage<XLDS> &st) {
-        const bool live = lu < w1;
-        const uint32_t col_b = (uint32_t)(lb * kCols);
-        st.w = load_b128(live ? qr : none, q_v + ((uint32_t)lt * 4u * (uint32_t)N + col_b) * 4u);
+        st.w = load_b128(qr, q_off);
         if constexpr (!XLDS) {
-            const uint32_t xo = (ragged && lt == S - 1) ? x_v_last : x_v;
-            st.x = load_b128(live ? xr : none, xo + (uint32_t)lt * 64u);
+            const int t = li < nA ? tA0 + li : li - nA;
+            const uint32_t xo = (ragged && t == S - 1 && !x_tail_ok) ? kOOB : x_off;
+            st.x = load_b128(xr, xo);
         }
+        st.s = load_b64(sr, s_off);
+        // advance to unit li + 1 (stay put at the last unit)
+        const bool more = li + 1 < n;
+        const bool jump = li + 1 == nA;
+        q_off += more ? (jump ? q_step + q_jump : q_step) : 0u;
+        if constexpr (!XLDS) x_off += more ? (jump ? 64u + x_jump : 64u) : 0u;
         if constexpr (SCALE_AFTER) {
-            // the group's scales are needed only where its sum is flushed
-            const bool flush = live && (lpos == group_steps - 1 || lt == S - 1 || lu == w1 - 1);
-            st.s = load_b64(flush ? sr : none, s_v + ((uint32_t)lgrp * (uint32_t)N + col_b) * 2u);
+            const bool grp_end = lpos + 1 == group_steps;
+            lpos = (grp_end || jump) ? 0 : lpos + 1;
+            const uint32_t s_next = s_off + (grp_end ? s_row : 0u);
+            s_off = more ? (jump ? s_tile0 : s_next) : s_off;
         } else {
-            st.s = load_b64(live ? sr : none,
-                            s_v + ((uint32_t)lt * 2u * (uint32_t)N + col_b) * 2u);
+            s_off = more ? (jump ? s_tile0 : s_off + 2u * s_row) : s_off;
         }
-        ++lu;
-        ++lt;
-        if constexpr (SCALE_AFTER) {
-            if (++lpos == group_steps) {
-                lpos = 0;
-                ++lgrp;
-            }
-        }
-        if (lt == S) {
-            lt = 0;
-            ++lb;
-            lpos = 0;
-            lgrp = 0;
-        }
+        ++li;
     };
 
     f4 acc[kNW], accg[kNW];
@@ -166,62 +173,69 @@ __device__ __forceinline__ void decode_units(
         accg[j] = f4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // Prologue loads in ring order: the compiler's wait counts at the loop
+    // head take the stricter of the prologue's and the loop's load order, so
+    // the scheduler must not reorder these.
     Stage<XLDS> ring[D];
 #pragma unroll
-    for (int u = 0; u < D; ++u) issue(ring[u]);
-    const uint32_t xl0 = after_prologue();
-    const bool xl0_moves = XLDS && (lane & 15) < xrows;
-
-    // compute cursor
-    int cu = w0, ct = 0, pos = 0, slot = 0;
-    if (w0 < w1) {
-        ct = w0 % S;
-        if (SCALE_AFTER) pos = ct % group_steps;
+    for (int u = 0; u < D; ++u) {
+        issue(ring[u]);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    while (cu < w1) {
+    // LDS activation address: rows < M advance 64 B per step, rows >= M stay
+    // on the zero chunk
+    const uint32_t xl0 = after_prologue();
+    const uint32_t xl_inc = (XLDS && c16 < M) ? 64u : 0u;
+    uint32_t xl = xl0 + xl_inc * (uint32_t)tA0;
+
+    int i = 0, pos = SCALE_AFTER ? tA0 % group_steps : 0;
+    // one unit of math on ring stage st (unit index i of this wave)
+    auto compute = [&](Stage<XLDS> &st) {
+        h8 a;
+        if constexpr (XLDS)
+            a = __builtin_bit_cast(h8, *reinterpret_cast<const u4 *>(xs + xl));
+        else
+            a = __builtin_bit_cast(h8, perm_x(st.x));
+        const bool seg_end = i == nA - 1 || i == n - 1;
+        if constexpr (SCALE_AFTER) {
+#pragma unroll
+            for (int j = 0; j < kNW; ++j)
+                accg[j] = mfma16x16x32(a, unpack_codes(st.w[j], uc), accg[j]);
+            if (pos == group_steps - 1 || seg_end) {
+#pragma unroll
+                for (int j = 0; j < kNW; ++j) {
+                    acc[j] += (float)scale_at(st.s, j) * accg[j];
+                    accg[j] = f4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            pos = (pos + 1 == group_steps) ? 0 : pos + 1;
+        } else {
+#pragma unroll
+            for (int j = 0; j < kNW; ++j)
+                acc[j] = mfma16x16x32(a, unpack_codes_scaled(st.w[j], uc, scale_at(st.s, j)),
+                                      acc[j]);
+        }
+        if (seg_end) {
+            dump(i < nA ? 0 : 1, acc);
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+            pos = 0;
+        }
+        if constexpr (XLDS) xl = seg_end ? xl0 : xl + xl_inc;   // a new segment starts at step 0
+        ++i;
+    };
+    // full rounds: every stage holds a live unit
+    for (; i + D <= n;) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            if (cu < w1) {
-                Stage<XLDS> &st = ring[u];
-                h8 a;
-                if constexpr (XLDS) {
-                    // lanes of rows >= M sit on the zero chunk and do not advance
-                    const uint32_t off = xl0 + (xl0_moves ? (uint32_t)ct * 64u : 0u);
-                    a = __builtin_bit_cast(h8, *reinterpret_cast<const u4 *>(xs + off));
-                } else {
-                    a = __builtin_bit_cast(h8, perm_x(st.x));
-                }
-                const bool tile_end = ct == S - 1 || cu == w1 - 1;
-                if constexpr (SCALE_AFTER) {
-#pragma unroll
-                    for (int j = 0; j < kNW; ++j)
-                        accg[j] = mfma16x16x32(a, unpack_codes(st.w[j], uc), accg[j]);
-                    if (pos == group_steps - 1 || tile_end) {
-#pragma unroll
-                        for (int j = 0; j < kNW; ++j) {
-                            acc[j] += (float)scale_at(st.s, j) * accg[j];
-                            accg[j] = f4{0.f, 0.f, 0.f, 0.f};
-                        }
-                    }
-                    if (++pos == group_steps) pos = 0;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < kNW; ++j)
-                        acc[j] = mfma16x16x32(a, unpack_codes_scaled(st.w[j], uc, scale_at(st.s, j)),
-                                              acc[j]);
-                }
-                if (tile_end) {
-                    dump(slot, acc);
-#pragma unroll
-                    for (int j = 0; j < kNW; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
-                    ++slot;
-                    pos = 0;
-                }
-                ++cu;
-                if (++ct == S) ct = 0;
-            }
+            compute(ring[u]);
             issue(ring[u]);
         }
+    }
+    // last, partial round
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+        if (i < n) compute(ring[u]);
     }
 }
 
@@ -249,12 +263,11 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
     const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
     const auto sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
-    const auto none = make_rsrc(qweight, 0u);
 
 #pragma unroll
     for (int j = 0; j < kNW; ++j) red[wave][j][lane] = f4{0.f, 0.f, 0.f, 0.f};
     decode_units<D, SCALE_AFTER, XLDS>(
-        xr, qr, sr, none, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
+        xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int, const f4(&acc)[kNW]) {
 #pragma unroll
             for (int j = 0; j < kNW; ++j) red[wave][j][lane] = acc[j];
@@ -331,10 +344,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
     const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
     const auto sr = make_rsrc(scales, (uint32_t)Gs * (uint32_t)N * 2u);
-    const auto none = make_rsrc(qweight, 0u);
 
     decode_units<D, SCALE_AFTER, XLDS>(
-        xr, qr, sr, none, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
+        xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int slot, const f4(&acc)[kNW]) {
             if (slot > 1) return;   // cannot happen: ranges hold <= S units
 #pragma unroll
