@@ -16,6 +16,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
@@ -113,6 +114,15 @@ __device__ __forceinline__ _Float16 half_hi(uint32_t v) {
 // K-block (l / 16); it receives D rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.
 __device__ __forceinline__ f4 mfma16x16x32(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32, fp32) += A(32x16, fp16) * B(16x32, fp16) on the matrix cores.
+// Lane l supplies A row (l % 32) and B column (l % 32), each as 8 values of
+// K-block (l / 32); register i of lane l receives D row
+// 8*(i/4) + 4*(l/32) + i%4 of column l % 32.  One wave per SIMD keeps the
+// matrix core busy with this instruction, which it does not with 16x16x32.
+__device__ __forceinline__ f16v mfma32x32x16(h8 a, h8 b, f16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Four fp32 values -> four fp16 (round to nearest even) packed in 8 bytes.

@@ -363,3 +363,34 @@ def test_decode_launches_of_different_grids_share_a_stream(dev):
             got = y.cpu().numpy()
             bad = np.flatnonzero(got != expect)
             assert bad.size == 0, (rep, case.name, bad[:8])
+
+
+def test_decode_after_other_launches(dev):
+    """Decode calls whose workgroups hold uneven parts of split tiles (some
+    waves get no units of a tile), run after prefill launches that leave LDS
+    full of other data and after decode launches of other shapes on the same
+    stream.  Every result must match the oracle on every repetition: a kernel
+    that reads LDS or workspace state it did not write itself fails here (a
+    regression test for per-tile wave sums that were summed unwritten)."""
+    cases = [workloads.tiny(), workloads.decode_up(), workloads.down_small_batch(16),
+             workloads.Case("hist_g-1", 1, 5120, 17408, -1, 4, scales="loguniform",
+                            zero_cell_frac=0.05),
+             workloads.Case("hist_n5120", 8, 5120, 5120, 16, 4, scales="loguniform")]
+    big = workloads.Case("hist_prefill", 256, 4096, 4096, 128, 41)
+    inp_b = workloads.generate(big)
+    xb = torch.from_numpy(inp_b.x).to(dev)
+    qb = torch.from_numpy(w4.pack_gptq_v2(inp_b.codes)).to(dev)
+    sb = torch.from_numpy(inp_b.scales).to(dev)
+    prepared = []
+    for c in cases:
+        inp = workloads.generate(c)
+        q_o = oracle.pack(inp.codes)
+        y_ref = oracle.linear(inp.x, q_o, inp.scales, c.group_size)
+        prepared.append((c, torch.from_numpy(inp.x).to(dev), torch.from_numpy(q_o).to(dev),
+                         torch.from_numpy(inp.scales).to(dev), y_ref))
+    for rep in range(2):
+        for c, x, q, s, y_ref in prepared:
+            w4.linear(xb, qb, sb, big.group_size, kernel=PRE)      # dirty every CU's LDS
+            y = w4.linear(x, q, s, c.group_size, kernel=DEC)
+            torch.cuda.synchronize()
+            check_parity(y.cpu().numpy(), y_ref, f"{c.name} after other launches, rep {rep}")
