@@ -30,9 +30,16 @@
  * Common rules:
  *   - Every argument is validated before any HIP call.  On error nothing is
  *     launched, y is untouched and a nonzero w4a16_status is returned.
- *   - The library allocates no device memory, keeps no copy of the weights
- *     (dense, dequantised or repacked) and holds no state beyond a per-device
- *     cache of the device's architecture.  It is thread-safe and reentrant.
+ *   - The library keeps no copy of the weights (dense, dequantised or
+ *     repacked).  Its only state is a per-device cache of the device's
+ *     architecture and one decode workspace per (device, stream): about
+ *     2 MiB on a 256-CU device (a counter and two 16x64 fp32 partial tiles
+ *     per CU), allocated and zero-filled on the first decode call on that
+ *     stream, left zeroed by every launch and kept until the process exits.
+ *     A decode call on a stream that is being captured into a graph and has
+ *     no workspace yet allocates nothing and runs a kernel that needs none.
+ *     Calls on one stream share its workspace in stream order; calls on
+ *     different streams never share one.  Thread-safe and reentrant.
  *   - Device calls are asynchronous on the given stream (a hipStream_t; 0 is
  *     the null stream); results are valid once the stream is synchronised.
  *     No call synchronises the device and nothing is printed.
