@@ -274,7 +274,7 @@ def main():
                             "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
                             "traffic": traffic, "algorithmic_flops": F,
-                            "kernel": "w4a16::prefill_kernel"}}
+                            "kernel": "w4a16::prefill_m256_kernel"}}
         if not args.no_cpu_baseline:
             pre["cpu_baseline"] = cpu_baseline_prefill(case, inp, args.cpu_seconds)
         if args.only == "prefill":

@@ -2,29 +2,37 @@
 //
 // The pages' prefill path ("GPTQ-Pro" README, "Ampere kernel architecture",
 // Tensor Core prefill) stages operands asynchronously, accumulates in FP32,
-// handles tails and stores FP16 vectors.  The CDNA4 design:
+// handles tails and stores FP16 vectors.  Two CDNA4 kernels share the
+// v_mfma_f32_32x32x16_f16 instruction, one wave per SIMD (the accumulators
+// fill the AGPRs) and weights that never touch registers other than their
+// own lane's: each qweight word is exactly one lane's 8-deep B fragment,
+// dequantised in registers to (q-8)*s in fp16 (one rounding).
 //
-//  * A workgroup of 4 waves owns a 128 (M) x 256 (N) output tile; wave w owns
-//    the 128 x 64 slice of columns 64w .. 64w+63 as 4 x 2 tiles of the
-//    v_mfma_f32_32x32x16_f16 instruction (128 fp32 accumulators per lane).
-//    With one wave per SIMD (the accumulators and the operand pipeline use
-//    most of the register file) this instruction keeps the matrix core busy;
-//    the 16x16x32 one does not.
-//  * Column tile j of a wave holds the columns 64w + 2c + j (c = 0..31): a
-//    lane's one 64-bit load per 16-deep step brings the two adjacent qweight
-//    words, the 8-deep B fragments of both column tiles, so each packed row
-//    is read in 256-byte runs.  Weights never touch LDS: they are dequantised
-//    in registers to (q-8)*s in fp16 (one rounding) and each fragment feeds
-//    the 4 row tiles.
-//  * Activations go global -> registers -> LDS, 64 K per stage.  Each 16-byte
-//    chunk is reordered on the way in to the K order the nibble unpack
-//    produces, so MFMA A fragments are plain ds_read_b128.
-//  * Pipeline: activations are loaded four stages ahead and stored to LDS two
-//    stages ahead (three LDS stages, one barrier per stage); weights and
-//    scales are loaded three stages ahead into a register ring.  The loop is
-//    unrolled three times so every ring index is static.
-//  * Tails: rows >= M and K >= K read as zero through buffer range checks;
-//    stores are masked per row and per column pair (N % 8 == 0).
+// prefill_m256_kernel (M > 128): 256 x 256 output tile per workgroup.
+//  * Wave w owns columns 64w .. 64w+63 of all 256 rows: 8 x 2 MFMA tiles,
+//    256 fp32 accumulators per lane.  Eight row tiles share every unpacked B
+//    fragment, which halves the unpack work per MFMA against 128-row tiles.
+//  * Activations, codes and scales go global -> LDS by buffer loads that
+//    write LDS directly (no registers), 64 K per stage, three LDS stages.
+//    Activation rows are 128 bytes with the 16-byte chunks XOR-swizzled by
+//    the row, so the column-major fragment reads are free of bank conflicts.
+//  * Nibbles are unpacked in natural K order (v_perm_b32 spreads the byte of
+//    a nibble pair into both halves of a dword), so activations need no
+//    reordering and can be copied to LDS as they are.
+//  * Per 16-deep step: the next step's fragments are read from LDS at its
+//    start and its B fragments unpacked one operation at a time between the
+//    16 MFMAs; the copies for the stage two ahead are issued three per step,
+//    also between the MFMAs, and the main loop has no branches.  One barrier
+//    per stage.
+//  * Tiles go to XCDs in blocks (workgroup id % 8 taken as the XCD).
+//
+// prefill_m128_kernel (M <= 128): 128 x 256 tile, 4 x 2 MFMA tiles per wave;
+//  activations go global -> registers -> LDS (reordered to the nibble unpack
+//  order on the way in), weights are loaded into registers three stages
+//  ahead, A fragments read one step ahead.
+//
+// Tails: rows >= M and K >= K read as zero through buffer range checks and
+// per-lane checks; stores are masked per row and per column pair (N % 8 == 0).
 
 #include "w4a16_device.hpp"
 #include "w4a16_launch.h"
@@ -40,7 +48,7 @@ constexpr int kPreRing = 3;               // LDS stages, register stages per ope
 constexpr int kPreSteps = kPreBK / 16;    // 16-deep MFMA steps per stage
 
 // gshift: log2(group_size), or -1 for a single group over K.
-__global__ __launch_bounds__(256) void prefill_kernel(
+__global__ __launch_bounds__(256) void prefill_m128_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
     int gshift) {
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     }
 }
 
-hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream) {
+static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream) {
     int K = (int)a.K, N = (int)a.N, M = (int)a.M;
     int gshift = -1;
     if (a.group_size != -1) gshift = __builtin_ctz((unsigned)a.group_size);
@@ -212,8 +220,353 @@ hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream) {
     void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift};
     dim3 grid((unsigned)((N + kPreBN - 1) / kPreBN), (unsigned)((M + kPreBM - 1) / kPreBM));
     dim3 block(256);
-    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_kernel), grid, block, args, 0,
+    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_m128_kernel), grid, block, args, 0,
                            stream);
+}
+
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+
+constexpr int kWBM = 256;
+constexpr int kWBN = 256;
+constexpr int kWBK = 64;
+constexpr int kWSteps = 4;
+constexpr int kWA = kWBM * 128;            // 256 rows x 64 fp16
+constexpr int kWB = 8 * kWBN * 4;           // 8 packed rows x 256 columns
+constexpr int kWS = kWSteps * kWBN * 2;    // 4 scale rows x 256 columns
+constexpr int kWAOff = 0;
+constexpr int kWBOff = 3 * kWA;
+constexpr int kWSOff = 3 * kWA + 3 * kWB;
+constexpr int kWLds = 3 * (kWA + kWB + kWS);
+
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
+__device__ __forceinline__ h8 unpack_nat_scaled(uint32_t w, _Float16 s, uint32_t mask, uint32_t magic,
+                                                h2 mul, h2 add) {
+    u4 r;
+    const h2 sv = {s, s};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t t = (__builtin_amdgcn_perm(w, w, 0x01010101u * d) & mask) | magic;
+        const h2 v = __builtin_elementwise_fma(__builtin_bit_cast(h2, t), mul, add) * sv;
+        r[d] = __builtin_bit_cast(uint32_t, v);
+    }
+    return __builtin_bit_cast(h8, r);
+}
+
+__global__ __launch_bounds__(256) void prefill_m256_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
+    int gshift, int tiles_m, int tiles, int per_xcd) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kWLds];
+    lds_u8_t *L = (lds_u8_t *)lds_raw;
+
+    // XCD-blocked tile order: workgroup id % 8 is taken as its XCD; XCD x
+    // takes tiles x*per_xcd .. in column-major order (row blocks fastest).
+    const int id = blockIdx.x;
+    const int tl = (id & 7) * per_xcd + (id >> 3);
+    if (tl >= tiles) return;
+    const int m0 = (tl % tiles_m) * kWBM;
+    const int n0 = (tl / tiles_m) * kWBN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kb = lane >> 5;
+    const int c32 = lane & 31;
+    const int G = gshift < 0 ? 1 : ((K - 1) >> gshift) + 1;
+    const int nst = (K + kWBK - 1) / kWBK;   // stages
+    const int nfull = K / kWBK;               // stages without a K tail
+
+    const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
+    const auto sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
+    const auto yr = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
+
+    // ---- DMA lane offsets (stage 0) ----
+    // A: instruction i moves rows 64w + 8i + lane/8; lane's physical 16-byte
+    // slot is lane%8, holding logical chunk (lane%8) ^ f(row),
+    // f(row) = (row & 7) ^ ((row >> 3) & 1).
+    uint32_t a_voff[8];
+    int a_c[8];
+    bool a_ok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 64 * wave + 8 * i + (lane >> 3);
+        const int c = (lane & 7) ^ (lane >> 3) ^ (i & 1);
+        a_c[i] = c;
+        a_ok[i] = m0 + r < M;
+        a_voff[i] = a_ok[i] ? ((uint32_t)(m0 + r) * (uint32_t)K + 8u * c) * 2u : kOOB;
+    }
+    // B: instruction i moves packed rows 4i + lane/16 of the stage, columns
+    // n0 + 64w + 4 (lane%16) .. +3.
+    const int b_col = n0 + 64 * wave + 4 * (lane & 15);
+    const bool b_ok = b_col < N;
+    uint32_t b_voff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        b_voff[i] = b_ok ? ((uint32_t)(4 * i + (lane >> 4)) * (uint32_t)N + b_col) * 4u : kOOB;
+    // S: instruction i moves the scale rows of steps 2i + lane/32, columns
+    // n0 + 64w + 2 (lane%32), +1.
+    const int s_col = n0 + 64 * wave + 2 * (lane & 31);
+    const bool s_ok = s_col < N;
+    const uint32_t s_voff = s_ok ? ((gshift == 4 ? (uint32_t)(lane >> 5) * (uint32_t)N : 0u) + s_col) * 2u : kOOB;
+
+    // DMA instruction idx (0..11) of stage st into LDS slot `slot`:
+    // 0..7 activations (8 rows per instruction), 8..9 codes, 10..11 scales.
+    // FULL: stage st exists and has no K tail (no per-lane K checks).
+    auto dma = [&](auto fullc, int st, int slot, int idx) {
+        constexpr bool FULL = decltype(fullc)::value;
+        const int k0 = st * kWBK;
+        if (FULL) {
+            if (idx < 8) {
+                lds_u8_t *la = L + kWAOff + slot * kWA + (64 * wave + 8 * idx) * 128;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)la, 16, a_voff[idx], 2u * (uint32_t)k0, 0, 0);
+            } else if (idx < 10) {
+                const int i = idx - 8;
+                lds_u8_t *lb = L + kWBOff + slot * kWB + wave * 2048 + i * 1024;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void_t *)lb, 16, b_voff[i], (uint32_t)st * (uint32_t)N * 32u, 0, 0);
+            } else {
+                const int i = idx - 10;
+                const uint32_t srow = gshift < 0 ? 0u : (uint32_t)(k0 + 32 * i) >> gshift;
+                lds_u8_t *ls = L + kWSOff + slot * kWS + wave * 512 + i * 256;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void_t *)ls, 4, s_voff, srow * (uint32_t)N * 2u, 0, 0);
+            }
+        } else {
+            // any stage, every lane offset checked against K
+            if (idx < 8) {
+                lds_u8_t *la = L + kWAOff + slot * kWA + (64 * wave + 8 * idx) * 128;
+                const bool ok = a_ok[idx] && k0 + 8 * a_c[idx] < K;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)la, 16,
+                                                         ok ? a_voff[idx] + 2u * (uint32_t)k0 : kOOB, 0, 0, 0);
+            } else if (idx < 10) {
+                const int i = idx - 8;
+                lds_u8_t *lb = L + kWBOff + slot * kWB + wave * 2048 + i * 1024;
+                const int prow = 8 * st + 4 * i + (lane >> 4);
+                const bool ok = b_ok && prow < (K >> 3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    qr, (lds_void_t *)lb, 16, ok ? ((uint32_t)prow * (uint32_t)N + b_col) * 4u : kOOB, 0, 0, 0);
+            } else {
+                const int i = idx - 10;
+                lds_u8_t *ls = L + kWSOff + slot * kWS + wave * 512 + i * 256;
+                const int k = k0 + 16 * (2 * i + (lane >> 5));
+                const uint32_t srow = gshift < 0 ? 0u : (uint32_t)k >> gshift;
+                const bool ok = s_ok && k < K;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    sr, (lds_void_t *)ls, 4, ok ? (srow * (uint32_t)N + s_col) * 2u : kOOB, 0, 0, 0);
+            }
+        }
+    };
+    // generic issue of instructions 3c .. 3c+2 of stage st (nothing past the last stage)
+    auto dma_chunk_any = [&](int st, int slot, int c) {
+        if (st < nst) {
+            if (st < nfull) {
+                dma(BoolC<true>(), st, slot, 3 * c);
+                dma(BoolC<true>(), st, slot, 3 * c + 1);
+                dma(BoolC<true>(), st, slot, 3 * c + 2);
+            } else {
+                dma(BoolC<false>(), st, slot, 3 * c);
+                dma(BoolC<false>(), st, slot, 3 * c + 1);
+                dma(BoolC<false>(), st, slot, 3 * c + 2);
+            }
+        }
+    };
+
+    // ---- LDS fragment reads ----
+    const int f = (c32 & 7) ^ ((c32 >> 3) & 1);
+    uint32_t a_rd[kWSteps];
+#pragma unroll
+    for (int h = 0; h < kWSteps; ++h) a_rd[h] = c32 * 128 + 16 * ((2 * h + kb) ^ f);
+    const uint32_t b_rd = wave * 2048 + kb * 256 + 8 * c32;
+    const uint32_t s_rd = wave * 512 + 4 * c32;
+
+    // Per step: A fragments (8 row tiles) and the unpacked, scaled B
+    // fragments (2 column tiles) of the current step are in registers; the
+    // next step's A fragments, words and scales are read from LDS at the start
+    // and its B fragments are unpacked between the current step's MFMAs.
+    h8 a_cur[8], a_nxt[8];
+    h8 b_cur0, b_cur1;
+    u2 w_nxt;
+    uint32_t s_nxt;
+
+    uint32_t mask = 0x00F0000Fu, magic = 0x64006400u;
+    asm volatile("" : "+v"(mask), "+v"(magic));
+    h2 mul = {(_Float16)1.0f, (_Float16)0.0625f};
+    h2 add = {(_Float16)-1032.0f, (_Float16)-72.0f};
+    {
+        uint32_t mu = __builtin_bit_cast(uint32_t, mul), ad = __builtin_bit_cast(uint32_t, add);
+        asm volatile("" : "+v"(mu), "+v"(ad));
+        mul = __builtin_bit_cast(h2, mu);
+        add = __builtin_bit_cast(h2, ad);
+    }
+
+    auto read_ws = [&](int slot, int h) {
+        w_nxt = *(const __attribute__((address_space(3))) u2 *)(L + kWBOff + slot * kWB + b_rd + h * 512);
+        s_nxt = *(const __attribute__((address_space(3))) uint32_t *)(L + kWSOff + slot * kWS + s_rd + h * 128);
+    };
+    auto read_a = [&](int slot, int h) {
+        const lds_u8_t *ab = L + kWAOff + slot * kWA + a_rd[h];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            a_nxt[mt] = __builtin_bit_cast(h8, *(const __attribute__((address_space(3))) u4 *)(ab + mt * 4096));
+    };
+
+    f16v acc[8][2];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mt][j][e] = 0.f;
+
+    // One 16-deep step on (a_cur, b_cur): reads step (slot, h) into the next
+    // registers, unpacks its B fragments one operation at a time between the
+    // MFMAs (fenced groups, so MFMA issue never waits behind a chain of
+    // dependent unpack operations) and, in the FAST form, issues DMA chunk
+    // dchunk of stage dst spread over the MFMAs.  The slow form issues the
+    // chunk up front, with its checks.
+    auto step = [&](auto fastc, int slot, int h, int dst, int dslot, int dchunk) {
+        constexpr bool FAST = decltype(fastc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if (!FAST) {
+            dma_chunk_any(dst, dslot, dchunk);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        read_ws(slot, h);
+        read_a(slot, h);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t tw[2][4];
+        const h2 s_lo = {half_lo(s_nxt), half_lo(s_nxt)};
+        const h2 s_hi = {half_hi(s_nxt), half_hi(s_nxt)};
+        auto valu = [&](int idx) {
+            const int j = idx >> 4, k = (idx >> 2) & 3, d = idx & 3;
+            const uint32_t w = j ? w_nxt.y : w_nxt.x;
+            if (k == 0) tw[j][d] = __builtin_amdgcn_perm(w, w, 0x01010101u * d);
+            else if (k == 1) tw[j][d] = (tw[j][d] & mask) | magic;
+            else if (k == 2)
+                tw[j][d] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(h2, tw[j][d]), mul, add));
+            else tw[j][d] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, tw[j][d]) * (j ? s_hi : s_lo));
+            asm volatile("" : "+v"(tw[j][d]));   // pin the operation to this group
+        };
+        auto mfma = [&](int idx) {
+            const int j = idx >> 3, mt = idx & 7;
+            acc[mt][j] = mfma32x32x16(a_cur[mt], j ? b_cur1 : b_cur0, acc[mt][j]);
+        };
+        mfma(0);
+        mfma(1);
+        mfma(2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 13; ++i) {
+            mfma(3 + i);
+            valu(2 * i);
+            valu(2 * i + 1);
+            if (FAST && (i == 2 || i == 6 || i == 10))
+                dma(BoolC<true>(), dst, dslot, 3 * dchunk + (i - 2) / 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 26; i < 32; ++i) valu(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) a_cur[mt] = a_nxt[mt];
+        b_cur0 = __builtin_bit_cast(h8, u4{tw[0][0], tw[0][1], tw[0][2], tw[0][3]});
+        b_cur1 = __builtin_bit_cast(h8, u4{tw[1][0], tw[1][1], tw[1][2], tw[1][3]});
+    };
+
+    // One stage st in slot r (r == st % 3).  DMA(s) goes to slot s % 3:
+    // chunk 0 right after the barrier that frees the slot (in stage s-3),
+    // chunks 1..3 during the first three steps of stage s-2.
+    // FAST: stages st+2 and st+3 exist and have no K tail.
+    auto stage = [&](auto fastc, int st, int r) {
+        constexpr bool FAST = decltype(fastc)::value;
+#pragma unroll
+        for (int h = 0; h < kWSteps - 1; ++h) step(fastc, r, h + 1, st + 2, (r + 2) % 3, h + 1);
+        // stage st+1 landed (each wave waits for its own DMA; all of stage
+        // st+2's is issued after it), and every wave is done reading slot r
+        if (FAST || st + 2 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(12));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+        lds_barrier();
+        // the last step reads step 0 of the next slot (stale after the last
+        // stage: read but unused) and starts stage st+3
+        step(fastc, (r + 1) % 3, 0, st + 3, r, 0);
+    };
+
+    // Prologue: stages 0 and 1 and the first chunk of stage 2 in flight;
+    // wait for stage 0.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dma_chunk_any(0, 0, c);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dma_chunk_any(1, 1, c);
+    dma_chunk_any(2, 2, 0);
+    if (nst > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(15));
+    else if (nst > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+    read_ws(0, 0);
+    read_a(0, 0);
+    b_cur0 = unpack_nat_scaled(w_nxt.x, half_lo(s_nxt), mask, magic, mul, add);
+    b_cur1 = unpack_nat_scaled(w_nxt.y, half_hi(s_nxt), mask, magic, mul, add);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) a_cur[mt] = a_nxt[mt];
+
+    int st0 = 0;
+    // branch-free main loop: every DMA target is a full stage
+    for (; st0 + 5 < nfull; st0 += 3) {
+        stage(BoolC<true>(), st0, 0);
+        stage(BoolC<true>(), st0 + 1, 1);
+        stage(BoolC<true>(), st0 + 2, 2);
+    }
+    for (; st0 < nst; st0 += 3) {
+        stage(BoolC<false>(), st0, 0);
+        if (st0 + 1 < nst) stage(BoolC<false>(), st0 + 1, 1);
+        if (st0 + 2 < nst) stage(BoolC<false>(), st0 + 2, 2);
+    }
+
+    // ---- epilogue: register i of tile (mt, j): row m0 + 32 mt + 8 (i/4) +
+    // 4 kb + i%4, column n0 + 64w + 2 c32 + j ----
+    const int n = n0 + 64 * wave + 2 * c32;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
+            const h2 v = {(_Float16)acc[mt][0][i], (_Float16)acc[mt][1][i]};
+            const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), yr, off, 0, 0);
+        }
+    }
+}
+
+static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream) {
+    int K = (int)a.K, N = (int)a.N, M = (int)a.M;
+    int gshift = -1;
+    if (a.group_size != -1) gshift = __builtin_ctz((unsigned)a.group_size);
+    int tiles_m = (M + kWBM - 1) / kWBM;
+    int tiles = tiles_m * ((N + kWBN - 1) / kWBN);
+    int per_xcd = (tiles + 7) / 8;
+    const void *xp = a.x;
+    const void *qp = a.qweight;
+    const void *sp = a.scales;
+    void *yp = a.y;
+    void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &tiles_m, &tiles, &per_xcd};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_m256_kernel), dim3(8 * per_xcd),
+                           dim3(256), args, 0, stream);
+}
+
+hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream) {
+    if (a.M > 128) return launch_prefill_m256(a, stream);
+    return launch_prefill_m128(a, stream);
 }
 
 }  // namespace w4a16

@@ -127,6 +127,8 @@ EXACT_SHAPES = [
     (33, 4096, 1032, 1024),
     (1, 17408, 64, 32),     # the longest K of the workloads
     (16, 17408, 64, -1),
+    (300, 336, 520, 16),    # 256-row tiles: ragged M and N, K % 64 == 16
+    (257, 48, 8, -1),       # 256-row tiles: K shorter than one stage
 ]
 
 
@@ -203,6 +205,8 @@ def test_dispatch_edges(dev, M):
     (4, 272, 5128, 256), (70, 272, 5128, 256),
     (1, 1040, 8, 1024), (19, 1040, 8, 1024),
     (16, 5120, 5128, 16), (96, 5120, 5128, 16),
+    (200, 48, 24, 32), (257, 272, 5128, 256), (300, 1040, 8, 1024), (129, 5120, 5128, 16),
+    (520, 336, 264, -1),
 ])
 def test_tails(dev, M, K, N, g):
     case = workloads.Case(f"tail_{M}_{K}_{N}_{g}", M, K, N, g, 13, scales="loguniform")
