@@ -33,9 +33,10 @@
  *   - The library keeps no copy of the weights (dense, dequantised or
  *     repacked).  Its only state is a per-device cache of the device's
  *     architecture and one decode workspace per (device, stream): about
- *     2 MiB on a 256-CU device (a counter and two 16x64 fp32 partial tiles
- *     per CU), allocated and zero-filled on the first decode call on that
- *     stream, left zeroed by every launch and kept until the process exits.
+ *     4 MiB on a 256-CU device (per CU: 16x64 exchange slots, a counter and
+ *     two 16x64 fp32 partial tiles), allocated and zero-filled on the first
+ *     decode call on that stream, left zeroed by every launch and kept until
+ *     the process exits.
  *     A decode call on a stream that is being captured into a graph and has
  *     no workspace yet allocates nothing and runs a kernel that needs none.
  *     Calls on one stream share its workspace in stream order; calls on

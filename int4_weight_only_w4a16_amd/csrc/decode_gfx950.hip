@@ -299,12 +299,25 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
 // Stream-K kernel: gridDim.x workgroups share the units evenly.
 //
 // Workspace for up to `capacity` workgroups (zero-filled once; every launch
-// leaves it zero again).  The layout depends only on the capacity, never on
-// the grid of a launch, so launches of any grid size can share it:
-//   counters: int[capacity], padded to 256 bytes   arrivals at a split tile,
-//                                                  indexed by its last contributor
-//   partials: float[capacity][2][16][kCols]        a workgroup's sums for its
-//                                                  first (0) and last (1) tile
+// leaves the slots and counters zero again).  The layout depends only on the
+// capacity, never on the grid of a launch, so launches of any grid size can
+// share it:
+//   slots:    uint64[capacity][16][kCols]   exchange slot per output element of
+//                                           a split tile (M <= kExchangeMaxM),
+//                                           indexed by the tile's later
+//                                           contributor; 0 when empty, else
+//                                           {fp32 partial, 1}
+//   counters: int[capacity], padded to 256 bytes   arrivals at a split tile
+//                                           (larger M), indexed by its later
+//                                           contributor
+//   partials: float[capacity][2][16][kCols] a workgroup's sums for its first (0)
+//                                           and last (1) tile (larger M)
+
+// Split tiles of batches up to this size meet through per-element exchange
+// slots (one memory round trip); larger batches publish whole partials and
+// count arrivals (three round trips, but 16x fewer atomics than the slots
+// would need).
+constexpr int kExchangeMaxM = 2;
 
 // s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima.
 constexpr unsigned kWaitVmcnt0 = 0x0F70u;
@@ -325,7 +338,8 @@ template <int WAVES, int D, bool SCALE_AFTER, bool XLDS>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
-    int group_steps, int *__restrict__ counters, float *__restrict__ partials) {
+    int group_steps, uint64_t *__restrict__ slots, int *__restrict__ counters,
+    float *__restrict__ partials) {
     constexpr int SLOT = 16 * kCols;             // floats per partial slot
     __shared__ f4 red[2][WAVES][kNW][64];
     __shared__ int last_arrival[2];
@@ -371,11 +385,60 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const bool row_ok = worker && m < M;
     const int b0 = u0 / S, b1 = (u1 - 1) / S;
 
-    // Phase 1: fixed-order sum over the waves for every tile of this range;
-    // whole tiles are stored, split tiles (at most the first and the last)
-    // are published.  Each XCD has its own L2 and agent-scope atomics are
-    // performed in the issuing XCD's L2, so the partials and the counters
-    // use system-scope atomics, which are coherent in memory across XCDs.
+    // Fixed-order sum over the waves for every tile of this range; whole
+    // tiles are stored.  Small batches: a split tile has exactly two
+    // contributors (the host keeps every range at least one tile long, or
+    // makes each tile exactly two ranges), and they meet per output element
+    // in the tile's exchange slot
+    // with one system-scope compare-and-swap: the first deposits {partial, 1},
+    // the second gets it back, adds its own partial (one fp32 add, so the
+    // result does not depend on which one came first), stores y and empties
+    // the slot.  Each XCD has its own L2; only system scope is coherent
+    // across them.
+    if (M <= kExchangeMaxM) {
+        for (int tau = b0; tau <= b1; ++tau) {
+            const int ta = tau * S, tb = ta + S;
+            float v[kNW] = {0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < WAVES; ++w) {
+                const int a0 = min(u1, u0 + w * pw), a1 = min(u1, a0 + pw);
+                if (a0 >= a1 || a1 <= ta || a0 >= tb) continue;
+                const int s = tau - a0 / S;
+                if (worker) {
+#pragma unroll
+                    for (int j = 0; j < kNW; ++j) v[j] += red[s][w][j][l][i];
+                }
+            }
+            const int n = tau * kCols + c;
+            if (!row_ok || n >= N) continue;
+            if (ta >= u0 && tb <= u1) {                 // the whole tile is here
+                store_row4(y + (size_t)m * N + n, v);
+                continue;
+            }
+            const int gl = sk.owner(tb - 1);           // the tile's later contributor
+            uint64_t *slot = slots + ((size_t)gl * 16 + m) * kCols + c;
+            uint64_t got[kNW];
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) {
+                got[j] = 0;
+                const uint64_t mine = (uint64_t)__builtin_bit_cast(uint32_t, v[j]) | ((uint64_t)1 << 32);
+                __hip_atomic_compare_exchange_strong(slot + j, &got[j], mine, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+            // per element (the two contributors' four exchanges may interleave):
+            // an empty slot means this one came first and deposited its value
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) {
+                if (got[j] == 0) continue;
+                const float r = __builtin_bit_cast(float, (uint32_t)got[j]) + v[j];
+                __hip_atomic_store(slot + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                y[(size_t)m * N + n + j] = __builtin_bit_cast(uint16_t, (_Float16)r);
+            }
+        }
+        return;
+    }
+
+    // Larger batches: split tiles (at most the first and the last of the
+    // range) are published as whole partials with system-scope stores.
     int split_tile[2] = {-1, -1};
     for (int tau = b0; tau <= b1; ++tau) {
         const int ta = tau * S, tb = ta + S;
@@ -406,8 +469,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     }
     if (split_tile[0] < 0 && split_tile[1] < 0) return;
 
-    // Phase 2: once every wave's partial stores are complete, count this
-    // workgroup's arrival at each split tile (one round for both).
+    // Once every wave's partial stores are complete, count this workgroup's
+    // arrival at each split tile (one round for both).
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (threadIdx.x < 2) {
@@ -422,8 +485,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     }
     __syncthreads();
 
-    // Phase 3: the last contributor of a split tile adds every partial in
-    // workgroup order, stores the tile and resets its counter.
+    // The last contributor of a split tile adds every partial in workgroup
+    // order, stores the tile and resets its counter.
 #pragma unroll
     for (int slot = 0; slot < 2; ++slot) {
         const int tau = split_tile[slot];
@@ -458,20 +521,27 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
 constexpr int kDecWaves = W4A16_DECODE_WAVES;
 constexpr int kDecD = W4A16_DECODE_D;
 
+static size_t slots_bytes(int capacity) { return (size_t)capacity * 16 * kCols * sizeof(uint64_t); }
 static size_t counters_bytes(int capacity) {
     return ((size_t)capacity * sizeof(int) + 255) & ~(size_t)255;
 }
 
 size_t decode_workspace_bytes(int capacity) {
-    return counters_bytes(capacity) + (size_t)capacity * 2 * 16 * kCols * sizeof(float);
+    return slots_bytes(capacity) + counters_bytes(capacity) +
+           (size_t)capacity * 2 * 16 * kCols * sizeof(float);
 }
 
+// Stream-K grid, or 0 for the tiles kernel.  Every tile must have at most two
+// contributors: either every range holds at least one tile (G <= T), or
+// G = 2T and each tile is exactly two ranges.
 int decode_streamk_grid(const LinearArgs &a, int num_cus) {
     const int64_t S = (a.K + 31) / 32;
     const int64_t T = (a.N + kCols - 1) / kCols;
     // a wave must hold at most S units, so that it meets at most two tiles
     if (T > (int64_t)kDecWaves * num_cus) return 0;
-    return (int)std::min<int64_t>(num_cus, T * S);
+    if (T >= num_cus) return num_cus;
+    if (2 * T <= num_cus && S >= 2) return (int)(2 * T);
+    return (int)T;
 }
 
 // Activations are staged in LDS when they fit in this many bytes.
@@ -498,11 +568,13 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
     const dim3 block(kDecWaves * 64);
     const size_t dyn = XLDS ? (size_t)M * 32 * S * 2 + 16 : 0;
     if (grid > 0) {
-        int *counters = static_cast<int *>(workspace);
+        char *ws = static_cast<char *>(workspace);
+        uint64_t *slots = reinterpret_cast<uint64_t *>(ws);
+        int *counters = reinterpret_cast<int *>(ws + slots_bytes(capacity));
         float *partials =
-            reinterpret_cast<float *>(static_cast<char *>(workspace) + counters_bytes(capacity));
+            reinterpret_cast<float *>(ws + slots_bytes(capacity) + counters_bytes(capacity));
         void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N,
-                        &group_steps, &counters, &partials};
+                        &group_steps, &slots, &counters, &partials};
         return hipLaunchKernel(
             reinterpret_cast<const void *>(
                 &decode_streamk_kernel<kDecWaves, kDecD, SCALE_AFTER, XLDS>),

@@ -398,3 +398,18 @@ def test_decode_after_other_launches(dev):
             y = w4.linear(x, q, s, c.group_size, kernel=DEC)
             torch.cuda.synchronize()
             check_parity(y.cpu().numpy(), y_ref, f"{c.name} after other launches, rep {rep}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 16])
+def test_decode_split_tiles_both_protocols(dev, M):
+    """Bench-like widths: most tiles are split between two workgroups; M <= 2
+    meets through per-element exchange slots, larger M through counters."""
+    for K, N, g in ((5120, 17408, 128), (17408, 5120, 32)):
+        case = workloads.Case(f"split_{M}_{K}_{N}", M, K, N, g, 41, scales="loguniform")
+        inp = workloads.generate(case)
+        q_o, q_dev, s_dev = _weights(case, inp, dev)
+        y_ref = oracle.linear(inp.x, q_o, inp.scales, g)
+        runs = [_run(inp, q_dev, s_dev, g, dev, DEC) for _ in range(3)]
+        check_parity(runs[0], y_ref, f"split M={M} K={K} N={N}")
+        for r in runs[1:]:
+            assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
