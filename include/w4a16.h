@@ -33,7 +33,7 @@
  *   - The library keeps no copy of the weights (dense, dequantised or
  *     repacked).  Its only state is a per-device cache of the device's
  *     architecture and one decode workspace per (device, stream): about
- *     4 MiB on a 256-CU device (per CU: 16x64 exchange slots, a counter and
+ *     3 MiB on a 256-CU device (per CU: 16x32 exchange slots, a counter and
  *     two 16x64 fp32 partial tiles), allocated and zero-filled on the first
  *     decode call on that stream, left zeroed by every launch and kept until
  *     the process exits.

@@ -58,19 +58,55 @@ struct Stage {
 
 // Activations staged in LDS: rows m < M of x, each zero-padded to Kp = 32*S
 // halves and already in unpack order (perm_x per 16-byte chunk), followed by
-// one zero chunk that the lanes of rows m >= M read.  Returns this lane's
-// byte address of step 0.
-__device__ __forceinline__ uint32_t stage_x_lds(unsigned char *xs, const __amdgpu_buffer_rsrc_t xr,
-                                                int M, int K, int S) {
+// one zero chunk that the lanes of rows m >= M read.  Staging is split in
+// two so that the first kXPre chunks of each thread are requested before the
+// weight prologue (they would otherwise queue behind it): stage_x_issue loads
+// them, stage_x_finish stores them and any further chunks and returns this
+// lane's byte address of step 0.
+constexpr int kXPre = 2;
+
+struct XPre {
+    u4 v[kXPre];
+};
+
+__device__ __forceinline__ u4 stage_x_load(const __amdgpu_buffer_rsrc_t xr, int c, int K,
+                                           int chunks_per_row) {
+    const int m = c / chunks_per_row;
+    const int k = 8 * (c - m * chunks_per_row);
+    return load_b128(xr, k < K ? ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 2u : kOOB);
+}
+
+__device__ __forceinline__ XPre stage_x_issue(const __amdgpu_buffer_rsrc_t xr, int M, int K,
+                                              int S) {
+    const int chunks_per_row = 4 * S;
+    const int total = M * chunks_per_row;
+    XPre pre;
+#pragma unroll
+    for (int r = 0; r < kXPre; ++r) {
+        const int c = threadIdx.x + r * blockDim.x;
+        pre.v[r] = stage_x_load(xr, c < total ? c : 0, K, chunks_per_row);
+    }
+    return pre;
+}
+
+__device__ __forceinline__ uint32_t stage_x_finish(unsigned char *xs,
+                                                   const __amdgpu_buffer_rsrc_t xr, int M, int K,
+                                                   int S, const XPre &pre) {
     const int Kp = 32 * S;
     const int chunks_per_row = Kp / 8;
     const int total = M * chunks_per_row;
-    for (int c = threadIdx.x; c < total; c += blockDim.x) {
+    auto put = [&](int c, const u4 &v) {
         const int m = c / chunks_per_row;
         const int k = 8 * (c - m * chunks_per_row);
-        const u4 v = load_b128(xr, k < K ? ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 2u : kOOB);
         *reinterpret_cast<u4 *>(xs + ((size_t)m * Kp + k) * 2) = perm_x(v);
+    };
+#pragma unroll
+    for (int r = 0; r < kXPre; ++r) {
+        const int c = threadIdx.x + r * blockDim.x;
+        if (c < total) put(c, pre.v[r]);
     }
+    for (int c = threadIdx.x + kXPre * blockDim.x; c < total; c += blockDim.x)
+        put(c, stage_x_load(xr, c, K, chunks_per_row));
     if (threadIdx.x == 0) *reinterpret_cast<u4 *>(xs + (size_t)M * Kp * 2) = u4{0u, 0u, 0u, 0u};
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, kb = lane >> 4;
@@ -266,6 +302,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
 
 #pragma unroll
     for (int j = 0; j < kNW; ++j) red[wave][j][lane] = f4{0.f, 0.f, 0.f, 0.f};
+    XPre xpre;
+    if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
+    __builtin_amdgcn_sched_barrier(0);
     decode_units<D, SCALE_AFTER, XLDS>(
         xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int, const f4(&acc)[kNW]) {
@@ -274,7 +313,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
         },
         [&]() -> uint32_t {
             if constexpr (XLDS) {
-                const uint32_t a = stage_x_lds(decode_dyn_lds, xr, M, K, S);
+                const uint32_t a = stage_x_finish(decode_dyn_lds, xr, M, K, S, xpre);
                 __syncthreads();
                 return a;
             }
@@ -302,11 +341,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
 // leaves the slots and counters zero again).  The layout depends only on the
 // capacity, never on the grid of a launch, so launches of any grid size can
 // share it:
-//   slots:    uint64[capacity][16][kCols]   exchange slot per output element of
-//                                           a split tile (M <= kExchangeMaxM),
-//                                           indexed by the tile's later
-//                                           contributor; 0 when empty, else
-//                                           {fp32 partial, 1}
+//   slots:    uint64[capacity][16][kCols/2] exchange slot per output column
+//                                           pair of a split tile (M <=
+//                                           kExchangeMaxM), indexed by the tile's
+//                                           later contributor; 0 when empty
 //   counters: int[capacity], padded to 256 bytes   arrivals at a split tile
 //                                           (larger M), indexed by its later
 //                                           contributor
@@ -318,6 +356,15 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
 // count arrivals (three round trips, but 16x fewer atomics than the slots
 // would need).
 constexpr int kExchangeMaxM = 2;
+
+// A slot holds two fp32 partials (adjacent columns), each XOR-ed with the bit
+// pattern of a NaN; NaN partials are first replaced by the canonical NaN, so
+// an occupied slot is never 0, the empty value.
+constexpr uint32_t kSlotKey = 0x7FBADBADu;
+
+__device__ __forceinline__ uint32_t slot_code(float v) {
+    return (v != v ? 0x7FC00000u : __builtin_bit_cast(uint32_t, v)) ^ kSlotKey;
+}
 
 // s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima.
 constexpr unsigned kWaitVmcnt0 = 0x0F70u;
@@ -359,6 +406,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
     const auto sr = make_rsrc(scales, (uint32_t)Gs * (uint32_t)N * 2u);
 
+    XPre xpre;
+    if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
+    __builtin_amdgcn_sched_barrier(0);
     decode_units<D, SCALE_AFTER, XLDS>(
         xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int slot, const f4(&acc)[kNW]) {
@@ -368,7 +418,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         },
         [&]() -> uint32_t {
             if constexpr (XLDS) {
-                const uint32_t a = stage_x_lds(decode_dyn_lds, xr, M, K, S);
+                const uint32_t a = stage_x_finish(decode_dyn_lds, xr, M, K, S, xpre);
                 __syncthreads();
                 return a;
             }
@@ -389,12 +439,11 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     // tiles are stored.  Small batches: a split tile has exactly two
     // contributors (the host keeps every range at least one tile long, or
     // makes each tile exactly two ranges), and they meet per output element
-    // in the tile's exchange slot
-    // with one system-scope compare-and-swap: the first deposits {partial, 1},
-    // the second gets it back, adds its own partial (one fp32 add, so the
-    // result does not depend on which one came first), stores y and empties
-    // the slot.  Each XCD has its own L2; only system scope is coherent
-    // across them.
+    // in the tile's exchange slots with one system-scope compare-and-swap per
+    // column pair: the first deposits its partials, the second gets them back,
+    // adds its own (one fp32 add each, so the result does not depend on which
+    // one came first), stores y and empties the slot.  Each XCD has its own
+    // L2; only system scope is coherent across them.
     if (M <= kExchangeMaxM) {
         for (int tau = b0; tau <= b1; ++tau) {
             const int ta = tau * S, tb = ta + S;
@@ -415,23 +464,25 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
                 continue;
             }
             const int gl = sk.owner(tb - 1);           // the tile's later contributor
-            uint64_t *slot = slots + ((size_t)gl * 16 + m) * kCols + c;
-            uint64_t got[kNW];
+            uint64_t *slot = slots + ((size_t)gl * 16 + m) * (kCols / 2) + c / 2;
+            uint64_t got[kNW / 2];
 #pragma unroll
-            for (int j = 0; j < kNW; ++j) {
+            for (int j = 0; j < kNW / 2; ++j) {
                 got[j] = 0;
-                const uint64_t mine = (uint64_t)__builtin_bit_cast(uint32_t, v[j]) | ((uint64_t)1 << 32);
+                const uint64_t mine = (uint64_t)slot_code(v[2 * j]) | ((uint64_t)slot_code(v[2 * j + 1]) << 32);
                 __hip_atomic_compare_exchange_strong(slot + j, &got[j], mine, __ATOMIC_RELAXED,
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             }
-            // per element (the two contributors' four exchanges may interleave):
-            // an empty slot means this one came first and deposited its value
+            // per column pair (the two contributors' exchanges may interleave):
+            // an empty slot means this one came first and deposited its values
 #pragma unroll
-            for (int j = 0; j < kNW; ++j) {
+            for (int j = 0; j < kNW / 2; ++j) {
                 if (got[j] == 0) continue;
-                const float r = __builtin_bit_cast(float, (uint32_t)got[j]) + v[j];
+                const float r0 = __builtin_bit_cast(float, (uint32_t)got[j] ^ kSlotKey) + v[2 * j];
+                const float r1 = __builtin_bit_cast(float, (uint32_t)(got[j] >> 32) ^ kSlotKey) + v[2 * j + 1];
                 __hip_atomic_store(slot + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                y[(size_t)m * N + n + j] = __builtin_bit_cast(uint16_t, (_Float16)r);
+                const h2 h = {(_Float16)r0, (_Float16)r1};
+                *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n + 2 * j) = __builtin_bit_cast(uint32_t, h);
             }
         }
         return;
@@ -521,7 +572,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
 constexpr int kDecWaves = W4A16_DECODE_WAVES;
 constexpr int kDecD = W4A16_DECODE_D;
 
-static size_t slots_bytes(int capacity) { return (size_t)capacity * 16 * kCols * sizeof(uint64_t); }
+static size_t slots_bytes(int capacity) { return (size_t)capacity * 16 * (kCols / 2) * sizeof(uint64_t); }
 static size_t counters_bytes(int capacity) {
     return ((size_t)capacity * sizeof(int) + 255) & ~(size_t)255;
 }
