@@ -32,14 +32,18 @@
  *     launched, y is untouched and a nonzero w4a16_status is returned.
  *   - The library keeps no copy of the weights (dense, dequantised or
  *     repacked).  Its only state is a per-device cache of the device's
- *     architecture and one decode workspace per (device, stream): about
- *     3 MiB on a 256-CU device (per CU: 16x32 exchange slots, a counter and
- *     two 16x64 fp32 partial tiles), allocated and zero-filled on the first
- *     decode call on that stream, left zeroed by every launch and kept until
- *     the process exits.
- *     A decode call on a stream that is being captured into a graph and has
- *     no workspace yet allocates nothing and runs a kernel that needs none.
- *     Calls on one stream share its workspace in stream order; calls on
+ *     architecture and up to two workspaces per (device, stream), each
+ *     allocated and zero-filled on the first call on that stream that needs
+ *     it and kept until the process exits:
+ *       decode: about 3 MiB on a 256-CU device (per CU: 16x32 exchange
+ *         slots, a counter and two 16x64 fp32 partial tiles), left zeroed by
+ *         every launch;
+ *       prefill: 64 MiB on a 256-CU device (one 256x256 fp32 partial tile
+ *         per CU), used by M > 128 when a last partial round of tiles is
+ *         split along K.
+ *     A call on a stream that is being captured into a graph and has no
+ *     workspace yet allocates nothing and runs a kernel that needs none.
+ *     Calls on one stream share its workspaces in stream order; calls on
  *     different streams never share one.  Thread-safe and reentrant.
  *   - Device calls are asynchronous on the given stream (a hipStream_t; 0 is
  *     the null stream); results are valid once the stream is synchronised.

@@ -34,6 +34,8 @@
 // Tails: rows >= M and K >= K read as zero through buffer range checks and
 // per-lane checks; stores are masked per row and per column pair (N % 8 == 0).
 
+#include <algorithm>
+
 #include "w4a16_device.hpp"
 #include "w4a16_launch.h"
 
@@ -264,34 +266,46 @@ __device__ __forceinline__ h8 unpack_nat_scaled(uint32_t w, _Float16 s, uint32_t
     return __builtin_bit_cast(h8, r);
 }
 
-__global__ __launch_bounds__(256) void prefill_m256_kernel(
-    const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
-    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
-    int gshift, int tiles_m, int tiles, int per_xcd) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kWLds];
-    lds_u8_t *L = (lds_u8_t *)lds_raw;
+// Operands of one wide-tile call: buffer resources and sizes.
+struct WideOperands {
+    __amdgpu_buffer_rsrc_t xr, qr, sr, yr;
+    int M, K, N, gshift;
+    int nst;     // 64-deep stages: ceil(K / 64)
+    int nfull;   // stages without a K tail: K / 64
+};
 
-    // XCD-blocked tile order: workgroup id % 8 is taken as its XCD; XCD x
-    // takes tiles x*per_xcd .. in column-major order (row blocks fastest).
-    const int id = blockIdx.x;
-    const int tl = (id & 7) * per_xcd + (id >> 3);
-    if (tl >= tiles) return;
-    const int m0 = (tl % tiles_m) * kWBM;
-    const int n0 = (tl / tiles_m) * kWBN;
+__device__ __forceinline__ WideOperands wide_operands(const uint16_t *x, const int32_t *qweight,
+                                                      const uint16_t *scales, uint16_t *y, int M,
+                                                      int K, int N, int gshift) {
+    const int G = gshift < 0 ? 1 : ((K - 1) >> gshift) + 1;
+    WideOperands p;
+    p.xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    p.qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
+    p.sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
+    p.yr = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
+    p.M = M;
+    p.K = K;
+    p.N = N;
+    p.gshift = gshift;
+    p.nst = (K + kWBK - 1) / kWBK;
+    p.nfull = K / kWBK;
+    return p;
+}
 
+// acc = the fp32 products of the 256 x 256 tile at (m0, n0) over the 64-deep
+// stages [sb, se) of K, 0 <= sb < se <= nst.  Uses the whole LDS area L; on
+// return every copy has landed, but other waves may still be reading L.
+__device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands &p, int m0, int n0,
+                                                int sb, int se, f16v (&acc)[8][2]) {
+    const int M = p.M, K = p.K, N = p.N, gshift = p.gshift, nfull = p.nfull;
+    const auto xr = p.xr;
+    const auto qr = p.qr;
+    const auto sr = p.sr;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kb = lane >> 5;
     const int c32 = lane & 31;
-    const int G = gshift < 0 ? 1 : ((K - 1) >> gshift) + 1;
-    const int nst = (K + kWBK - 1) / kWBK;   // stages
-    const int nfull = K / kWBK;               // stages without a K tail
-
-    const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-    const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
-    const auto sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
-    const auto yr = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
 
     // ---- DMA lane offsets (stage 0) ----
     // A: instruction i moves rows 64w + 8i + lane/8; lane's physical 16-byte
@@ -367,9 +381,9 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
             }
         }
     };
-    // generic issue of instructions 3c .. 3c+2 of stage st (nothing past the last stage)
+    // generic issue of instructions 3c .. 3c+2 of stage st (nothing past the range)
     auto dma_chunk_any = [&](int st, int slot, int c) {
-        if (st < nst) {
+        if (st < se) {
             if (st < nfull) {
                 dma(BoolC<true>(), st, slot, 3 * c);
                 dma(BoolC<true>(), st, slot, 3 * c + 1);
@@ -421,7 +435,6 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
             a_nxt[mt] = __builtin_bit_cast(h8, *(const __attribute__((address_space(3))) u4 *)(ab + mt * 4096));
     };
 
-    f16v acc[8][2];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -487,14 +500,14 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
     // One stage st in slot r (r == st % 3).  DMA(s) goes to slot s % 3:
     // chunk 0 right after the barrier that frees the slot (in stage s-3),
     // chunks 1..3 during the first three steps of stage s-2.
-    // FAST: stages st+2 and st+3 exist and have no K tail.
+    // FAST: stages st+2 and st+3 are in the range and have no K tail.
     auto stage = [&](auto fastc, int st, int r) {
         constexpr bool FAST = decltype(fastc)::value;
 #pragma unroll
         for (int h = 0; h < kWSteps - 1; ++h) step(fastc, r, h + 1, st + 2, (r + 2) % 3, h + 1);
         // stage st+1 landed (each wave waits for its own DMA; all of stage
         // st+2's is issued after it), and every wave is done reading slot r
-        if (FAST || st + 2 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(12));
+        if (FAST || st + 2 < se) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(12));
         else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
         lds_barrier();
         // the last step reads step 0 of the next slot (stale after the last
@@ -502,15 +515,15 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
         step(fastc, (r + 1) % 3, 0, st + 3, r, 0);
     };
 
-    // Prologue: stages 0 and 1 and the first chunk of stage 2 in flight;
-    // wait for stage 0.
+    // Prologue: stages sb and sb+1 and the first chunk of sb+2 in flight;
+    // wait for stage sb.
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dma_chunk_any(0, 0, c);
+    for (int c = 0; c < 4; ++c) dma_chunk_any(sb, 0, c);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dma_chunk_any(1, 1, c);
-    dma_chunk_any(2, 2, 0);
-    if (nst > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(15));
-    else if (nst > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
+    for (int c = 0; c < 4; ++c) dma_chunk_any(sb + 1, 1, c);
+    dma_chunk_any(sb + 2, 2, 0);
+    if (se - sb > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(15));
+    else if (se - sb > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
     read_ws(0, 0);
@@ -520,52 +533,212 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) a_cur[mt] = a_nxt[mt];
 
-    int st0 = 0;
-    // branch-free main loop: every DMA target is a full stage
-    for (; st0 + 5 < nfull; st0 += 3) {
+    // slot of stage st: (st - sb) % 3
+    int st0 = sb;
+    const int fast_end = se < nfull ? se : nfull;
+    // branch-free main loop: every DMA target is a full stage of the range
+    for (; st0 + 5 < fast_end; st0 += 3) {
         stage(BoolC<true>(), st0, 0);
         stage(BoolC<true>(), st0 + 1, 1);
         stage(BoolC<true>(), st0 + 2, 2);
     }
-    for (; st0 < nst; st0 += 3) {
+    for (; st0 < se; st0 += 3) {
         stage(BoolC<false>(), st0, 0);
-        if (st0 + 1 < nst) stage(BoolC<false>(), st0 + 1, 1);
-        if (st0 + 2 < nst) stage(BoolC<false>(), st0 + 2, 2);
+        if (st0 + 1 < se) stage(BoolC<false>(), st0 + 1, 1);
+        if (st0 + 2 < se) stage(BoolC<false>(), st0 + 2, 2);
     }
+    // every copy of the range has landed (the last stage waited for them);
+    // the last step's reads of the next slot are stale and unused.  Each
+    // workgroup runs one range, so no wave waits for the others here.
+}
 
-    // ---- epilogue: register i of tile (mt, j): row m0 + 32 mt + 8 (i/4) +
-    // 4 kb + i%4, column n0 + 64w + 2 c32 + j ----
-    const int n = n0 + 64 * wave + 2 * c32;
+// Rounds row tile mt of the tile's sums (column tiles v0, v1) to fp16 and
+// stores it: register i of lane (c32, kb) in wave w is row m0 + 32 mt +
+// 8 (i/4) + 4 kb + i%4, columns n0 + 64w + 2 c32 + {0, 1}; rows >= M and
+// columns >= N are dropped.
+__device__ __forceinline__ void wide_store_rows(const WideOperands &p, int m0, int n0, int mt,
+                                                const f16v &v0, const f16v &v1) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int kb = lane >> 5;
+    const int n = n0 + 64 * wave + 2 * (lane & 31);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
-            const h2 v = {(_Float16)acc[mt][0][i], (_Float16)acc[mt][1][i]};
-            const uint32_t off = (m < M && n < N) ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), yr, off, 0, 0);
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
+        const h2 v = {(_Float16)v0[i], (_Float16)v1[i]};
+        const uint32_t off = (m < p.M && n < p.N) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), p.yr, off, 0, 0);
     }
 }
 
-static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream) {
+__device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0,
+                                           const f16v (&acc)[8][2]) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) wide_store_rows(p, m0, n0, mt, acc[mt][0], acc[mt][1]);
+}
+
+// The wide kernel.  Workgroups [0, 8 * per_xcd) take one tile each of the
+// first tiles_dp tiles (whole rounds), in XCD-blocked order: workgroup id % 8
+// is taken as its XCD, and XCD x takes tiles x*per_xcd .. in column-major
+// order (row blocks fastest), so the workgroups of one XCD share activation
+// rows.  The remaining tiles (a last, partial round) are split along K into
+// `chunks` equal stage ranges, one workgroup each, run in the same launch;
+// each writes its fp32 partial to partials[item] in lane order and
+// prefill_tail_reduce_kernel adds them.  Every workgroup streams K from its
+// range start with the others, nothing is exchanged inside the kernel.
+constexpr int kWSlot = kWBM * kWBN;              // floats per partial slot
+
+__global__ __launch_bounds__(256) void prefill_m256_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
+    int gshift, int tiles_m, int tiles_dp, int per_xcd, int chunks, float *__restrict__ partials) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kWLds];
+    const WideOperands p = wide_operands(x, qweight, scales, y, M, K, N, gshift);
+    const int id = blockIdx.x;
+    const int ndp = 8 * per_xcd;
+    // one call of the pipeline for both kinds of workgroup (two inlined
+    // copies would not fit the register file)
+    int m0, n0, sb, se, j = -1;
+    if (id < ndp) {
+        const int tl = (id & 7) * per_xcd + (id >> 3);
+        if (tl >= tiles_dp) return;
+        m0 = (tl % tiles_m) * kWBM;
+        n0 = (tl / tiles_m) * kWBN;
+        sb = 0;
+        se = p.nst;
+    } else {
+        // split tail: item j = tile tiles_dp + j / chunks, K chunk j % chunks
+        j = id - ndp;
+        const int t = tiles_dp + j / chunks, c = j % chunks;
+        m0 = (t % tiles_m) * kWBM;
+        n0 = (t / tiles_m) * kWBN;
+        sb = (int)((int64_t)p.nst * c / chunks);
+        se = (int)((int64_t)p.nst * (c + 1) / chunks);
+    }
+    f16v acc[8][2];
+    wide_tile_range((lds_u8_t *)lds_raw, p, m0, n0, sb, se, acc);
+    if (j < 0) {
+        wide_store(p, m0, n0, acc);
+        return;
+    }
+    // lane order: 64-bit word (mt, jt, e2) of this wave and lane at
+    // ((wave*16 + mt*2 + jt)*8 + e2)*64 + lane, holding elements 2e2, 2e2+1
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint64_t *dst = reinterpret_cast<uint64_t *>(partials) + (size_t)j * (kWSlot / 2) +
+                    (size_t)wave * 16 * 8 * 64 + lane;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+                // copy the elements out first: a bit cast of a vector element
+                // in place reads the vector's first element
+                const float lo = acc[mt][jt][2 * e2], hi = acc[mt][jt][2 * e2 + 1];
+                dst[((mt * 2 + jt) * 8 + e2) * 64] =
+                    (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+            }
+}
+
+// Sums the split tiles' partials in chunk order (fixed, so results are
+// bit-reproducible) and stores y.  One thread per (tile, wave, mt, e2, lane):
+// elements 2e2 and 2e2+1 (two consecutive rows) of both column tiles (two
+// adjacent columns).
+__global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
+    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int tiles_m,
+    int tiles_dp, int chunks, int tail_tiles) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int tt = (int)(gid >> 14);                      // 16384 threads per tile
+    if (tt >= tail_tiles) return;
+    const int r = (int)(gid & 16383);
+    const int lane = r & 63, e2 = (r >> 6) & 7, mt = (r >> 9) & 7, wave = r >> 12;
+    const int t = tiles_dp + tt;
+    const int m0 = (t % tiles_m) * kWBM;
+    const int n0 = (t / tiles_m) * kWBN;
+    const uint64_t *src = reinterpret_cast<const uint64_t *>(partials) +
+                          (size_t)tt * chunks * (kWSlot / 2) + (size_t)wave * 16 * 8 * 64 + lane;
+    const int o0 = ((mt * 2 + 0) * 8 + e2) * 64, o1 = ((mt * 2 + 1) * 8 + e2) * 64;
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;   // (row e, col 0/1), (row e+1, col 0/1)
+    for (int c = 0; c < chunks; ++c) {
+        const uint64_t *q = src + (size_t)c * (kWSlot / 2);
+        const uint64_t u0 = q[o0], u1 = q[o1];
+        a0 += __builtin_bit_cast(float, (uint32_t)u0);
+        b0 += __builtin_bit_cast(float, (uint32_t)(u0 >> 32));
+        a1 += __builtin_bit_cast(float, (uint32_t)u1);
+        b1 += __builtin_bit_cast(float, (uint32_t)(u1 >> 32));
+    }
+    const int e = 2 * e2;
+    const int m = m0 + 32 * mt + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    const int n = n0 + 64 * wave + 2 * (lane & 31);
+    if (n >= N) return;
+    const h2 va = {(_Float16)a0, (_Float16)a1};
+    const h2 vb = {(_Float16)b0, (_Float16)b1};
+    if (m < M) *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) = __builtin_bit_cast(uint32_t, va);
+    if (m + 1 < M) *reinterpret_cast<uint32_t *>(y + (size_t)(m + 1) * N + n) = __builtin_bit_cast(uint32_t, vb);
+}
+
+// Split of the wide kernel's tiles: whole rounds of one tile per workgroup;
+// a last partial round of `tail` tiles (at most half a round) split into
+// `chunks` >= 2 stage ranges of at least 8 stages, so that tail * chunks
+// workgroups fill about one round.
+struct WidePlan {
+    int tiles, tiles_dp, tail, chunks;
+};
+
+static WidePlan wide_plan(const LinearArgs &a, int num_cus) {
+    WidePlan w;
+    w.tiles = (int)(((a.M + kWBM - 1) / kWBM) * ((a.N + kWBN - 1) / kWBN));
+    w.tiles_dp = w.tiles;
+    w.tail = 0;
+    w.chunks = 1;
+    const int nst = (int)((a.K + kWBK - 1) / kWBK);
+    if (num_cus <= 0) return w;
+    const int tail = w.tiles % num_cus;
+    if (tail == 0 || 2 * tail > num_cus) return w;
+    const int chunks = std::min(num_cus / tail, nst / 8);
+    if (chunks < 2) return w;
+    w.tail = tail;
+    w.chunks = chunks;
+    w.tiles_dp = w.tiles - tail;
+    return w;
+}
+
+size_t prefill_workspace_bytes(int capacity) { return (size_t)capacity * kWSlot * sizeof(float); }
+
+bool prefill_wants_workspace(const LinearArgs &a, int num_cus) {
+    return a.M > 128 && wide_plan(a, num_cus).chunks > 1;
+}
+
+static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, void *workspace,
+                                      int capacity, int num_cus) {
     int K = (int)a.K, N = (int)a.N, M = (int)a.M;
     int gshift = -1;
     if (a.group_size != -1) gshift = __builtin_ctz((unsigned)a.group_size);
     int tiles_m = (M + kWBM - 1) / kWBM;
-    int tiles = tiles_m * ((N + kWBN - 1) / kWBN);
-    int per_xcd = (tiles + 7) / 8;
+    WidePlan w = wide_plan(a, num_cus);
+    if (w.chunks > 1 && (!workspace || w.tail * w.chunks > capacity)) w = WidePlan{w.tiles, w.tiles, 0, 1};
+    int tiles_dp = w.tiles_dp, chunks = w.chunks, tail = w.tail;
+    int per_xcd = (tiles_dp + 7) / 8;
+    float *partials = static_cast<float *>(workspace);
     const void *xp = a.x;
     const void *qp = a.qweight;
     const void *sp = a.scales;
     void *yp = a.y;
-    void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &tiles_m, &tiles, &per_xcd};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_m256_kernel), dim3(8 * per_xcd),
-                           dim3(256), args, 0, stream);
+    void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &tiles_m, &tiles_dp, &per_xcd,
+                    &chunks, &partials};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_m256_kernel),
+                                   dim3(8 * per_xcd + tail * chunks), dim3(256), args, 0, stream);
+    if (e != hipSuccess || tail == 0) return e;
+    const float *pc = partials;
+    void *rargs[] = {&pc, &yp, &M, &N, &tiles_m, &tiles_dp, &chunks, &tail};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_tail_reduce_kernel),
+                           dim3(64 * tail), dim3(256), rargs, 0, stream);
 }
 
-hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream) {
-    if (a.M > 128) return launch_prefill_m256(a, stream);
+hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
+                          int num_cus) {
+    if (a.M > 128) return launch_prefill_m256(a, stream, workspace, capacity, num_cus);
     return launch_prefill_m128(a, stream);
 }
 

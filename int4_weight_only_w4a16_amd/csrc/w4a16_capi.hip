@@ -12,6 +12,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "../../include/w4a16.h"
@@ -75,17 +76,19 @@ int usable_device(int *num_cus, size_t *max_lds) {
     return state == 1 ? dev : -1;
 }
 
-// Decode workspace, one per (device, stream): calls on one stream run in
-// stream order and calls on different streams use different workspaces, so
-// the kernels never share one concurrently.  Created on the first call on a
-// stream (not while it is being captured into a graph), zero-filled in
-// stream order, kept until the process exits.
+// Kernel workspaces, one per (device, stream, kind): calls on one stream run
+// in stream order and calls on different streams use different workspaces,
+// so the kernels never share one concurrently.  Created on the first call on
+// a stream that needs it (not while the stream is being captured into a
+// graph), zero-filled in stream order, kept until the process exits.
+//   kind 0: decode stream-K (exchange slots, counters and partials, ~3 MiB)
+//   kind 1: prefill split tail (one 256 x 256 fp32 partial per CU, 64 MiB)
 std::mutex g_ws_mu;
-std::map<std::pair<int, uintptr_t>, std::pair<void *, size_t>> g_ws;
+std::map<std::tuple<int, uintptr_t, int>, std::pair<void *, size_t>> g_ws;
 
-void *stream_workspace(int dev, hipStream_t stream, size_t bytes) {
+void *stream_workspace(int dev, hipStream_t stream, int kind, size_t bytes) {
     std::lock_guard<std::mutex> lock(g_ws_mu);
-    const auto key = std::make_pair(dev, reinterpret_cast<uintptr_t>(stream));
+    const auto key = std::make_tuple(dev, reinterpret_cast<uintptr_t>(stream), kind);
     auto it = g_ws.find(key);
     if (it != g_ws.end() && it->second.second >= bytes) return it->second.first;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -132,12 +135,15 @@ extern "C" int w4a16_linear_ex(const void *x, const int32_t *qweight, const void
         int grid = w4a16::decode_streamk_grid(a, num_cus);
         void *ws = nullptr;
         if (grid > 0) {
-            ws = stream_workspace(dev, s, w4a16::decode_workspace_bytes(num_cus));
+            ws = stream_workspace(dev, s, 0, w4a16::decode_workspace_bytes(num_cus));
             if (!ws) grid = 0;                   // under capture with no workspace yet
         }
         e = w4a16::launch_decode(a, s, ws, num_cus, grid, max_lds);
     } else {
-        e = w4a16::launch_prefill(a, s);
+        void *ws = nullptr;
+        if (w4a16::prefill_wants_workspace(a, num_cus))   // null under capture with none yet
+            ws = stream_workspace(dev, s, 1, w4a16::prefill_workspace_bytes(num_cus));
+        e = w4a16::launch_prefill(a, s, ws, num_cus, num_cus);
     }
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }

@@ -413,3 +413,24 @@ def test_decode_split_tiles_both_protocols(dev, M):
         check_parity(runs[0], y_ref, f"split M={M} K={K} N={N}")
         for r in runs[1:]:
             assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
+
+
+def test_prefill_split_tail_ragged(dev):
+    """A last partial round of 256 x 256 tiles split along K (on a 256-CU
+    device: 272 tiles, the last 16 split in two, the second chunk ending in a
+    K tail), ragged M and N: every output of the tail tiles' columns, a
+    sample of the rest, and bitwise equal runs."""
+    M, K, N, g = 2000, 1040, 8456, 16
+    case = workloads.Case("split_tail", M, K, N, g, 43, scales="loguniform")
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    tail_cols = np.arange(8192, N)
+    ms = np.repeat(np.arange(M), tail_cols.size)
+    ns = np.tile(tail_cols, M)
+    sm, sn = sample_indices(M, N, 4096, seed=44)
+    ms = np.concatenate([ms, sm]).astype(np.int64)
+    ns = np.concatenate([ns, sn]).astype(np.int64)
+    y_ref = oracle.linear_at(inp.x, q_o, inp.scales, g, ms, ns)
+    runs = [_run(inp, q_dev, s_dev, g, dev, PRE) for _ in range(2)]
+    check_parity(runs[0][ms, ns], y_ref, "split tail (sampled)")
+    assert np.array_equal(runs[0].view(np.uint16), runs[1].view(np.uint16))
