@@ -269,6 +269,8 @@ __device__ __forceinline__ h8 unpack_nat_scaled(uint32_t w, _Float16 s, uint32_t
 // Operands of one wide-tile call: buffer resources and sizes.
 struct WideOperands {
     __amdgpu_buffer_rsrc_t xr, qr, sr, yr;
+    uint16_t *ybase;
+    uint32_t ybytes;
     int M, K, N, gshift;
     int nst;     // 64-deep stages: ceil(K / 64)
     int nfull;   // stages without a K tail: K / 64
@@ -283,6 +285,8 @@ __device__ __forceinline__ WideOperands wide_operands(const uint16_t *x, const i
     p.qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
     p.sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
     p.yr = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
+    p.ybase = y;
+    p.ybytes = (uint32_t)M * (uint32_t)N * 2u;
     p.M = M;
     p.K = K;
     p.N = N;
@@ -552,29 +556,51 @@ __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands 
     // workgroup runs one range, so no wave waits for the others here.
 }
 
-// Rounds row tile mt of the tile's sums (column tiles v0, v1) to fp16 and
-// stores it: register i of lane (c32, kb) in wave w is row m0 + 32 mt +
-// 8 (i/4) + 4 kb + i%4, columns n0 + 64w + 2 c32 + {0, 1}; rows >= M and
-// columns >= N are dropped.
-__device__ __forceinline__ void wide_store_rows(const WideOperands &p, int m0, int n0, int mt,
-                                                const f16v &v0, const f16v &v1) {
+constexpr int kWSlot = kWBM * kWBN;   // floats per partial tile
+
+// Stores the tile's sums.  Register i of lane (c32, kb) in wave w holds row
+// m0 + 32 mt + 8 (i/4) + 4 kb + i%4 of column tiles v0 = acc[mt][0] and
+// v1 = acc[mt][1], at columns n0 + 64w + 2 c32 + {0, 1}.  With part_mask == 0
+// the pair is rounded to fp16 and stored to y (rows >= M and columns >= N
+// dropped); with part_mask == ~0 both fp32 values go to the partial tile
+// `pr` instead, at floats ((w*8 + mt)*16 + i)*128 + {0, 64} + lane.  One
+// copy of the code serves both kinds of workgroup: every element issues the
+// same two stores, the ones that do not apply get an out-of-range offset
+// (two copies of the epilogue would not fit the register file).
+__device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0,
+                                           const f16v (&acc)[8][2], float *partial,
+                                           uint32_t part_mask) {
+    // keep the mask opaque, so that the compiler does not split the stores
+    // into one copy per kind of workgroup
+    part_mask = __builtin_amdgcn_readfirstlane(part_mask);
+    asm volatile("" : "+s"(part_mask));
+    const uint64_t mask64 = (uint64_t)(int64_t)(int32_t)part_mask;
+    const uint64_t base = ((uint64_t)(uintptr_t)partial & mask64) |
+                          ((uint64_t)(uintptr_t)p.ybase & ~mask64);
+    const uint32_t bytes = ((uint32_t)kWSlot * 4u & part_mask) | (p.ybytes & ~part_mask);
+    const __amdgpu_buffer_rsrc_t r1 = make_rsrc((const void *)(uintptr_t)base, bytes);
+    const __amdgpu_buffer_rsrc_t r2 = make_rsrc(partial, (uint32_t)kWSlot * 4u & part_mask);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int kb = lane >> 5;
     const int n = n0 + 64 * wave + 2 * (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
-        const h2 v = {(_Float16)v0[i], (_Float16)v1[i]};
-        const uint32_t off = (m < p.M && n < p.N) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOOB;
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), p.yr, off, 0, 0);
-    }
-}
-
-__device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0,
-                                           const f16v (&acc)[8][2]) {
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) wide_store_rows(p, m0, n0, mt, acc[mt][0], acc[mt][1]);
+        for (int i = 0; i < 16; ++i) {
+            const float f0 = acc[mt][0][i], f1 = acc[mt][1][i];
+            const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
+            const h2 v = {(_Float16)f0, (_Float16)f1};
+            const uint32_t oy =
+                (m < p.M && n < p.N) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOOB;
+            const uint32_t op = ((uint32_t)((wave * 8 + mt) * 16 + i) * 128u + (uint32_t)lane) * 4u;
+            const uint32_t v1 = (__builtin_bit_cast(uint32_t, f0) & part_mask) |
+                                (__builtin_bit_cast(uint32_t, v) & ~part_mask);
+            const uint32_t o1 = (op & part_mask) | (oy & ~part_mask);
+            const uint32_t o2 = ((op + 256u) & part_mask) | (kOOB & ~part_mask);
+            __builtin_amdgcn_raw_buffer_store_b32(v1, r1, o1, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, f1), r2, o2, 0, 0);
+        }
 }
 
 // The wide kernel.  Workgroups [0, 8 * per_xcd) take one tile each of the
@@ -583,10 +609,9 @@ __device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0
 // order (row blocks fastest), so the workgroups of one XCD share activation
 // rows.  The remaining tiles (a last, partial round) are split along K into
 // `chunks` equal stage ranges, one workgroup each, run in the same launch;
-// each writes its fp32 partial to partials[item] in lane order and
+// each writes its fp32 partial tile to partials[item] (wide_store) and
 // prefill_tail_reduce_kernel adds them.  Every workgroup streams K from its
 // range start with the others, nothing is exchanged inside the kernel.
-constexpr int kWSlot = kWBM * kWBN;              // floats per partial slot
 
 __global__ __launch_bounds__(256) void prefill_m256_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
@@ -617,65 +642,35 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
     }
     f16v acc[8][2];
     wide_tile_range((lds_u8_t *)lds_raw, p, m0, n0, sb, se, acc);
-    if (j < 0) {
-        wide_store(p, m0, n0, acc);
-        return;
-    }
-    // lane order: 64-bit word (mt, jt, e2) of this wave and lane at
-    // ((wave*16 + mt*2 + jt)*8 + e2)*64 + lane, holding elements 2e2, 2e2+1
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    uint64_t *dst = reinterpret_cast<uint64_t *>(partials) + (size_t)j * (kWSlot / 2) +
-                    (size_t)wave * 16 * 8 * 64 + lane;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) {
-                // copy the elements out first: a bit cast of a vector element
-                // in place reads the vector's first element
-                const float lo = acc[mt][jt][2 * e2], hi = acc[mt][jt][2 * e2 + 1];
-                dst[((mt * 2 + jt) * 8 + e2) * 64] =
-                    (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
-            }
+    wide_store(p, m0, n0, acc, j < 0 ? partials : partials + (size_t)j * kWSlot, j < 0 ? 0u : ~0u);
 }
 
 // Sums the split tiles' partials in chunk order (fixed, so results are
-// bit-reproducible) and stores y.  One thread per (tile, wave, mt, e2, lane):
-// elements 2e2 and 2e2+1 (two consecutive rows) of both column tiles (two
-// adjacent columns).
+// bit-reproducible) and stores y.  One thread per (tile, wave, mt, i, lane):
+// register i of row tile mt, both column tiles, as laid out by wide_store.
 __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
     const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int tiles_m,
     int tiles_dp, int chunks, int tail_tiles) {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int tt = (int)(gid >> 14);                      // 16384 threads per tile
+    const int tt = (int)(gid >> 15);                      // 32768 threads per tile
     if (tt >= tail_tiles) return;
-    const int r = (int)(gid & 16383);
-    const int lane = r & 63, e2 = (r >> 6) & 7, mt = (r >> 9) & 7, wave = r >> 12;
+    const int r = (int)(gid & 32767);
+    const int lane = r & 63, i = (r >> 6) & 15, mt = (r >> 10) & 7, wave = r >> 13;
     const int t = tiles_dp + tt;
     const int m0 = (t % tiles_m) * kWBM;
     const int n0 = (t / tiles_m) * kWBN;
-    const uint64_t *src = reinterpret_cast<const uint64_t *>(partials) +
-                          (size_t)tt * chunks * (kWSlot / 2) + (size_t)wave * 16 * 8 * 64 + lane;
-    const int o0 = ((mt * 2 + 0) * 8 + e2) * 64, o1 = ((mt * 2 + 1) * 8 + e2) * 64;
-    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;   // (row e, col 0/1), (row e+1, col 0/1)
+    const float *src = partials + (size_t)tt * chunks * kWSlot +
+                       (size_t)((wave * 8 + mt) * 16 + i) * 128 + lane;
+    float a0 = 0.f, a1 = 0.f;
     for (int c = 0; c < chunks; ++c) {
-        const uint64_t *q = src + (size_t)c * (kWSlot / 2);
-        const uint64_t u0 = q[o0], u1 = q[o1];
-        a0 += __builtin_bit_cast(float, (uint32_t)u0);
-        b0 += __builtin_bit_cast(float, (uint32_t)(u0 >> 32));
-        a1 += __builtin_bit_cast(float, (uint32_t)u1);
-        b1 += __builtin_bit_cast(float, (uint32_t)(u1 >> 32));
+        a0 += src[(size_t)c * kWSlot];
+        a1 += src[(size_t)c * kWSlot + 64];
     }
-    const int e = 2 * e2;
-    const int m = m0 + 32 * mt + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
     const int n = n0 + 64 * wave + 2 * (lane & 31);
-    if (n >= N) return;
-    const h2 va = {(_Float16)a0, (_Float16)a1};
-    const h2 vb = {(_Float16)b0, (_Float16)b1};
-    if (m < M) *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) = __builtin_bit_cast(uint32_t, va);
-    if (m + 1 < M) *reinterpret_cast<uint32_t *>(y + (size_t)(m + 1) * N + n) = __builtin_bit_cast(uint32_t, vb);
+    if (m >= M || n >= N) return;
+    const h2 v = {(_Float16)a0, (_Float16)a1};
+    *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) = __builtin_bit_cast(uint32_t, v);
 }
 
 // Split of the wide kernel's tiles: whole rounds of one tile per workgroup;
@@ -733,7 +728,7 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
     const float *pc = partials;
     void *rargs[] = {&pc, &yp, &M, &N, &tiles_m, &tiles_dp, &chunks, &tail};
     return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_tail_reduce_kernel),
-                           dim3(64 * tail), dim3(256), rargs, 0, stream);
+                           dim3(128 * tail), dim3(256), rargs, 0, stream);
 }
 
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
