@@ -381,6 +381,21 @@ struct StreamK {
     }
 };
 
+// Older waves of a workgroup are served first when several are ready to
+// issue (two waves share each SIMD), so with equal shares the older half
+// finishes well before the younger one: the older half of the waves takes
+// this share (per mille) of the workgroup's units.
+constexpr int kOldShare = 610;
+
+// Start of wave w's share of n units, w in [0, WAVES].
+template <int WAVES>
+__host__ __device__ __forceinline__ int wave_share(int n, int w) {
+    constexpr int H = WAVES / 2;
+    const int nold = (int)((int64_t)n * kOldShare / 1000);
+    if (w <= H) return nold * w / H;
+    return nold + (n - nold) * (w - H) / (WAVES - H);
+}
+
 template <int WAVES, int D, bool SCALE_AFTER, bool XLDS>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
@@ -398,8 +413,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const StreamK sk{T * S, (int)gridDim.x};
     const int g = blockIdx.x;
     const int u0 = sk.begin(g), u1 = sk.begin(g + 1);
-    const int pw = (u1 - u0 + WAVES - 1) / WAVES;   // host keeps pw <= S: <= 2 tiles per wave
-    const int w0 = min(u1, u0 + wave * pw), w1 = min(u1, w0 + pw);
+    // the host keeps every wave's share <= S units: at most two tiles per wave
+    const int w0 = u0 + wave_share<WAVES>(u1 - u0, wave);
+    const int w1 = u0 + wave_share<WAVES>(u1 - u0, wave + 1);
 
     const int Gs = SCALE_AFTER ? (S + group_steps - 1) / group_steps : (K + 15) >> 4;
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
@@ -449,7 +465,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             const int ta = tau * S, tb = ta + S;
             float v[kNW] = {0.f, 0.f, 0.f, 0.f};
             for (int w = 0; w < WAVES; ++w) {
-                const int a0 = min(u1, u0 + w * pw), a1 = min(u1, a0 + pw);
+                const int a0 = u0 + wave_share<WAVES>(u1 - u0, w);
+            const int a1 = u0 + wave_share<WAVES>(u1 - u0, w + 1);
                 if (a0 >= a1 || a1 <= ta || a0 >= tb) continue;
                 const int s = tau - a0 / S;
                 if (worker) {
@@ -495,7 +512,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         const int ta = tau * S, tb = ta + S;
         float v[kNW] = {0.f, 0.f, 0.f, 0.f};
         for (int w = 0; w < WAVES; ++w) {
-            const int a0 = min(u1, u0 + w * pw), a1 = min(u1, a0 + pw);
+            const int a0 = u0 + wave_share<WAVES>(u1 - u0, w);
+            const int a1 = u0 + wave_share<WAVES>(u1 - u0, w + 1);
             if (a0 >= a1 || a1 <= ta || a0 >= tb) continue;
             const int s = tau - a0 / S;
             if (worker) {
@@ -588,9 +606,16 @@ size_t decode_workspace_bytes(int capacity) {
 int decode_streamk_grid(const LinearArgs &a, int num_cus) {
     const int64_t S = (a.K + 31) / 32;
     const int64_t T = (a.N + kCols - 1) / kCols;
-    // a wave must hold at most S units, so that it meets at most two tiles
-    if (T > (int64_t)kDecWaves * num_cus) return 0;
-    if (T >= num_cus) return num_cus;
+    if (T >= num_cus) {
+        // every wave's share of a range must be at most S units, so that it
+        // meets at most two tiles
+        if (T > (int64_t)kDecWaves * num_cus) return 0;
+        const int nmax = (int)((T * S + num_cus - 1) / num_cus);
+        for (int n = nmax - 1; n <= nmax; ++n)      // the two range lengths
+            for (int w = 0; w < kDecWaves; ++w)
+                if (wave_share<kDecWaves>(n, w + 1) - wave_share<kDecWaves>(n, w) > S) return 0;
+        return num_cus;
+    }
     if (2 * T <= num_cus && S >= 2) return (int)(2 * T);
     return (int)T;
 }
