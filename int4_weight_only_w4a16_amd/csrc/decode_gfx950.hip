@@ -137,11 +137,16 @@ __device__ __forceinline__ void store_row4(uint16_t *dst, const float (&v)[4]) {
 // XLDS: activations come from LDS staged by `after_prologue` (called once the
 // first D weight loads are in flight; it returns this lane's LDS byte address
 // of step 0 and ends with a workgroup barrier); otherwise from global.
-template <int D, bool SCALE_AFTER, bool XLDS, typename Dump, typename AfterPrologue>
+// SCALE: 0 scales each 8-deep block before the MFMA (g = 16); 1 sums a
+// group's products in fp32 and scales once per group (scale-after); 2 is
+// scale-after with one step per group (g = 32): every MFMA starts from zero
+// and its result is scaled straight into the sum.
+template <int D, int SCALE, bool XLDS, typename Dump, typename AfterPrologue>
 __device__ __forceinline__ void decode_units(
     const __amdgpu_buffer_rsrc_t xr, const __amdgpu_buffer_rsrc_t qr,
     const __amdgpu_buffer_rsrc_t sr, const unsigned char *xs, int M, int K, int N, int S,
     int group_steps, int w0, int w1, Dump &&dump, AfterPrologue &&after_prologue) {
+    constexpr bool SCALE_AFTER = SCALE != 0;
     const int lane = threadIdx.x & 63;
     const int kb = lane >> 4;
     const int c16 = lane & 15;
@@ -233,7 +238,13 @@ __device__ __forceinline__ void decode_units(
         else
             a = __builtin_bit_cast(h8, perm_x(st.x));
         const bool seg_end = i == nA - 1 || i == n - 1;
-        if constexpr (SCALE_AFTER) {
+        if constexpr (SCALE == 2) {
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) {
+                const f4 t = mfma16x16x32(a, unpack_codes(st.w[j], uc), f4{0.f, 0.f, 0.f, 0.f});
+                acc[j] += (float)scale_at(st.s, j) * t;
+            }
+        } else if constexpr (SCALE_AFTER) {
 #pragma unroll
             for (int j = 0; j < kNW; ++j)
                 accg[j] = mfma16x16x32(a, unpack_codes(st.w[j], uc), accg[j]);
@@ -280,7 +291,7 @@ __device__ __forceinline__ void decode_units(
 extern __shared__ __attribute__((aligned(16))) unsigned char decode_dyn_lds[];
 
 // Tiles kernel: one workgroup per column tile, its waves split K.
-template <int WAVES, int D, bool SCALE_AFTER, bool XLDS>
+template <int WAVES, int D, int SCALE, bool XLDS>
 __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -295,7 +306,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     const int w0 = tile * S + min(S, wave * per);
     const int w1 = tile * S + min(S, wave * per + per);
 
-    const int G = SCALE_AFTER ? (S + group_steps - 1) / group_steps : (K + 15) >> 4;
+    const int G = SCALE != 0 ? (S + group_steps - 1) / group_steps : (K + 15) >> 4;
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
     const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
     const auto sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
     __builtin_amdgcn_sched_barrier(0);
-    decode_units<D, SCALE_AFTER, XLDS>(
+    decode_units<D, SCALE, XLDS>(
         xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int, const f4(&acc)[kNW]) {
 #pragma unroll
@@ -396,7 +407,7 @@ __host__ __device__ __forceinline__ int wave_share(int n, int w) {
     return nold + (n - nold) * (w - H) / (WAVES - H);
 }
 
-template <int WAVES, int D, bool SCALE_AFTER, bool XLDS>
+template <int WAVES, int D, int SCALE, bool XLDS>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -417,7 +428,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const int w0 = u0 + wave_share<WAVES>(u1 - u0, wave);
     const int w1 = u0 + wave_share<WAVES>(u1 - u0, wave + 1);
 
-    const int Gs = SCALE_AFTER ? (S + group_steps - 1) / group_steps : (K + 15) >> 4;
+    const int Gs = SCALE != 0 ? (S + group_steps - 1) / group_steps : (K + 15) >> 4;
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
     const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
     const auto sr = make_rsrc(scales, (uint32_t)Gs * (uint32_t)N * 2u);
@@ -425,7 +436,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
     __builtin_amdgcn_sched_barrier(0);
-    decode_units<D, SCALE_AFTER, XLDS>(
+    decode_units<D, SCALE, XLDS>(
         xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int slot, const f4(&acc)[kNW]) {
             if (slot > 1) return;   // cannot happen: ranges hold <= S units
@@ -630,13 +641,13 @@ static size_t static_lds(const void *kernel) {
     return attr.sharedSizeBytes;
 }
 
-template <bool SCALE_AFTER, bool XLDS>
+template <int SCALE, bool XLDS>
 static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *workspace,
                             int capacity, int grid) {
     const int K = (int)a.K, N = (int)a.N, M = (int)a.M;
     const int S = (K + 31) / 32;
     int group_steps = 0;
-    if (SCALE_AFTER) group_steps = a.group_size == -1 ? S : (int)a.group_size / 32;
+    if (SCALE != 0) group_steps = a.group_size == -1 ? S : (int)a.group_size / 32;
     const void *xp = a.x;
     const void *qp = a.qweight;
     const void *sp = a.scales;
@@ -653,28 +664,28 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
                         &group_steps, &slots, &counters, &partials};
         return hipLaunchKernel(
             reinterpret_cast<const void *>(
-                &decode_streamk_kernel<kDecWaves, kDecD, SCALE_AFTER, XLDS>),
+                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS>),
             dim3(grid), block, args, dyn, stream);
     }
     void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
     const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);
     return hipLaunchKernel(
         reinterpret_cast<const void *>(
-            &decode_tiles_kernel<kDecWaves, kDecD, SCALE_AFTER, XLDS>),
+            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS>),
         dim3(tiles), block, args, dyn, stream);
 }
 
 // Whether the activations can be staged in LDS: at most kXStageMax bytes,
 // and the kernel's static LDS plus the staging area within the device's
 // per-workgroup LDS limit (a launch beyond it is rejected by the device).
-template <bool SCALE_AFTER>
+template <int SCALE>
 static bool stage_fits(const LinearArgs &a, int grid, size_t max_lds) {
     const size_t dyn = (size_t)a.M * 32 * ((a.K + 31) / 32) * 2 + 16;
     if (dyn > kXStageMax) return false;
     static const size_t sk_static = static_lds(reinterpret_cast<const void *>(
-        &decode_streamk_kernel<kDecWaves, kDecD, SCALE_AFTER, true>));
+        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true>));
     static const size_t tiles_static = static_lds(reinterpret_cast<const void *>(
-        &decode_tiles_kernel<kDecWaves, kDecD, SCALE_AFTER, true>));
+        &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true>));
     const size_t st = grid > 0 ? sk_static : tiles_static;
     return st != (size_t)-1 && st + dyn <= max_lds;
 }
@@ -683,12 +694,18 @@ hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspac
                          int grid, size_t max_lds) {
     if (grid > capacity) return hipErrorInvalidValue;
     if (a.group_size == 16)
-        return stage_fits<false>(a, grid, max_lds)
-                   ? launch_sa<false, true>(a, stream, workspace, capacity, grid)
-                   : launch_sa<false, false>(a, stream, workspace, capacity, grid);
-    return stage_fits<true>(a, grid, max_lds)
-               ? launch_sa<true, true>(a, stream, workspace, capacity, grid)
-               : launch_sa<true, false>(a, stream, workspace, capacity, grid);
+        return stage_fits<0>(a, grid, max_lds)
+                   ? launch_sa<0, true>(a, stream, workspace, capacity, grid)
+                   : launch_sa<0, false>(a, stream, workspace, capacity, grid);
+    // one 32-deep step per group: g = 32, or one group over K <= 32
+    const int64_t S = (a.K + 31) / 32;
+    if (a.group_size == 32 || (a.group_size == -1 && S == 1))
+        return stage_fits<2>(a, grid, max_lds)
+                   ? launch_sa<2, true>(a, stream, workspace, capacity, grid)
+                   : launch_sa<2, false>(a, stream, workspace, capacity, grid);
+    return stage_fits<1>(a, grid, max_lds)
+               ? launch_sa<1, true>(a, stream, workspace, capacity, grid)
+               : launch_sa<1, false>(a, stream, workspace, capacity, grid);
 }
 
 }  // namespace w4a16
