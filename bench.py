@@ -195,6 +195,28 @@ def parity_summary(y_gpu, y_ref):
             "mean_rel": float(d.sum() / np.abs(y_ref).sum())}
 
 
+def read_ceiling(torch, w4, nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """Attainable HBM read rate (GB/s): the library's streaming-read probe over
+    nbytes of device memory, timed with HIP events on the launch stream."""
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    s = torch.cuda.current_stream()
+    for _ in range(3):
+        w4.w4a16_read_probe(buf, nbytes, sink, s)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        w4.w4a16_read_probe(buf, nbytes, sink, s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del buf, sink
+    torch.cuda.empty_cache()
+    return nbytes / sec / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +229,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", choices=("all", "decode", "prefill"), default="all")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args()
@@ -252,6 +276,11 @@ def main():
                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                            "traffic": traffic, "algorithmic_bytes": B,
                            "kernel": "w4a16::decode_streamk_kernel"}
+        if not args.no_ceiling:
+            ceil = read_ceiling(torch, w4)
+            out["hbm_read_ceiling"] = {"value": round(ceil, 1), "unit": "GB/s",
+                                       "bytes": 1 << 30, "kernel": "w4a16::read_probe_kernel"}
+            out["roofline"]["frac_of_measured_ceiling"] = round(gbs / ceil, 4)
         if not args.no_cpu_baseline:
             cb, y_ref = cpu_baseline_decode(case, inp, args.cpu_seconds)
             out["cpu_baseline"] = cb

@@ -113,6 +113,20 @@ int pack_gptq_v2(const uint8_t *codes, int32_t *qweight, int64_t K, int64_t N);
 /* Exact inverse of pack_gptq_v2: host int32 [K/8, N] -> host uint8 [K, N]. */
 int unpack_gptq_v2(const int32_t *qweight, uint8_t *codes, int64_t K, int64_t N);
 
+/* Streaming-read probe, a measurement aid beside the linear (the pages ask
+ * for achieved HBM bandwidth against peak for decode; this gives the
+ * attainable read rate on the device, measured with a plain kernel):
+ * reads `bytes` bytes at `data` once with 16-byte loads spread over the
+ * whole device.
+ *   data   : device pointer, 16-byte aligned; bytes > 0, bytes % 16 == 0
+ *   sink   : device pointer to 4 writable bytes, 4-byte aligned (written
+ *            only when the XOR of the words one thread read equals a fixed
+ *            constant; its contents mean nothing)
+ *   stream : hipStream_t to enqueue on (0 = null stream)
+ * Returns W4A16_ERR_SHAPE, _NULL, _ALIGN, _DEVICE or _LAUNCH on failure,
+ * before any HIP call for the first three. */
+int w4a16_read_probe(const void *data, int64_t bytes, void *sink, void *stream);
+
 /* Static, human-readable name of a status code (never null). */
 const char *w4a16_status_string(int status);
 

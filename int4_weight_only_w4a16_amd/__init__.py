@@ -7,7 +7,7 @@ not a gfx950, calls raise.
 
 Names match the C ABI in ``include/w4a16.h``:
   w4a16_linear, w4a16_linear_ex, pack_gptq_v2, unpack_gptq_v2,
-  w4a16_status_string
+  w4a16_status_string, and the measurement aid w4a16_read_probe
 plus ``linear`` (allocates y with torch, then calls w4a16_linear_ex).
 """
 
@@ -38,7 +38,7 @@ W4A16_KERNEL_DECODE = 1
 W4A16_KERNEL_PREFILL = 2
 
 EXPORTS = ("w4a16_linear", "w4a16_linear_ex", "pack_gptq_v2", "unpack_gptq_v2",
-           "w4a16_status_string")
+           "w4a16_read_probe", "w4a16_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -68,6 +68,8 @@ def load_library() -> ctypes.CDLL:
     lib.pack_gptq_v2.restype = i32
     lib.unpack_gptq_v2.argtypes = [p, p, i64, i64]
     lib.unpack_gptq_v2.restype = i32
+    lib.w4a16_read_probe.argtypes = [p, i64, p, p]
+    lib.w4a16_read_probe.restype = i32
     lib.w4a16_status_string.argtypes = [i32]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -113,6 +115,15 @@ def w4a16_linear(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
                  stream=None) -> None:
     """Same as the C ``w4a16_linear`` (kernel chosen by M)."""
     w4a16_linear_ex(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO)
+
+
+def w4a16_read_probe(data, nbytes: int, sink, stream=None) -> None:
+    """Enqueue the streaming-read probe over nbytes at data (a measurement
+    aid: the attainable HBM read rate); raises W4A16Error on a nonzero status."""
+    st = load_library().w4a16_read_probe(_addr(data), int(nbytes), _addr(sink),
+                                         _stream_handle(stream))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_read_probe")
 
 
 def pack_gptq_v2(codes: np.ndarray) -> np.ndarray:

@@ -187,6 +187,18 @@ extern "C" int unpack_gptq_v2(const int32_t *qweight, uint8_t *codes, int64_t K,
     return W4A16_OK;
 }
 
+extern "C" int w4a16_read_probe(const void *data, int64_t bytes, void *sink, void *stream) {
+    if (bytes <= 0 || bytes % 16 != 0) return W4A16_ERR_SHAPE;
+    if (!data || !sink) return W4A16_ERR_NULL;
+    if (!aligned16(data) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return W4A16_ERR_ALIGN;
+    int num_cus = 0;
+    size_t max_lds = 0;
+    if (usable_device(&num_cus, &max_lds) < 0) return W4A16_ERR_DEVICE;
+    const hipError_t e = w4a16::launch_read_probe(data, bytes, sink,
+                                                  reinterpret_cast<hipStream_t>(stream), num_cus);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
 extern "C" const char *w4a16_status_string(int status) {
     switch (status) {
         case W4A16_OK: return "ok";

@@ -36,4 +36,8 @@ bool prefill_wants_workspace(const LinearArgs &a, int num_cus);
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                           int num_cus);
 
+// Streaming-read probe over `bytes` (a multiple of 16) at data.
+hipError_t launch_read_probe(const void *data, int64_t bytes, void *sink, hipStream_t stream,
+                             int num_cus);
+
 }  // namespace w4a16

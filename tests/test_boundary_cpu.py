@@ -127,3 +127,16 @@ def test_pack_rejects_bad_input(lib):
     assert lib.pack_gptq_v2(None, None, 8, 8) == w4.W4A16_ERR_NULL
     assert lib.unpack_gptq_v2(None, None, 8, 8) == w4.W4A16_ERR_NULL
     assert lib.unpack_gptq_v2(None, None, 7, 8) == w4.W4A16_ERR_SHAPE
+
+
+@pytest.mark.parametrize("data, nbytes, sink, status", [
+    (0x1000, 0, 0x2000, w4.W4A16_ERR_SHAPE),
+    (0x1000, -16, 0x2000, w4.W4A16_ERR_SHAPE),
+    (0x1000, 24, 0x2000, w4.W4A16_ERR_SHAPE),       # not a multiple of 16
+    (None, 64, 0x2000, w4.W4A16_ERR_NULL),
+    (0x1000, 64, None, w4.W4A16_ERR_NULL),
+    (0x1008, 64, 0x2000, w4.W4A16_ERR_ALIGN),
+    (0x1000, 64, 0x2002, w4.W4A16_ERR_ALIGN),
+])
+def test_read_probe_rejects_bad_arguments_before_any_hip_call(lib, data, nbytes, sink, status):
+    assert lib.w4a16_read_probe(data, nbytes, sink, None) == status
