@@ -116,8 +116,8 @@ int unpack_gptq_v2(const int32_t *qweight, uint8_t *codes, int64_t K, int64_t N)
 /* Streaming-read probe, a measurement aid beside the linear (the pages ask
  * for achieved HBM bandwidth against peak for decode; this gives the
  * attainable read rate on the device, measured with a plain kernel):
- * reads `bytes` bytes at `data` once with 16-byte loads spread over the
- * whole device.
+ * reads `bytes` bytes at `data` once with 16-byte non-temporal loads spread
+ * over the whole device.
  *   data   : device pointer, 16-byte aligned; bytes > 0, bytes % 16 == 0
  *   sink   : device pointer to 4 writable bytes, 4-byte aligned (written
  *            only when the XOR of the words one thread read equals a fixed

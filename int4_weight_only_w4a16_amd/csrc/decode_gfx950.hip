@@ -184,7 +184,7 @@ __device__ __forceinline__ void decode_units(
     // issue side: unit index li of this wave (loads beyond n - 1 repeat the last unit)
     int li = 0;
     auto issue = [&](Stage<XLDS> &st) {
-        st.w = load_b128(qr, q_off);
+        st.w = load_b128_nt(qr, q_off);           // every weight word is read once
         if constexpr (!XLDS) {
             const int t = li < nA ? tA0 + li : li - nA;
             const uint32_t xo = (ragged && t == S - 1 && !x_tail_ok) ? kOOB : x_off;

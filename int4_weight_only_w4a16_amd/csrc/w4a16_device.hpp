@@ -36,6 +36,12 @@ __device__ __forceinline__ u4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t byte_
     return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// 16-byte load with the non-temporal hint (data read once, streamed past the
+// caches): cache policy bit 1 is "nt" on gfx950.
+__device__ __forceinline__ u4 load_b128_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
+}
+
 __device__ __forceinline__ u2 load_b64(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
