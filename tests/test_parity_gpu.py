@@ -186,6 +186,29 @@ def test_deterministic_bitwise(dev, kernel, M):
         assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
 
 
+@pytest.mark.parametrize("M,K,N,g", [
+    (1, 5120, 17408, 128),    # stream-K, nearly every tile split: exchange slots
+    (2, 5120, 17408, 128),
+    (4, 17408, 5120, 32),     # counter protocol
+    (16, 5120, 17408, 16),
+    (2048, 5120, 17408, 128),  # prefill with a split last round and its reduce pass
+])
+def test_deterministic_bitwise_full_size(dev, M, K, N, g):
+    """Repeated launches at full size give bit-identical y: every split tile and
+    split round is added in a fixed order, whichever contributor comes first."""
+    print(f"determinism: M={M} K={K} N={N} g={g}", flush=True)
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    G = 1 if g == -1 else K // g
+    q = torch.randint(-2**31, 2**31 - 1, (K // 8, N), dtype=torch.int32, generator=gen).to(dev)
+    s = (torch.rand((G, N), generator=gen) * 0.02 + 0.001).half().to(dev)
+    x = torch.randn((M, K), generator=gen).half().to(dev)
+    ys = [w4.linear(x, q, s, g) for _ in range(8)]
+    torch.cuda.synchronize()
+    base = ys[0].view(torch.int16)
+    for i, y in enumerate(ys[1:], 1):
+        assert torch.equal(y.view(torch.int16), base), f"launch {i} differs"
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 63, 64, 65, 127, 128, 129, 512])
 def test_dispatch_edges(dev, M):
     case = workloads.Case(f"edge_M{M}", M, 1024, 520, 128, 9)
