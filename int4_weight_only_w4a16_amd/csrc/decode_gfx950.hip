@@ -349,23 +349,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
 // Stream-K kernel: gridDim.x workgroups share the units evenly.
 //
 // Workspace for up to `capacity` workgroups (zero-filled once; every launch
-// leaves the slots and counters zero again).  The layout depends only on the
-// capacity, never on the grid of a launch, so launches of any grid size can
-// share it:
+// leaves the slots zero again).  The layout depends only on the capacity,
+// never on the grid of a launch, so launches of any grid size can share it:
 //   slots:    uint64[capacity][16][kCols/2] exchange slot per output column
 //                                           pair of a split tile (M <=
 //                                           kExchangeMaxM), indexed by the tile's
 //                                           later contributor; 0 when empty
-//   counters: int[capacity], padded to 256 bytes   arrivals at a split tile
-//                                           (larger M), indexed by its later
-//                                           contributor
 //   partials: float[capacity][2][16][kCols] a workgroup's sums for its first (0)
 //                                           and last (1) tile (larger M)
 
 // Split tiles of batches up to this size meet through per-element exchange
-// slots (one memory round trip); larger batches publish whole partials and
-// count arrivals (three round trips, but 16x fewer atomics than the slots
-// would need).
+// slots (one memory round trip at the end of the kernel); larger batches
+// store whole partials and a second kernel adds them (per-element atomics
+// would be 16x more at M = 16, and slow in bulk).
 constexpr int kExchangeMaxM = 2;
 
 // A slot holds two fp32 partials (adjacent columns), each XOR-ed with the bit
@@ -376,9 +372,6 @@ constexpr uint32_t kSlotKey = 0x7FBADBADu;
 __device__ __forceinline__ uint32_t slot_code(float v) {
     return (v != v ? 0x7FC00000u : __builtin_bit_cast(uint32_t, v)) ^ kSlotKey;
 }
-
-// s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima.
-constexpr unsigned kWaitVmcnt0 = 0x0F70u;
 
 struct StreamK {
     int U, G;
@@ -411,11 +404,10 @@ template <int WAVES, int D, int SCALE, bool XLDS>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
-    int group_steps, uint64_t *__restrict__ slots, int *__restrict__ counters,
+    int group_steps, uint64_t *__restrict__ slots,
     float *__restrict__ partials) {
     constexpr int SLOT = 16 * kCols;             // floats per partial slot
     __shared__ f4 red[2][WAVES][kNW][64];
-    __shared__ int last_arrival[2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -516,9 +508,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         return;
     }
 
-    // Larger batches: split tiles (at most the first and the last of the
-    // range) are published as whole partials with system-scope stores.
-    int split_tile[2] = {-1, -1};
+    // Larger batches: whole tiles are stored here; the partials of split
+    // tiles (at most the first and the last of the range) go to this
+    // workgroup's two partial slots, and decode_split_reduce_kernel, launched
+    // next on the same stream, adds them.
     for (int tau = b0; tau <= b1; ++tau) {
         const int ta = tau * S, tb = ta + S;
         float v[kNW] = {0.f, 0.f, 0.f, 0.f};
@@ -537,56 +530,36 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             if (row_ok && n < N) store_row4(y + (size_t)m * N + n, v);
             continue;
         }
-        const int slot = tau == b0 ? 0 : 1;
-        split_tile[slot] = tau;
-        float *mine = partials + ((size_t)g * 2 + slot) * SLOT;
-        if (row_ok) {
-#pragma unroll
-            for (int j = 0; j < kNW; ++j)
-                __hip_atomic_store(mine + m * kCols + c + j, v[j], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_SYSTEM);
-        }
+        float *mine = partials + ((size_t)g * 2 + (tau == b0 ? 0 : 1)) * SLOT;
+        if (row_ok) *reinterpret_cast<f4 *>(mine + m * kCols + c) = f4{v[0], v[1], v[2], v[3]};
     }
-    if (split_tile[0] < 0 && split_tile[1] < 0) return;
+}
 
-    // Once every wave's partial stores are complete, count this workgroup's
-    // arrival at each split tile (one round for both).
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (threadIdx.x < 2) {
-        const int tau = split_tile[threadIdx.x];
-        int last = 0;
-        if (tau >= 0) {
-            const int gf = sk.owner(tau * S), gl = sk.owner(tau * S + S - 1);
-            last = __hip_atomic_fetch_add(&counters[gl], 1, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_SYSTEM) == gl - gf;
-        }
-        last_arrival[threadIdx.x] = last;
-    }
-    __syncthreads();
-
-    // The last contributor of a split tile adds every partial in workgroup
-    // order, stores the tile and resets its counter.
+// Larger batches: adds the partials of every split tile of a stream-K launch
+// of G workgroups in workgroup order (fixed, so results are bit-reproducible)
+// and stores y.  One workgroup per tile; thread (m, q) handles row m and
+// columns 4q .. 4q+3 of the tile.  Tiles that lie whole inside one range
+// were stored by the stream-K kernel.
+__global__ __launch_bounds__(256) void decode_split_reduce_kernel(
+    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S, int G) {
+    constexpr int SLOT = 16 * kCols;
+    const int T = (N + kCols - 1) / kCols;
+    const StreamK sk{T * S, G};
+    const int tau = blockIdx.x;
+    const int gf = sk.owner(tau * S), gl = sk.owner(tau * S + S - 1);
+    if (gf == gl) return;
+    const int m = threadIdx.x >> 4, q = threadIdx.x & 15;
+    const int n = tau * kCols + kNW * q;
+    if (m >= M || n >= N) return;
+    float r[kNW] = {0.f, 0.f, 0.f, 0.f};
+    for (int h = gf; h <= gl; ++h) {
+        const int hs = tau == sk.begin(h) / S ? 0 : 1;
+        const f4 p = *reinterpret_cast<const f4 *>(partials + ((size_t)h * 2 + hs) * SLOT +
+                                                   m * kCols + kNW * q);
 #pragma unroll
-    for (int slot = 0; slot < 2; ++slot) {
-        const int tau = split_tile[slot];
-        if (tau < 0 || !last_arrival[slot]) continue;
-        const int gf = sk.owner(tau * S), gl = sk.owner(tau * S + S - 1);
-        float r[kNW] = {0.f, 0.f, 0.f, 0.f};
-        for (int h = gf; h <= gl; ++h) {
-            const int hs = tau == sk.begin(h) / S ? 0 : 1;
-            if (row_ok) {
-                const float *q = partials + ((size_t)h * 2 + hs) * SLOT + m * kCols + c;
-#pragma unroll
-                for (int j = 0; j < kNW; ++j)
-                    r[j] += __hip_atomic_load(q + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            }
-        }
-        const int n = tau * kCols + c;
-        if (row_ok && n < N) store_row4(y + (size_t)m * N + n, r);
-        if (threadIdx.x == 0)
-            __hip_atomic_store(&counters[gl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int j = 0; j < kNW; ++j) r[j] += p[j];
     }
+    store_row4(y + (size_t)m * N + n, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -602,13 +575,9 @@ constexpr int kDecWaves = W4A16_DECODE_WAVES;
 constexpr int kDecD = W4A16_DECODE_D;
 
 static size_t slots_bytes(int capacity) { return (size_t)capacity * 16 * (kCols / 2) * sizeof(uint64_t); }
-static size_t counters_bytes(int capacity) {
-    return ((size_t)capacity * sizeof(int) + 255) & ~(size_t)255;
-}
 
 size_t decode_workspace_bytes(int capacity) {
-    return slots_bytes(capacity) + counters_bytes(capacity) +
-           (size_t)capacity * 2 * 16 * kCols * sizeof(float);
+    return slots_bytes(capacity) + (size_t)capacity * 2 * 16 * kCols * sizeof(float);
 }
 
 // Stream-K grid, or 0 for the tiles kernel.  Every tile must have at most two
@@ -657,15 +626,21 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
     if (grid > 0) {
         char *ws = static_cast<char *>(workspace);
         uint64_t *slots = reinterpret_cast<uint64_t *>(ws);
-        int *counters = reinterpret_cast<int *>(ws + slots_bytes(capacity));
-        float *partials =
-            reinterpret_cast<float *>(ws + slots_bytes(capacity) + counters_bytes(capacity));
+        float *partials = reinterpret_cast<float *>(ws + slots_bytes(capacity));
         void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N,
-                        &group_steps, &slots, &counters, &partials};
-        return hipLaunchKernel(
+                        &group_steps, &slots, &partials};
+        hipError_t e = hipLaunchKernel(
             reinterpret_cast<const void *>(
                 &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS>),
             dim3(grid), block, args, dyn, stream);
+        // split tiles exist unless every range is exactly one tile (G = T)
+        if (e != hipSuccess || M <= kExchangeMaxM || grid == (N + kCols - 1) / kCols) return e;
+        const float *pc = partials;
+        int Sv = S, G = grid;
+        void *rargs[] = {&pc, &yp, (void *)&M, (void *)&N, &Sv, &G};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel),
+                               dim3((unsigned)((N + kCols - 1) / kCols)), dim3(256), rargs, 0,
+                               stream);
     }
     void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
     const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);
