@@ -35,9 +35,8 @@
  *     architecture and up to two workspaces per (device, stream), each
  *     allocated and zero-filled on the first call on that stream that needs
  *     it and kept until the process exits:
- *       decode: about 2.6 MiB on a 256-CU device (per CU: 16x32 exchange
- *         slots, left zeroed by every launch, and two 16x64 fp32 partial
- *         tiles, written before they are read);
+ *       decode: 1 MiB on a 256-CU device (per CU: 16x32 64-bit exchange
+ *         slots), left zeroed by every launch;
  *       prefill: 64 MiB on a 256-CU device (one 256x256 fp32 partial tile
  *         per CU), used by M > 128 when a last partial round of tiles is
  *         split along K.

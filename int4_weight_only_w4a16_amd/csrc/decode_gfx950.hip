@@ -30,9 +30,10 @@
 //    tile-major order; its waves split that range contiguously and keep
 //    their load rings running across tile boundaries.  A tile that lies
 //    wholly inside one workgroup is finished there; a tile split between
-//    workgroups is finished by whichever contributor arrives last, which
-//    adds every contributor's fp32 partial in workgroup order (a fixed
-//    order, so results are bit-reproducible) and resets the tile's counter.
+//    two workgroups is finished by whichever comes second, through one
+//    compare-and-swap per output column pair: it adds the other's fp32
+//    partial to its own (one add, so the result does not depend on the
+//    order of arrival).
 //  * When there are many more tiles than CUs the tiles kernel (one
 //    workgroup per tile, its waves splitting K) is balanced on its own and
 //    needs no workspace.
@@ -349,20 +350,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
 // Stream-K kernel: gridDim.x workgroups share the units evenly.
 //
 // Workspace for up to `capacity` workgroups (zero-filled once; every launch
-// leaves the slots zero again).  The layout depends only on the capacity,
-// never on the grid of a launch, so launches of any grid size can share it:
-//   slots:    uint64[capacity][16][kCols/2] exchange slot per output column
-//                                           pair of a split tile (M <=
-//                                           kExchangeMaxM), indexed by the tile's
-//                                           later contributor; 0 when empty
-//   partials: float[capacity][2][16][kCols] a workgroup's sums for its first (0)
-//                                           and last (1) tile (larger M)
-
-// Split tiles of batches up to this size meet through per-element exchange
-// slots (one memory round trip at the end of the kernel); larger batches
-// store whole partials and a second kernel adds them (per-element atomics
-// would be 16x more at M = 16, and slow in bulk).
-constexpr int kExchangeMaxM = 2;
+// leaves it zero again): uint64 slots[capacity][16][kCols/2], one exchange
+// slot per (row, output column pair) of a split tile, indexed by the tile's
+// later contributor; 0 when empty.  The layout depends only on the capacity,
+// never on the grid of a launch, so launches of any grid size share it.
 
 // A slot holds two fp32 partials (adjacent columns), each XOR-ed with the bit
 // pattern of a NaN; NaN partials are first replaced by the canonical NaN, so
@@ -404,9 +395,7 @@ template <int WAVES, int D, int SCALE, bool XLDS>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
-    int group_steps, uint64_t *__restrict__ slots,
-    float *__restrict__ partials) {
-    constexpr int SLOT = 16 * kCols;             // floats per partial slot
+    int group_steps, uint64_t *__restrict__ slots) {
     __shared__ f4 red[2][WAVES][kNW][64];
 
     const int lane = threadIdx.x & 63;
@@ -455,63 +444,14 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const int b0 = u0 / S, b1 = (u1 - 1) / S;
 
     // Fixed-order sum over the waves for every tile of this range; whole
-    // tiles are stored.  Small batches: a split tile has exactly two
-    // contributors (the host keeps every range at least one tile long, or
-    // makes each tile exactly two ranges), and they meet per output element
-    // in the tile's exchange slots with one system-scope compare-and-swap per
-    // column pair: the first deposits its partials, the second gets them back,
-    // adds its own (one fp32 add each, so the result does not depend on which
-    // one came first), stores y and empties the slot.  Each XCD has its own
-    // L2; only system scope is coherent across them.
-    if (M <= kExchangeMaxM) {
-        for (int tau = b0; tau <= b1; ++tau) {
-            const int ta = tau * S, tb = ta + S;
-            float v[kNW] = {0.f, 0.f, 0.f, 0.f};
-            for (int w = 0; w < WAVES; ++w) {
-                const int a0 = u0 + wave_share<WAVES>(u1 - u0, w);
-            const int a1 = u0 + wave_share<WAVES>(u1 - u0, w + 1);
-                if (a0 >= a1 || a1 <= ta || a0 >= tb) continue;
-                const int s = tau - a0 / S;
-                if (worker) {
-#pragma unroll
-                    for (int j = 0; j < kNW; ++j) v[j] += red[s][w][j][l][i];
-                }
-            }
-            const int n = tau * kCols + c;
-            if (!row_ok || n >= N) continue;
-            if (ta >= u0 && tb <= u1) {                 // the whole tile is here
-                store_row4(y + (size_t)m * N + n, v);
-                continue;
-            }
-            const int gl = sk.owner(tb - 1);           // the tile's later contributor
-            uint64_t *slot = slots + ((size_t)gl * 16 + m) * (kCols / 2) + c / 2;
-            uint64_t got[kNW / 2];
-#pragma unroll
-            for (int j = 0; j < kNW / 2; ++j) {
-                got[j] = 0;
-                const uint64_t mine = (uint64_t)slot_code(v[2 * j]) | ((uint64_t)slot_code(v[2 * j + 1]) << 32);
-                __hip_atomic_compare_exchange_strong(slot + j, &got[j], mine, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            }
-            // per column pair (the two contributors' exchanges may interleave):
-            // an empty slot means this one came first and deposited its values
-#pragma unroll
-            for (int j = 0; j < kNW / 2; ++j) {
-                if (got[j] == 0) continue;
-                const float r0 = __builtin_bit_cast(float, (uint32_t)got[j] ^ kSlotKey) + v[2 * j];
-                const float r1 = __builtin_bit_cast(float, (uint32_t)(got[j] >> 32) ^ kSlotKey) + v[2 * j + 1];
-                __hip_atomic_store(slot + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                const h2 h = {(_Float16)r0, (_Float16)r1};
-                *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n + 2 * j) = __builtin_bit_cast(uint32_t, h);
-            }
-        }
-        return;
-    }
-
-    // Larger batches: whole tiles are stored here; the partials of split
-    // tiles (at most the first and the last of the range) go to this
-    // workgroup's two partial slots, and decode_split_reduce_kernel, launched
-    // next on the same stream, adds them.
+    // tiles are stored.  A split tile has exactly two contributors (the host
+    // keeps every range at least one tile long, or makes each tile exactly
+    // two ranges), and they meet per output element in the tile's exchange
+    // slots with one system-scope compare-and-swap per column pair: the first
+    // deposits its partials, the second gets them back, adds its own (one
+    // fp32 add each, so the result does not depend on which one came first),
+    // stores y and empties the slot.  Each XCD has its own L2; only system
+    // scope is coherent across them.
     for (int tau = b0; tau <= b1; ++tau) {
         const int ta = tau * S, tb = ta + S;
         float v[kNW] = {0.f, 0.f, 0.f, 0.f};
@@ -526,40 +466,33 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             }
         }
         const int n = tau * kCols + c;
+        if (!row_ok || n >= N) continue;
         if (ta >= u0 && tb <= u1) {                 // the whole tile is here
-            if (row_ok && n < N) store_row4(y + (size_t)m * N + n, v);
+            store_row4(y + (size_t)m * N + n, v);
             continue;
         }
-        float *mine = partials + ((size_t)g * 2 + (tau == b0 ? 0 : 1)) * SLOT;
-        if (row_ok) *reinterpret_cast<f4 *>(mine + m * kCols + c) = f4{v[0], v[1], v[2], v[3]};
-    }
-}
-
-// Larger batches: adds the partials of every split tile of a stream-K launch
-// of G workgroups in workgroup order (fixed, so results are bit-reproducible)
-// and stores y.  One workgroup per tile; thread (m, q) handles row m and
-// columns 4q .. 4q+3 of the tile.  Tiles that lie whole inside one range
-// were stored by the stream-K kernel.
-__global__ __launch_bounds__(256) void decode_split_reduce_kernel(
-    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S, int G) {
-    constexpr int SLOT = 16 * kCols;
-    const int T = (N + kCols - 1) / kCols;
-    const StreamK sk{T * S, G};
-    const int tau = blockIdx.x;
-    const int gf = sk.owner(tau * S), gl = sk.owner(tau * S + S - 1);
-    if (gf == gl) return;
-    const int m = threadIdx.x >> 4, q = threadIdx.x & 15;
-    const int n = tau * kCols + kNW * q;
-    if (m >= M || n >= N) return;
-    float r[kNW] = {0.f, 0.f, 0.f, 0.f};
-    for (int h = gf; h <= gl; ++h) {
-        const int hs = tau == sk.begin(h) / S ? 0 : 1;
-        const f4 p = *reinterpret_cast<const f4 *>(partials + ((size_t)h * 2 + hs) * SLOT +
-                                                   m * kCols + kNW * q);
+        const int gl = sk.owner(tb - 1);           // the tile's later contributor
+        uint64_t *slot = slots + ((size_t)gl * 16 + m) * (kCols / 2) + c / 2;
+        uint64_t got[kNW / 2];
 #pragma unroll
-        for (int j = 0; j < kNW; ++j) r[j] += p[j];
+        for (int j = 0; j < kNW / 2; ++j) {
+            got[j] = 0;
+            const uint64_t mine = (uint64_t)slot_code(v[2 * j]) | ((uint64_t)slot_code(v[2 * j + 1]) << 32);
+            __hip_atomic_compare_exchange_strong(slot + j, &got[j], mine, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        // per column pair (the two contributors' exchanges may interleave):
+        // an empty slot means this one came first and deposited its values
+#pragma unroll
+        for (int j = 0; j < kNW / 2; ++j) {
+            if (got[j] == 0) continue;
+            const float r0 = __builtin_bit_cast(float, (uint32_t)got[j] ^ kSlotKey) + v[2 * j];
+            const float r1 = __builtin_bit_cast(float, (uint32_t)(got[j] >> 32) ^ kSlotKey) + v[2 * j + 1];
+            __hip_atomic_store(slot + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            const h2 h = {(_Float16)r0, (_Float16)r1};
+            *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n + 2 * j) = __builtin_bit_cast(uint32_t, h);
+        }
     }
-    store_row4(y + (size_t)m * N + n, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -574,10 +507,8 @@ __global__ __launch_bounds__(256) void decode_split_reduce_kernel(
 constexpr int kDecWaves = W4A16_DECODE_WAVES;
 constexpr int kDecD = W4A16_DECODE_D;
 
-static size_t slots_bytes(int capacity) { return (size_t)capacity * 16 * (kCols / 2) * sizeof(uint64_t); }
-
 size_t decode_workspace_bytes(int capacity) {
-    return slots_bytes(capacity) + (size_t)capacity * 2 * 16 * kCols * sizeof(float);
+    return (size_t)capacity * 16 * (kCols / 2) * sizeof(uint64_t);
 }
 
 // Stream-K grid, or 0 for the tiles kernel.  Every tile must have at most two
@@ -624,23 +555,13 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
     const dim3 block(kDecWaves * 64);
     const size_t dyn = XLDS ? (size_t)M * 32 * S * 2 + 16 : 0;
     if (grid > 0) {
-        char *ws = static_cast<char *>(workspace);
-        uint64_t *slots = reinterpret_cast<uint64_t *>(ws);
-        float *partials = reinterpret_cast<float *>(ws + slots_bytes(capacity));
+        uint64_t *slots = static_cast<uint64_t *>(workspace);
         void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N,
-                        &group_steps, &slots, &partials};
-        hipError_t e = hipLaunchKernel(
+                        &group_steps, &slots};
+        return hipLaunchKernel(
             reinterpret_cast<const void *>(
                 &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS>),
             dim3(grid), block, args, dyn, stream);
-        // split tiles exist unless every range is exactly one tile (G = T)
-        if (e != hipSuccess || M <= kExchangeMaxM || grid == (N + kCols - 1) / kCols) return e;
-        const float *pc = partials;
-        int Sv = S, G = grid;
-        void *rargs[] = {&pc, &yp, (void *)&M, (void *)&N, &Sv, &G};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel),
-                               dim3((unsigned)((N + kCols - 1) / kCols)), dim3(256), rargs, 0,
-                               stream);
     }
     void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
     const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);
