@@ -35,8 +35,9 @@
  *     architecture and up to two workspaces per (device, stream), each
  *     allocated and zero-filled on the first call on that stream that needs
  *     it and kept until the process exits:
- *       decode: 1 MiB on a 256-CU device (per CU: 16x32 64-bit exchange
- *         slots), left zeroed by every launch;
+ *       decode: 3 MiB on a 256-CU device (per CU: 16x32 64-bit exchange
+ *         slots, left zeroed by every launch, and two 16x64 fp32 partial
+ *         tiles, written before they are read);
  *       prefill: 64 MiB on a 256-CU device (one 256x256 fp32 partial tile
  *         per CU), used by M > 128 when a last partial round of tiles is
  *         split along K.

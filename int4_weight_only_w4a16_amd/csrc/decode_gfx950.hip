@@ -349,11 +349,15 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
 // ---------------------------------------------------------------------------
 // Stream-K kernel: gridDim.x workgroups share the units evenly.
 //
-// Workspace for up to `capacity` workgroups (zero-filled once; every launch
-// leaves it zero again): uint64 slots[capacity][16][kCols/2], one exchange
-// slot per (row, output column pair) of a split tile, indexed by the tile's
-// later contributor; 0 when empty.  The layout depends only on the capacity,
-// never on the grid of a launch, so launches of any grid size share it.
+// Workspace for up to `capacity` workgroups (zero-filled once).  The layout
+// depends only on the capacity, never on the grid of a launch, so launches
+// of any grid size share it:
+//   slots:    uint64[capacity][16][kCols/2] one exchange slot per (row,
+//             output column pair) of a split tile, indexed by the tile's
+//             later contributor; 0 when empty, and every launch leaves them 0
+//   partials: float[capacity][2][16][kCols] a workgroup's sums for its first
+//             (0) and last (1) tile, for launches whose tiles may have more
+//             than two contributors (written before they are read)
 
 // A slot holds two fp32 partials (adjacent columns), each XOR-ed with the bit
 // pattern of a NaN; NaN partials are first replaced by the canonical NaN, so
@@ -395,7 +399,8 @@ template <int WAVES, int D, int SCALE, bool XLDS>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
-    int group_steps, uint64_t *__restrict__ slots) {
+    int group_steps, uint64_t *__restrict__ slots, float *__restrict__ partials) {
+    constexpr int SLOT = 16 * kCols;             // floats per partial slot
     __shared__ f4 red[2][WAVES][kNW][64];
 
     const int lane = threadIdx.x & 63;
@@ -444,14 +449,17 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const int b0 = u0 / S, b1 = (u1 - 1) / S;
 
     // Fixed-order sum over the waves for every tile of this range; whole
-    // tiles are stored.  A split tile has exactly two contributors (the host
-    // keeps every range at least one tile long, or makes each tile exactly
-    // two ranges), and they meet per output element in the tile's exchange
-    // slots with one system-scope compare-and-swap per column pair: the first
-    // deposits its partials, the second gets them back, adds its own (one
-    // fp32 add each, so the result does not depend on which one came first),
-    // stores y and empties the slot.  Each XCD has its own L2; only system
-    // scope is coherent across them.
+    // tiles are stored.  Without `partials`, a split tile has exactly two
+    // contributors (the host keeps every range at least one tile long, or
+    // makes each tile exactly two ranges), and they meet per output element
+    // in the tile's exchange slots with one system-scope compare-and-swap per
+    // column pair: the first deposits its partials, the second gets them
+    // back, adds its own (one fp32 add each, so the result does not depend on
+    // which one came first), stores y and empties the slot.  Each XCD has its
+    // own L2; only system scope is coherent across them.  With `partials`
+    // (tiles with more contributors), split tiles go to this workgroup's two
+    // partial slots and decode_split_reduce_kernel, launched next on the same
+    // stream, adds them.
     for (int tau = b0; tau <= b1; ++tau) {
         const int ta = tau * S, tb = ta + S;
         float v[kNW] = {0.f, 0.f, 0.f, 0.f};
@@ -469,6 +477,11 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         if (!row_ok || n >= N) continue;
         if (ta >= u0 && tb <= u1) {                 // the whole tile is here
             store_row4(y + (size_t)m * N + n, v);
+            continue;
+        }
+        if (partials) {
+            float *mine = partials + ((size_t)g * 2 + (tau == b0 ? 0 : 1)) * SLOT;
+            *reinterpret_cast<f4 *>(mine + m * kCols + c) = f4{v[0], v[1], v[2], v[3]};
             continue;
         }
         const int gl = sk.owner(tb - 1);           // the tile's later contributor
@@ -495,6 +508,33 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     }
 }
 
+// Adds the partials of every split tile of a stream-K launch of G workgroups
+// that used partial slots, in workgroup order (fixed, so results are
+// bit-reproducible), and stores y.  One workgroup per tile; thread (m, q)
+// handles row m and columns 4q .. 4q+3 of the tile.  Tiles that lie whole
+// inside one range were stored by the stream-K kernel.
+__global__ __launch_bounds__(256) void decode_split_reduce_kernel(
+    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S, int G) {
+    constexpr int SLOT = 16 * kCols;
+    const int T = (N + kCols - 1) / kCols;
+    const StreamK sk{T * S, G};
+    const int tau = blockIdx.x;
+    const int gf = sk.owner(tau * S), gl = sk.owner(tau * S + S - 1);
+    if (gf == gl) return;
+    const int m = threadIdx.x >> 4, q = threadIdx.x & 15;
+    const int n = tau * kCols + kNW * q;
+    if (m >= M || n >= N) return;
+    float r[kNW] = {0.f, 0.f, 0.f, 0.f};
+    for (int h = gf; h <= gl; ++h) {
+        const int hs = tau == sk.begin(h) / S ? 0 : 1;
+        const f4 p = *reinterpret_cast<const f4 *>(partials + ((size_t)h * 2 + hs) * SLOT +
+                                                   m * kCols + kNW * q);
+#pragma unroll
+        for (int j = 0; j < kNW; ++j) r[j] += p[j];
+    }
+    store_row4(y + (size_t)m * N + n, r);
+}
+
 // ---------------------------------------------------------------------------
 
 #ifndef W4A16_DECODE_WAVES
@@ -507,9 +547,23 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
 constexpr int kDecWaves = W4A16_DECODE_WAVES;
 constexpr int kDecD = W4A16_DECODE_D;
 
+static size_t slots_bytes(int capacity) { return (size_t)capacity * 16 * (kCols / 2) * sizeof(uint64_t); }
+
 size_t decode_workspace_bytes(int capacity) {
-    return (size_t)capacity * 16 * (kCols / 2) * sizeof(uint64_t);
+    return slots_bytes(capacity) + (size_t)capacity * 2 * 16 * kCols * sizeof(float);
 }
+
+// Stream-K launches whose tiles may have more than two contributors (more
+// ranges than 2T) use partial slots and the reduce kernel; the others use the
+// exchange slots.
+static bool uses_partials(int grid, int T) { return grid > 2 * T; }
+
+// With fewer than half as many tiles as CUs, batches above two rows spread
+// over every CU (a tile then has several contributors) when K is long: the
+// work per range is then large enough that the extra CUs outweigh the second
+// kernel.  Measured on N = 5120 (80 tiles): a gain from S = 432 at M = 4 and
+// from S = 256 at M = 16, a loss at S = 256, M = 4 and none at S = 128.
+static bool spread_wide(int64_t M, int64_t S) { return M > 2 && (S >= 384 || (M >= 8 && S >= 256)); }
 
 // Stream-K grid, or 0 for the tiles kernel.  Every tile must have at most two
 // contributors: either every range holds at least one tile (G <= T), or
@@ -527,6 +581,8 @@ int decode_streamk_grid(const LinearArgs &a, int num_cus) {
                 if (wave_share<kDecWaves>(n, w + 1) - wave_share<kDecWaves>(n, w) > S) return 0;
         return num_cus;
     }
+    // G > 2T: partial slots (a tile may have more than two contributors)
+    if (2 * T < num_cus && spread_wide(a.M, S)) return num_cus;
     if (2 * T <= num_cus && S >= 2) return (int)(2 * T);
     return (int)T;
 }
@@ -555,13 +611,23 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
     const dim3 block(kDecWaves * 64);
     const size_t dyn = XLDS ? (size_t)M * 32 * S * 2 + 16 : 0;
     if (grid > 0) {
-        uint64_t *slots = static_cast<uint64_t *>(workspace);
+        char *ws = static_cast<char *>(workspace);
+        uint64_t *slots = reinterpret_cast<uint64_t *>(ws);
+        const int T = (N + kCols - 1) / kCols;
+        const bool part = uses_partials(grid, T);
+        float *partials = part ? reinterpret_cast<float *>(ws + slots_bytes(capacity)) : nullptr;
         void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N,
-                        &group_steps, &slots};
-        return hipLaunchKernel(
+                        &group_steps, &slots, &partials};
+        hipError_t e = hipLaunchKernel(
             reinterpret_cast<const void *>(
                 &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS>),
             dim3(grid), block, args, dyn, stream);
+        if (e != hipSuccess || !part) return e;
+        const float *pc = partials;
+        int Sv = S, G = grid;
+        void *rargs[] = {&pc, &yp, (void *)&M, (void *)&N, &Sv, &G};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel),
+                               dim3((unsigned)T), dim3(256), rargs, 0, stream);
     }
     void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
     const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);

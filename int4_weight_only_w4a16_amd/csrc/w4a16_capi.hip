@@ -81,7 +81,7 @@ int usable_device(int *num_cus, size_t *max_lds) {
 // so the kernels never share one concurrently.  Created on the first call on
 // a stream that needs it (not while the stream is being captured into a
 // graph), zero-filled in stream order, kept until the process exits.
-//   kind 0: decode stream-K (exchange slots, 1 MiB)
+//   kind 0: decode stream-K (exchange slots and partial tiles, 3 MiB)
 //   kind 1: prefill split tail (one 256 x 256 fp32 partial per CU, 64 MiB)
 std::mutex g_ws_mu;
 std::map<std::tuple<int, uintptr_t, int>, std::pair<void *, size_t>> g_ws;

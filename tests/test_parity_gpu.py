@@ -438,6 +438,21 @@ def test_decode_split_tiles_exchange(dev, M):
             assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
 
 
+@pytest.mark.parametrize("M", [3, 5, 16])
+def test_decode_wide_partials_ragged(dev, M):
+    """Few tiles and long K with M > 2: every CU takes a range, a tile has up
+    to many contributors, and a second kernel adds their partials; ragged K
+    (the last 32-deep step half inside K) and ragged N."""
+    case = workloads.Case(f"wide_{M}", M, 16400, 1032, 16, 45, scales="loguniform")
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    y_ref = oracle.linear(inp.x, q_o, inp.scales, 16)
+    runs = [_run(inp, q_dev, s_dev, 16, dev, DEC) for _ in range(3)]
+    check_parity(runs[0], y_ref, f"wide M={M}")
+    for r in runs[1:]:
+        assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
+
+
 def test_prefill_split_tail_ragged(dev):
     """A last partial round of 256 x 256 tiles split along K (on a 256-CU
     device: 272 tiles, the last 16 split in two, the second chunk ending in a
