@@ -484,7 +484,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             *reinterpret_cast<f4 *>(mine + m * kCols + c) = f4{v[0], v[1], v[2], v[3]};
             continue;
         }
-        const int gl = sk.owner(tb - 1);           // the tile's later contributor
+        // the tile's later contributor: with two contributors, this workgroup
+        // if the tile ends inside its range, else the next one
+        const int gl = tb <= u1 ? g : g + 1;
         uint64_t *slot = slots + ((size_t)gl * 16 + m) * (kCols / 2) + c / 2;
         uint64_t got[kNW / 2];
 #pragma unroll
