@@ -368,12 +368,15 @@ __device__ __forceinline__ uint32_t slot_code(float v) {
     return (v != v ? 0x7FC00000u : __builtin_bit_cast(uint32_t, v)) ^ kSlotKey;
 }
 
+// Stream-K ranges in 32-bit arithmetic: the host keeps U * G < 2^32.
 struct StreamK {
     int U, G;
-    __device__ __forceinline__ int begin(int g) const { return (int)((int64_t)U * g / G); }
+    __device__ __forceinline__ int begin(int g) const {
+        return (int)((uint32_t)U * (uint32_t)g / (uint32_t)G);
+    }
     // workgroup whose range holds unit u
     __device__ __forceinline__ int owner(int u) const {
-        int g = (int)((int64_t)u * G / U);
+        int g = (int)((uint32_t)u * (uint32_t)G / (uint32_t)U);
         while (g + 1 < G && begin(g + 1) <= u) ++g;
         while (g > 0 && begin(g) > u) --g;
         return g;
@@ -460,14 +463,21 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     // (tiles with more contributors), split tiles go to this workgroup's two
     // partial slots and decode_split_reduce_kernel, launched next on the same
     // stream, adds them.
+    // every wave's range and first tile, once
+    int wa0[WAVES], wa1[WAVES], wt0[WAVES];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        wa0[w] = u0 + wave_share<WAVES>(u1 - u0, w);
+        wa1[w] = u0 + wave_share<WAVES>(u1 - u0, w + 1);
+        wt0[w] = wa0[w] / S;
+    }
     for (int tau = b0; tau <= b1; ++tau) {
         const int ta = tau * S, tb = ta + S;
         float v[kNW] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            const int a0 = u0 + wave_share<WAVES>(u1 - u0, w);
-            const int a1 = u0 + wave_share<WAVES>(u1 - u0, w + 1);
-            if (a0 >= a1 || a1 <= ta || a0 >= tb) continue;
-            const int s = tau - a0 / S;
+            if (wa0[w] >= wa1[w] || wa1[w] <= ta || wa0[w] >= tb) continue;
+            const int s = tau - wt0[w];
             if (worker) {
 #pragma unroll
                 for (int j = 0; j < kNW; ++j) v[j] += red[s][w][j][l][i];
@@ -573,6 +583,8 @@ static bool spread_wide(int64_t M, int64_t S) { return M > 2 && (S >= 384 || (M 
 int decode_streamk_grid(const LinearArgs &a, int num_cus) {
     const int64_t S = (a.K + 31) / 32;
     const int64_t T = (a.N + kCols - 1) / kCols;
+    // the kernels compute ranges in 32-bit arithmetic (units times grid)
+    if (T * S * (int64_t)num_cus >= ((int64_t)1 << 32)) return 0;
     if (T >= num_cus) {
         // every wave's share of a range must be at most S units, so that it
         // meets at most two tiles
