@@ -404,7 +404,14 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
     int group_steps, uint64_t *__restrict__ slots, float *__restrict__ partials) {
     constexpr int SLOT = 16 * kCols;             // floats per partial slot
-    __shared__ f4 red[2][WAVES][kNW][64];
+    // Wave partials: block s*WAVES + w (256 f4: [lane][i]) holds wave w's
+    // sums of its segment s, row i of the lane's quad, its four columns
+    // together (one 16-byte read back); block 2*WAVES holds -0.0, which
+    // leaves any fp32 sum unchanged when added (the stand-in for a wave that
+    // has no part of a tile, so the reduction reads without branches).
+    constexpr int kZeroBlock = 2 * WAVES;
+    __shared__ f4 red[(2 * WAVES + 1) * 256];
+    __shared__ int wtile[WAVES][2];              // each wave's first and last tile
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -430,7 +437,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         [&](int slot, const f4(&acc)[kNW]) {
             if (slot > 1) return;   // cannot happen: ranges hold <= S units
 #pragma unroll
-            for (int j = 0; j < kNW; ++j) red[slot][wave][j][lane] = acc[j];
+            for (int r = 0; r < 4; ++r)
+                red[(slot * WAVES + wave) * 256 + lane * 4 + r] =
+                    f4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
         },
         [&]() -> uint32_t {
             if constexpr (XLDS) {
@@ -440,6 +449,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             }
             return 0u;
         });
+    // tiles of the range and of this wave's share (last < first: no units),
+    // worked out once the wave's loads are done and kept before the barrier
+    int b0 = u0 / S, b1 = (u1 - 1) / S;
+    {
+        const int wf = w0 / S;
+        const int wl = w1 > w0 ? (w1 - 1) / S : wf - 1;
+        if (lane == 0) {
+            wtile[wave][0] = wf;
+            wtile[wave][1] = wl;
+        }
+    }
+    if (threadIdx.x < 256) red[kZeroBlock * 256 + threadIdx.x] = f4{-0.f, -0.f, -0.f, -0.f};
+    asm volatile("" : "+s"(b0), "+s"(b1));
     __syncthreads();
     if (u0 >= u1) return;
 
@@ -448,8 +470,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const bool worker = threadIdx.x < 256;          // one (lane, row-in-quad) pair each
     const int m = 4 * (l >> 4) + i;
     const int c = kNW * (l & 15);
-    const bool row_ok = worker && m < M;
-    const int b0 = u0 / S, b1 = (u1 - 1) / S;
+    if (!worker || m >= M) return;                  // no barrier follows
 
     // Fixed-order sum over the waves for every tile of this range; whole
     // tiles are stored.  Without `partials`, a split tile has exactly two
@@ -463,28 +484,30 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     // (tiles with more contributors), split tiles go to this workgroup's two
     // partial slots and decode_split_reduce_kernel, launched next on the same
     // stream, adds them.
-    // every wave's range and first tile, once
-    int wa0[WAVES], wa1[WAVES], wt0[WAVES];
+    int tf[WAVES], tl[WAVES];
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
-        wa0[w] = u0 + wave_share<WAVES>(u1 - u0, w);
-        wa1[w] = u0 + wave_share<WAVES>(u1 - u0, w + 1);
-        wt0[w] = wa0[w] / S;
+        tf[w] = wtile[w][0];
+        tl[w] = wtile[w][1];
     }
     for (int tau = b0; tau <= b1; ++tau) {
         const int ta = tau * S, tb = ta + S;
+        // every wave's part of tile tau (its segment tau - tf, or -0.0),
+        // added in wave order; the reads are unconditional and issue together
+        f4 rw[WAVES];
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const int blk = tf[w] <= tau && tau <= tl[w] ? (tau - tf[w]) * WAVES + w : kZeroBlock;
+            rw[w] = red[blk * 256 + l * 4 + i];
+        }
         float v[kNW] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            if (wa0[w] >= wa1[w] || wa1[w] <= ta || wa0[w] >= tb) continue;
-            const int s = tau - wt0[w];
-            if (worker) {
 #pragma unroll
-                for (int j = 0; j < kNW; ++j) v[j] += red[s][w][j][l][i];
-            }
+            for (int j = 0; j < kNW; ++j) v[j] += rw[w][j];
         }
         const int n = tau * kCols + c;
-        if (!row_ok || n >= N) continue;
+        if (n >= N) continue;
         if (ta >= u0 && tb <= u1) {                 // the whole tile is here
             store_row4(y + (size_t)m * N + n, v);
             continue;
