@@ -465,12 +465,18 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     __syncthreads();
     if (u0 >= u1) return;
 
+    // thread: (tile phase h, row i of the lane's quad, lane l); the WAVES/4
+    // groups of four waves take turns over the tiles of the range, so a
+    // range with two split tiles works on both (and waits for both
+    // exchanges) at the same time
+    static_assert(WAVES % 4 == 0, "the epilogue takes groups of four waves");
+    constexpr int kPhases = WAVES / 4;
     const int l = threadIdx.x & 63;
     const int i = (threadIdx.x >> 6) & 3;
-    const bool worker = threadIdx.x < 256;          // one (lane, row-in-quad) pair each
+    const int h = threadIdx.x >> 8;
     const int m = 4 * (l >> 4) + i;
     const int c = kNW * (l & 15);
-    if (!worker || m >= M) return;                  // no barrier follows
+    if (m >= M) return;                             // no barrier follows
 
     // Fixed-order sum over the waves for every tile of this range; whole
     // tiles are stored.  Without `partials`, a split tile has exactly two
@@ -490,7 +496,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         tf[w] = wtile[w][0];
         tl[w] = wtile[w][1];
     }
-    for (int tau = b0; tau <= b1; ++tau) {
+    for (int tau = b0 + h; tau <= b1; tau += kPhases) {
         const int ta = tau * S, tb = ta + S;
         // every wave's part of tile tau (its segment tau - tf, or -0.0),
         // added in wave order; the reads are unconditional and issue together
