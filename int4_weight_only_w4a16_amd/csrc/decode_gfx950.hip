@@ -595,9 +595,13 @@ size_t decode_workspace_bytes(int capacity) {
 }
 
 // Stream-K launches whose tiles may have more than two contributors (more
-// ranges than 2T) use partial slots and the reduce kernel; the others use the
-// exchange slots.
-static bool uses_partials(int grid, int T) { return grid > 2 * T; }
+// ranges than 2T) use partial slots and the reduce kernel; so do batches of
+// 15 or 16 rows, where the exchange's compare-and-swaps (one per row and
+// column pair) cost more than the second kernel (measured at M = 16: -0.7
+// us on K = 5120, N = 17408 and -1.5 us on N = 27648; at M = 12 +0.25 us).
+// The other launches use the exchange slots.
+constexpr int kPartialsMinM = 15;
+static bool uses_partials(int grid, int T, int M) { return grid > 2 * T || M >= kPartialsMinM; }
 
 // With fewer than half as many tiles as CUs, batches above two rows spread
 // over every CU (a tile then has several contributors) when K is long: the
@@ -657,7 +661,7 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
         char *ws = static_cast<char *>(workspace);
         uint64_t *slots = reinterpret_cast<uint64_t *>(ws);
         const int T = (N + kCols - 1) / kCols;
-        const bool part = uses_partials(grid, T);
+        const bool part = uses_partials(grid, T, M);
         float *partials = part ? reinterpret_cast<float *>(ws + slots_bytes(capacity)) : nullptr;
         void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N,
                         &group_steps, &slots, &partials};

@@ -423,10 +423,11 @@ def test_decode_after_other_launches(dev):
             check_parity(y.cpu().numpy(), y_ref, f"{c.name} after other launches, rep {rep}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 8, 14, 15, 16])
 def test_decode_split_tiles_exchange(dev, M):
     """Bench-like widths: most tiles are split between two workgroups, which
-    meet per output column pair in an exchange slot, for every M <= 16."""
+    meet per output column pair in an exchange slot (M <= 14), or leave
+    partial tiles that a second kernel adds (M = 15, 16)."""
     for K, N, g in ((5120, 17408, 128), (17408, 5120, 32)):
         case = workloads.Case(f"split_{M}_{K}_{N}", M, K, N, g, 41, scales="loguniform")
         inp = workloads.generate(case)
