@@ -46,6 +46,21 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
+_ACTS = {"f16": 0, "bf16": 1}
+
+
+def _act_bits(x: np.ndarray, act: str) -> np.ndarray:
+    """Activations as contiguous uint16 bit patterns: fp16 values for "f16",
+    bfloat16 bit patterns (given as uint16) for "bf16"."""
+    if act == "f16":
+        return np.ascontiguousarray(x, dtype=np.float16).view(np.uint16)
+    if act == "bf16":
+        if x.dtype != np.uint16:
+            raise TypeError("bf16 activations are passed as uint16 bit patterns")
+        return np.ascontiguousarray(x)
+    raise ValueError(f"unknown activation type {act!r}")
+
+
 def _check(rc: int, what: str) -> None:
     if rc != 0:
         raise ValueError(f"oracle {what}: invalid arguments (rc={rc})")
@@ -62,8 +77,12 @@ class Oracle:
         lib.oracle_dequant.argtypes = [p, p, i64, i64, i64, p]
         lib.oracle_linear.argtypes = [p, p, p, i64, i64, i64, i64, p]
         lib.oracle_linear_at.argtypes = [p, p, p, i64, i64, i64, i64, p, p, i64, p]
+        i32 = ctypes.c_int
+        lib.oracle_linear_ex.argtypes = [p, i32, i32, p, p, i64, i64, i64, i64, p]
+        lib.oracle_linear_at_ex.argtypes = [p, i32, i32, p, p, i64, i64, i64, i64, p, p, i64, p]
         for f in (lib.oracle_unpack, lib.oracle_pack, lib.oracle_dequant,
-                  lib.oracle_linear, lib.oracle_linear_at):
+                  lib.oracle_linear, lib.oracle_linear_at, lib.oracle_linear_ex,
+                  lib.oracle_linear_at_ex):
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -99,36 +118,51 @@ class Oracle:
         return out
 
     def linear(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
-               group_size: int) -> np.ndarray:
-        """y [M, N] float64 = x [M, K] fp16 . dequant(qweight, scales)."""
-        x = np.ascontiguousarray(x, dtype=np.float16)
+               group_size: int, act: str = "f16", absval: bool = False) -> np.ndarray:
+        """y [M, N] float64 = x [M, K] . dequant(qweight, scales).
+
+        act "f16": x is fp16; act "bf16": x holds bfloat16 bit patterns (uint16).
+        absval: return sum_k |x| * |w| instead (the error-bound magnitude)."""
+        xb = _act_bits(x, act)
         qweight = np.ascontiguousarray(qweight, dtype=np.int32)
         scales = np.ascontiguousarray(scales, dtype=np.float16)
-        M, K = x.shape
+        M, K = xb.shape
         N = qweight.shape[1]
         if qweight.shape[0] * 8 != K:
             raise ValueError("qweight rows must be K/8")
         y = np.empty((M, N), dtype=np.float64)
-        _check(self.lib.oracle_linear(_ptr(x.view(np.uint16)), _ptr(qweight),
-                                      _ptr(scales.view(np.uint16)), M, K, N, group_size,
-                                      _ptr(y)), "linear")
+        if act == "f16" and not absval:
+            rc = self.lib.oracle_linear(_ptr(xb), _ptr(qweight), _ptr(scales.view(np.uint16)),
+                                        M, K, N, group_size, _ptr(y))
+        else:
+            rc = self.lib.oracle_linear_ex(_ptr(xb), _ACTS[act], int(absval), _ptr(qweight),
+                                           _ptr(scales.view(np.uint16)), M, K, N, group_size,
+                                           _ptr(y))
+        _check(rc, "linear")
         return y
 
     def linear_at(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
-                  group_size: int, ms: np.ndarray, ns: np.ndarray) -> np.ndarray:
-        """y[ms[i], ns[i]] for sampled outputs, each computed from the definition."""
-        x = np.ascontiguousarray(x, dtype=np.float16)
+                  group_size: int, ms: np.ndarray, ns: np.ndarray, act: str = "f16",
+                  absval: bool = False) -> np.ndarray:
+        """y[ms[i], ns[i]] for sampled outputs, each computed from the definition
+        (act and absval as in linear)."""
+        xb = _act_bits(x, act)
         qweight = np.ascontiguousarray(qweight, dtype=np.int32)
         scales = np.ascontiguousarray(scales, dtype=np.float16)
         ms = np.ascontiguousarray(ms, dtype=np.int64)
         ns = np.ascontiguousarray(ns, dtype=np.int64)
-        M, K = x.shape
+        M, K = xb.shape
         N = qweight.shape[1]
         out = np.empty(ms.shape[0], dtype=np.float64)
-        _check(self.lib.oracle_linear_at(_ptr(x.view(np.uint16)), _ptr(qweight),
-                                         _ptr(scales.view(np.uint16)), M, K, N, group_size,
-                                         _ptr(ms), _ptr(ns), ms.shape[0], _ptr(out)),
-               "linear_at")
+        if act == "f16" and not absval:
+            rc = self.lib.oracle_linear_at(_ptr(xb), _ptr(qweight), _ptr(scales.view(np.uint16)),
+                                           M, K, N, group_size, _ptr(ms), _ptr(ns), ms.shape[0],
+                                           _ptr(out))
+        else:
+            rc = self.lib.oracle_linear_at_ex(_ptr(xb), _ACTS[act], int(absval), _ptr(qweight),
+                                              _ptr(scales.view(np.uint16)), M, K, N, group_size,
+                                              _ptr(ms), _ptr(ns), ms.shape[0], _ptr(out))
+        _check(rc, "linear_at")
         return out
 
 
@@ -161,9 +195,9 @@ def dequant(qweight, scales, group_size):
     return default().dequant(qweight, scales, group_size)
 
 
-def linear(x, qweight, scales, group_size):
-    return default().linear(x, qweight, scales, group_size)
+def linear(x, qweight, scales, group_size, act="f16", absval=False):
+    return default().linear(x, qweight, scales, group_size, act, absval)
 
 
-def linear_at(x, qweight, scales, group_size, ms, ns):
-    return default().linear_at(x, qweight, scales, group_size, ms, ns)
+def linear_at(x, qweight, scales, group_size, ms, ns, act="f16", absval=False):
+    return default().linear_at(x, qweight, scales, group_size, ms, ns, act, absval)

@@ -31,6 +31,16 @@
  * implicit zero point of 8 (the GPTQ_V2 layout of the benchmark spec).
  *
  * The result y is returned in float64 and is never rounded to fp16.
+ *
+ * bfloat16 activations (oracle_linear_ex / oracle_linear_at_ex with act = 1):
+ * the same definition with x given as bfloat16 bit patterns (1 sign, 8
+ * exponent, 7 fraction bits), decoded field by field below; scales stay
+ * fp16.  The pages serve this checkpoint with bfloat16 activations
+ * ("Qwen3.8-27B-GPTQ-Int4" model card, "4. Deployment": the verified serving
+ * command runs with the bfloat16 dtype), while the GPTQ-Pro fork keeps native
+ * BF16 outside its own kernels ("GPTQ-Pro" README, "Runtime contract").
+ * With absval = 1 the same loops return sum_k |x[m,k]| * |w[k,n]| instead, the
+ * magnitude that bounds the rounding error of any evaluation order.
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math).  OpenMP only
  * splits rows m and column blocks of n, never the sum over k.
  */
@@ -60,6 +70,33 @@ static double half_to_double(uint16_t h) {
         v = ldexp((double)(man | 0x400), exp - 25);  /* (1.man) * 2^(exp-15) */
     }
     return sign ? -v : v;
+}
+
+/* bfloat16 bits -> double, decoded field by field: 1 sign bit, 8 exponent
+ * bits (bias 127), 7 fraction bits. */
+static double bf16_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int exp = (h >> 7) & 0xFF;
+    int man = h & 0x7F;
+    double v;
+    if (exp == 0) {
+        v = ldexp((double)man, -133);                /* subnormal or zero */
+    } else if (exp == 255) {
+        v = man ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(man | 0x80), exp - 134);  /* (1.man) * 2^(exp-127) */
+    }
+    return sign ? -v : v;
+}
+
+/* An activation's bits -> double: act 0 is fp16, act 1 bfloat16. */
+static double act_to_double(uint16_t h, int act) {
+    return act ? bf16_to_double(h) : half_to_double(h);
+}
+
+/* One product term, or its magnitude. */
+static inline double term(double xk, double w, int absval) {
+    return absval ? fabs(xk) * fabs(w) : xk * w;
 }
 
 static int group_ok(int64_t K, int64_t g) {
@@ -142,9 +179,10 @@ int oracle_dequant(const int32_t *qweight, const uint16_t *scales, int64_t K, in
  * fp16 bit patterns.  The dequantised weight is built once as fp32 and reused
  * for every row; the loop runs m -> k -> n with a row of fp64 accumulators, so
  * every output still adds its K products in ascending k. */
-int oracle_linear(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
-                  int64_t M, int64_t K, int64_t N, int64_t g, double *y) {
-    if (!shape_ok(M, K, N) || !group_ok(K, g)) return OR_ERR_ARG;
+static int linear_impl(const uint16_t *x, int act, int absval, const int32_t *qweight,
+                       const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
+                       double *y) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || (act != 0 && act != 1)) return OR_ERR_ARG;
     if (M == 0) return OR_OK;
     if (!x || !qweight || !scales || !y) return OR_ERR_ARG;
     float *W = (float *)malloc((size_t)K * (size_t)N * sizeof(float));
@@ -159,9 +197,9 @@ int oracle_linear(const uint16_t *x, const int32_t *qweight, const uint16_t *sca
             double acc[256];
             for (int64_t n = n0; n < n1; ++n) acc[n - n0] = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                double xk = half_to_double(x[m * K + k]);
+                double xk = act_to_double(x[m * K + k], act);
                 const float *wrow = W + k * N;
-                for (int64_t n = n0; n < n1; ++n) acc[n - n0] += xk * (double)wrow[n];
+                for (int64_t n = n0; n < n1; ++n) acc[n - n0] += term(xk, (double)wrow[n], absval);
             }
             for (int64_t n = n0; n < n1; ++n) y[m * N + n] = acc[n - n0];
         }
@@ -170,13 +208,27 @@ int oracle_linear(const uint16_t *x, const int32_t *qweight, const uint16_t *sca
     return OR_OK;
 }
 
+int oracle_linear(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                  int64_t M, int64_t K, int64_t N, int64_t g, double *y) {
+    return linear_impl(x, 0, 0, qweight, scales, M, K, N, g, y);
+}
+
+/* As oracle_linear, with x of type act (0 fp16, 1 bfloat16) and, when absval
+ * is 1, sum_k |x| * |w| in place of the sum of products. */
+int oracle_linear_ex(const uint16_t *x, int act, int absval, const int32_t *qweight,
+                     const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
+                     double *y) {
+    return linear_impl(x, act, absval ? 1 : 0, qweight, scales, M, K, N, g, y);
+}
+
 /* out[i] <- y[ms[i], ns[i]] for sampled outputs, each from the definition
  * directly (no dequantised matrix): used at sizes where the full product is
  * too slow for a test. */
-int oracle_linear_at(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
-                     int64_t M, int64_t K, int64_t N, int64_t g,
-                     const int64_t *ms, const int64_t *ns, int64_t count, double *out) {
-    if (!shape_ok(M, K, N) || !group_ok(K, g) || count < 0) return OR_ERR_ARG;
+static int linear_at_impl(const uint16_t *x, int act, int absval, const int32_t *qweight,
+                          const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
+                          const int64_t *ms, const int64_t *ns, int64_t count, double *out) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || count < 0 || (act != 0 && act != 1))
+        return OR_ERR_ARG;
     if (count == 0) return OR_OK;
     if (!x || !qweight || !scales || !ms || !ns || !out) return OR_ERR_ARG;
     for (int64_t i = 0; i < count; ++i)
@@ -186,8 +238,22 @@ int oracle_linear_at(const uint16_t *x, const int32_t *qweight, const uint16_t *
         int64_t m = ms[i], n = ns[i];
         double acc = 0.0;
         for (int64_t k = 0; k < K; ++k)
-            acc += half_to_double(x[m * K + k]) * (double)weight_at(qweight, scales, N, g, k, n);
+            acc += term(act_to_double(x[m * K + k], act),
+                        (double)weight_at(qweight, scales, N, g, k, n), absval);
         out[i] = acc;
     }
     return OR_OK;
+}
+
+int oracle_linear_at(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+                     int64_t M, int64_t K, int64_t N, int64_t g,
+                     const int64_t *ms, const int64_t *ns, int64_t count, double *out) {
+    return linear_at_impl(x, 0, 0, qweight, scales, M, K, N, g, ms, ns, count, out);
+}
+
+int oracle_linear_at_ex(const uint16_t *x, int act, int absval, const int32_t *qweight,
+                        const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
+                        const int64_t *ms, const int64_t *ns, int64_t count, double *out) {
+    return linear_at_impl(x, act, absval ? 1 : 0, qweight, scales, M, K, N, g, ms, ns, count,
+                          out);
 }

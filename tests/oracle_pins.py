@@ -11,7 +11,12 @@ when it disagrees with:
   - brute force on tiny inputs with W built from the codes, never from the
     packed words;
   - exact rational arithmetic on an adversarial cancellation case;
-  - metamorphic relations (scale doubling, column permutation, linearity).
+  - metamorphic relations (scale doubling, column permutation, linearity);
+  - for bfloat16 activations, numpy's own decoding (a float32's top half) over
+    every bfloat16 bit pattern, and exact agreement with the fp16 path on
+    values both formats hold;
+  - for the magnitude sum sum_k |x||w|, a dense product of magnitudes and the
+    bounds |y| <= sum|x||w| (equality when every term is non-negative).
 ``tests/test_oracle_mutants.py`` plants plausible mistakes in copies of the
 oracle source and checks that every one of them trips at least one pin.
 """
@@ -246,6 +251,112 @@ def pin_sampled_matches_full(o):
     ms = rng.integers(0, M, size=40)
     ns = rng.integers(0, N, size=40)
     assert np.array_equal(o.linear_at(x, q, scales, g, ms, ns), y[ms, ns])
+
+
+# --- bfloat16 activations and the magnitude sum ---------------------------------
+
+def _bf16_value(bits: np.ndarray) -> np.ndarray:
+    """numpy's own decoding of bfloat16 bit patterns: the top half of a float32."""
+    with np.errstate(invalid="ignore"):
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_bf16_decode_all_patterns(o):
+    """Every bfloat16 pattern, as x[m, 0] against unit weights, comes back as
+    numpy's own float32-top-half decoding of it."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    M, K, N = 65536, 16, 8
+    x = np.zeros((M, K), dtype=np.uint16)
+    x[:, 0] = bits
+    q = o.pack(np.full((K, N), 9, dtype=np.uint8))            # q - 8 = 1 -> w = s = 1
+    y = o.linear(x, q, np.ones((1, N), dtype=np.float16), -1, act="bf16")[:, 3]
+    ref = _bf16_value(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(y), nan)
+    assert np.array_equal(y[~nan], ref[~nan])
+    nz = ~nan & (ref != 0)
+    assert np.array_equal(np.signbit(y[nz]), np.signbit(ref[nz]))
+
+
+def _shared_values(rng, shape):
+    """Values with at most 8 significant bits inside fp16's normal range, so that
+    fp16 and bfloat16 both hold them exactly."""
+    mant = rng.integers(128, 256, size=shape) * rng.choice([-1, 1], size=shape)
+    exp = rng.integers(-21, 8, size=shape)
+    return np.ldexp(mant.astype(np.float64), exp)
+
+
+def pin_bf16_agrees_with_half(o):
+    """On values both formats hold exactly, bfloat16 and fp16 activations give
+    bit-identical y."""
+    rng = np.random.default_rng(19)
+    for M, K, N, g in ((3, 64, 16, 16), (2, 256, 40, 128), (4, 96, 8, -1)):
+        G = 1 if g == -1 else -(-K // g)
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        scales = rng.uniform(1e-3, 2e-2, size=(G, N)).astype(np.float16)
+        v = _shared_values(rng, (M, K))
+        xh = v.astype(np.float16)
+        assert np.array_equal(xh.astype(np.float64), v)
+        xb = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(_bf16_value(xb), v)
+        q = o.pack(codes)
+        assert np.array_equal(o.linear(xb, q, scales, g, act="bf16"), o.linear(xh, q, scales, g))
+
+
+def _brute_abs(codes, scales, xv, g):
+    K = codes.shape[0]
+    gidx = np.zeros(K, dtype=np.int64) if g == -1 else np.arange(K) // g
+    W = (codes.astype(np.float64) - 8.0) * scales.astype(np.float64)[gidx]
+    return np.abs(xv) @ np.abs(W)
+
+
+def pin_abs_brute_force(o):
+    """sum_k |x||w| against a dense fp64 product of magnitudes, W built from the
+    codes; fp16 and bfloat16 activations."""
+    rng = np.random.default_rng(20)
+    for M, K, N, g in ((1, 16, 8, 16), (3, 64, 24, 32), (2, 256, 16, -1), (4, 80, 40, 16)):
+        G = 1 if g == -1 else -(-K // g)
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        scales = rng.uniform(1e-3, 2e-2, size=(G, N)).astype(np.float16)
+        q = o.pack(codes)
+        xh = rng.standard_normal((M, K)).astype(np.float16)
+        xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        for x, act, xv in ((xh, "f16", xh.astype(np.float64)), (xb, "bf16", _bf16_value(xb))):
+            a = o.linear(x, q, scales, g, act=act, absval=True)
+            ref = _brute_abs(codes, scales, xv, g)
+            assert np.abs(a - ref).max() <= 1e-12 * max(1.0, float(ref.max())), (M, K, N, g, act)
+
+
+def pin_abs_bounds_signed(o):
+    """|y| <= sum|x||w| everywhere, with equality when every term is >= 0."""
+    rng = np.random.default_rng(21)
+    M, K, N, g = 4, 128, 32, 32
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    scales = rng.uniform(1e-3, 2e-2, size=(K // g, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    q = o.pack(codes)
+    y = o.linear(x, q, scales, g)
+    a = o.linear(x, q, scales, g, absval=True)
+    assert np.all(np.abs(y) <= a * (1 + 1e-12))
+    pos_codes = rng.integers(8, 16, size=(K, N), dtype=np.uint8)
+    xp = np.abs(x)
+    qp = o.pack(pos_codes)
+    assert np.array_equal(o.linear(xp, qp, scales, g, absval=True), o.linear(xp, qp, scales, g))
+
+
+def pin_sampled_matches_full_bf16_abs(o):
+    rng = np.random.default_rng(22)
+    M, K, N, g = 4, 256, 48, 32
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    q = o.pack(codes)
+    scales = rng.uniform(1e-3, 2e-2, size=(K // g, N)).astype(np.float16)
+    xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ms = rng.integers(0, M, size=30)
+    ns = rng.integers(0, N, size=30)
+    for absval in (False, True):
+        y = o.linear(xb, q, scales, g, act="bf16", absval=absval)
+        assert np.array_equal(o.linear_at(xb, q, scales, g, ms, ns, act="bf16", absval=absval),
+                              y[ms, ns]), absval
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

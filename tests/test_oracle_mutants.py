@@ -18,7 +18,14 @@ MUTANTS = {
     "dropped_last_k": ("for (int64_t k = 0; k < K; ++k) {\n                double xk",
                        "for (int64_t k = 0; k < K - 1; ++k) {\n                double xk"),
     "fp32_accumulator": ("double acc[256];", "float acc[256];"),
-    "x_transposed": ("half_to_double(x[m * K + k]);", "half_to_double(x[k * M + m]);"),
+    "x_transposed": ("act_to_double(x[m * K + k], act);", "act_to_double(x[k * M + m], act);"),
+    "bf16_exponent_bias": ("exp - 134", "exp - 133"),
+    "bf16_subnormal_scale": ("ldexp((double)man, -133)", "ldexp((double)man, -132)"),
+    "bf16_fraction_width": ("int man = h & 0x7F;", "int man = h & 0xFF;"),
+    "bf16_read_as_half": ("return act ? bf16_to_double(h) : half_to_double(h);",
+                          "return half_to_double(h);"),
+    "abs_sign_kept": ("return absval ? fabs(xk) * fabs(w) : xk * w;",
+                      "return absval ? fabs(xk) * w : xk * w;"),
     "half_exponent_bias": ("exp - 25", "exp - 24"),
     "half_subnormal_scale": ("ldexp((double)man, -24)", "ldexp((double)man, -23)"),
     "half_sign_dropped": ("return sign ? -v : v;", "return v;"),
