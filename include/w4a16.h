@@ -101,6 +101,29 @@ int w4a16_linear_ex(const void *x, const int32_t *qweight, const void *scales, v
                     int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
                     int kernel);
 
+/* y = x . dequant(qweight, scales) with bfloat16 activations and output: the
+ * dtype the pages serve this checkpoint with ("Qwen3.8-27B-GPTQ-Int4" model
+ * card, "4. Deployment": the verified serving command passes the bfloat16
+ * dtype; the "GPTQ-Pro" README's "Runtime contract" keeps native BF16
+ * outside its own kernels).
+ *   x : device bfloat16 [M, K];  y : device bfloat16 [M, N];
+ *   qweight, scales (fp16), shapes, group sizes, alignment, stream, dispatch,
+ *   errors and workspaces exactly as for w4a16_linear.
+ * Arithmetic: every weight (q - 8) * s is formed exactly in fp32 and rounded
+ * once to bfloat16 (nearest even) for the bfloat16 matrix instructions;
+ * products accumulate in fp32; y is rounded once to bfloat16 (nearest even).
+ * Hence |y - y_exact| <= 2^-8 |y_exact| + (2^-8 + K 2^-24) sum_k |x||w| per
+ * element (both roundings at most half a bfloat16 ulp, fp32 accumulation).
+ * Results are deterministic, as for fp16. */
+int w4a16_linear_bf16(const void *x, const int32_t *qweight, const void *scales, void *y,
+                      int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream);
+
+/* As w4a16_linear_bf16 with the kernel chosen by the caller, as in
+ * w4a16_linear_ex. */
+int w4a16_linear_bf16_ex(const void *x, const int32_t *qweight, const void *scales, void *y,
+                         int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
+                         int kernel);
+
 /* Host-side packing into the GPTQ_V2 layout (native int32 qweight, "GPTQ-Pro"
  * README, "Runtime contract"):
  *   qweight[r][n] = sum_{j=0..7} codes[8r+j][n] << 4j   (as a 32-bit pattern)

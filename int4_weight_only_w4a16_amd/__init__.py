@@ -6,9 +6,11 @@ streams.  There is no fallback: if the library is missing or the device is
 not a gfx950, calls raise.
 
 Names match the C ABI in ``include/w4a16.h``:
-  w4a16_linear, w4a16_linear_ex, pack_gptq_v2, unpack_gptq_v2,
-  w4a16_status_string, and the measurement aid w4a16_read_probe
-plus ``linear`` (allocates y with torch, then calls w4a16_linear_ex).
+  w4a16_linear, w4a16_linear_ex, w4a16_linear_bf16, w4a16_linear_bf16_ex,
+  pack_gptq_v2, unpack_gptq_v2, w4a16_status_string, and the measurement aid
+  w4a16_read_probe
+plus ``linear`` (allocates y with torch, then calls w4a16_linear_ex or, for
+bfloat16 x, w4a16_linear_bf16_ex).
 """
 
 from __future__ import annotations
@@ -37,8 +39,8 @@ W4A16_KERNEL_AUTO = 0
 W4A16_KERNEL_DECODE = 1
 W4A16_KERNEL_PREFILL = 2
 
-EXPORTS = ("w4a16_linear", "w4a16_linear_ex", "pack_gptq_v2", "unpack_gptq_v2",
-           "w4a16_read_probe", "w4a16_status_string")
+EXPORTS = ("w4a16_linear", "w4a16_linear_ex", "w4a16_linear_bf16", "w4a16_linear_bf16_ex",
+           "pack_gptq_v2", "unpack_gptq_v2", "w4a16_read_probe", "w4a16_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -64,6 +66,10 @@ def load_library() -> ctypes.CDLL:
     lib.w4a16_linear.restype = i32
     lib.w4a16_linear_ex.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i32]
     lib.w4a16_linear_ex.restype = i32
+    lib.w4a16_linear_bf16.argtypes = [p, p, p, p, i64, i64, i64, i64, p]
+    lib.w4a16_linear_bf16.restype = i32
+    lib.w4a16_linear_bf16_ex.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i32]
+    lib.w4a16_linear_bf16_ex.restype = i32
     lib.pack_gptq_v2.argtypes = [p, p, i64, i64]
     lib.pack_gptq_v2.restype = i32
     lib.unpack_gptq_v2.argtypes = [p, p, i64, i64]
@@ -117,6 +123,22 @@ def w4a16_linear(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
     w4a16_linear_ex(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO)
 
 
+def w4a16_linear_bf16_ex(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
+                         stream=None, kernel: int = W4A16_KERNEL_AUTO) -> None:
+    """As w4a16_linear_ex with bfloat16 x and y (scales stay fp16)."""
+    st = load_library().w4a16_linear_bf16_ex(_addr(x), _addr(qweight), _addr(scales), _addr(y),
+                                             int(M), int(K), int(N), int(group_size),
+                                             _stream_handle(stream), int(kernel))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_linear_bf16")
+
+
+def w4a16_linear_bf16(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
+                      stream=None) -> None:
+    """Same as the C ``w4a16_linear_bf16`` (kernel chosen by M)."""
+    w4a16_linear_bf16_ex(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO)
+
+
 def w4a16_read_probe(data, nbytes: int, sink, stream=None) -> None:
     """Enqueue the streaming-read probe over nbytes at data (a measurement
     aid: the attainable HBM read rate); raises W4A16Error on a nonzero status."""
@@ -150,12 +172,14 @@ def unpack_gptq_v2(qweight: np.ndarray) -> np.ndarray:
 
 def linear(x, qweight, scales, group_size: int, out=None, stream=None,
            kernel: int = W4A16_KERNEL_AUTO):
-    """Allocate y (fp16 [M, N]) with torch on x's device and run the linear.
+    """Allocate y (x's dtype, [M, N]) with torch on x's device and run the linear.
 
-    x: fp16 [M, K]; qweight: int32 [K/8, N]; scales: fp16 [G, N]; all CUDA
-    (HIP) tensors, contiguous."""
+    x: fp16 or bfloat16 [M, K] (y has the same dtype); qweight: int32 [K/8, N];
+    scales: fp16 [G, N]; all CUDA (HIP) tensors, contiguous."""
     import torch
-    for name, t, dt in (("x", x, torch.float16), ("qweight", qweight, torch.int32),
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be float16 or bfloat16")
+    for name, t, dt in (("x", x, x.dtype), ("qweight", qweight, torch.int32),
                         ("scales", scales, torch.float16)):
         if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {dt} device tensor")
@@ -164,6 +188,9 @@ def linear(x, qweight, scales, group_size: int, out=None, stream=None,
     if qweight.shape[0] * 8 != K:
         raise ValueError("qweight must be [K/8, N]")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    w4a16_linear_ex(x, qweight, scales, out, M, K, N, group_size, stream, kernel)
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    elif out.dtype != x.dtype:
+        raise ValueError("out must have x's dtype")
+    call = w4a16_linear_bf16_ex if x.dtype == torch.bfloat16 else w4a16_linear_ex
+    call(x, qweight, scales, out, M, K, N, group_size, stream, kernel)
     return out

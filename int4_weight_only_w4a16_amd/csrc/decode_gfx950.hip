@@ -119,8 +119,9 @@ __device__ __forceinline__ _Float16 scale_at(const u2 &s, int j) {
     return (j & 1) ? half_hi(d) : half_lo(d);
 }
 
+template <bool BF>
 __device__ __forceinline__ void store_row4(uint16_t *dst, const float (&v)[4]) {
-    *reinterpret_cast<u2 *>(dst) = pack4_f16(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<u2 *>(dst) = pack4<BF>(v[0], v[1], v[2], v[3]);
 }
 
 // One wave's pass over a contiguous range [w0, w1) of units (tile-major:
@@ -141,8 +142,12 @@ __device__ __forceinline__ void store_row4(uint16_t *dst, const float (&v)[4]) {
 // SCALE: 0 scales each 8-deep block before the MFMA (g = 16); 1 sums a
 // group's products in fp32 and scales once per group (scale-after); 2 is
 // scale-after with one step per group (g = 32): every MFMA starts from zero
-// and its result is scaled straight into the sum.
-template <int D, int SCALE, bool XLDS, typename Dump, typename AfterPrologue>
+// and its result is scaled straight into the sum.  SCALE picks which scale
+// row each unit loads.
+// BF: bfloat16 activations.  Every weight is then dequantised before the
+// MFMA, (q - 8) * s exactly in fp32 and rounded once to bfloat16
+// (dequant_bf16), for every group size.
+template <int D, int SCALE, bool XLDS, bool BF, typename Dump, typename AfterPrologue>
 __device__ __forceinline__ void decode_units(
     const __amdgpu_buffer_rsrc_t xr, const __amdgpu_buffer_rsrc_t qr,
     const __amdgpu_buffer_rsrc_t sr, const unsigned char *xs, int M, int K, int N, int S,
@@ -239,7 +244,13 @@ __device__ __forceinline__ void decode_units(
         else
             a = __builtin_bit_cast(h8, perm_x(st.x));
         const bool seg_end = i == nA - 1 || i == n - 1;
-        if constexpr (SCALE == 2) {
+        if constexpr (BF) {
+#pragma unroll
+            for (int j = 0; j < kNW; ++j)
+                acc[j] = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a),
+                                              dequant_bf16<false>(st.w[j], (float)scale_at(st.s, j)),
+                                              acc[j]);
+        } else if constexpr (SCALE == 2) {
 #pragma unroll
             for (int j = 0; j < kNW; ++j) {
                 const f4 t = mfma16x16x32(a, unpack_codes(st.w[j], uc), f4{0.f, 0.f, 0.f, 0.f});
@@ -292,7 +303,7 @@ __device__ __forceinline__ void decode_units(
 extern __shared__ __attribute__((aligned(16))) unsigned char decode_dyn_lds[];
 
 // Tiles kernel: one workgroup per column tile, its waves split K.
-template <int WAVES, int D, int SCALE, bool XLDS>
+template <int WAVES, int D, int SCALE, bool XLDS, bool BF>
 __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -317,7 +328,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
     __builtin_amdgcn_sched_barrier(0);
-    decode_units<D, SCALE, XLDS>(
+    decode_units<D, SCALE, XLDS, BF>(
         xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int, const f4(&acc)[kNW]) {
 #pragma unroll
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
 #pragma unroll
             for (int j = 0; j < kNW; ++j) v[j] += red[w][j][l][i];
         }
-        if (m < M && n < N) store_row4(y + (size_t)m * N + n, v);
+        if (m < M && n < N) store_row4<BF>(y + (size_t)m * N + n, v);
     }
 }
 
@@ -398,7 +409,7 @@ __host__ __device__ __forceinline__ int wave_share(int n, int w) {
     return nold + (n - nold) * (w - H) / (WAVES - H);
 }
 
-template <int WAVES, int D, int SCALE, bool XLDS>
+template <int WAVES, int D, int SCALE, bool XLDS, bool BF>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -432,7 +443,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
     __builtin_amdgcn_sched_barrier(0);
-    decode_units<D, SCALE, XLDS>(
+    decode_units<D, SCALE, XLDS, BF>(
         xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int slot, const f4(&acc)[kNW]) {
             if (slot > 1) return;   // cannot happen: ranges hold <= S units
@@ -515,7 +526,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         const int n = tau * kCols + c;
         if (n >= N) continue;
         if (ta >= u0 && tb <= u1) {                 // the whole tile is here
-            store_row4(y + (size_t)m * N + n, v);
+            store_row4<BF>(y + (size_t)m * N + n, v);
             continue;
         }
         if (partials) {
@@ -543,8 +554,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             const float r0 = __builtin_bit_cast(float, (uint32_t)got[j] ^ kSlotKey) + v[2 * j];
             const float r1 = __builtin_bit_cast(float, (uint32_t)(got[j] >> 32) ^ kSlotKey) + v[2 * j + 1];
             __hip_atomic_store(slot + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            const h2 h = {(_Float16)r0, (_Float16)r1};
-            *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n + 2 * j) = __builtin_bit_cast(uint32_t, h);
+            *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n + 2 * j) = pack2<BF>(r0, r1);
         }
     }
 }
@@ -554,6 +564,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
 // bit-reproducible), and stores y.  One workgroup per tile; thread (m, q)
 // handles row m and columns 4q .. 4q+3 of the tile.  Tiles that lie whole
 // inside one range were stored by the stream-K kernel.
+template <bool BF>
 __global__ __launch_bounds__(256) void decode_split_reduce_kernel(
     const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S, int G) {
     constexpr int SLOT = 16 * kCols;
@@ -573,7 +584,7 @@ __global__ __launch_bounds__(256) void decode_split_reduce_kernel(
 #pragma unroll
         for (int j = 0; j < kNW; ++j) r[j] += p[j];
     }
-    store_row4(y + (size_t)m * N + n, r);
+    store_row4<BF>(y + (size_t)m * N + n, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -644,7 +655,7 @@ static size_t static_lds(const void *kernel) {
     return attr.sharedSizeBytes;
 }
 
-template <int SCALE, bool XLDS>
+template <int SCALE, bool XLDS, bool BF>
 static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *workspace,
                             int capacity, int grid) {
     const int K = (int)a.K, N = (int)a.N, M = (int)a.M;
@@ -667,54 +678,61 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
                         &group_steps, &slots, &partials};
         hipError_t e = hipLaunchKernel(
             reinterpret_cast<const void *>(
-                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS>),
+                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF>),
             dim3(grid), block, args, dyn, stream);
         if (e != hipSuccess || !part) return e;
         const float *pc = partials;
         int Sv = S, G = grid;
         void *rargs[] = {&pc, &yp, (void *)&M, (void *)&N, &Sv, &G};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel),
+        return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel<BF>),
                                dim3((unsigned)T), dim3(256), rargs, 0, stream);
     }
     void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
     const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);
     return hipLaunchKernel(
         reinterpret_cast<const void *>(
-            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS>),
+            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS, BF>),
         dim3(tiles), block, args, dyn, stream);
 }
 
 // Whether the activations can be staged in LDS: at most kXStageMax bytes,
 // and the kernel's static LDS plus the staging area within the device's
 // per-workgroup LDS limit (a launch beyond it is rejected by the device).
-template <int SCALE>
+template <int SCALE, bool BF>
 static bool stage_fits(const LinearArgs &a, int grid, size_t max_lds) {
     const size_t dyn = (size_t)a.M * 32 * ((a.K + 31) / 32) * 2 + 16;
     if (dyn > kXStageMax) return false;
     static const size_t sk_static = static_lds(reinterpret_cast<const void *>(
-        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true>));
+        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true, BF>));
     static const size_t tiles_static = static_lds(reinterpret_cast<const void *>(
-        &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true>));
+        &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true, BF>));
     const size_t st = grid > 0 ? sk_static : tiles_static;
     return st != (size_t)-1 && st + dyn <= max_lds;
+}
+
+template <int SCALE, bool BF>
+static hipError_t launch_scale(const LinearArgs &a, hipStream_t stream, void *workspace,
+                               int capacity, int grid, size_t max_lds) {
+    return stage_fits<SCALE, BF>(a, grid, max_lds)
+               ? launch_sa<SCALE, true, BF>(a, stream, workspace, capacity, grid)
+               : launch_sa<SCALE, false, BF>(a, stream, workspace, capacity, grid);
 }
 
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                          int grid, size_t max_lds) {
     if (grid > capacity) return hipErrorInvalidValue;
-    if (a.group_size == 16)
-        return stage_fits<0>(a, grid, max_lds)
-                   ? launch_sa<0, true>(a, stream, workspace, capacity, grid)
-                   : launch_sa<0, false>(a, stream, workspace, capacity, grid);
+    // bfloat16 dequantises before the MFMA for every group size; SCALE only
+    // picks the scale rows there (per 16-deep block for g = 16, per group
+    // otherwise)
+    if (a.bf16)
+        return a.group_size == 16 ? launch_scale<0, true>(a, stream, workspace, capacity, grid, max_lds)
+                                  : launch_scale<1, true>(a, stream, workspace, capacity, grid, max_lds);
+    if (a.group_size == 16) return launch_scale<0, false>(a, stream, workspace, capacity, grid, max_lds);
     // one 32-deep step per group: g = 32, or one group over K <= 32
     const int64_t S = (a.K + 31) / 32;
     if (a.group_size == 32 || (a.group_size == -1 && S == 1))
-        return stage_fits<2>(a, grid, max_lds)
-                   ? launch_sa<2, true>(a, stream, workspace, capacity, grid)
-                   : launch_sa<2, false>(a, stream, workspace, capacity, grid);
-    return stage_fits<1>(a, grid, max_lds)
-               ? launch_sa<1, true>(a, stream, workspace, capacity, grid)
-               : launch_sa<1, false>(a, stream, workspace, capacity, grid);
+        return launch_scale<2, false>(a, stream, workspace, capacity, grid, max_lds);
+    return launch_scale<1, false>(a, stream, workspace, capacity, grid, max_lds);
 }
 
 }  // namespace w4a16

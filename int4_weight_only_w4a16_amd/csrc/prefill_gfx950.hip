@@ -49,7 +49,9 @@ constexpr int kPreStageBytes = kPreBM * kPreRowBytes;
 constexpr int kPreRing = 3;               // LDS stages, register stages per operand
 constexpr int kPreSteps = kPreBK / 16;    // 16-deep MFMA steps per stage
 
-// gshift: log2(group_size), or -1 for a single group over K.
+// gshift: log2(group_size), or -1 for a single group over K.  BF: bfloat16
+// activations and output (weights dequantised by dequant_bf16).
+template <bool BF>
 __global__ __launch_bounds__(256) void prefill_m128_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -140,12 +142,18 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
             h8 an[4];
             if (h + 1 < kPreSteps) read_a(an, slot, h + 1);
             else read_a(an, next, 0);
-            const h8 b0 = unpack_codes_scaled(w[h].x, uc, half_lo(s[h]));
-            const h8 b1 = unpack_codes_scaled(w[h].y, uc, half_hi(s[h]));
+            u4 b0, b1;
+            if constexpr (BF) {
+                b0 = dequant_bf16<false>(w[h].x, (float)half_lo(s[h]));
+                b1 = dequant_bf16<false>(w[h].y, (float)half_hi(s[h]));
+            } else {
+                b0 = __builtin_bit_cast(u4, unpack_codes_scaled(w[h].x, uc, half_lo(s[h])));
+                b1 = __builtin_bit_cast(u4, unpack_codes_scaled(w[h].y, uc, half_hi(s[h])));
+            }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                acc[mt][0] = mfma32x32x16(a[mt], b0, acc[mt][0]);
-                acc[mt][1] = mfma32x32x16(a[mt], b1, acc[mt][1]);
+                acc[mt][0] = mfma32x32x16_t<BF>(__builtin_bit_cast(u4, a[mt]), b0, acc[mt][0]);
+                acc[mt][1] = mfma32x32x16_t<BF>(__builtin_bit_cast(u4, a[mt]), b1, acc[mt][1]);
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) a[mt] = an[mt];
@@ -202,10 +210,9 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
-                if (m < M) {
-                    const h2 v = {(_Float16)acc[mt][0][i], (_Float16)acc[mt][1][i]};
-                    *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) = __builtin_bit_cast(uint32_t, v);
-                }
+                if (m < M)
+                    *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) =
+                        pack2<BF>(acc[mt][0][i], acc[mt][1][i]);
             }
         }
     }
@@ -222,8 +229,9 @@ static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream) {
     void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift};
     dim3 grid((unsigned)((N + kPreBN - 1) / kPreBN), (unsigned)((M + kPreBM - 1) / kPreBM));
     dim3 block(256);
-    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_m128_kernel), grid, block, args, 0,
-                           stream);
+    const void *k = a.bf16 ? reinterpret_cast<const void *>(&prefill_m128_kernel<true>)
+                           : reinterpret_cast<const void *>(&prefill_m128_kernel<false>);
+    return hipLaunchKernel(k, grid, block, args, 0, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -299,6 +307,7 @@ __device__ __forceinline__ WideOperands wide_operands(const uint16_t *x, const i
 // acc = the fp32 products of the 256 x 256 tile at (m0, n0) over the 64-deep
 // stages [sb, se) of K, 0 <= sb < se <= nst.  Uses the whole LDS area L; on
 // return every copy has landed, but other waves may still be reading L.
+template <bool BF>
 __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands &p, int m0, int n0,
                                                 int sb, int se, f16v (&acc)[8][2]) {
     const int M = p.M, K = p.K, N = p.N, gshift = p.gshift, nfull = p.nfull;
@@ -465,6 +474,38 @@ __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands 
         const lds_u8_t *ab = L + kWAOff + slot * kWA + a_rd[h];
         uint32_t tw[2][4];
         h2 s_lo, s_hi;
+        // bfloat16: 25 operations per word (dequant_bf16's steps, pinned one
+        // by one): the fp32 scale and -8 s, the even and odd nibble bytes,
+        // then per dword two byte converts, two fmas and one pack
+        float bsf = 0.f, bm8 = 0.f, bqa = 0.f, bqb = 0.f;
+        uint32_t blo = 0, bhi = 0;
+        auto valu_bf = [&](int idx) {
+            const int j = idx / 25, r = idx % 25;
+            const uint32_t w = j ? w_nxt.y : w_nxt.x;
+            if (r == 0) {
+                bsf = (float)(j ? half_hi(s_nxt) : half_lo(s_nxt));
+                asm volatile("" : "+v"(bsf));
+            } else if (r == 1) {
+                bm8 = -8.0f * bsf;
+                asm volatile("" : "+v"(bm8));
+            } else if (r == 2) {
+                blo = w & 0x0F0F0F0Fu;
+                asm volatile("" : "+v"(blo));
+            } else if (r == 3) {
+                bhi = w >> 4;
+                asm volatile("" : "+v"(bhi));
+            } else if (r == 4) {
+                bhi &= 0x0F0F0F0Fu;
+                asm volatile("" : "+v"(bhi));
+            } else {
+                const int d = (r - 5) / 5, o = (r - 5) % 5;
+                if (o == 0) { bqa = ubyte_f32(blo, d); asm volatile("" : "+v"(bqa)); }
+                else if (o == 1) { bqb = ubyte_f32(bhi, d); asm volatile("" : "+v"(bqb)); }
+                else if (o == 2) { bqa = __builtin_fmaf(bqa, bsf, bm8); asm volatile("" : "+v"(bqa)); }
+                else if (o == 3) { bqb = __builtin_fmaf(bqb, bsf, bm8); asm volatile("" : "+v"(bqb)); }
+                else { tw[j][d] = pack2<true>(bqa, bqb); asm volatile("" : "+v"(tw[j][d])); }
+            }
+        };
         auto valu = [&](int idx) {
             const int j = idx >> 4, k = (idx >> 2) & 3, d = idx & 3;
             const uint32_t w = j ? w_nxt.y : w_nxt.x;
@@ -477,7 +518,8 @@ __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands 
         };
         auto mfma = [&](int idx) {
             const int j = idx >> 3, mt = idx & 7;
-            acc[mt][j] = mfma32x32x16(a_cur[mt], j ? b_cur1 : b_cur0, acc[mt][j]);
+            acc[mt][j] = mfma32x32x16_t<BF>(__builtin_bit_cast(u4, a_cur[mt]),
+                                            __builtin_bit_cast(u4, j ? b_cur1 : b_cur0), acc[mt][j]);
         };
 #pragma unroll
         for (int si = 0; si < 16; ++si) {
@@ -488,14 +530,24 @@ __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands 
                 for (int mt = 2 * si - 2; mt < 2 * si; ++mt)
                     a_nxt[mt] = __builtin_bit_cast(h8, *(const __attribute__((address_space(3))) u4 *)(ab + mt * 4096));
             }
-            if (si == 5) {
-                s_lo = h2{half_lo(s_nxt), half_lo(s_nxt)};
-                s_hi = h2{half_hi(s_nxt), half_hi(s_nxt)};
-            }
-            if (si >= 5) {
-                const int v0 = 3 * (si - 5);
+            if constexpr (BF) {
+                // 50 operations over slots 5-15: five per slot, then four
+                if (si >= 5) {
+                    const int v0 = si <= 10 ? 5 * (si - 5) : 30 + 4 * (si - 11);
+                    const int v1 = si <= 10 ? v0 + 5 : v0 + 4;
 #pragma unroll
-                for (int v = v0; v < v0 + 3 && v < 32; ++v) valu(v);
+                    for (int v = v0; v < v1; ++v) valu_bf(v);
+                }
+            } else {
+                if (si == 5) {
+                    s_lo = h2{half_lo(s_nxt), half_lo(s_nxt)};
+                    s_hi = h2{half_hi(s_nxt), half_hi(s_nxt)};
+                }
+                if (si >= 5) {
+                    const int v0 = 3 * (si - 5);
+#pragma unroll
+                    for (int v = v0; v < v0 + 3 && v < 32; ++v) valu(v);
+                }
             }
             if (FAST && (si == 10 || si == 13 || si == 15))
                 dma(BoolC<true>(), dst, dslot, 3 * dchunk + (si == 10 ? 0 : si == 13 ? 1 : 2));
@@ -538,8 +590,13 @@ __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands 
     lds_barrier();
     read_ws(0, 0);
     read_a(0, 0);
-    b_cur0 = unpack_nat_scaled(w_nxt.x, half_lo(s_nxt), mask, magic, mul, add);
-    b_cur1 = unpack_nat_scaled(w_nxt.y, half_hi(s_nxt), mask, magic, mul, add);
+    if constexpr (BF) {
+        b_cur0 = __builtin_bit_cast(h8, dequant_bf16<true>(w_nxt.x, (float)half_lo(s_nxt)));
+        b_cur1 = __builtin_bit_cast(h8, dequant_bf16<true>(w_nxt.y, (float)half_hi(s_nxt)));
+    } else {
+        b_cur0 = unpack_nat_scaled(w_nxt.x, half_lo(s_nxt), mask, magic, mul, add);
+        b_cur1 = unpack_nat_scaled(w_nxt.y, half_hi(s_nxt), mask, magic, mul, add);
+    }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) a_cur[mt] = a_nxt[mt];
 
@@ -573,6 +630,7 @@ constexpr int kWSlot = kWBM * kWBN;   // floats per partial tile
 // copy of the code serves both kinds of workgroup: every element issues the
 // same two stores, the ones that do not apply get an out-of-range offset
 // (two copies of the epilogue would not fit the register file).
+template <bool BF>
 __device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0,
                                            const f16v (&acc)[8][2], float *partial,
                                            uint32_t part_mask) {
@@ -596,12 +654,12 @@ __device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0
         for (int i = 0; i < 16; ++i) {
             const float f0 = acc[mt][0][i], f1 = acc[mt][1][i];
             const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
-            const h2 v = {(_Float16)f0, (_Float16)f1};
+            const uint32_t v = pack2<BF>(f0, f1);
             const uint32_t oy =
                 (m < p.M && n < p.N) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOOB;
             const uint32_t op = ((uint32_t)((wave * 8 + mt) * 16 + i) * 128u + (uint32_t)lane) * 4u;
             const uint32_t v1 = (__builtin_bit_cast(uint32_t, f0) & part_mask) |
-                                (__builtin_bit_cast(uint32_t, v) & ~part_mask);
+                                (v & ~part_mask);
             const uint32_t o1 = (op & part_mask) | (oy & ~part_mask);
             const uint32_t o2 = ((op + 256u) & part_mask) | (kOOB & ~part_mask);
             __builtin_amdgcn_raw_buffer_store_b32(v1, r1, o1, 0, 0);
@@ -619,6 +677,7 @@ __device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0
 // prefill_tail_reduce_kernel adds them.  Every workgroup streams K from its
 // range start with the others, nothing is exchanged inside the kernel.
 
+template <bool BF>
 __global__ __launch_bounds__(256) void prefill_m256_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -647,13 +706,15 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
         se = (int)((int64_t)p.nst * (c + 1) / chunks);
     }
     f16v acc[8][2];
-    wide_tile_range((lds_u8_t *)lds_raw, p, m0, n0, sb, se, acc);
-    wide_store(p, m0, n0, acc, j < 0 ? partials : partials + (size_t)j * kWSlot, j < 0 ? 0u : ~0u);
+    wide_tile_range<BF>((lds_u8_t *)lds_raw, p, m0, n0, sb, se, acc);
+    wide_store<BF>(p, m0, n0, acc, j < 0 ? partials : partials + (size_t)j * kWSlot,
+                   j < 0 ? 0u : ~0u);
 }
 
 // Sums the split tiles' partials in chunk order (fixed, so results are
 // bit-reproducible) and stores y.  One thread per (tile, wave, mt, i, lane):
 // register i of row tile mt, both column tiles, as laid out by wide_store.
+template <bool BF>
 __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
     const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int tiles_m,
     int tiles_dp, int chunks, int tail_tiles) {
@@ -675,8 +736,7 @@ __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
     const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
     const int n = n0 + 64 * wave + 2 * (lane & 31);
     if (m >= M || n >= N) return;
-    const h2 v = {(_Float16)a0, (_Float16)a1};
-    *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) = __builtin_bit_cast(uint32_t, v);
+    *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) = pack2<BF>(a0, a1);
 }
 
 // Split of the wide kernel's tiles: whole rounds of one tile per workgroup;
@@ -728,13 +788,15 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
     void *yp = a.y;
     void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &tiles_m, &tiles_dp, &per_xcd,
                     &chunks, &partials};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_m256_kernel),
-                                   dim3(8 * per_xcd + tail * chunks), dim3(256), args, 0, stream);
+    const void *k = a.bf16 ? reinterpret_cast<const void *>(&prefill_m256_kernel<true>)
+                           : reinterpret_cast<const void *>(&prefill_m256_kernel<false>);
+    hipError_t e = hipLaunchKernel(k, dim3(8 * per_xcd + tail * chunks), dim3(256), args, 0, stream);
     if (e != hipSuccess || tail == 0) return e;
     const float *pc = partials;
     void *rargs[] = {&pc, &yp, &M, &N, &tiles_m, &tiles_dp, &chunks, &tail};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_tail_reduce_kernel),
-                           dim3(128 * tail), dim3(256), rargs, 0, stream);
+    const void *rk = a.bf16 ? reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<true>)
+                            : reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<false>);
+    return hipLaunchKernel(rk, dim3(128 * tail), dim3(256), rargs, 0, stream);
 }
 
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,

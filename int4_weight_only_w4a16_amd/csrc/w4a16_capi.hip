@@ -111,9 +111,10 @@ void *stream_workspace(int dev, hipStream_t stream, int kind, size_t bytes) {
 
 }  // namespace
 
-extern "C" int w4a16_linear_ex(const void *x, const int32_t *qweight, const void *scales,
-                               void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
-                               void *stream, int kernel) {
+// One linear call, fp16 or bfloat16 (bf16) activations and outputs.
+static int linear_call(const void *x, const int32_t *qweight, const void *scales, void *y,
+                       int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
+                       int kernel, bool bf16) {
     const int st = validate(x, qweight, scales, y, M, K, N, group_size);
     if (st != W4A16_OK) return st;
     if (kernel == W4A16_KERNEL_AUTO)
@@ -128,7 +129,7 @@ extern "C" int w4a16_linear_ex(const void *x, const int32_t *qweight, const void
     size_t max_lds = 0;
     const int dev = usable_device(&num_cus, &max_lds);
     if (dev < 0) return W4A16_ERR_DEVICE;
-    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size};
+    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, bf16};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (kernel == W4A16_KERNEL_DECODE) {
@@ -148,11 +149,30 @@ extern "C" int w4a16_linear_ex(const void *x, const int32_t *qweight, const void
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
+extern "C" int w4a16_linear_ex(const void *x, const int32_t *qweight, const void *scales,
+                               void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                               void *stream, int kernel) {
+    return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, kernel, false);
+}
+
 extern "C" int w4a16_linear(const void *x, const int32_t *qweight, const void *scales, void *y,
                             int64_t M, int64_t K, int64_t N, int64_t group_size,
                             void *stream) {
-    return w4a16_linear_ex(x, qweight, scales, y, M, K, N, group_size, stream,
-                           W4A16_KERNEL_AUTO);
+    return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO,
+                       false);
+}
+
+extern "C" int w4a16_linear_bf16_ex(const void *x, const int32_t *qweight, const void *scales,
+                                    void *y, int64_t M, int64_t K, int64_t N,
+                                    int64_t group_size, void *stream, int kernel) {
+    return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, kernel, true);
+}
+
+extern "C" int w4a16_linear_bf16(const void *x, const int32_t *qweight, const void *scales,
+                                 void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                                 void *stream) {
+    return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO,
+                       true);
 }
 
 extern "C" int pack_gptq_v2(const uint8_t *codes, int32_t *qweight, int64_t K, int64_t N) {

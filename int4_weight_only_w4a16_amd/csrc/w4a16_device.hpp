@@ -15,6 +15,8 @@ namespace w4a16 {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
@@ -136,6 +138,81 @@ __device__ __forceinline__ u2 pack4_f16(float a, float b, float c, float d) {
     h2 lo = {(_Float16)a, (_Float16)b};
     h2 hi = {(_Float16)c, (_Float16)d};
     u2 r = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    return r;
+}
+
+// ---- the activation type: fp16, or bfloat16 when BF ----
+// bfloat16 activations and outputs are the pages' serving dtype for this
+// checkpoint ("Qwen3.8-27B-GPTQ-Int4" model card, "4. Deployment"); scales
+// stay fp16 and accumulation fp32.
+
+// Two fp32 values rounded to nearest even in the activation type, packed
+// low-first in one dword (bfloat16: one v_cvt_pk_bf16_f32).
+template <bool BF>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (BF) {
+        const b2 v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        const h2 v = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+template <bool BF>
+__device__ __forceinline__ u2 pack4(float a, float b, float c, float d) {
+    return u2{pack2<BF>(a, b), pack2<BF>(c, d)};
+}
+
+// The MFMAs above on 16-bit operands given as raw bits (eight values each).
+template <bool BF>
+__device__ __forceinline__ f4 mfma16x16x32_t(u4 a, u4 b, f4 c) {
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a),
+                                                       __builtin_bit_cast(b8, b), c, 0, 0, 0);
+    else
+        return mfma16x16x32(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c);
+}
+
+template <bool BF>
+__device__ __forceinline__ f16v mfma32x32x16_t(u4 a, u4 b, f16v c) {
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, a),
+                                                       __builtin_bit_cast(b8, b), c, 0, 0, 0);
+    else
+        return mfma32x32x16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c);
+}
+
+// One byte of a dword as fp32 (v_cvt_f32_ubyte<d>).
+__device__ __forceinline__ float ubyte_f32(uint32_t v, int d) {
+    return (float)((v >> (8 * d)) & 0xFFu);
+}
+
+// The eight weights of word w as bfloat16: (q - 8) * s computed in fp32 as
+// fma(q, s, -8 s), exact there (a 4-bit integer times an fp16 scale), then
+// rounded once to nearest even.  gfx950 has no packed bfloat16 arithmetic,
+// so the magic-number trick of the fp16 path does not carry over.  lo holds
+// the even nibbles in its bytes (q0, q2, q4, q6), hi the odd ones.
+// NATURAL: order (q0, q1, ..., q7), else the fp16 unpack order (q0, q4, q1,
+// q5, q2, q6, q3, q7).
+template <bool NATURAL>
+__device__ __forceinline__ u4 dequant_bf16(uint32_t w, float s) {
+    const float m8s = -8.0f * s;
+    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    // opaque, so that each nibble is one v_cvt_f32_ubyte<d> of the masked
+    // word rather than a bit-field extract and a convert
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    auto wq = [&](uint32_t src, int d) { return __builtin_fmaf(ubyte_f32(src, d), s, m8s); };
+    u4 r;
+    if constexpr (NATURAL) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) r[d] = pack2<true>(wq(lo, d), wq(hi, d));
+    } else {
+        r[0] = pack2<true>(wq(lo, 0), wq(lo, 2));
+        r[1] = pack2<true>(wq(hi, 0), wq(hi, 2));
+        r[2] = pack2<true>(wq(lo, 1), wq(lo, 3));
+        r[3] = pack2<true>(wq(hi, 1), wq(hi, 3));
+    }
     return r;
 }
 

@@ -14,6 +14,7 @@ struct LinearArgs {
     const void *scales;
     void *y;
     int64_t M, K, N, group_size;
+    bool bf16;   // x and y are bfloat16 (else fp16); scales are fp16 either way
 };
 
 // Decode (M <= 16).  grid > 0 runs the stream-K kernel on `grid` workgroups

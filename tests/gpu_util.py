@@ -31,6 +31,38 @@ def check_parity(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = "") -> dict:
     return {"max_abs": float(d.max()) if d.size else 0.0, "bound": bound, "mean_rel": mean_rel}
 
 
+# bfloat16 activations and output: the bar follows from the arithmetic the C
+# ABI states for w4a16_linear_bf16 (each weight rounded once to bfloat16, fp32
+# accumulation, y rounded once to bfloat16; u = 2^-8 is half a bfloat16 ulp
+# relative):  |y - y_ref| <= u |y_ref| + 1.02 (u + K 2^-24) sum_k |x||w| per
+# element, with sum|x||w| from the oracle; and, so that a wrong term cannot
+# hide inside that worst-case bound, sum|y - y_ref| / sum|y_ref| <= u.
+BF16_U = 2.0 ** -8
+
+
+def check_parity_bf16(y_gpu: np.ndarray, y_ref: np.ndarray, mag: np.ndarray, K: int,
+                      what: str = "") -> dict:
+    y = y_gpu.astype(np.float64)
+    d = np.abs(y - y_ref)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    bound = BF16_U * np.abs(y_ref) + 1.02 * (BF16_U + K * 2.0 ** -24) * mag + 1e-30
+    bad = d > bound
+    worst = int(np.argmax(d - bound)) if d.size else 0
+    assert not np.any(bad), \
+        f"{what}: {int(bad.sum())} elements beyond the bound; worst at flat index {worst}: " \
+        f"|d| {float(d.flat[worst]):.4g} > {float(bound.flat[worst]):.4g}"
+    denom = float(np.abs(y_ref).sum())
+    mean_rel = float(d.sum()) / denom if denom > 0 else float(d.sum())
+    assert mean_rel <= BF16_U, f"{what}: mean relative error {mean_rel:.4g} > {BF16_U}"
+    return {"max_abs": float(d.max()) if d.size else 0.0, "mean_rel": mean_rel}
+
+
+def bf16_to_float(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16 or int16) -> float64 (the top half of a float32)."""
+    b = np.asarray(bits).view(np.uint16).astype(np.uint32)
+    return (b << 16).view(np.float32).astype(np.float64)
+
+
 class Runner:
     """Uploads a case's inputs and runs the HIP path through the C ABI."""
 

@@ -53,8 +53,10 @@ def test_header_compiles_as_c():
                         src, "-o", os.path.join(d, "t")], check=True)
 
 
-def _call(lib, x=0x1000, q=0x2000, s=0x3000, y=0x4000, M=1, K=32, N=8, g=32, kernel=0):
-    return lib.w4a16_linear_ex(x, q, s, y, M, K, N, g, None, kernel)
+def _call(lib, x=0x1000, q=0x2000, s=0x3000, y=0x4000, M=1, K=32, N=8, g=32, kernel=0,
+          bf16=False):
+    f = lib.w4a16_linear_bf16_ex if bf16 else lib.w4a16_linear_ex
+    return f(x, q, s, y, M, K, N, g, None, kernel)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -82,16 +84,19 @@ def _call(lib, x=0x1000, q=0x2000, s=0x3000, y=0x4000, M=1, K=32, N=8, g=32, ker
     (dict(kernel=3), w4.W4A16_ERR_KERNEL),
     (dict(kernel=-1), w4.W4A16_ERR_KERNEL),
 ])
-def test_invalid_arguments_rejected_before_any_hip_call(lib, kw, status):
-    assert _call(lib, **kw) == status
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp16", "bf16"])
+def test_invalid_arguments_rejected_before_any_hip_call(lib, kw, status, bf16):
+    assert _call(lib, bf16=bf16, **kw) == status
 
 
-def test_empty_batch_is_a_noop(lib):
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp16", "bf16"])
+def test_empty_batch_is_a_noop(lib, bf16):
     # M == 0: OK without touching the (null) pointers or the device
-    assert _call(lib, x=0, q=0, s=0, y=0, M=0) == w4.W4A16_OK
-    assert lib.w4a16_linear(0, 0, 0, 0, 0, 5120, 17408, 128, None) == w4.W4A16_OK
+    assert _call(lib, x=0, q=0, s=0, y=0, M=0, bf16=bf16) == w4.W4A16_OK
+    auto = lib.w4a16_linear_bf16 if bf16 else lib.w4a16_linear
+    assert auto(0, 0, 0, 0, 0, 5120, 17408, 128, None) == w4.W4A16_OK
     # ...but an invalid shape is still an error at M == 0
-    assert _call(lib, M=0, K=40) == w4.W4A16_ERR_SHAPE
+    assert _call(lib, M=0, K=40, bf16=bf16) == w4.W4A16_ERR_SHAPE
 
 
 def test_status_strings(lib):

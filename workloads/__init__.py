@@ -89,7 +89,21 @@ def _draw_x(rng: np.random.Generator, kind: str, M: int, K: int) -> np.ndarray:
     raise ValueError(f"unknown x recipe {kind!r}")
 
 
-def generate(case: Case) -> Inputs:
+def bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Values -> bfloat16 bit patterns (uint16): through float32, then rounded
+    to nearest even on the top 16 bits (finite inputs).  Activations for the
+    bfloat16 variant are the same draws as for fp16, given in this type."""
+    f = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((f + 0x7FFF + ((f >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def generate_bf16(case: Case) -> Inputs:
+    """As generate, with x as bfloat16 bit patterns (uint16 [M, K]) of the
+    same draws."""
+    return generate(case, act="bf16")
+
+
+def generate(case: Case, act: str = "f16") -> Inputs:
     """Draw one case's inputs in the fixed order stated in the module docstring."""
     rng = np.random.default_rng(case.seed)
     K, N, M, G, g = case.K, case.N, case.M, case.G, case.group_size
@@ -111,7 +125,7 @@ def generate(case: Case) -> Inputs:
         n_out = int(round(case.outlier_frac * K))
         outliers = np.sort(rng.choice(K, size=n_out, replace=False))
         x64[:, outliers] *= 20.0
-    x = x64.astype(np.float16)
+    x = bf16_bits(x64) if act == "bf16" else x64.astype(np.float16)
     return Inputs(codes=codes, scales=scales, x=x, zero_cells=zero_cells,
                   outlier_channels=outliers)
 
