@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 MALL_BYTES = 256 * 2 ** 20
 
 
@@ -115,14 +116,17 @@ class Timed:
         return e0.elapsed_time(e1) / 1e3 / steps
 
 
-def prepare(torch, w4, case, inp, rotations):
+def prepare(torch, w4, case, inp, rotations, bf16=False):
     dev = torch.device("cuda:0")
     q = torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev)
     s = torch.from_numpy(inp.scales).to(dev)
     qs = [q] + [q.clone() for _ in range(rotations - 1)]
     ss = [s] + [s.clone() for _ in range(rotations - 1)]
-    x = torch.from_numpy(inp.x).to(dev)
-    y = torch.empty((case.M, case.N), dtype=torch.float16, device=dev)
+    if bf16:   # bfloat16 bit patterns -> a bfloat16 tensor
+        x = torch.from_numpy(inp.x.view("int16")).view(torch.bfloat16).to(dev)
+    else:
+        x = torch.from_numpy(inp.x).to(dev)
+    y = torch.empty((case.M, case.N), dtype=x.dtype, device=dev)
     return x, qs, ss, y
 
 
@@ -130,15 +134,16 @@ def rotations_for(weight_bytes: int, minimum: int = 2) -> int:
     return max(minimum, -(-2 * MALL_BYTES // weight_bytes))
 
 
-def bench_case(torch, w4, case, steps, warmup, eager):
+def bench_case(torch, w4, case, steps, warmup, eager, bf16=False):
     import workloads
-    inp = workloads.generate(case)
+    inp = workloads.generate_bf16(case) if bf16 else workloads.generate(case)
     wbytes = case.K * case.N // 2 + 2 * case.G * case.N
     R = rotations_for(wbytes)
-    x, qs, ss, y = prepare(torch, w4, case, inp, R)
+    x, qs, ss, y = prepare(torch, w4, case, inp, R, bf16)
+    call = w4.w4a16_linear_bf16 if bf16 else w4.w4a16_linear
 
     def step(i):
-        w4.w4a16_linear(x, qs[i % R], ss[i % R], y, case.M, case.K, case.N, case.group_size)
+        call(x, qs[i % R], ss[i % R], y, case.M, case.K, case.N, case.group_size)
 
     sec = Timed(torch).run(step, steps, warmup, eager)
     return inp, y, sec, R
@@ -231,6 +236,8 @@ def main():
     ap.add_argument("--only", choices=("all", "decode", "prefill"), default="all")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement")
+    ap.add_argument("--no-bf16", action="store_true",
+                    help="skip the bfloat16-activation variant's decode and prefill lines")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args()
@@ -315,6 +322,33 @@ def main():
                 out["cpu_baseline"] = pre["cpu_baseline"]
         else:
             out["prefill"] = pre
+
+    if args.only == "all" and not args.no_bf16:
+        # the bfloat16-activation variant on the same two workloads (same
+        # algorithmic bytes and flops; x and y in bfloat16)
+        bf = {}
+        case = workloads.decode_up()
+        _, _, sec, R = bench_case(torch, w4, case, args.steps, args.warmup, args.eager, True)
+        gbs = algorithmic_bytes(case.M, case.K, case.N, case.G) / sec / 1e9
+        bf["decode"] = {"workload": out["config"]["workload"] + ", bfloat16 x/y",
+                        "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": sec * 1e3,
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+        torch.cuda.empty_cache()
+        case = workloads.prefill_up()
+        psteps = args.prefill_steps or max(10, args.steps // 4)
+        _, _, sec, R = bench_case(torch, w4, case, psteps, max(1, min(args.warmup, psteps)),
+                                  args.eager, True)
+        tflops = 2.0 * case.M * case.N * case.K / sec / 1e12
+        bf["prefill"] = {"workload": "prefill up-projection GEMM M=2048 K=5120 N=17408 g=128, "
+                                     "bfloat16 x/y",
+                         "value": round(tflops, 1), "unit": "TFLOP/s", "ms_per_step": sec * 1e3,
+                         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}}
+        torch.cuda.empty_cache()
+        out["bf16"] = bf
 
     out["device"] = dev_name
     out["timing"] = "eager launches" if args.eager else "one HIP graph of K steps"
