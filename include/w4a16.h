@@ -39,8 +39,9 @@
  *         slots, left zeroed by every launch, and two 16x64 fp32 partial
  *         tiles, written before they are read);
  *       prefill: 64 MiB on a 256-CU device (one 256x256 fp32 partial tile
- *         per CU), used by M > 128 when a last partial round of tiles is
- *         split along K.
+ *         per CU), used when a last partial round of tiles is split along
+ *         K (M > 128) and when fewer tiles than CUs are split along K
+ *         (M <= 128: fp32 partials of y, one per K chunk).
  *     A call on a stream that is being captured into a graph and has no
  *     workspace yet allocates nothing and runs a kernel that needs none.
  *     Calls on one stream share its workspaces in stream order; calls on
@@ -48,7 +49,10 @@
  *   - Device calls are asynchronous on the given stream (a hipStream_t; 0 is
  *     the null stream); results are valid once the stream is synchronised.
  *     No call synchronises the device and nothing is printed.
- *   - Results are deterministic: the same inputs give bit-identical y.
+ *   - Results are deterministic: the same inputs give bit-identical y on
+ *     a given device.  (A call under capture on a stream with no workspace
+ *     yet runs a kernel that needs none, whose summation order, and so
+ *     whose last bits, may differ.)
  */
 #ifndef W4A16_H
 #define W4A16_H

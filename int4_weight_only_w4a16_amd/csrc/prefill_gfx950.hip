@@ -51,11 +51,14 @@ constexpr int kPreSteps = kPreBK / 16;    // 16-deep MFMA steps per stage
 
 // gshift: log2(group_size), or -1 for a single group over K.  BF: bfloat16
 // activations and output (weights dequantised by dequant_bf16).
+// Split K: workgroup z of `chunks` takes the 64-deep stages [sb, se) of its
+// tile; with chunks > 1 it writes its fp32 sums to partials[z][M][N] and
+// prefill_chunk_reduce_kernel adds the chunks, else it stores y.
 template <bool BF>
 __global__ __launch_bounds__(256) void prefill_m128_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
-    int gshift) {
+    int gshift, int chunks, float *__restrict__ partials) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kPreRing * kPreStageBytes];
 
     const int tid = threadIdx.x;
@@ -66,6 +69,10 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
     const int m0 = blockIdx.y * kPreBM;
     const int n = blockIdx.x * kPreBN + wave * 64 + 2 * c32;   // the lane's two columns
     const int G = gshift < 0 ? 1 : ((K - 1) >> gshift) + 1;
+    const int nst = (K + kPreBK - 1) / kPreBK;
+    const int cz = blockIdx.z;
+    const int sb = (int)((int64_t)nst * cz / chunks);
+    const int se = (int)((int64_t)nst * (cz + 1) / chunks);
 
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
     const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
@@ -86,11 +93,12 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
         a_goff[i] = ((uint32_t)(m0 + row) * (uint32_t)K + 8u * kc) * 2u;
         a_loff[i] = row * kPreRowBytes + kc * 16;
     }
+    // stages outside [sb, se) read zero (the ring runs up to two past se)
     auto load_a = [&](u4 (&r)[4], int st) {
         const int k0 = st * kPreBK;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool ok = a_row_ok[i] && (k0 + 8 * a_kc[i] < K);
+            const bool ok = a_row_ok[i] && st < se && (k0 + 8 * a_kc[i] < K);
             r[i] = load_b128(xr, ok ? a_goff[i] + (uint32_t)k0 * 2u : kOOB);
         }
     };
@@ -108,8 +116,10 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
         for (int h = 0; h < kPreSteps; ++h) {
             const int t = kPreSteps * st + h;
             const uint32_t srow = gshift < 0 ? 0u : (uint32_t)(16 * t) >> gshift;
-            w[h] = load_b64(qr, q_off0 + (uint32_t)t * q_step);
-            s[h] = __builtin_amdgcn_raw_buffer_load_b32(sr, (srow * (uint32_t)N + (uint32_t)n) * 2u, 0, 0);
+            const bool in = st < se;
+            w[h] = load_b64(qr, in ? q_off0 + (uint32_t)t * q_step : kOOB);
+            s[h] = __builtin_amdgcn_raw_buffer_load_b32(
+                sr, in ? (srow * (uint32_t)N + (uint32_t)n) * 2u : kOOB, 0, 0);
         }
     };
 
@@ -160,7 +170,6 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
         }
     };
 
-    const int nst = (K + kPreBK - 1) / kPreBK;
     u4 areg[kPreRing][4];
     u2 wreg[kPreRing][kPreSteps];
     uint32_t sreg[kPreRing][kPreSteps];
@@ -168,29 +177,29 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
     // Prologue in the loop's issue order (stage st's loop iteration issues A
     // of st+4, then B of st+3), so the compiler's wait counts in the loop
     // stay deep.  Loads past the last stage read zero and are not used.
-    load_a(areg[0], 0);
+    load_a(areg[0], sb);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(areg[1], 1);
+    load_a(areg[1], sb + 1);
     __builtin_amdgcn_sched_barrier(0);
-    load_b(wreg[0], sreg[0], 0);
+    load_b(wreg[0], sreg[0], sb);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(areg[2], 2);
+    load_a(areg[2], sb + 2);
     __builtin_amdgcn_sched_barrier(0);
-    load_b(wreg[1], sreg[1], 1);
+    load_b(wreg[1], sreg[1], sb + 1);
     __builtin_amdgcn_sched_barrier(0);
     store_a(areg[0], 0);
-    load_a(areg[0], 3);
+    load_a(areg[0], sb + 3);
     __builtin_amdgcn_sched_barrier(0);
-    load_b(wreg[2], sreg[2], 2);
+    load_b(wreg[2], sreg[2], sb + 2);
     __builtin_amdgcn_sched_barrier(0);
     store_a(areg[1], 1);
     __syncthreads();
     h8 afrag[4];
     read_a(afrag, 0, 0);
 
-    // Stages past nst (up to two, to finish a round of three) compute on
-    // zeros: every load there is out of range.
-    for (int st0 = 0; st0 < nst; st0 += kPreRing) {
+    // Stages past se (up to two, to finish a round of three) compute on
+    // zeros: every load there reads zero.
+    for (int st0 = sb; st0 < se; st0 += kPreRing) {
 #pragma unroll
         for (int r = 0; r < kPreRing; ++r) {
             const int st = st0 + r;
@@ -205,12 +214,17 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
     // ---- epilogue: register i of tile (mt, j) is row m0 + 32 mt + 8 (i/4) +
     // 4 kb + i%4, column n + j; the two columns of a lane go out together ----
     if (n < N) {
+        float *pz = partials ? partials + (size_t)cz * M * N : nullptr;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
-                if (m < M)
+                if (m >= M) continue;
+                if (pz)
+                    *reinterpret_cast<float2 *>(pz + (size_t)m * N + n) =
+                        float2{acc[mt][0][i], acc[mt][1][i]};
+                else
                     *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) =
                         pack2<BF>(acc[mt][0][i], acc[mt][1][i]);
             }
@@ -218,20 +232,66 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
     }
 }
 
-static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream) {
+// y = the sum of the chunks' partials[c][M][N] in chunk order (fixed, so
+// results are bit-reproducible); four consecutive elements per thread
+// (N % 8 == 0, so they stay in one row).
+template <bool BF>
+__global__ __launch_bounds__(256) void prefill_chunk_reduce_kernel(
+    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int chunks) {
+    const int64_t total = (int64_t)M * N;
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= total) return;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < chunks; ++c) {
+        const f4 p = *reinterpret_cast<const f4 *>(partials + (size_t)c * total + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] += p[j];
+    }
+    *reinterpret_cast<u2 *>(y + e) = pack4<BF>(v[0], v[1], v[2], v[3]);
+}
+
+// K chunks for the 128-row kernel: with fewer tiles than CUs, split each
+// tile's K into about CUs / tiles chunks of at least 8 stages, as long as the
+// partials fit the prefill workspace (capacity x 256 KiB).
+static int m128_chunks(const LinearArgs &a, int num_cus) {
+    if (num_cus <= 0) return 1;
+    const int64_t tiles = ((a.N + kPreBN - 1) / kPreBN) * ((a.M + kPreBM - 1) / kPreBM);
+    const int64_t nst = (a.K + kPreBK - 1) / kPreBK;
+    int64_t chunks = std::min<int64_t>(num_cus / tiles, nst / 8);
+    const int64_t fit = (int64_t)num_cus * 256 * 256 / (a.M * a.N);
+    chunks = std::min(chunks, fit);
+    return chunks < 2 ? 1 : (int)chunks;
+}
+
+static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream, void *workspace,
+                                      int capacity, int num_cus) {
     int K = (int)a.K, N = (int)a.N, M = (int)a.M;
     int gshift = -1;
     if (a.group_size != -1) gshift = __builtin_ctz((unsigned)a.group_size);
+    int chunks = m128_chunks(a, num_cus);
+    if (chunks > 1 && (!workspace ||
+                       (size_t)chunks * M * N * sizeof(float) > (size_t)capacity * 256 * 256 * 4))
+        chunks = 1;
+    float *partials = chunks > 1 ? static_cast<float *>(workspace) : nullptr;
     const void *xp = a.x;
     const void *qp = a.qweight;
     const void *sp = a.scales;
     void *yp = a.y;
-    void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift};
-    dim3 grid((unsigned)((N + kPreBN - 1) / kPreBN), (unsigned)((M + kPreBM - 1) / kPreBM));
+    void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &chunks, &partials};
+    dim3 grid((unsigned)((N + kPreBN - 1) / kPreBN), (unsigned)((M + kPreBM - 1) / kPreBM),
+              (unsigned)chunks);
     dim3 block(256);
     const void *k = a.bf16 ? reinterpret_cast<const void *>(&prefill_m128_kernel<true>)
                            : reinterpret_cast<const void *>(&prefill_m128_kernel<false>);
-    return hipLaunchKernel(k, grid, block, args, 0, stream);
+    hipError_t e = hipLaunchKernel(k, grid, block, args, 0, stream);
+    if (e != hipSuccess || chunks == 1) return e;
+    const float *pc = partials;
+    void *rargs[] = {&pc, &yp, &M, &N, &chunks};
+    const void *rk = a.bf16 ? reinterpret_cast<const void *>(&prefill_chunk_reduce_kernel<true>)
+                            : reinterpret_cast<const void *>(&prefill_chunk_reduce_kernel<false>);
+    const int64_t threads = ((int64_t)M * N + 3) / 4;
+    return hipLaunchKernel(rk, dim3((unsigned)((threads + 255) / 256)), dim3(256), rargs, 0,
+                           stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -768,7 +828,8 @@ static WidePlan wide_plan(const LinearArgs &a, int num_cus) {
 size_t prefill_workspace_bytes(int capacity) { return (size_t)capacity * kWSlot * sizeof(float); }
 
 bool prefill_wants_workspace(const LinearArgs &a, int num_cus) {
-    return a.M > 128 && wide_plan(a, num_cus).chunks > 1;
+    if (a.M > 128) return wide_plan(a, num_cus).chunks > 1;
+    return m128_chunks(a, num_cus) > 1;
 }
 
 static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, void *workspace,
@@ -802,7 +863,7 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                           int num_cus) {
     if (a.M > 128) return launch_prefill_m256(a, stream, workspace, capacity, num_cus);
-    return launch_prefill_m128(a, stream);
+    return launch_prefill_m128(a, stream, workspace, capacity, num_cus);
 }
 
 }  // namespace w4a16

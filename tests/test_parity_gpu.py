@@ -336,36 +336,48 @@ def test_decode_tiles_kernel_path(dev):
 
 
 def test_graph_capture_and_replay(dev):
-    """Decode and prefill captured in a HIP graph on a fresh stream, replayed
-    several times with eager work in between; every replay matches eager."""
+    """Decode and prefill captured in a HIP graph, replayed several times with
+    eager work in between; every replay matches the oracle.  On a fresh stream
+    (no workspace yet) the captured calls run kernels that need none; on a
+    stream that already has its workspaces the graph runs the same kernels as
+    eager calls there (split-K partials and their reduce included), so every
+    replay equals those bit for bit."""
     cases = [workloads.Case("g_dec", 4, 5120, 2048, 128, 29),
-             workloads.Case("g_pre", 96, 1024, 1032, 64, 30)]
+             workloads.Case("g_pre", 96, 1024, 1032, 64, 30),
+             workloads.Case("g_pre_wide", 300, 2048, 2048, 128, 31)]
     prepared = []
     for c in cases:
         inp = workloads.generate(c)
+        y_ref = oracle.linear(inp.x, oracle.pack(inp.codes), inp.scales, c.group_size)
         prepared.append((c, torch.from_numpy(inp.x).to(dev),
                          torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev),
-                         torch.from_numpy(inp.scales).to(dev)))
-    eager = [w4.linear(x, q, s, c.group_size) for c, x, q, s in prepared]
-    torch.cuda.synchronize()
-    outs = [torch.empty_like(e) for e in eager]
-    st = torch.cuda.Stream()           # no workspace exists for this stream yet
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=st):
-        for (c, x, q, s), y in zip(prepared, outs):
-            w4.w4a16_linear(x, q, s, y, c.M, c.K, c.N, c.group_size, st)
-    for rep in range(4):
-        for y in outs:
-            y.fill_(-1.0)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        for (c, x, q, s), y, e in zip(prepared, outs, eager):
-            inp = workloads.generate(c)
-            y_ref = oracle.linear(inp.x, oracle.pack(inp.codes), inp.scales, c.group_size)
-            check_parity(y.cpu().numpy(), y_ref, f"{c.name} replay {rep}")
-            if c.M > w4.W4A16_DECODE_MAX_M:
-                assert torch.equal(y, e)
+                         torch.from_numpy(inp.scales).to(dev), y_ref))
+    for warm in (False, True):
+        st = torch.cuda.Stream()
+        eager = None
+        if warm:                       # the stream gets its workspaces eagerly first
+            eager = []
+            for c, x, q, s, _ in prepared:
+                e = torch.empty((c.M, c.N), dtype=torch.float16, device=dev)
+                w4.w4a16_linear(x, q, s, e, c.M, c.K, c.N, c.group_size, st)
+                eager.append(e)
+            torch.cuda.synchronize()
+        outs = [torch.empty((c.M, c.N), dtype=torch.float16, device=dev)
+                for c, *_ in prepared]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for (c, x, q, s, _), y in zip(prepared, outs):
+                w4.w4a16_linear(x, q, s, y, c.M, c.K, c.N, c.group_size, st)
+        for rep in range(4):
+            for y in outs:
+                y.fill_(-1.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for i, ((c, x, q, s, y_ref), y) in enumerate(zip(prepared, outs)):
+                check_parity(y.cpu().numpy(), y_ref, f"{c.name} warm={warm} replay {rep}")
+                if warm:
+                    assert torch.equal(y, eager[i]), (c.name, rep)
 
 
 def test_decode_launches_of_different_grids_share_a_stream(dev):
@@ -450,6 +462,29 @@ def test_decode_wide_partials_ragged(dev, M):
     y_ref = oracle.linear(inp.x, q_o, inp.scales, 16)
     runs = [_run(inp, q_dev, s_dev, 16, dev, DEC) for _ in range(3)]
     check_parity(runs[0], y_ref, f"wide M={M}")
+    for r in runs[1:]:
+        assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N,g,full", [
+    (64, 2064, 1032, 16, True),      # 5 tiles x 4 chunks; last stage half inside K
+    (17, 5120, 17408, 128, False),   # 68 tiles x 3 chunks
+    (128, 17408, 5120, 32, False),   # 20 tiles x 12 chunks
+    (100, 1024, 264, -1, True),      # 2 tiles x 2 chunks (16 stages), ragged M and N
+])
+def test_prefill_m128_split_k(dev, M, K, N, g, full):
+    """M <= 128 with fewer tiles than CUs: each tile's K is split into chunks
+    whose fp32 partials a second kernel adds in chunk order."""
+    case = workloads.Case(f"m128split_{M}_{K}_{N}", M, K, N, g, 46, scales="loguniform")
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    runs = [_run(inp, q_dev, s_dev, g, dev, PRE) for _ in range(3)]
+    if full:
+        check_parity(runs[0], oracle.linear(inp.x, q_o, inp.scales, g), f"{case.name}")
+    else:
+        ms, ns = sample_indices(M, N, 4096, seed=47)
+        y_ref = oracle.linear_at(inp.x, q_o, inp.scales, g, ms, ns)
+        check_parity(runs[0][ms, ns], y_ref, f"{case.name} (sampled)")
     for r in runs[1:]:
         assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
 
