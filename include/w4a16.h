@@ -113,11 +113,16 @@ int w4a16_linear_ex(const void *x, const int32_t *qweight, const void *scales, v
  *   x : device bfloat16 [M, K];  y : device bfloat16 [M, N];
  *   qweight, scales (fp16), shapes, group sizes, alignment, stream, dispatch,
  *   errors and workspaces exactly as for w4a16_linear.
- * Arithmetic: every weight (q - 8) * s is formed exactly in fp32 and rounded
- * once to bfloat16 (nearest even) for the bfloat16 matrix instructions;
- * products accumulate in fp32; y is rounded once to bfloat16 (nearest even).
- * Hence |y - y_exact| <= 2^-8 |y_exact| + (2^-8 + K 2^-24) sum_k |x||w| per
- * element (both roundings at most half a bfloat16 ulp, fp32 accumulation).
+ * Arithmetic: products accumulate in fp32 and y is rounded once to bfloat16
+ * (nearest even).  Prefill, and decode with g = 16, form every weight
+ * (q - 8) * s exactly in fp32 and round it once to bfloat16 for the bfloat16
+ * matrix instructions; decode with g >= 32 (or -1) sums x * (128 + q), exact
+ * in bfloat16, and x * 136 over each group and takes s * (the difference) in
+ * fp32 (a group whose codes are all 8 adds exactly zero).
+ * Hence, per element, |y - y_exact| <= 2^-8 |y_exact|
+ *   + (2^-8 + K 2^-24) sum_k |x||w| + 35 K 2^-24 * 8 sum_k |x| s
+ * (each rounding at most half a bfloat16 ulp; fp32 accumulation, including
+ * the cancellation of the 128 offset).
  * Results are deterministic, as for fp16. */
 int w4a16_linear_bf16(const void *x, const int32_t *qweight, const void *scales, void *y,
                       int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream);

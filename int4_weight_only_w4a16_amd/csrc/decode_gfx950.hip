@@ -144,9 +144,13 @@ __device__ __forceinline__ void store_row4(uint16_t *dst, const float (&v)[4]) {
 // scale-after with one step per group (g = 32): every MFMA starts from zero
 // and its result is scaled straight into the sum.  SCALE picks which scale
 // row each unit loads.
-// BF: bfloat16 activations.  Every weight is then dequantised before the
-// MFMA, (q - 8) * s exactly in fp32 and rounded once to bfloat16
-// (dequant_bf16), for every group size.
+// BF: bfloat16 activations.  With SCALE 0 (g = 16) every weight is
+// dequantised before the MFMA, (q - 8) * s exactly in fp32 and rounded once
+// to bfloat16 (dequant_bf16).  Otherwise the MFMA sums x * (128 + q) over the
+// group (codes128_bf16, exact) and a second MFMA sums x * 136 over the same
+// steps; at the group's end acc += s * (sum - sum136) in fp32.  Where every
+// code of a group is 8 the two sums are the same operations on the same
+// values, so that group adds exactly zero, as (8 - 8) * s does.
 template <int D, int SCALE, bool XLDS, bool BF, typename Dump, typename AfterPrologue>
 __device__ __forceinline__ void decode_units(
     const __amdgpu_buffer_rsrc_t xr, const __amdgpu_buffer_rsrc_t qr,
@@ -213,7 +217,7 @@ __device__ __forceinline__ void decode_units(
         ++li;
     };
 
-    f4 acc[kNW], accg[kNW];
+    f4 acc[kNW], accg[kNW], accx = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kNW; ++j) {
         acc[j] = f4{0.f, 0.f, 0.f, 0.f};
@@ -244,12 +248,31 @@ __device__ __forceinline__ void decode_units(
         else
             a = __builtin_bit_cast(h8, perm_x(st.x));
         const bool seg_end = i == nA - 1 || i == n - 1;
-        if constexpr (BF) {
+        if constexpr (BF && SCALE == 0) {
 #pragma unroll
             for (int j = 0; j < kNW; ++j)
                 acc[j] = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a),
                                               dequant_bf16<false>(st.w[j], (float)scale_at(st.s, j)),
                                               acc[j]);
+        } else if constexpr (BF) {
+            const u4 b136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};   // bf16 136.0
+#pragma unroll
+            for (int j = 0; j < kNW; ++j)
+                accg[j] = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), codes128_bf16(st.w[j], uc),
+                                               accg[j]);
+            accx = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), b136, accx);
+            if (pos == group_steps - 1 || seg_end) {
+#pragma unroll
+                for (int j = 0; j < kNW; ++j) {
+                    const float sj = (float)scale_at(st.s, j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[j][e] = __builtin_fmaf(sj, accg[j][e] - accx[e], acc[j][e]);
+                    accg[j] = f4{0.f, 0.f, 0.f, 0.f};
+                }
+                accx = f4{0.f, 0.f, 0.f, 0.f};
+            }
+            pos = (pos + 1 == group_steps) ? 0 : pos + 1;
         } else if constexpr (SCALE == 2) {
 #pragma unroll
             for (int j = 0; j < kNW; ++j) {

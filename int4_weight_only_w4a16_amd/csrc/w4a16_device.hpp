@@ -188,6 +188,20 @@ __device__ __forceinline__ float ubyte_f32(uint32_t v, int d) {
     return (float)((v >> (8 * d)) & 0xFFu);
 }
 
+// The eight codes of word w as bfloat16 128 + q, exactly (q in the low
+// mantissa bits of 128.0 = 0x4300), in the fp16 unpack order (q0, q4, q1,
+// q5, q2, q6, q3, q7): one v_and_or_b32 per pair.  A sum of x * (128 + q)
+// minus the sum of x * 136 is the sum of x * (q - 8).
+__device__ __forceinline__ u4 codes128_bf16(uint32_t w, const UnpackConsts &c) {
+    const uint32_t magic = 0x43004300u;
+    u4 r;
+    r[0] = (w & c.lo) | magic;
+    r[1] = ((w >> 4) & c.lo) | magic;
+    r[2] = ((w >> 8) & c.lo) | magic;
+    r[3] = ((w >> 12) & c.lo) | magic;
+    return r;
+}
+
 // The eight weights of word w as bfloat16: (q - 8) * s computed in fp32 as
 // fma(q, s, -8 s), exact there (a 4-bit integer times an fp16 scale), then
 // rounded once to nearest even.  gfx950 has no packed bfloat16 arithmetic,

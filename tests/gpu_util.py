@@ -32,20 +32,25 @@ def check_parity(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = "") -> dict:
 
 
 # bfloat16 activations and output: the bar follows from the arithmetic the C
-# ABI states for w4a16_linear_bf16 (each weight rounded once to bfloat16, fp32
-# accumulation, y rounded once to bfloat16; u = 2^-8 is half a bfloat16 ulp
-# relative):  |y - y_ref| <= u |y_ref| + 1.02 (u + K 2^-24) sum_k |x||w| per
-# element, with sum|x||w| from the oracle; and, so that a wrong term cannot
-# hide inside that worst-case bound, sum|y - y_ref| / sum|y_ref| <= u.
+# ABI states for w4a16_linear_bf16 (u = 2^-8 is half a bfloat16 ulp relative):
+# weights rounded once to bfloat16 or summed exactly as 128 + q with the bias
+# removed in fp32, fp32 accumulation, y rounded once to bfloat16:
+#   |y - y_ref| <= u |y_ref| + 1.02 (u + K 2^-24) sum_k |x||w|
+#                  + 1.02 * 35 K 2^-24 * 8 sum_k |x| s          (mag0)
+# per element, with sum|x||w| and 8 sum|x| s (the magnitude sum of all-zero
+# codes) from the oracle; and, so that a wrong term cannot hide inside that
+# worst-case bound, sum|y - y_ref| / sum|y_ref| <= u.
 BF16_U = 2.0 ** -8
 
 
 def check_parity_bf16(y_gpu: np.ndarray, y_ref: np.ndarray, mag: np.ndarray, K: int,
-                      what: str = "") -> dict:
+                      what: str = "", mag0=None) -> dict:
     y = y_gpu.astype(np.float64)
     d = np.abs(y - y_ref)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
     bound = BF16_U * np.abs(y_ref) + 1.02 * (BF16_U + K * 2.0 ** -24) * mag + 1e-30
+    if mag0 is not None:
+        bound = bound + 1.02 * 35 * K * 2.0 ** -24 * mag0
     bad = d > bound
     worst = int(np.argmax(d - bound)) if d.size else 0
     assert not np.any(bad), \

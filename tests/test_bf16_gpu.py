@@ -60,15 +60,18 @@ def _run(x, q, s, g, kernel):
     (64, 1040, 776, -1, (PRE,)),        # 128-row prefill kernel, ragged K and N
     (300, 1536, 1032, 512, (PRE,)),     # 256-row prefill kernel, ragged M and N
     (2, 2048, 4096, 1024, (DEC,)),
+    (4, 5120, 2048, 32, (DEC,)),        # one step per group (group end every unit)
+    (7, 8192, 1032, -1, (DEC,)),        # one group over K: the longest bias sums
 ])
 def test_bf16_parity_full(dev, M, K, N, g, kernels):
     case = workloads.Case(f"bf16_{M}_{K}_{N}_{g}", M, K, N, g, 50 + M, scales="loguniform")
     inp, q_o, x, q, s = _upload(case, dev)
     y_ref = oracle.linear(inp.x, q_o, inp.scales, g, act="bf16")
     mag = oracle.linear(inp.x, q_o, inp.scales, g, act="bf16", absval=True)
+    mag0 = oracle.linear(inp.x, np.zeros_like(q_o), inp.scales, g, act="bf16", absval=True)
     for k in kernels:
         y = bf16_to_float(_run(x, q, s, g, k))
-        check_parity_bf16(y, y_ref, mag, K, f"{case.name} kernel={k}")
+        check_parity_bf16(y, y_ref, mag, K, f"{case.name} kernel={k}", mag0)
 
 
 @pytest.mark.parametrize("M,K,N,g", [
@@ -82,8 +85,11 @@ def test_bf16_parity_model_shapes_sampled(dev, M, K, N, g):
     ms, ns = sample_indices(M, N, 2048, seed=61)
     y_ref = oracle.linear_at(inp.x, q_o, inp.scales, g, ms, ns, act="bf16")
     mag = oracle.linear_at(inp.x, q_o, inp.scales, g, ms, ns, act="bf16", absval=True)
+    mag0 = oracle.linear_at(inp.x, np.zeros_like(q_o), inp.scales, g, ms, ns, act="bf16",
+                            absval=True)
     runs = [_run(x, q, s, g, AUTO) for _ in range(2)]
-    check_parity_bf16(bf16_to_float(runs[0])[ms, ns], y_ref, mag, K, f"{case.name} (sampled)")
+    check_parity_bf16(bf16_to_float(runs[0])[ms, ns], y_ref, mag, K, f"{case.name} (sampled)",
+                      mag0)
     assert np.array_equal(runs[0], runs[1]), "bfloat16 results differ between runs"
 
 
