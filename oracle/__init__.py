@@ -80,9 +80,10 @@ class Oracle:
         i32 = ctypes.c_int
         lib.oracle_linear_ex.argtypes = [p, i32, i32, p, p, i64, i64, i64, i64, p]
         lib.oracle_linear_at_ex.argtypes = [p, i32, i32, p, p, i64, i64, i64, i64, p, p, i64, p]
+        lib.oracle_gate_up_silu.argtypes = [p, i32, p, p, i64, i64, i64, i64, p]
         for f in (lib.oracle_unpack, lib.oracle_pack, lib.oracle_dequant,
                   lib.oracle_linear, lib.oracle_linear_at, lib.oracle_linear_ex,
-                  lib.oracle_linear_at_ex):
+                  lib.oracle_linear_at_ex, lib.oracle_gate_up_silu):
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -166,6 +167,22 @@ class Oracle:
         return out
 
 
+    def gate_up_silu(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+                     group_size: int, act: str = "f16") -> np.ndarray:
+        """out [M, N/2] float64 = silu(y[:, 0::2]) * y[:, 1::2], y the linear (columns
+        alternate gate and up)."""
+        xb = _act_bits(x, act)
+        qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+        scales = np.ascontiguousarray(scales, dtype=np.float16)
+        M, K = xb.shape
+        N = qweight.shape[1]
+        out = np.empty((M, N // 2), dtype=np.float64)
+        _check(self.lib.oracle_gate_up_silu(_ptr(xb), _ACTS[act], _ptr(qweight),
+                                            _ptr(scales.view(np.uint16)), M, K, N, group_size,
+                                            _ptr(out)), "gate_up_silu")
+        return out
+
+
 _default: Optional[Oracle] = None
 
 
@@ -201,3 +218,7 @@ def linear(x, qweight, scales, group_size, act="f16", absval=False):
 
 def linear_at(x, qweight, scales, group_size, ms, ns, act="f16", absval=False):
     return default().linear_at(x, qweight, scales, group_size, ms, ns, act, absval)
+
+
+def gate_up_silu(x, qweight, scales, group_size, act="f16"):
+    return default().gate_up_silu(x, qweight, scales, group_size, act)

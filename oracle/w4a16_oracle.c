@@ -41,6 +41,17 @@
  * BF16 outside its own kernels ("GPTQ-Pro" README, "Runtime contract").
  * With absval = 1 the same loops return sum_k |x[m,k]| * |w[k,n]| instead, the
  * magnitude that bounds the rounding error of any evaluation order.
+ *
+ * Merged gate/up projection with SiLU * mul (oracle_gate_up_silu): the
+ * columns of qweight and scales alternate gate (even n) and up (odd n); with
+ * g = y[m,2j] and u = y[m,2j+1] of the definition above,
+ *   out[m,j] = silu(g) * u,   silu(z) = z / (1 + exp(-z))      (in fp64)
+ * The pages name the merged gate_up_proj module ("GPT-QModel" README,
+ * "Dynamic Quantization", "Fused Modules in Inference Engines": gate_proj
+ * and up_proj merge into gate_up_proj) and serve with the fused silu_and_mul
+ * custom op enabled ("Qwen3.8-27B GPTQ-Pro Hybrid INT8" model card,
+ * "Text-only serving"); they print neither the column order of the merge
+ * nor SiLU, which is its textbook definition here.
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math).  OpenMP only
  * splits rows m and column blocks of n, never the sum over k.
  */
@@ -243,6 +254,27 @@ static int linear_at_impl(const uint16_t *x, int act, int absval, const int32_t 
         out[i] = acc;
     }
     return OR_OK;
+}
+
+/* SiLU, as defined: z / (1 + exp(-z)). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* out[m*(N/2) + j] <- silu(y[m,2j]) * y[m,2j+1], y the linear of x (type act). */
+int oracle_gate_up_silu(const uint16_t *x, int act, const int32_t *qweight,
+                        const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
+                        double *out) {
+    if (!shape_ok(M, K, N) || N % 2 != 0) return OR_ERR_ARG;
+    if (M == 0) return OR_OK;
+    if (!out) return OR_ERR_ARG;
+    double *y = (double *)malloc((size_t)M * (size_t)N * sizeof(double));
+    if (!y) return OR_ERR_ARG;
+    int rc = linear_impl(x, act, 0, qweight, scales, M, K, N, g, y);
+    if (rc == OR_OK)
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t j = 0; j < N / 2; ++j)
+                out[m * (N / 2) + j] = silu(y[m * N + 2 * j]) * y[m * N + 2 * j + 1];
+    free(y);
+    return rc;
 }
 
 int oracle_linear_at(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,

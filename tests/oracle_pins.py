@@ -17,6 +17,8 @@ when it disagrees with:
     values both formats hold;
   - for the magnitude sum sum_k |x||w|, a dense product of magnitudes and the
     bounds |y| <= sum|x||w| (equality when every term is non-negative).
+  - for the merged gate/up with SiLU * mul, numpy's own exp on the brute-force
+    product, and closed forms (zero gate or up weights give exactly 0).
 ``tests/test_oracle_mutants.py`` plants plausible mistakes in copies of the
 oracle source and checks that every one of them trips at least one pin.
 """
@@ -357,6 +359,54 @@ def pin_sampled_matches_full_bf16_abs(o):
         y = o.linear(xb, q, scales, g, act="bf16", absval=absval)
         assert np.array_equal(o.linear_at(xb, q, scales, g, ms, ns, act="bf16", absval=absval),
                               y[ms, ns]), absval
+
+
+# --- merged gate/up with SiLU * mul --------------------------------------------
+
+def pin_gate_up_silu_brute_force(o):
+    """silu(gate) * up against numpy: W from the codes, numpy's own exp, both
+    activation types."""
+    rng = np.random.default_rng(23)
+    for M, K, N, g in ((1, 16, 8, 16), (3, 64, 24, 32), (2, 256, 16, -1), (4, 96, 40, 16)):
+        G = 1 if g == -1 else -(-K // g)
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        scales = rng.uniform(1e-2, 8e-2, size=(G, N)).astype(np.float16)
+        q = o.pack(codes)
+        xh = rng.standard_normal((M, K)).astype(np.float16)
+        xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        for x, act, xv in ((xh, "f16", xh.astype(np.float64)), (xb, "bf16", _bf16_value(xb))):
+            y = _brute(codes, scales, xv, g)
+            gate, up = y[:, 0::2], y[:, 1::2]
+            ref = gate * up / (1.0 + np.exp(-gate))
+            out = o.gate_up_silu(x, q, scales, g, act=act)
+            assert out.shape == (M, N // 2)
+            assert np.abs(out - ref).max() <= 1e-12 * max(1.0, float(np.abs(ref).max())), \
+                (M, K, N, g, act)
+
+
+def pin_gate_up_silu_closed_forms(o):
+    """Zero gate weights give silu(0) = 0, zero up weights give 0 (exactly);
+    with gate = ln 3 and up = 1, silu(ln 3) * 1 = 0.75 ln 3."""
+    K, N = 32, 8
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((2, K)).astype(np.float16)
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    s = np.ones((1, N), dtype=np.float16)
+    c_gate0 = codes.copy()
+    c_gate0[:, 0::2] = 8
+    assert np.all(o.gate_up_silu(x, o.pack(c_gate0), s, -1) == 0.0)
+    c_up0 = codes.copy()
+    c_up0[:, 1::2] = 8
+    assert np.all(o.gate_up_silu(x, o.pack(c_up0), s, -1) == 0.0)
+    # one nonzero x = ln 3 (fp16-rounded) on a code 9 (w = 1) column pair
+    xv = np.zeros((1, K), dtype=np.float16)
+    xv[0, 0] = np.float16(np.log(3.0))
+    c = np.full((K, N), 8, dtype=np.uint8)
+    c[0, :] = 9
+    z = float(xv[0, 0])
+    out = o.gate_up_silu(xv, o.pack(c), s, -1)
+    assert np.allclose(out, z * z / (1.0 + np.exp(-z)), rtol=1e-15, atol=0)
+    assert abs(z / (1.0 + np.exp(-z)) - 0.75 * z) < 1e-3
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -26,6 +26,9 @@ MUTANTS = {
                           "return half_to_double(h);"),
     "abs_sign_kept": ("return absval ? fabs(xk) * fabs(w) : xk * w;",
                       "return absval ? fabs(xk) * w : xk * w;"),
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "gate_up_swapped": ("silu(y[m * N + 2 * j]) * y[m * N + 2 * j + 1]",
+                        "silu(y[m * N + 2 * j + 1]) * y[m * N + 2 * j]"),
     "half_exponent_bias": ("exp - 25", "exp - 24"),
     "half_subnormal_scale": ("ldexp((double)man, -24)", "ldexp((double)man, -23)"),
     "half_sign_dropped": ("return sign ? -v : v;", "return v;"),
