@@ -133,6 +133,32 @@ int w4a16_linear_bf16_ex(const void *x, const int32_t *qweight, const void *scal
                          int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
                          int kernel);
 
+/* Merged gate/up projection with the SiLU * mul epilogue fused: the pages'
+ * engines merge gate_proj and up_proj into one gate_up_proj module ("GPT-QModel"
+ * README, "Dynamic Quantization": "Fused Modules in Inference Engines") and
+ * serve with the fused silu_and_mul op ("Qwen3.8-27B GPTQ-Pro Hybrid INT8"
+ * model card, "Text-only serving").
+ *   qweight int32 [K/8, N], scales fp16 [G, N]: the columns alternate gate
+ *     (even n) and up (odd n), each column in the GPTQ_V2 layout above (the
+ *     caller merges gate_proj and up_proj by interleaving their columns);
+ *   y : device [M, N/2], y[m,j] = silu(g) * u with g, u the fp32 sums of
+ *     columns 2j and 2j+1 (never rounded), silu(z) = z / (1 + e^-z) in fp32,
+ *     rounded once to the output type;
+ *   N % 16 == 0 (else W4A16_ERR_SHAPE), everything else as for w4a16_linear.
+ * The _bf16 forms take bfloat16 x and write bfloat16 y (arithmetic as in
+ * w4a16_linear_bf16); the _ex forms choose the kernel as w4a16_linear_ex.
+ * Prefill with M > 128 runs whole tiles only (no split last round). */
+int w4a16_gate_up_silu(const void *x, const int32_t *qweight, const void *scales, void *y,
+                       int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream);
+int w4a16_gate_up_silu_ex(const void *x, const int32_t *qweight, const void *scales, void *y,
+                          int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
+                          int kernel);
+int w4a16_gate_up_silu_bf16(const void *x, const int32_t *qweight, const void *scales, void *y,
+                            int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream);
+int w4a16_gate_up_silu_bf16_ex(const void *x, const int32_t *qweight, const void *scales,
+                               void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                               void *stream, int kernel);
+
 /* Host-side packing into the GPTQ_V2 layout (native int32 qweight, "GPTQ-Pro"
  * README, "Runtime contract"):
  *   qweight[r][n] = sum_{j=0..7} codes[8r+j][n] << 4j   (as a 32-bit pattern)

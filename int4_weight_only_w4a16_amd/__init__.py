@@ -7,10 +7,10 @@ not a gfx950, calls raise.
 
 Names match the C ABI in ``include/w4a16.h``:
   w4a16_linear, w4a16_linear_ex, w4a16_linear_bf16, w4a16_linear_bf16_ex,
-  pack_gptq_v2, unpack_gptq_v2, w4a16_status_string, and the measurement aid
-  w4a16_read_probe
-plus ``linear`` (allocates y with torch, then calls w4a16_linear_ex or, for
-bfloat16 x, w4a16_linear_bf16_ex).
+  w4a16_gate_up_silu(_ex, _bf16, _bf16_ex), pack_gptq_v2, unpack_gptq_v2,
+  w4a16_status_string, and the measurement aid w4a16_read_probe
+plus ``linear`` and ``gate_up_silu`` (allocate y with torch, then call the
+_ex entry point of x's dtype).
 """
 
 from __future__ import annotations
@@ -40,7 +40,9 @@ W4A16_KERNEL_DECODE = 1
 W4A16_KERNEL_PREFILL = 2
 
 EXPORTS = ("w4a16_linear", "w4a16_linear_ex", "w4a16_linear_bf16", "w4a16_linear_bf16_ex",
-           "pack_gptq_v2", "unpack_gptq_v2", "w4a16_read_probe", "w4a16_status_string")
+           "w4a16_gate_up_silu", "w4a16_gate_up_silu_ex", "w4a16_gate_up_silu_bf16",
+           "w4a16_gate_up_silu_bf16_ex", "pack_gptq_v2", "unpack_gptq_v2", "w4a16_read_probe",
+           "w4a16_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -70,6 +72,12 @@ def load_library() -> ctypes.CDLL:
     lib.w4a16_linear_bf16.restype = i32
     lib.w4a16_linear_bf16_ex.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i32]
     lib.w4a16_linear_bf16_ex.restype = i32
+    for name in ("w4a16_gate_up_silu", "w4a16_gate_up_silu_bf16"):
+        getattr(lib, name).argtypes = [p, p, p, p, i64, i64, i64, i64, p]
+        getattr(lib, name).restype = i32
+    for name in ("w4a16_gate_up_silu_ex", "w4a16_gate_up_silu_bf16_ex"):
+        getattr(lib, name).argtypes = [p, p, p, p, i64, i64, i64, i64, p, i32]
+        getattr(lib, name).restype = i32
     lib.pack_gptq_v2.argtypes = [p, p, i64, i64]
     lib.pack_gptq_v2.restype = i32
     lib.unpack_gptq_v2.argtypes = [p, p, i64, i64]
@@ -137,6 +145,55 @@ def w4a16_linear_bf16(x, qweight, scales, y, M: int, K: int, N: int, group_size:
                       stream=None) -> None:
     """Same as the C ``w4a16_linear_bf16`` (kernel chosen by M)."""
     w4a16_linear_bf16_ex(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO)
+
+
+def w4a16_gate_up_silu_ex(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
+                          stream=None, kernel: int = W4A16_KERNEL_AUTO, bf16: bool = False) -> None:
+    """Merged gate/up projection with SiLU * mul: y [M, N/2] = silu(gate) * up, the
+    columns of qweight and scales alternating gate and up (the C
+    w4a16_gate_up_silu_ex, or its _bf16 form when bf16)."""
+    lib = load_library()
+    f = lib.w4a16_gate_up_silu_bf16_ex if bf16 else lib.w4a16_gate_up_silu_ex
+    st = f(_addr(x), _addr(qweight), _addr(scales), _addr(y), int(M), int(K), int(N),
+           int(group_size), _stream_handle(stream), int(kernel))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_gate_up_silu")
+
+
+def w4a16_gate_up_silu(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
+                       stream=None) -> None:
+    """Same as the C ``w4a16_gate_up_silu`` (fp16, kernel chosen by M)."""
+    w4a16_gate_up_silu_ex(x, qweight, scales, y, M, K, N, group_size, stream)
+
+
+def w4a16_gate_up_silu_bf16(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
+                            stream=None) -> None:
+    """Same as the C ``w4a16_gate_up_silu_bf16``."""
+    w4a16_gate_up_silu_ex(x, qweight, scales, y, M, K, N, group_size, stream, bf16=True)
+
+
+def gate_up_silu(x, qweight, scales, group_size: int, out=None, stream=None,
+                 kernel: int = W4A16_KERNEL_AUTO):
+    """Allocate y ([M, N/2], x's dtype) and run the merged gate/up projection with
+    SiLU * mul (columns of qweight and scales alternate gate and up)."""
+    import torch
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be float16 or bfloat16")
+    for name, t, dt in (("x", x, x.dtype), ("qweight", qweight, torch.int32),
+                        ("scales", scales, torch.float16)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    M, K = x.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K:
+        raise ValueError("qweight must be [K/8, N]")
+    if out is None:
+        out = torch.empty((M, N // 2), dtype=x.dtype, device=x.device)
+    elif out.dtype != x.dtype:
+        raise ValueError("out must have x's dtype")
+    w4a16_gate_up_silu_ex(x, qweight, scales, out, M, K, N, group_size, stream, kernel,
+                          x.dtype == torch.bfloat16)
+    return out
 
 
 def w4a16_read_probe(data, nbytes: int, sink, stream=None) -> None:

@@ -119,10 +119,6 @@ __device__ __forceinline__ _Float16 scale_at(const u2 &s, int j) {
     return (j & 1) ? half_hi(d) : half_lo(d);
 }
 
-template <bool BF>
-__device__ __forceinline__ void store_row4(uint16_t *dst, const float (&v)[4]) {
-    *reinterpret_cast<u2 *>(dst) = pack4<BF>(v[0], v[1], v[2], v[3]);
-}
 
 // One wave's pass over a contiguous range [w0, w1) of units (tile-major:
 // unit u = tile u / S, step u % S).  The host keeps w1 - w0 <= S, so the
@@ -326,7 +322,7 @@ __device__ __forceinline__ void decode_units(
 extern __shared__ __attribute__((aligned(16))) unsigned char decode_dyn_lds[];
 
 // Tiles kernel: one workgroup per column tile, its waves split K.
-template <int WAVES, int D, int SCALE, bool XLDS, bool BF>
+template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU>
 __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -376,7 +372,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
 #pragma unroll
             for (int j = 0; j < kNW; ++j) v[j] += red[w][j][l][i];
         }
-        if (m < M && n < N) store_row4<BF>(y + (size_t)m * N + n, v);
+        if (m < M && n < N) store_quad<BF, SILU>(y, m, N, n, v);
     }
 }
 
@@ -432,7 +428,7 @@ __host__ __device__ __forceinline__ int wave_share(int n, int w) {
     return nold + (n - nold) * (w - H) / (WAVES - H);
 }
 
-template <int WAVES, int D, int SCALE, bool XLDS, bool BF>
+template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -549,7 +545,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         const int n = tau * kCols + c;
         if (n >= N) continue;
         if (ta >= u0 && tb <= u1) {                 // the whole tile is here
-            store_row4<BF>(y + (size_t)m * N + n, v);
+            store_quad<BF, SILU>(y, m, N, n, v);
             continue;
         }
         if (partials) {
@@ -577,7 +573,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             const float r0 = __builtin_bit_cast(float, (uint32_t)got[j] ^ kSlotKey) + v[2 * j];
             const float r1 = __builtin_bit_cast(float, (uint32_t)(got[j] >> 32) ^ kSlotKey) + v[2 * j + 1];
             __hip_atomic_store(slot + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n + 2 * j) = pack2<BF>(r0, r1);
+            store_pair<BF, SILU>(y, m, N, n + 2 * j, r0, r1);
         }
     }
 }
@@ -587,7 +583,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
 // bit-reproducible), and stores y.  One workgroup per tile; thread (m, q)
 // handles row m and columns 4q .. 4q+3 of the tile.  Tiles that lie whole
 // inside one range were stored by the stream-K kernel.
-template <bool BF>
+template <bool BF, bool SILU>
 __global__ __launch_bounds__(256) void decode_split_reduce_kernel(
     const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S, int G) {
     constexpr int SLOT = 16 * kCols;
@@ -607,7 +603,7 @@ __global__ __launch_bounds__(256) void decode_split_reduce_kernel(
 #pragma unroll
         for (int j = 0; j < kNW; ++j) r[j] += p[j];
     }
-    store_row4<BF>(y + (size_t)m * N + n, r);
+    store_quad<BF, SILU>(y, m, N, n, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -678,7 +674,7 @@ static size_t static_lds(const void *kernel) {
     return attr.sharedSizeBytes;
 }
 
-template <int SCALE, bool XLDS, bool BF>
+template <int SCALE, bool XLDS, bool BF, bool SILU>
 static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *workspace,
                             int capacity, int grid) {
     const int K = (int)a.K, N = (int)a.N, M = (int)a.M;
@@ -701,20 +697,20 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
                         &group_steps, &slots, &partials};
         hipError_t e = hipLaunchKernel(
             reinterpret_cast<const void *>(
-                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF>),
+                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU>),
             dim3(grid), block, args, dyn, stream);
         if (e != hipSuccess || !part) return e;
         const float *pc = partials;
         int Sv = S, G = grid;
         void *rargs[] = {&pc, &yp, (void *)&M, (void *)&N, &Sv, &G};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel<BF>),
+        return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel<BF, SILU>),
                                dim3((unsigned)T), dim3(256), rargs, 0, stream);
     }
     void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
     const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);
     return hipLaunchKernel(
         reinterpret_cast<const void *>(
-            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS, BF>),
+            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU>),
         dim3(tiles), block, args, dyn, stream);
 }
 
@@ -726,9 +722,9 @@ static bool stage_fits(const LinearArgs &a, int grid, size_t max_lds) {
     const size_t dyn = (size_t)a.M * 32 * ((a.K + 31) / 32) * 2 + 16;
     if (dyn > kXStageMax) return false;
     static const size_t sk_static = static_lds(reinterpret_cast<const void *>(
-        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true, BF>));
+        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true, BF, false>));
     static const size_t tiles_static = static_lds(reinterpret_cast<const void *>(
-        &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true, BF>));
+        &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true, BF, false>));
     const size_t st = grid > 0 ? sk_static : tiles_static;
     return st != (size_t)-1 && st + dyn <= max_lds;
 }
@@ -736,9 +732,12 @@ static bool stage_fits(const LinearArgs &a, int grid, size_t max_lds) {
 template <int SCALE, bool BF>
 static hipError_t launch_scale(const LinearArgs &a, hipStream_t stream, void *workspace,
                                int capacity, int grid, size_t max_lds) {
-    return stage_fits<SCALE, BF>(a, grid, max_lds)
-               ? launch_sa<SCALE, true, BF>(a, stream, workspace, capacity, grid)
-               : launch_sa<SCALE, false, BF>(a, stream, workspace, capacity, grid);
+    const bool xlds = stage_fits<SCALE, BF>(a, grid, max_lds);
+    if (a.silu)
+        return xlds ? launch_sa<SCALE, true, BF, true>(a, stream, workspace, capacity, grid)
+                    : launch_sa<SCALE, false, BF, true>(a, stream, workspace, capacity, grid);
+    return xlds ? launch_sa<SCALE, true, BF, false>(a, stream, workspace, capacity, grid)
+                : launch_sa<SCALE, false, BF, false>(a, stream, workspace, capacity, grid);
 }
 
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,

@@ -54,7 +54,7 @@ constexpr int kPreSteps = kPreBK / 16;    // 16-deep MFMA steps per stage
 // Split K: workgroup z of `chunks` takes the 64-deep stages [sb, se) of its
 // tile; with chunks > 1 it writes its fp32 sums to partials[z][M][N] and
 // prefill_chunk_reduce_kernel adds the chunks, else it stores y.
-template <bool BF>
+template <bool BF, bool SILU>
 __global__ __launch_bounds__(256) void prefill_m128_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -225,8 +225,7 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
                     *reinterpret_cast<float2 *>(pz + (size_t)m * N + n) =
                         float2{acc[mt][0][i], acc[mt][1][i]};
                 else
-                    *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) =
-                        pack2<BF>(acc[mt][0][i], acc[mt][1][i]);
+                    store_pair<BF, SILU>(y, m, N, n, acc[mt][0][i], acc[mt][1][i]);
             }
         }
     }
@@ -235,7 +234,7 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
 // y = the sum of the chunks' partials[c][M][N] in chunk order (fixed, so
 // results are bit-reproducible); four consecutive elements per thread
 // (N % 8 == 0, so they stay in one row).
-template <bool BF>
+template <bool BF, bool SILU>
 __global__ __launch_bounds__(256) void prefill_chunk_reduce_kernel(
     const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int chunks) {
     const int64_t total = (int64_t)M * N;
@@ -247,7 +246,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_reduce_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] += p[j];
     }
-    *reinterpret_cast<u2 *>(y + e) = pack4<BF>(v[0], v[1], v[2], v[3]);
+    store_quad<BF, SILU>(y, e / N, N, (int)(e % N), v);
 }
 
 // K chunks for the 128-row kernel: with fewer tiles than CUs, split each
@@ -281,14 +280,20 @@ static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream, v
     dim3 grid((unsigned)((N + kPreBN - 1) / kPreBN), (unsigned)((M + kPreBM - 1) / kPreBM),
               (unsigned)chunks);
     dim3 block(256);
-    const void *k = a.bf16 ? reinterpret_cast<const void *>(&prefill_m128_kernel<true>)
-                           : reinterpret_cast<const void *>(&prefill_m128_kernel<false>);
+    const void *k =
+        a.silu ? (a.bf16 ? reinterpret_cast<const void *>(&prefill_m128_kernel<true, true>)
+                         : reinterpret_cast<const void *>(&prefill_m128_kernel<false, true>))
+               : (a.bf16 ? reinterpret_cast<const void *>(&prefill_m128_kernel<true, false>)
+                         : reinterpret_cast<const void *>(&prefill_m128_kernel<false, false>));
     hipError_t e = hipLaunchKernel(k, grid, block, args, 0, stream);
     if (e != hipSuccess || chunks == 1) return e;
     const float *pc = partials;
     void *rargs[] = {&pc, &yp, &M, &N, &chunks};
-    const void *rk = a.bf16 ? reinterpret_cast<const void *>(&prefill_chunk_reduce_kernel<true>)
-                            : reinterpret_cast<const void *>(&prefill_chunk_reduce_kernel<false>);
+    const void *rk =
+        a.silu ? (a.bf16 ? reinterpret_cast<const void *>(&prefill_chunk_reduce_kernel<true, true>)
+                         : reinterpret_cast<const void *>(&prefill_chunk_reduce_kernel<false, true>))
+               : (a.bf16 ? reinterpret_cast<const void *>(&prefill_chunk_reduce_kernel<true, false>)
+                         : reinterpret_cast<const void *>(&prefill_chunk_reduce_kernel<false, false>));
     const int64_t threads = ((int64_t)M * N + 3) / 4;
     return hipLaunchKernel(rk, dim3((unsigned)((threads + 255) / 256)), dim3(256), rargs, 0,
                            stream);
@@ -690,10 +695,25 @@ constexpr int kWSlot = kWBM * kWBN;   // floats per partial tile
 // copy of the code serves both kinds of workgroup: every element issues the
 // same two stores, the ones that do not apply get an out-of-range offset
 // (two copies of the epilogue would not fit the register file).
-template <bool BF>
+template <bool BF, bool SILU>
 __device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0,
                                            const f16v (&acc)[8][2], float *partial,
                                            uint32_t part_mask) {
+    if constexpr (SILU) {
+        // merged gate/up: whole tiles only (the host never splits them), one
+        // value silu(gate) * up per column pair
+        const int lane = threadIdx.x & 63;
+        const int n = n0 + 64 * (threadIdx.x >> 6) + 2 * (lane & 31);
+        if (n >= p.N) return;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (m < p.M) store_pair<BF, true>(p.ybase, m, p.N, n, acc[mt][0][i], acc[mt][1][i]);
+            }
+        return;
+    }
     // keep the mask opaque, so that the compiler does not split the stores
     // into one copy per kind of workgroup
     part_mask = __builtin_amdgcn_readfirstlane(part_mask);
@@ -737,7 +757,7 @@ __device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0
 // prefill_tail_reduce_kernel adds them.  Every workgroup streams K from its
 // range start with the others, nothing is exchanged inside the kernel.
 
-template <bool BF>
+template <bool BF, bool SILU>
 __global__ __launch_bounds__(256) void prefill_m256_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -767,8 +787,8 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
     }
     f16v acc[8][2];
     wide_tile_range<BF>((lds_u8_t *)lds_raw, p, m0, n0, sb, se, acc);
-    wide_store<BF>(p, m0, n0, acc, j < 0 ? partials : partials + (size_t)j * kWSlot,
-                   j < 0 ? 0u : ~0u);
+    wide_store<BF, SILU>(p, m0, n0, acc, j < 0 ? partials : partials + (size_t)j * kWSlot,
+                         j < 0 ? 0u : ~0u);
 }
 
 // Sums the split tiles' partials in chunk order (fixed, so results are
@@ -814,7 +834,7 @@ static WidePlan wide_plan(const LinearArgs &a, int num_cus) {
     w.tail = 0;
     w.chunks = 1;
     const int nst = (int)((a.K + kWBK - 1) / kWBK);
-    if (num_cus <= 0) return w;
+    if (num_cus <= 0 || a.silu) return w;     // the SiLU epilogue stores whole tiles only
     const int tail = w.tiles % num_cus;
     if (tail == 0 || 2 * tail > num_cus) return w;
     const int chunks = std::min(num_cus / tail, nst / 8);
@@ -849,8 +869,11 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
     void *yp = a.y;
     void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &tiles_m, &tiles_dp, &per_xcd,
                     &chunks, &partials};
-    const void *k = a.bf16 ? reinterpret_cast<const void *>(&prefill_m256_kernel<true>)
-                           : reinterpret_cast<const void *>(&prefill_m256_kernel<false>);
+    const void *k =
+        a.silu ? (a.bf16 ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, true>)
+                         : reinterpret_cast<const void *>(&prefill_m256_kernel<false, true>))
+               : (a.bf16 ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, false>)
+                         : reinterpret_cast<const void *>(&prefill_m256_kernel<false, false>));
     hipError_t e = hipLaunchKernel(k, dim3(8 * per_xcd + tail * chunks), dim3(256), args, 0, stream);
     if (e != hipSuccess || tail == 0) return e;
     const float *pc = partials;

@@ -111,12 +111,14 @@ void *stream_workspace(int dev, hipStream_t stream, int kind, size_t bytes) {
 
 }  // namespace
 
-// One linear call, fp16 or bfloat16 (bf16) activations and outputs.
+// One linear call, fp16 or bfloat16 (bf16) activations and outputs; silu:
+// the merged gate/up projection (N % 16 == 0, y is [M, N/2]).
 static int linear_call(const void *x, const int32_t *qweight, const void *scales, void *y,
                        int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
-                       int kernel, bool bf16) {
+                       int kernel, bool bf16, bool silu = false) {
     const int st = validate(x, qweight, scales, y, M, K, N, group_size);
     if (st != W4A16_OK) return st;
+    if (silu && N % 16 != 0) return W4A16_ERR_SHAPE;
     if (kernel == W4A16_KERNEL_AUTO)
         kernel = M <= W4A16_DECODE_MAX_M ? W4A16_KERNEL_DECODE : W4A16_KERNEL_PREFILL;
     if (kernel == W4A16_KERNEL_DECODE) {
@@ -129,7 +131,7 @@ static int linear_call(const void *x, const int32_t *qweight, const void *scales
     size_t max_lds = 0;
     const int dev = usable_device(&num_cus, &max_lds);
     if (dev < 0) return W4A16_ERR_DEVICE;
-    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, bf16};
+    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, bf16, silu};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (kernel == W4A16_KERNEL_DECODE) {
@@ -173,6 +175,33 @@ extern "C" int w4a16_linear_bf16(const void *x, const int32_t *qweight, const vo
                                  void *stream) {
     return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO,
                        true);
+}
+
+extern "C" int w4a16_gate_up_silu_ex(const void *x, const int32_t *qweight, const void *scales,
+                                     void *y, int64_t M, int64_t K, int64_t N,
+                                     int64_t group_size, void *stream, int kernel) {
+    return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, kernel, false, true);
+}
+
+extern "C" int w4a16_gate_up_silu(const void *x, const int32_t *qweight, const void *scales,
+                                  void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                                  void *stream) {
+    return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO,
+                       false, true);
+}
+
+extern "C" int w4a16_gate_up_silu_bf16_ex(const void *x, const int32_t *qweight,
+                                          const void *scales, void *y, int64_t M, int64_t K,
+                                          int64_t N, int64_t group_size, void *stream,
+                                          int kernel) {
+    return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, kernel, true, true);
+}
+
+extern "C" int w4a16_gate_up_silu_bf16(const void *x, const int32_t *qweight,
+                                       const void *scales, void *y, int64_t M, int64_t K,
+                                       int64_t N, int64_t group_size, void *stream) {
+    return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO,
+                       true, true);
 }
 
 extern "C" int pack_gptq_v2(const uint8_t *codes, int32_t *qweight, int64_t K, int64_t N) {

@@ -164,6 +164,35 @@ __device__ __forceinline__ u2 pack4(float a, float b, float c, float d) {
     return u2{pack2<BF>(a, b), pack2<BF>(c, d)};
 }
 
+// ---- final stores: plain, or the merged gate/up projection's SiLU * mul ----
+// With SILU the columns alternate gate (even) and up (odd) and the pair
+// (gate, up) becomes one value silu(gate) * up at column n/2 of a y with N/2
+// columns (vLLM's silu_and_mul, which the pages serve with: "Qwen3.8-27B
+// GPTQ-Pro Hybrid INT8" model card, "Text-only serving"), taken from the fp32
+// sums before any rounding.  SiLU(z) = z / (1 + e^-z).
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// Columns n, n + 1 (n even) of row m.
+template <bool BF, bool SILU>
+__device__ __forceinline__ void store_pair(uint16_t *y, int64_t m, int N, int n, float a,
+                                           float b) {
+    if constexpr (SILU)
+        y[m * (N / 2) + n / 2] = (uint16_t)pack2<BF>(silu_f32(a) * b, 0.f);
+    else
+        *reinterpret_cast<uint32_t *>(y + m * N + n) = pack2<BF>(a, b);
+}
+
+// Columns n .. n + 3 (n % 4 == 0) of row m.
+template <bool BF, bool SILU>
+__device__ __forceinline__ void store_quad(uint16_t *y, int64_t m, int N, int n,
+                                           const float (&v)[4]) {
+    if constexpr (SILU)
+        *reinterpret_cast<uint32_t *>(y + m * (N / 2) + n / 2) =
+            pack2<BF>(silu_f32(v[0]) * v[1], silu_f32(v[2]) * v[3]);
+    else
+        *reinterpret_cast<u2 *>(y + m * N + n) = pack4<BF>(v[0], v[1], v[2], v[3]);
+}
+
 // The MFMAs above on 16-bit operands given as raw bits (eight values each).
 template <bool BF>
 __device__ __forceinline__ f4 mfma16x16x32_t(u4 a, u4 b, f4 c) {

@@ -15,6 +15,7 @@ struct LinearArgs {
     void *y;
     int64_t M, K, N, group_size;
     bool bf16;   // x and y are bfloat16 (else fp16); scales are fp16 either way
+    bool silu;   // merged gate/up: columns alternate gate and up; y[M, N/2] = silu(gate) * up
 };
 
 // Decode (M <= 16).  grid > 0 runs the stream-K kernel on `grid` workgroups

@@ -62,6 +62,44 @@ def check_parity_bf16(y_gpu: np.ndarray, y_ref: np.ndarray, mag: np.ndarray, K: 
     return {"max_abs": float(d.max()) if d.size else 0.0, "mean_rel": mean_rel}
 
 
+# Merged gate/up with SiLU * mul: the kernels form the gate and up sums g, u
+# as the linear does (error at most eps * sum|x||w| per column), take
+# silu(g) * u in fp32 (|silu'| <= 1.1) and round once (half an ulp, r):
+#   |y - y_ref| <= r |y_ref| + 1.02 (1.1 |u| eps A_g + |silu(g)| eps A_u
+#                                    + 1.1 eps^2 A_g A_u) + 4e-7 |y_ref|
+# with A_g, A_u the oracle's magnitude sums of the two columns; plus the mean
+# relative error of the linear's bar.
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def check_gate_up(y, ref, lin, mag, mag0, K, bf16, what):
+    """y [M, N/2] from the GPU; lin, mag (and mag0 for bf16) [M, N] from the oracle."""
+    g, u = lin[:, 0::2], lin[:, 1::2]
+    a_g, a_u = mag[:, 0::2], mag[:, 1::2]
+    if bf16:
+        r = 2.0 ** -8
+        eps_g = r + K * 2.0 ** -24 + 35 * K * 2.0 ** -24 * mag0[:, 0::2] / np.maximum(a_g, 1e-300)
+        eps_u = r + K * 2.0 ** -24 + 35 * K * 2.0 ** -24 * mag0[:, 1::2] / np.maximum(a_u, 1e-300)
+        mean_bar = 2.0 ** -8
+    else:
+        r = 2.0 ** -11
+        eps_g = eps_u = 2.0 ** -11 + K * 2.0 ** -24
+        mean_bar = 1e-3
+    dg, du = eps_g * a_g, eps_u * a_u
+    bound = (r * np.abs(ref) + 1.02 * (1.1 * np.abs(u) * dg + np.abs(_silu(g)) * du + 1.1 * dg * du)
+             + 4e-7 * np.abs(ref) + 1e-30)
+    d = np.abs(y - ref)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    worst = int(np.argmax(d - bound))
+    assert np.all(d <= bound), \
+        f"{what}: |d| {float(d.flat[worst]):.4g} > {float(bound.flat[worst]):.4g} at {worst}"
+    denom = float(np.abs(ref).sum())
+    mean_rel = float(d.sum()) / denom if denom > 0 else float(d.sum())
+    assert mean_rel <= mean_bar, f"{what}: mean relative error {mean_rel:.4g}"
+
+
+
 def bf16_to_float(bits: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns (uint16 or int16) -> float64 (the top half of a float32)."""
     b = np.asarray(bits).view(np.uint16).astype(np.uint32)

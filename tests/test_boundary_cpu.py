@@ -99,6 +99,19 @@ def test_empty_batch_is_a_noop(lib, bf16):
     assert _call(lib, M=0, K=40, bf16=bf16) == w4.W4A16_ERR_SHAPE
 
 
+@pytest.mark.parametrize("name", ["w4a16_gate_up_silu_ex", "w4a16_gate_up_silu_bf16_ex"])
+def test_gate_up_validation(lib, name):
+    f = getattr(lib, name)
+    # the output has N/2 columns: N must be a multiple of 16
+    assert f(0x1000, 0x2000, 0x3000, 0x4000, 1, 32, 8, 32, None, 0) == w4.W4A16_ERR_SHAPE
+    assert f(0x1000, 0x2000, 0x3000, 0x4000, 1, 32, 24, 32, None, 0) == w4.W4A16_ERR_SHAPE
+    assert f(0x1000, 0x2000, 0x3000, 0x4000, 1, 32, 16, 48, None, 0) == w4.W4A16_ERR_GROUP
+    assert f(0, 0x2000, 0x3000, 0x4000, 1, 32, 16, 32, None, 0) == w4.W4A16_ERR_NULL
+    assert f(0x1008, 0x2000, 0x3000, 0x4000, 1, 32, 16, 32, None, 0) == w4.W4A16_ERR_ALIGN
+    assert f(0x1000, 0x2000, 0x3000, 0x4000, 17, 32, 16, 32, None, 1) == w4.W4A16_ERR_KERNEL
+    assert f(0, 0, 0, 0, 0, 32, 16, 32, None, 0) == w4.W4A16_OK
+
+
 def test_status_strings(lib):
     for st in range(0, 9):
         assert w4.w4a16_status_string(st)
