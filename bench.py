@@ -134,13 +134,17 @@ def rotations_for(weight_bytes: int, minimum: int = 2) -> int:
     return max(minimum, -(-2 * MALL_BYTES // weight_bytes))
 
 
-def bench_case(torch, w4, case, steps, warmup, eager, bf16=False):
+def bench_case(torch, w4, case, steps, warmup, eager, bf16=False, gate_up=False):
     import workloads
     inp = workloads.generate_bf16(case) if bf16 else workloads.generate(case)
     wbytes = case.K * case.N // 2 + 2 * case.G * case.N
     R = rotations_for(wbytes)
     x, qs, ss, y = prepare(torch, w4, case, inp, R, bf16)
-    call = w4.w4a16_linear_bf16 if bf16 else w4.w4a16_linear
+    if gate_up:
+        y = y[:, : case.N // 2].contiguous()
+        call = w4.w4a16_gate_up_silu_bf16 if bf16 else w4.w4a16_gate_up_silu
+    else:
+        call = w4.w4a16_linear_bf16 if bf16 else w4.w4a16_linear
 
     def step(i):
         call(x, qs[i % R], ss[i % R], y, case.M, case.K, case.N, case.group_size)
@@ -236,6 +240,8 @@ def main():
     ap.add_argument("--only", choices=("all", "decode", "prefill"), default="all")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement")
+    ap.add_argument("--no-gate-up", action="store_true",
+                    help="skip the merged gate/up (SiLU * mul) decode and prefill lines")
     ap.add_argument("--no-bf16", action="store_true",
                     help="skip the bfloat16-activation variant's decode and prefill lines")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -349,6 +355,36 @@ def main():
                                       "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}}
         torch.cuda.empty_cache()
         out["bf16"] = bf
+
+    if args.only == "all" and not args.no_gate_up:
+        # the merged gate/up projection with the fused SiLU * mul epilogue at
+        # the model's MLP shape (gate and up of 17408 columns each)
+        gu = {}
+        case = workloads.gate_up_decode()
+        _, _, sec, R = bench_case(torch, w4, case, args.steps, args.warmup, args.eager,
+                                  gate_up=True)
+        B = algorithmic_bytes(case.M, case.K, case.N, case.G) - case.M * case.N   # y is N/2 wide
+        gbs = B / sec / 1e9
+        gu["decode"] = {"workload": "gate_up + SiLU*mul GEMV M=1 K=5120 N=2x17408 g=128",
+                        "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": sec * 1e3,
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                     "algorithmic_bytes": B}}
+        torch.cuda.empty_cache()
+        case = workloads.gate_up_prefill()
+        psteps = max(5, (args.prefill_steps or max(10, args.steps // 4)) // 2)
+        _, _, sec, R = bench_case(torch, w4, case, psteps, max(1, min(args.warmup, psteps)),
+                                  args.eager, gate_up=True)
+        tflops = 2.0 * case.M * case.N * case.K / sec / 1e12
+        gu["prefill"] = {"workload": "gate_up + SiLU*mul GEMM M=2048 K=5120 N=2x17408 g=128",
+                         "value": round(tflops, 1), "unit": "TFLOP/s", "ms_per_step": sec * 1e3,
+                         "steps": psteps,
+                         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4)}}
+        torch.cuda.empty_cache()
+        out["gate_up_silu"] = gu
 
     out["device"] = dev_name
     out["timing"] = "eager launches" if args.eager else "one HIP graph of K steps"

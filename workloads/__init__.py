@@ -160,6 +160,17 @@ SWEEP_SHAPES = ((5120, 17408), (17408, 5120), (5120, 5120))
 SWEEP_MS = (1, 8, 64, 512)
 
 
+def gate_up_decode() -> Case:
+    """Merged gate/up projection (gate and up of 17408 columns each, interleaved:
+    N = 34816), M=1, K=5120, g=128, weights drawn as for the up-projection, seed 1."""
+    return Case("gate_up_decode", 1, 5120, 34816, 128, 1)
+
+
+def gate_up_prefill() -> Case:
+    """Merged gate/up projection, M=2048, K=5120, N=34816, g=128, seed 3."""
+    return Case("gate_up_prefill", 2048, 5120, 34816, 128, 3, x_dist="normal")
+
+
 def sweep() -> List[Case]:
     """Group-size and shape sweep: 6 g x 3 (K,N) x 4 M = 72 cases, 5% zero cells, seed 4."""
     out = []
