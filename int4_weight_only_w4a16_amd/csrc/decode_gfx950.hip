@@ -250,6 +250,20 @@ __device__ __forceinline__ void decode_units(
                 acc[j] = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a),
                                               dequant_bf16<false>(st.w[j], (float)scale_at(st.s, j)),
                                               acc[j]);
+        } else if constexpr (BF && SCALE == 2) {
+            // one step per group: both sums start from zero in the MFMA and go
+            // straight into acc (no accumulators to reset)
+            const u4 b136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};   // bf16 136.0
+            const f4 zero = {0.f, 0.f, 0.f, 0.f};
+            const f4 tx = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), b136, zero);
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) {
+                const f4 t = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), codes128_bf16(st.w[j], uc),
+                                                  zero);
+                const float sj = (float)scale_at(st.s, j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(sj, t[e] - tx[e], acc[j][e]);
+            }
         } else if constexpr (BF) {
             const u4 b136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};   // bf16 136.0
 #pragma unroll
@@ -743,17 +757,18 @@ static hipError_t launch_scale(const LinearArgs &a, hipStream_t stream, void *wo
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                          int grid, size_t max_lds) {
     if (grid > capacity) return hipErrorInvalidValue;
-    // bfloat16 dequantises before the MFMA for every group size; SCALE only
-    // picks the scale rows there (per 16-deep block for g = 16, per group
-    // otherwise)
-    if (a.bf16)
-        return a.group_size == 16 ? launch_scale<0, true>(a, stream, workspace, capacity, grid, max_lds)
-                                  : launch_scale<1, true>(a, stream, workspace, capacity, grid, max_lds);
-    if (a.group_size == 16) return launch_scale<0, false>(a, stream, workspace, capacity, grid, max_lds);
-    // one 32-deep step per group: g = 32, or one group over K <= 32
+    // bfloat16: SCALE 0 dequantises before the MFMA (g = 16); 1 and 2 sum
+    // 128 + q and fold the offset out per group (2: one step per group)
     const int64_t S = (a.K + 31) / 32;
-    if (a.group_size == 32 || (a.group_size == -1 && S == 1))
-        return launch_scale<2, false>(a, stream, workspace, capacity, grid, max_lds);
+    // one 32-deep step per group: g = 32, or one group over K <= 32
+    const bool one_step = a.group_size == 32 || (a.group_size == -1 && S == 1);
+    if (a.bf16) {
+        if (a.group_size == 16) return launch_scale<0, true>(a, stream, workspace, capacity, grid, max_lds);
+        if (one_step) return launch_scale<2, true>(a, stream, workspace, capacity, grid, max_lds);
+        return launch_scale<1, true>(a, stream, workspace, capacity, grid, max_lds);
+    }
+    if (a.group_size == 16) return launch_scale<0, false>(a, stream, workspace, capacity, grid, max_lds);
+    if (one_step) return launch_scale<2, false>(a, stream, workspace, capacity, grid, max_lds);
     return launch_scale<1, false>(a, stream, workspace, capacity, grid, max_lds);
 }
 
