@@ -41,11 +41,10 @@
 
 namespace w4a16 {
 
-constexpr int kPreBM = 128;               // rows per workgroup tile
+constexpr int kPreBM = 128;               // rows per workgroup tile (at most)
 constexpr int kPreBN = 256;               // columns per workgroup tile
 constexpr int kPreBK = 64;                // K per stage
 constexpr int kPreRowBytes = 144;         // 128 B of a row + 16 B pad (bank spread)
-constexpr int kPreStageBytes = kPreBM * kPreRowBytes;
 constexpr int kPreRing = 3;               // LDS stages, register stages per operand
 constexpr int kPreSteps = kPreBK / 16;    // 16-deep MFMA steps per stage
 
@@ -54,19 +53,21 @@ constexpr int kPreSteps = kPreBK / 16;    // 16-deep MFMA steps per stage
 // Split K: workgroup z of `chunks` takes the 64-deep stages [sb, se) of its
 // tile; with chunks > 1 it writes its fp32 sums to partials[z][M][N] and
 // prefill_chunk_reduce_kernel adds the chunks, else it stores y.
-template <bool BF, bool SILU>
+template <bool BF, bool SILU, int MT>
 __global__ __launch_bounds__(256) void prefill_m128_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
     int gshift, int chunks, float *__restrict__ partials) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kPreRing * kPreStageBytes];
+    constexpr int BM = 32 * MT;                    // rows per tile
+    constexpr int kStage = BM * kPreRowBytes;      // LDS bytes per stage
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kPreRing * kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int kb = lane >> 5;                 // K block (8 deep) of the 16-deep step
     const int c32 = lane & 31;                // row / column of the 32 x 32 tile
-    const int m0 = blockIdx.y * kPreBM;
+    const int m0 = blockIdx.y * BM;
     const int n = blockIdx.x * kPreBN + wave * 64 + 2 * c32;   // the lane's two columns
     const int G = gshift < 0 ? 1 : ((K - 1) >> gshift) + 1;
     const int nst = (K + kPreBK - 1) / kPreBK;
@@ -78,14 +79,14 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
     const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
     const auto sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
 
-    // ---- activation staging: thread tid moves chunks tid + 256 i, i < 4 ----
+    // ---- activation staging: thread tid moves chunks tid + 256 i, i < MT ----
     // chunk c: row c / 8, 8-deep K block c % 8 of the stage.
-    uint32_t a_goff[4];
-    bool a_row_ok[4];
-    int a_kc[4];
-    uint32_t a_loff[4];
+    uint32_t a_goff[MT];
+    bool a_row_ok[MT];
+    int a_kc[MT];
+    uint32_t a_loff[MT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MT; ++i) {
         const int c = tid + 256 * i;
         const int row = c >> 3, kc = c & 7;
         a_row_ok[i] = m0 + row < M;
@@ -94,18 +95,18 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
         a_loff[i] = row * kPreRowBytes + kc * 16;
     }
     // stages outside [sb, se) read zero (the ring runs up to two past se)
-    auto load_a = [&](u4 (&r)[4], int st) {
+    auto load_a = [&](u4 (&r)[MT], int st) {
         const int k0 = st * kPreBK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MT; ++i) {
             const bool ok = a_row_ok[i] && st < se && (k0 + 8 * a_kc[i] < K);
             r[i] = load_b128(xr, ok ? a_goff[i] + (uint32_t)k0 * 2u : kOOB);
         }
     };
-    auto store_a = [&](const u4 (&r)[4], int slot) {
+    auto store_a = [&](const u4 (&r)[MT], int slot) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u4 *>(lds + slot * kPreStageBytes + a_loff[i]) = perm_x(r[i]);
+        for (int i = 0; i < MT; ++i)
+            *reinterpret_cast<u4 *>(lds + slot * kStage + a_loff[i]) = perm_x(r[i]);
     };
 
     // ---- weights: words of packed row 2t + kb, columns n, n+1 (t = 16-deep step) ----
@@ -124,20 +125,20 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
     };
 
     const UnpackConsts uc = unpack_consts();
-    f16v acc[4][2];
+    f16v acc[MT][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[mt][j][e] = 0.f;
 
     // A fragments of step h of LDS slot `slot` (4 row tiles)
-    auto read_a = [&](h8 (&a)[4], int slot, int h) {
+    auto read_a = [&](h8 (&a)[MT], int slot, int h) {
         const unsigned char *abase =
-            lds + slot * kPreStageBytes + c32 * kPreRowBytes + kb * 16 + h * 32;
+            lds + slot * kStage + c32 * kPreRowBytes + kb * 16 + h * 32;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
             a[mt] = __builtin_bit_cast(h8, *reinterpret_cast<const u4 *>(abase + mt * 32 * kPreRowBytes));
     };
     // One stage: 4 steps x (4 row tiles x 2 column tiles) MFMAs.  The A
@@ -146,10 +147,10 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
     // with one wave per SIMD.  On entry `a` holds step 0 of this stage; on
     // exit step 0 of the next stage (slot `next`, stored two stages ago).
     auto compute = [&](int slot, int next, const u2 (&w)[kPreSteps], const uint32_t (&s)[kPreSteps],
-                       h8 (&a)[4]) {
+                       h8 (&a)[MT]) {
 #pragma unroll
         for (int h = 0; h < kPreSteps; ++h) {
-            h8 an[4];
+            h8 an[MT];
             if (h + 1 < kPreSteps) read_a(an, slot, h + 1);
             else read_a(an, next, 0);
             u4 b0, b1;
@@ -161,16 +162,16 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
                 b1 = __builtin_bit_cast(u4, unpack_codes_scaled(w[h].y, uc, half_hi(s[h])));
             }
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
                 acc[mt][0] = mfma32x32x16_t<BF>(__builtin_bit_cast(u4, a[mt]), b0, acc[mt][0]);
                 acc[mt][1] = mfma32x32x16_t<BF>(__builtin_bit_cast(u4, a[mt]), b1, acc[mt][1]);
             }
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) a[mt] = an[mt];
+            for (int mt = 0; mt < MT; ++mt) a[mt] = an[mt];
         }
     };
 
-    u4 areg[kPreRing][4];
+    u4 areg[kPreRing][MT];
     u2 wreg[kPreRing][kPreSteps];
     uint32_t sreg[kPreRing][kPreSteps];
 
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
     __builtin_amdgcn_sched_barrier(0);
     store_a(areg[1], 1);
     __syncthreads();
-    h8 afrag[4];
+    h8 afrag[MT];
     read_a(afrag, 0, 0);
 
     // Stages past se (up to two, to finish a round of three) compute on
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
     if (n < N) {
         float *pz = partials ? partials + (size_t)cz * M * N : nullptr;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
@@ -249,17 +250,35 @@ __global__ __launch_bounds__(256) void prefill_chunk_reduce_kernel(
     store_quad<BF, SILU>(y, e / N, N, (int)(e % N), v);
 }
 
-// K chunks for the 128-row kernel: with fewer tiles than CUs, split each
+// Row tiles of the small-M kernel: 32 * MT rows, the fewest 32-row MFMA
+// tiles that cover M (up to 4), so the matrix work does not grow with the
+// padding of small batches.
+static int m128_mt(int64_t M) { return M <= 32 ? 1 : M <= 64 ? 2 : 4; }
+
+// K chunks for the small-M kernel: with fewer tiles than CUs, split each
 // tile's K into about CUs / tiles chunks of at least 8 stages, as long as the
 // partials fit the prefill workspace (capacity x 256 KiB).
 static int m128_chunks(const LinearArgs &a, int num_cus) {
     if (num_cus <= 0) return 1;
-    const int64_t tiles = ((a.N + kPreBN - 1) / kPreBN) * ((a.M + kPreBM - 1) / kPreBM);
+    const int64_t bm = 32 * m128_mt(a.M);
+    const int64_t tiles = ((a.N + kPreBN - 1) / kPreBN) * ((a.M + bm - 1) / bm);
     const int64_t nst = (a.K + kPreBK - 1) / kPreBK;
     int64_t chunks = std::min<int64_t>(num_cus / tiles, nst / 8);
     const int64_t fit = (int64_t)num_cus * 256 * 256 / (a.M * a.N);
     chunks = std::min(chunks, fit);
     return chunks < 2 ? 1 : (int)chunks;
+}
+
+template <bool BF, bool SILU>
+static const void *m128_kernel_mt(int mt) {
+    if (mt == 1) return reinterpret_cast<const void *>(&prefill_m128_kernel<BF, SILU, 1>);
+    if (mt == 2) return reinterpret_cast<const void *>(&prefill_m128_kernel<BF, SILU, 2>);
+    return reinterpret_cast<const void *>(&prefill_m128_kernel<BF, SILU, 4>);
+}
+
+static const void *m128_kernel(bool bf16, bool silu, int mt) {
+    if (bf16) return silu ? m128_kernel_mt<true, true>(mt) : m128_kernel_mt<true, false>(mt);
+    return silu ? m128_kernel_mt<false, true>(mt) : m128_kernel_mt<false, false>(mt);
 }
 
 static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream, void *workspace,
@@ -277,14 +296,11 @@ static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream, v
     const void *sp = a.scales;
     void *yp = a.y;
     void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &chunks, &partials};
-    dim3 grid((unsigned)((N + kPreBN - 1) / kPreBN), (unsigned)((M + kPreBM - 1) / kPreBM),
+    const int mt = m128_mt(M);
+    dim3 grid((unsigned)((N + kPreBN - 1) / kPreBN), (unsigned)((M + 32 * mt - 1) / (32 * mt)),
               (unsigned)chunks);
     dim3 block(256);
-    const void *k =
-        a.silu ? (a.bf16 ? reinterpret_cast<const void *>(&prefill_m128_kernel<true, true>)
-                         : reinterpret_cast<const void *>(&prefill_m128_kernel<false, true>))
-               : (a.bf16 ? reinterpret_cast<const void *>(&prefill_m128_kernel<true, false>)
-                         : reinterpret_cast<const void *>(&prefill_m128_kernel<false, false>));
+    const void *k = m128_kernel(a.bf16, a.silu, mt);
     hipError_t e = hipLaunchKernel(k, grid, block, args, 0, stream);
     if (e != hipSuccess || chunks == 1) return e;
     const float *pc = partials;

@@ -471,6 +471,8 @@ def test_decode_wide_partials_ragged(dev, M):
     (17, 5120, 17408, 128, False),   # 68 tiles x 3 chunks
     (128, 17408, 5120, 32, False),   # 20 tiles x 12 chunks
     (100, 1024, 264, -1, True),      # 2 tiles x 2 chunks (16 stages), ragged M and N
+    (32, 2048, 1032, 128, True),     # 32-row tiles, exactly full
+    (33, 2048, 1032, 32, True),      # 64-row tiles, one row into the second 32
 ])
 def test_prefill_m128_split_k(dev, M, K, N, g, full):
     """M <= 128 with fewer tiles than CUs: each tile's K is split into chunks
