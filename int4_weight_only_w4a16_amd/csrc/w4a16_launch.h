@@ -29,10 +29,11 @@ int decode_streamk_grid(const LinearArgs &a, int num_cus);   // 0: use the tiles
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                          int grid, size_t max_lds);
 
-// Prefill (any M).  For M > 128 a last partial round of tiles can be split
-// along K; that needs `workspace` (prefill_workspace_bytes(capacity) bytes of
-// fp32 partials, no initial contents) when prefill_wants_workspace(a,
-// num_cus).  Without it (or with too small a capacity) every tile runs whole.
+// Prefill (any M).  For M <= 128 the K range can be split into chunks, and
+// for M > 128 a last partial round of tiles can be split along K; either
+// needs `workspace` (prefill_workspace_bytes(capacity) bytes of fp32
+// partials, no initial contents) when prefill_wants_workspace(a, num_cus).
+// Without it (or with too small a capacity) every tile runs whole.
 size_t prefill_workspace_bytes(int capacity);
 bool prefill_wants_workspace(const LinearArgs &a, int num_cus);
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
