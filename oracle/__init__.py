@@ -81,9 +81,15 @@ class Oracle:
         lib.oracle_linear_ex.argtypes = [p, i32, i32, p, p, i64, i64, i64, i64, p]
         lib.oracle_linear_at_ex.argtypes = [p, i32, i32, p, p, i64, i64, i64, i64, p, p, i64, p]
         lib.oracle_gate_up_silu.argtypes = [p, i32, p, p, i64, i64, i64, i64, p]
+        f64 = ctypes.c_double
+        lib.oracle_lora_shrink.argtypes = [p, p, i32, i32, i64, i64, i64, p]
+        lib.oracle_lora_expand.argtypes = [p, p, i32, i32, f64, i64, i64, i64, p]
+        lib.oracle_lora_expand_at.argtypes = [p, p, i32, i32, f64, i64, i64, i64, p, p, i64, p]
+        lib.oracle_linear_lora.argtypes = [p, i32, p, p, p, p, f64, i64, i64, i64, i64, i64, p]
         for f in (lib.oracle_unpack, lib.oracle_pack, lib.oracle_dequant,
                   lib.oracle_linear, lib.oracle_linear_at, lib.oracle_linear_ex,
-                  lib.oracle_linear_at_ex, lib.oracle_gate_up_silu):
+                  lib.oracle_linear_at_ex, lib.oracle_gate_up_silu, lib.oracle_lora_shrink,
+                  lib.oracle_lora_expand, lib.oracle_lora_expand_at, lib.oracle_linear_lora):
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -182,6 +188,69 @@ class Oracle:
                                             _ptr(out)), "gate_up_silu")
         return out
 
+    # ---- LoRA adapter: A [r, K] and B [N, r] in the activation type ----
+
+    def lora_shrink(self, x: np.ndarray, A: np.ndarray, act: str = "f16",
+                    absval: bool = False) -> np.ndarray:
+        """t [M, r] float64 = x . A^T (absval: sum_k |x| |A|)."""
+        xb, Ab = _act_bits(x, act), _act_bits(A, act)
+        M, K = xb.shape
+        r = Ab.shape[0]
+        if Ab.shape[1] != K:
+            raise ValueError("A must be [r, K]")
+        t = np.empty((M, r), dtype=np.float64)
+        _check(self.lib.oracle_lora_shrink(_ptr(xb), _ptr(Ab), _ACTS[act], int(absval), M, K,
+                                           r, _ptr(t)), "lora_shrink")
+        return t
+
+    def lora_expand(self, t: np.ndarray, B: np.ndarray, scale: float, act: str = "f16",
+                    absval: bool = False) -> np.ndarray:
+        """d [M, N] float64 = scale * t . B^T (absval: |scale| sum_j |t| |B|)."""
+        t = np.ascontiguousarray(t, dtype=np.float64)
+        Bb = _act_bits(B, act)
+        M, r = t.shape
+        N = Bb.shape[0]
+        if Bb.shape[1] != r:
+            raise ValueError("B must be [N, r]")
+        d = np.empty((M, N), dtype=np.float64)
+        _check(self.lib.oracle_lora_expand(_ptr(t), _ptr(Bb), _ACTS[act], int(absval),
+                                           float(scale), M, N, r, _ptr(d)), "lora_expand")
+        return d
+
+    def lora_expand_at(self, t: np.ndarray, B: np.ndarray, scale: float, ms: np.ndarray,
+                       ns: np.ndarray, act: str = "f16", absval: bool = False) -> np.ndarray:
+        """d[ms[i], ns[i]] for sampled outputs (arguments as lora_expand)."""
+        t = np.ascontiguousarray(t, dtype=np.float64)
+        Bb = _act_bits(B, act)
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        M, r = t.shape
+        N = Bb.shape[0]
+        out = np.empty(ms.shape[0], dtype=np.float64)
+        _check(self.lib.oracle_lora_expand_at(_ptr(t), _ptr(Bb), _ACTS[act], int(absval),
+                                              float(scale), M, N, r, _ptr(ms), _ptr(ns),
+                                              ms.shape[0], _ptr(out)), "lora_expand_at")
+        return out
+
+    def linear_lora(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+                    group_size: int, A: np.ndarray, B: np.ndarray, scale: float,
+                    act: str = "f16") -> np.ndarray:
+        """y [M, N] float64 = x . dequant(qweight, scales) + scale * (x . A^T) . B^T."""
+        xb, Ab, Bb = _act_bits(x, act), _act_bits(A, act), _act_bits(B, act)
+        qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+        scales = np.ascontiguousarray(scales, dtype=np.float16)
+        M, K = xb.shape
+        N = qweight.shape[1]
+        r = Ab.shape[0]
+        if Ab.shape != (r, K) or Bb.shape != (N, r):
+            raise ValueError("A must be [r, K] and B [N, r]")
+        y = np.empty((M, N), dtype=np.float64)
+        _check(self.lib.oracle_linear_lora(_ptr(xb), _ACTS[act], _ptr(qweight),
+                                           _ptr(scales.view(np.uint16)), _ptr(Ab), _ptr(Bb),
+                                           float(scale), M, K, N, group_size, r, _ptr(y)),
+               "linear_lora")
+        return y
+
 
 _default: Optional[Oracle] = None
 
@@ -222,3 +291,19 @@ def linear_at(x, qweight, scales, group_size, ms, ns, act="f16", absval=False):
 
 def gate_up_silu(x, qweight, scales, group_size, act="f16"):
     return default().gate_up_silu(x, qweight, scales, group_size, act)
+
+
+def lora_shrink(x, A, act="f16", absval=False):
+    return default().lora_shrink(x, A, act, absval)
+
+
+def lora_expand(t, B, scale, act="f16", absval=False):
+    return default().lora_expand(t, B, scale, act, absval)
+
+
+def lora_expand_at(t, B, scale, ms, ns, act="f16", absval=False):
+    return default().lora_expand_at(t, B, scale, ms, ns, act, absval)
+
+
+def linear_lora(x, qweight, scales, group_size, A, B, scale, act="f16"):
+    return default().linear_lora(x, qweight, scales, group_size, A, B, scale, act)

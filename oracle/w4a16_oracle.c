@@ -52,6 +52,22 @@
  * custom op enabled ("Qwen3.8-27B GPTQ-Pro Hybrid INT8" model card,
  * "Text-only serving"); they print neither the column order of the merge
  * nor SiLU, which is its textbook definition here.
+ * LoRA adapter on the quantised linear (oracle_lora_shrink, oracle_lora_expand,
+ * oracle_linear_lora): with A [r, K] and B [N, r] in the activation type and
+ * a scaling factor s,
+ *   t[m,j]   = sum_{k} x[m,k] * A[j,k]                 (fp64, k ascending)
+ *   d[m,n]   = s * sum_{j} t[m,j] * B[n,j]             (fp64, j ascending)
+ *   out[m,n] = y[m,n] + d[m,n]                         (y the linear above)
+ * The pages list LoRA adapters on the quantised linear path as part of the
+ * runtime contract ("GPTQ-Pro" README, "Runtime contract" table), load an
+ * adapter of a given rank (32 suggested, up to 256) beside the quantised
+ * model ("GPT-QModel" README, "EoRA Accuracy Recovery") and keep it separate
+ * from the packed weights, since a LoRA delta cannot be merged into them
+ * ("PEFT LoRA Training and Adapter Loading").  They print no formula; this
+ * file takes the textbook low-rank update in PEFT's storage order (lora_A
+ * weight [r, K], lora_B weight [N, r]) with s given as a number (alpha / r
+ * for plain LoRA).  With absval = 1 the functions return the magnitudes
+ * sum |x| |A| and |s| sum |t| |B| instead.
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math).  OpenMP only
  * splits rows m and column blocks of n, never the sum over k.
  */
@@ -288,4 +304,84 @@ int oracle_linear_at_ex(const uint16_t *x, int act, int absval, const int32_t *q
                         const int64_t *ms, const int64_t *ns, int64_t count, double *out) {
     return linear_at_impl(x, act, absval ? 1 : 0, qweight, scales, M, K, N, g, ms, ns, count,
                           out);
+}
+
+/* ---- LoRA adapter ---- */
+
+/* t[m*r + j] <- sum_k x[m,k] * A[j,k] (fp64, k ascending); x and A of type act,
+ * A stored [r, K].  absval: sum_k |x| * |A| instead. */
+int oracle_lora_shrink(const uint16_t *x, const uint16_t *A, int act, int absval, int64_t M,
+                       int64_t K, int64_t r, double *t) {
+    if (M < 0 || K <= 0 || r <= 0 || (act != 0 && act != 1)) return OR_ERR_ARG;
+    if (M == 0) return OR_OK;
+    if (!x || !A || !t) return OR_ERR_ARG;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += term(act_to_double(x[m * K + k], act), act_to_double(A[j * K + k], act),
+                            absval);
+            t[m * r + j] = acc;
+        }
+    }
+    return OR_OK;
+}
+
+/* One LoRA output: s * sum_j t[m,j] * B[n,j] (j ascending), or its magnitude. */
+static double lora_delta_at(const double *t, const uint16_t *B, int act, int absval,
+                            double scale, int64_t r, int64_t m, int64_t n) {
+    double acc = 0.0;
+    for (int64_t j = 0; j < r; ++j)
+        acc += term(t[m * r + j], act_to_double(B[n * r + j], act), absval);
+    return (absval ? fabs(scale) : scale) * acc;
+}
+
+/* d[m*N + n] <- s * sum_j t[m,j] * B[n,j]; t [M, r] in fp64, B [N, r] of type
+ * act.  absval: |s| * sum_j |t| * |B| (t given as magnitudes then). */
+int oracle_lora_expand(const double *t, const uint16_t *B, int act, int absval, double scale,
+                       int64_t M, int64_t N, int64_t r, double *d) {
+    if (M < 0 || N <= 0 || r <= 0 || (act != 0 && act != 1)) return OR_ERR_ARG;
+    if (M == 0) return OR_OK;
+    if (!t || !B || !d) return OR_ERR_ARG;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            d[m * N + n] = lora_delta_at(t, B, act, absval, scale, r, m, n);
+    return OR_OK;
+}
+
+/* out[i] <- d[ms[i], ns[i]] for sampled outputs (arguments as oracle_lora_expand). */
+int oracle_lora_expand_at(const double *t, const uint16_t *B, int act, int absval,
+                          double scale, int64_t M, int64_t N, int64_t r, const int64_t *ms,
+                          const int64_t *ns, int64_t count, double *out) {
+    if (M < 0 || N <= 0 || r <= 0 || count < 0 || (act != 0 && act != 1)) return OR_ERR_ARG;
+    if (count == 0) return OR_OK;
+    if (!t || !B || !ms || !ns || !out) return OR_ERR_ARG;
+    for (int64_t i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return OR_ERR_ARG;
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = lora_delta_at(t, B, act, absval, scale, r, ms[i], ns[i]);
+    return OR_OK;
+}
+
+/* out[m*N + n] <- linear(x)[m,n] + s * sum_j t[m,j] * B[n,j], t = x . A^T. */
+int oracle_linear_lora(const uint16_t *x, int act, const int32_t *qweight,
+                       const uint16_t *scales, const uint16_t *A, const uint16_t *B,
+                       double scale, int64_t M, int64_t K, int64_t N, int64_t g, int64_t r,
+                       double *out) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || r <= 0) return OR_ERR_ARG;
+    if (M == 0) return OR_OK;
+    if (!out) return OR_ERR_ARG;
+    double *t = (double *)malloc((size_t)M * (size_t)r * sizeof(double));
+    double *d = (double *)malloc((size_t)M * (size_t)N * sizeof(double));
+    int rc = (t && d) ? OR_OK : OR_ERR_ARG;
+    if (rc == OR_OK) rc = linear_impl(x, act, 0, qweight, scales, M, K, N, g, out);
+    if (rc == OR_OK) rc = oracle_lora_shrink(x, A, act, 0, M, K, r, t);
+    if (rc == OR_OK) rc = oracle_lora_expand(t, B, act, 0, scale, M, N, r, d);
+    if (rc == OR_OK)
+        for (int64_t i = 0; i < M * N; ++i) out[i] += d[i];
+    free(t);
+    free(d);
+    return rc;
 }

@@ -19,6 +19,9 @@ when it disagrees with:
     bounds |y| <= sum|x||w| (equality when every term is non-negative).
   - for the merged gate/up with SiLU * mul, numpy's own exp on the brute-force
     product, and closed forms (zero gate or up weights give exactly 0).
+  - for the LoRA adapter, the merged dense weight W + s A^T B^T through
+    numpy's matmul, one-hot closed forms (A picking a channel of x, B = I),
+    pure-Python loops on tiny inputs, and exact scaling relations.
 ``tests/test_oracle_mutants.py`` plants plausible mistakes in copies of the
 oracle source and checks that every one of them trips at least one pin.
 """
@@ -407,6 +410,113 @@ def pin_gate_up_silu_closed_forms(o):
     out = o.gate_up_silu(xv, o.pack(c), s, -1)
     assert np.allclose(out, z * z / (1.0 + np.exp(-z)), rtol=1e-15, atol=0)
     assert abs(z / (1.0 + np.exp(-z)) - 0.75 * z) < 1e-3
+
+
+# --- LoRA adapter: A [r, K], B [N, r] in the activation type ---------------------
+
+def _lora_case(rng, M, K, N, g, r, act):
+    """Codes, scales, x, A and B with decoded values, for either activation type."""
+    G = 1 if g == -1 else -(-K // g)
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    scales = rng.uniform(1e-2, 8e-2, size=(G, N)).astype(np.float16)
+    x = rng.standard_normal((M, K))
+    A = rng.uniform(-1.0, 1.0, size=(r, K)) / np.sqrt(K)
+    B = 0.25 * rng.standard_normal((N, r))
+    if act == "f16":
+        vals = [v.astype(np.float16) for v in (x, A, B)]
+        return codes, scales, vals, [v.astype(np.float64) for v in vals]
+    bits = [(v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16) for v in (x, A, B)]
+    return codes, scales, bits, [_bf16_value(b) for b in bits]
+
+
+def pin_lora_merged_weight(o):
+    """The adapter equals a dense weight update: x . (W + s A^T B^T) with W built
+    from the codes and the products taken by numpy's matmul in fp64."""
+    rng = np.random.default_rng(31)
+    for M, K, N, g, r, s in ((1, 64, 16, 16, 8, 2.0), (5, 128, 40, 32, 16, 0.5),
+                             (3, 256, 24, -1, 32, -1.25), (2, 96, 8, 16, 4, 3.0)):
+        for act in ("f16", "bf16"):
+            codes, scales, (x, A, B), (xv, Av, Bv) = _lora_case(rng, M, K, N, g, r, act)
+            q = o.pack(codes)
+            G = scales.shape[0]
+            grp = np.zeros(K, dtype=np.int64) if g == -1 else np.arange(K) // g
+            W = (codes.astype(np.float64) - 8.0) * scales.astype(np.float64)[grp]
+            ref = xv @ (W + s * (Av.T @ Bv.T))
+            y = o.linear_lora(x, q, scales, g, A, B, s, act=act)
+            assert y.shape == (M, N) and G == scales.shape[0]
+            tol = 1e-12 * max(1.0, float(np.abs(ref).max()))
+            assert np.abs(y - ref).max() <= tol, (M, K, N, g, r, act)
+            t = o.lora_shrink(x, A, act=act)
+            assert np.abs(t - xv @ Av.T).max() <= 1e-13 * max(1.0, float(np.abs(t).max()))
+            d = o.lora_expand(t, B, s, act=act)
+            assert np.abs(d - s * (t @ Bv.T)).max() <= 1e-13 * max(1.0, float(np.abs(d).max()))
+
+
+def pin_lora_brute_force_tiny(o):
+    """Pure-Python loops over decoded values on tiny inputs (no numpy products)."""
+    rng = np.random.default_rng(32)
+    M, K, N, g, r, s = 2, 16, 8, 16, 3, 1.5
+    for act in ("f16", "bf16"):
+        codes, scales, (x, A, B), (xv, Av, Bv) = _lora_case(rng, M, K, N, g, r, act)
+        y = o.linear_lora(x, o.pack(codes), scales, g, A, B, s, act=act)
+        for m in range(M):
+            t = [sum(float(xv[m, k]) * float(Av[j, k]) for k in range(K)) for j in range(r)]
+            for n in range(N):
+                base = sum(float(xv[m, k]) * (int(codes[k, n]) - 8) * float(scales[k // g, n])
+                           for k in range(K))
+                want = base + s * sum(t[j] * float(Bv[n, j]) for j in range(r))
+                assert abs(y[m, n] - want) <= 1e-12 * max(1.0, abs(want)), (act, m, n)
+
+
+def pin_lora_closed_forms(o):
+    """One-hot A rows pick channels of x and B = I copies t: d[m, n] = s x[m, c_n]
+    exactly.  A zero adapter or s = 0 leaves the linear unchanged; d is odd and
+    linear in s (exact in binary floating point for s -> 2s and s -> -s)."""
+    rng = np.random.default_rng(33)
+    M, K, N, r, s = 3, 32, 8, 8, 0.75
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    chans = rng.choice(K, size=r, replace=False)
+    A = np.zeros((r, K), dtype=np.float16)
+    A[np.arange(r), chans] = 1.0
+    B = np.eye(N, r, dtype=np.float16)
+    d = o.lora_expand(o.lora_shrink(x, A), B, s)
+    assert np.array_equal(d, s * x[:, chans].astype(np.float64))
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    scales = rng.uniform(1e-2, 8e-2, size=(1, N)).astype(np.float16)
+    q = o.pack(codes)
+    base = o.linear(x, q, scales, -1)
+    assert np.array_equal(o.linear_lora(x, q, scales, -1, A, B, 0.0), base)
+    assert np.array_equal(o.linear_lora(x, q, scales, -1, np.zeros_like(A), B, s), base)
+    assert np.array_equal(o.linear_lora(x, q, scales, -1, A, np.zeros_like(B), s), base)
+    assert np.array_equal(o.linear_lora(x, q, scales, -1, A, B, s), base + d)
+    Ar = (rng.standard_normal((r, K)) * 0.2).astype(np.float16)
+    Br = (rng.standard_normal((N, r)) * 0.2).astype(np.float16)
+    t = o.lora_shrink(x, Ar)
+    d1 = o.lora_expand(t, Br, s)
+    assert np.array_equal(o.lora_expand(t, Br, 2 * s), 2 * d1)
+    assert np.array_equal(o.lora_expand(t, Br, -s), -d1)
+
+
+def pin_lora_magnitudes_and_samples(o):
+    """absval returns dense products of magnitudes (|x| |A|^T, |s| |t| |B|^T) that
+    bound the signed results, and the sampled expansion equals the full one."""
+    rng = np.random.default_rng(34)
+    M, K, N, r, s = 4, 64, 24, 16, -0.5
+    for act in ("f16", "bf16"):
+        _, _, (x, A, B), (xv, Av, Bv) = _lora_case(rng, M, K, N, 16, r, act)
+        t = o.lora_shrink(x, A, act=act)
+        ta = o.lora_shrink(x, A, act=act, absval=True)
+        assert np.abs(ta - np.abs(xv) @ np.abs(Av).T).max() <= 1e-13 * float(ta.max())
+        assert np.all(np.abs(t) <= ta * (1 + 1e-12))
+        d = o.lora_expand(t, B, s, act=act)
+        da = o.lora_expand(t, B, s, act=act, absval=True)
+        assert np.abs(da - abs(s) * (np.abs(t) @ np.abs(Bv).T)).max() <= 1e-13 * float(da.max())
+        assert np.all(np.abs(d) <= da * (1 + 1e-12))
+        ms = rng.integers(0, M, size=40)
+        ns = rng.integers(0, N, size=40)
+        assert np.array_equal(o.lora_expand_at(t, B, s, ms, ns, act=act), d[ms, ns])
+        assert np.array_equal(o.lora_expand_at(t, B, s, ms, ns, act=act, absval=True),
+                              da[ms, ns])
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

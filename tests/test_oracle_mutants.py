@@ -33,6 +33,13 @@ MUTANTS = {
     "half_subnormal_scale": ("ldexp((double)man, -24)", "ldexp((double)man, -23)"),
     "half_sign_dropped": ("return sign ? -v : v;", "return v;"),
     "scale_column_offset": ("scales[group_of(k, g) * N + n]", "scales[group_of(k, g) * N + (n ^ 1)]"),
+    "lora_a_transposed": ("act_to_double(A[j * K + k], act)", "act_to_double(A[k * r + j], act)"),
+    "lora_b_row_offset": ("act_to_double(B[n * r + j], act)", "act_to_double(B[(n ^ 1) * r + j], act)"),
+    "lora_scale_dropped": ("return (absval ? fabs(scale) : scale) * acc;", "return acc;"),
+    "lora_delta_subtracted": ("out[i] += d[i];", "out[i] -= d[i];"),
+    "lora_a_read_as_half": ("act_to_double(A[j * K + k], act)", "act_to_double(A[j * K + k], 0)"),
+    "lora_last_rank_dropped": ("for (int64_t j = 0; j < r; ++j)\n        acc +=",
+                               "for (int64_t j = 0; j + 1 < r; ++j)\n        acc +="),
 }
 
 

@@ -171,6 +171,28 @@ def gate_up_prefill() -> Case:
     return Case("gate_up_prefill", 2048, 5120, 34816, 128, 3, x_dist="normal")
 
 
+LORA_SCALE = 2.0          # alpha / r with alpha = 2r
+LORA_RANKS = (8, 16, 32, 64, 128, 256)
+
+
+def lora_adapter(K: int, N: int, rank: int, seed: int, act: str = "f16"):
+    """A seeded LoRA adapter (A [rank, K], B [N, rank]) from its own generator.
+
+    A ~ U(-1/sqrt(K), 1/sqrt(K)), the bound of PEFT's default initialisation
+    of lora_A; B ~ N(0, 0.25^2), a stand-in for a trained adapter whose term is
+    of the order of the base output (PEFT initialises B to zero, which would
+    make the term vanish).  The pages suggest rank 32, then 64, with 128 and
+    256 as larger choices ("GPT-QModel" README, "EoRA Accuracy Recovery").
+    Draw order: A, then B.  Returned as fp16 arrays, or bfloat16 bit patterns
+    (uint16) when act is "bf16"."""
+    rng = np.random.default_rng(seed)
+    A = rng.uniform(-1.0, 1.0, size=(rank, K)) / math.sqrt(K)
+    B = 0.25 * rng.standard_normal((N, rank))
+    if act == "bf16":
+        return bf16_bits(A), bf16_bits(B)
+    return A.astype(np.float16), B.astype(np.float16)
+
+
 def sweep() -> List[Case]:
     """Group-size and shape sweep: 6 g x 3 (K,N) x 4 M = 72 cases, 5% zero cells, seed 4."""
     out = []
