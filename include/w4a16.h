@@ -57,6 +57,7 @@
 #ifndef W4A16_H
 #define W4A16_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -73,7 +74,9 @@ typedef enum {
     W4A16_ERR_CODE = 5,    /* pack_gptq_v2: a code above 15 */
     W4A16_ERR_DEVICE = 6,  /* no usable HIP device, or the current one is not gfx950 */
     W4A16_ERR_LAUNCH = 7,  /* the kernel launch reported an error */
-    W4A16_ERR_KERNEL = 8   /* w4a16_linear_ex: the requested kernel cannot take this M */
+    W4A16_ERR_KERNEL = 8,  /* w4a16_linear_ex: the requested kernel cannot take this M */
+    W4A16_ERR_RANK = 9,    /* LoRA rank not a multiple of 8 in [8, W4A16_LORA_MAX_RANK] */
+    W4A16_ERR_WORKSPACE = 10  /* LoRA workspace smaller than w4a16_lora_workspace_bytes */
 } w4a16_status;
 
 /* Largest M the small-batch (decode) kernel takes; larger M runs the MFMA
@@ -158,6 +161,50 @@ int w4a16_gate_up_silu_bf16(const void *x, const int32_t *qweight, const void *s
 int w4a16_gate_up_silu_bf16_ex(const void *x, const int32_t *qweight, const void *scales,
                                void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
                                void *stream, int kernel);
+
+/* LoRA adapter on the quantised linear: y = x . dequant(qweight, scales)
+ * + s * (x . A^T) . B^T.  The pages list LoRA adapters on the quantised
+ * linear path in the runtime contract ("GPTQ-Pro" README, "Runtime contract"
+ * table), keep the adapter beside the packed weights rather than merged into
+ * them ("GPT-QModel" README, "PEFT LoRA Training and Adapter Loading") and
+ * suggest ranks 32 and 64, with 128 and 256 as larger choices ("EoRA Accuracy
+ * Recovery").  The update is the textbook low-rank one in PEFT's storage
+ * order:
+ *   lora_a : device [rank, K], the activation type (lora_A weight)
+ *   lora_b : device [N, rank], the activation type (lora_B weight)
+ *   lora_scale : s (alpha / rank for plain LoRA), applied in fp32
+ *   rank : a multiple of 8 in [8, W4A16_LORA_MAX_RANK] (else W4A16_ERR_RANK)
+ *   workspace : device buffer of at least w4a16_lora_workspace_bytes(M, K,
+ *     rank) bytes, 16-byte aligned, no initial contents, owned by the caller;
+ *     calls that overlap in time must not share one (else a race).  Too small:
+ *     W4A16_ERR_WORKSPACE.
+ *   x, qweight, scales, y, shapes, group sizes, stream and the other errors
+ *   as for w4a16_linear (the _bf16 form: bfloat16 x, A, B and y, as for
+ *   w4a16_linear_bf16).  All checks run before any HIP call.
+ * Steps on the stream: the linear writes y (its own kernel choice); a
+ * shrink kernel forms t = x . A^T as fp32 partial sums over chunks of K; an
+ * expand kernel adds the chunks in a fixed order, rounds t to the
+ * activation type, forms delta = t . B^T in fp32 on the matrix cores and
+ * writes y = round(y + s * delta).
+ * Hence, per element and beyond the linear's own bound (u = 2^-11 for fp16,
+ * 2^-8 for bfloat16): u |y_lin| + u |y| + |s| sum_j |B[n,j]| (u |t_j|
+ * + K 2^-24 sum_k |x[m,k]| |A[j,k]|) + rank 2^-24 |s| sum_j |t_j| |B[n,j]|,
+ * to first order; fp16 needs every t_j inside the fp16 range.
+ * Deterministic, as w4a16_linear. */
+#define W4A16_LORA_MAX_RANK 1024
+int w4a16_linear_lora(const void *x, const int32_t *qweight, const void *scales,
+                      const void *lora_a, const void *lora_b, float lora_scale, void *y,
+                      int64_t M, int64_t K, int64_t N, int64_t group_size, int64_t rank,
+                      void *workspace, size_t workspace_bytes, void *stream);
+int w4a16_linear_lora_bf16(const void *x, const int32_t *qweight, const void *scales,
+                           const void *lora_a, const void *lora_b, float lora_scale, void *y,
+                           int64_t M, int64_t K, int64_t N, int64_t group_size, int64_t rank,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace w4a16_linear_lora needs for (M, K, rank): fp32 partial
+ * sums of x . A^T, at most 16 chunks of [M rounded up to 16, rank].  0 for
+ * M <= 0 or arguments the linear would reject. */
+size_t w4a16_lora_workspace_bytes(int64_t M, int64_t K, int64_t rank);
 
 /* Host-side packing into the GPTQ_V2 layout (native int32 qweight, "GPTQ-Pro"
  * README, "Runtime contract"):

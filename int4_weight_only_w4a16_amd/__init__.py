@@ -7,10 +7,11 @@ not a gfx950, calls raise.
 
 Names match the C ABI in ``include/w4a16.h``:
   w4a16_linear, w4a16_linear_ex, w4a16_linear_bf16, w4a16_linear_bf16_ex,
-  w4a16_gate_up_silu(_ex, _bf16, _bf16_ex), pack_gptq_v2, unpack_gptq_v2,
+  w4a16_gate_up_silu(_ex, _bf16, _bf16_ex), w4a16_linear_lora(_bf16),
+  w4a16_lora_workspace_bytes, pack_gptq_v2, unpack_gptq_v2,
   w4a16_status_string, and the measurement aid w4a16_read_probe
-plus ``linear`` and ``gate_up_silu`` (allocate y with torch, then call the
-_ex entry point of x's dtype).
+plus ``linear``, ``gate_up_silu`` and ``linear_lora`` (allocate y, and the
+LoRA workspace, with torch, then call the entry point of x's dtype).
 """
 
 from __future__ import annotations
@@ -33,6 +34,9 @@ W4A16_ERR_CODE = 5
 W4A16_ERR_DEVICE = 6
 W4A16_ERR_LAUNCH = 7
 W4A16_ERR_KERNEL = 8
+W4A16_ERR_RANK = 9
+W4A16_ERR_WORKSPACE = 10
+W4A16_LORA_MAX_RANK = 1024
 
 W4A16_DECODE_MAX_M = 16
 W4A16_KERNEL_AUTO = 0
@@ -41,7 +45,8 @@ W4A16_KERNEL_PREFILL = 2
 
 EXPORTS = ("w4a16_linear", "w4a16_linear_ex", "w4a16_linear_bf16", "w4a16_linear_bf16_ex",
            "w4a16_gate_up_silu", "w4a16_gate_up_silu_ex", "w4a16_gate_up_silu_bf16",
-           "w4a16_gate_up_silu_bf16_ex", "pack_gptq_v2", "unpack_gptq_v2", "w4a16_read_probe",
+           "w4a16_gate_up_silu_bf16_ex", "w4a16_linear_lora", "w4a16_linear_lora_bf16",
+           "w4a16_lora_workspace_bytes", "pack_gptq_v2", "unpack_gptq_v2", "w4a16_read_probe",
            "w4a16_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -78,6 +83,12 @@ def load_library() -> ctypes.CDLL:
     for name in ("w4a16_gate_up_silu_ex", "w4a16_gate_up_silu_bf16_ex"):
         getattr(lib, name).argtypes = [p, p, p, p, i64, i64, i64, i64, p, i32]
         getattr(lib, name).restype = i32
+    f32, sz = ctypes.c_float, ctypes.c_size_t
+    for name in ("w4a16_linear_lora", "w4a16_linear_lora_bf16"):
+        getattr(lib, name).argtypes = [p, p, p, p, p, f32, p, i64, i64, i64, i64, i64, p, sz, p]
+        getattr(lib, name).restype = i32
+    lib.w4a16_lora_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.w4a16_lora_workspace_bytes.restype = sz
     lib.pack_gptq_v2.argtypes = [p, p, i64, i64]
     lib.pack_gptq_v2.restype = i32
     lib.unpack_gptq_v2.argtypes = [p, p, i64, i64]
@@ -193,6 +204,67 @@ def gate_up_silu(x, qweight, scales, group_size: int, out=None, stream=None,
         raise ValueError("out must have x's dtype")
     w4a16_gate_up_silu_ex(x, qweight, scales, out, M, K, N, group_size, stream, kernel,
                           x.dtype == torch.bfloat16)
+    return out
+
+
+def w4a16_lora_workspace_bytes(M: int, K: int, rank: int) -> int:
+    """Workspace bytes w4a16_linear_lora needs (0 for arguments it rejects)."""
+    return int(load_library().w4a16_lora_workspace_bytes(int(M), int(K), int(rank)))
+
+
+def w4a16_linear_lora(x, qweight, scales, lora_a, lora_b, lora_scale: float, y, M: int, K: int,
+                      N: int, group_size: int, rank: int, workspace, workspace_bytes: int,
+                      stream=None, bf16: bool = False) -> None:
+    """y = x . dequant(qweight, scales) + lora_scale * (x . A^T) . B^T with
+    A = lora_a [rank, K] and B = lora_b [N, rank] (the C w4a16_linear_lora, or
+    its _bf16 form when bf16)."""
+    lib = load_library()
+    f = lib.w4a16_linear_lora_bf16 if bf16 else lib.w4a16_linear_lora
+    st = f(_addr(x), _addr(qweight), _addr(scales), _addr(lora_a), _addr(lora_b),
+           float(lora_scale), _addr(y), int(M), int(K), int(N), int(group_size), int(rank),
+           _addr(workspace), int(workspace_bytes), _stream_handle(stream))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_linear_lora")
+
+
+def w4a16_linear_lora_bf16(x, qweight, scales, lora_a, lora_b, lora_scale: float, y, M: int,
+                           K: int, N: int, group_size: int, rank: int, workspace,
+                           workspace_bytes: int, stream=None) -> None:
+    """Same as the C ``w4a16_linear_lora_bf16``."""
+    w4a16_linear_lora(x, qweight, scales, lora_a, lora_b, lora_scale, y, M, K, N, group_size,
+                      rank, workspace, workspace_bytes, stream, bf16=True)
+
+
+def linear_lora(x, qweight, scales, group_size: int, lora_a, lora_b, lora_scale: float,
+                out=None, workspace=None, stream=None):
+    """Allocate y (x's dtype, [M, N]) and, unless given, the workspace (a uint8
+    device tensor) with torch, then run the linear with the LoRA term.  lora_a
+    [rank, K] and lora_b [N, rank] have x's dtype."""
+    import torch
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be float16 or bfloat16")
+    for name, t, dt in (("x", x, x.dtype), ("qweight", qweight, torch.int32),
+                        ("scales", scales, torch.float16), ("lora_a", lora_a, x.dtype),
+                        ("lora_b", lora_b, x.dtype)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    M, K = x.shape
+    N = qweight.shape[1]
+    rank = lora_a.shape[0]
+    if qweight.shape[0] * 8 != K:
+        raise ValueError("qweight must be [K/8, N]")
+    if tuple(lora_a.shape) != (rank, K) or tuple(lora_b.shape) != (N, rank):
+        raise ValueError("lora_a must be [rank, K] and lora_b [N, rank]")
+    need = w4a16_lora_workspace_bytes(M, K, rank)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    elif out.dtype != x.dtype:
+        raise ValueError("out must have x's dtype")
+    w4a16_linear_lora(x, qweight, scales, lora_a, lora_b, lora_scale, out, M, K, N, group_size,
+                      rank, workspace, workspace.numel() * workspace.element_size(), stream,
+                      x.dtype == torch.bfloat16)
     return out
 
 

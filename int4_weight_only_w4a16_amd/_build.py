@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libw4a16.so")
 
-SOURCES = ("w4a16_capi.hip", "decode_gfx950.hip", "prefill_gfx950.hip", "probe_gfx950.hip")
+SOURCES = ("w4a16_capi.hip", "decode_gfx950.hip", "prefill_gfx950.hip", "lora_gfx950.hip",
+           "probe_gfx950.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

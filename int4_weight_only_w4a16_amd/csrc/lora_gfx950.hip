@@ -1,0 +1,217 @@
+// LoRA adapter term on the quantised linear, gfx950: y += s * (x . A^T) . B^T
+// after the W4A16 linear has written y.
+//
+// The pages list LoRA adapters on the quantised linear path in the runtime
+// contract ("GPTQ-Pro" README, "Runtime contract" table) and keep an adapter
+// separate from the packed weights, since a LoRA delta cannot be merged into
+// them ("GPT-QModel" README, "PEFT LoRA Training and Adapter Loading"); the
+// suggested ranks are 32 and 64, with 128 and 256 as larger choices ("EoRA
+// Accuracy Recovery").  The update is the textbook low-rank one in PEFT's
+// storage order: A [r, K] (lora_A weight) and B [N, r] (lora_B weight), both
+// in the activation type, and a scaling s given as a number.
+//
+// Two kernels, both on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
+//   lora_shrink_kernel  t = x . A^T as fp32 partial sums over S chunks of K,
+//                       one [Mp, r] slab per chunk (Mp = M rounded up to 16);
+//   lora_expand_kernel  sums the S slabs of a 16-row block in a fixed order,
+//                       rounds t to the activation type, multiplies by B^T,
+//                       and adds s times the result to y in place:
+//                       y = round(y + s * delta), one rounding of the sum.
+// Both operands of every MFMA are contiguous along the contracted index (x
+// and A rows along K, t rows and B rows along r), so each lane loads its
+// eight values with one 16-byte load.  The result is deterministic.
+
+#include "w4a16_device.hpp"
+#include "w4a16_launch.h"
+
+namespace w4a16 {
+namespace {
+
+constexpr int kLoraTargetGroups = 512;   // shrink workgroups aimed for (2 per CU)
+constexpr int kLoraMaxSplits = 16;       // K chunks of the shrink, at most
+
+template <bool BF>
+__device__ __forceinline__ float act_lo(uint32_t v) {
+    if constexpr (BF) return __uint_as_float(v << 16);
+    else return (float)half_lo(v);
+}
+
+template <bool BF>
+__device__ __forceinline__ float act_hi(uint32_t v) {
+    if constexpr (BF) return __uint_as_float(v & 0xFFFF0000u);
+    else return (float)half_hi(v);
+}
+
+// One workgroup (4 waves) computes the partial t of a 16-row block of x over
+// one K chunk, for 64 columns of t (blockIdx.z): the waves take alternate
+// 32-wide K steps of the chunk and their sums are added in LDS in wave order.
+template <bool BF>
+__global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ A,
+                                                          float *__restrict__ tp, int M, int K,
+                                                          int r, int Mp, int chunk_steps) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int mb = blockIdx.x, s = blockIdx.y, jc = blockIdx.z;
+    const int nsteps = (K + 31) / 32;
+    const int kb = s * chunk_steps;
+    const int ke = min(kb + chunk_steps, nsteps);
+    const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const auto ar = make_rsrc(A, (uint32_t)r * (uint32_t)K * 2u);
+    const int row = 16 * mb + (lane & 15);
+    const int kofs = 8 * (lane >> 4);
+    f4 acc[4] = {};
+    for (int st = kb + w; st < ke; st += 4) {
+        const int k = 32 * st + kofs;             // K % 8 == 0: eight in or eight out
+        const bool kin = k < K;
+        const uint32_t xo = (row < M && kin) ? (uint32_t)(row * K + k) * 2u : kOOB;
+        const u4 xa = load_b128(xr, xo);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const int j = 64 * jc + 16 * jb + (lane & 15);
+            const uint32_t ao = (j < r && kin) ? (uint32_t)(j * K + k) * 2u : kOOB;
+            acc[jb] = mfma16x16x32_t<BF>(xa, load_b128(ar, ao), acc[jb]);
+        }
+    }
+    __shared__ f4 red[4][4][64];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) red[w][jb][lane] = acc[jb];
+    __syncthreads();
+    // thread (w, lane) finishes column block w of the four
+    const f4 v = ((red[0][w][lane] + red[1][w][lane]) + red[2][w][lane]) + red[3][w][lane];
+    const int j = 64 * jc + 16 * w + (lane & 15);
+    if (j < r) {
+        float *dst = tp + ((size_t)s * Mp + 16 * mb + 4 * (lane >> 4)) * r + j;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)i * r] = v[i];
+    }
+}
+
+// One workgroup (4 waves) adds the adapter term to a 16-row by 64*NB-column
+// tile of y; wave w owns columns [16*NB*w, 16*NB*(w+1)) of the tile.
+template <bool BF, int NB>
+__global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restrict__ tp,
+                                                          const uint16_t *__restrict__ B,
+                                                          uint16_t *__restrict__ y, float scale,
+                                                          int M, int N, int r, int Mp, int S) {
+    constexpr int TN = 64 * NB;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int nt = blockIdx.x, mb = blockIdx.y;
+    const int n0 = nt * TN + 16 * NB * w;
+    const auto br = make_rsrc(B, (uint32_t)N * (uint32_t)r * 2u);
+    const auto tr = make_rsrc(tp, (uint32_t)S * (uint32_t)Mp * (uint32_t)r * 4u);
+    const int trow = 16 * mb + (lane & 15);       // < Mp always
+    const int kofs = 8 * (lane >> 4);
+    f4 acc[NB] = {};
+    for (int kk = 0; kk < r; kk += 32) {
+        const int j = kk + kofs;                  // r % 8 == 0: eight in or eight out
+        const bool jin = j < r;
+        float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S; ++s) {             // fixed order: deterministic
+            const uint32_t o = jin ? (uint32_t)(((s * Mp + trow) * r + j) * 4) : kOOB;
+            const f4 lo = __builtin_bit_cast(f4, load_b128(tr, o));
+            const f4 hi = __builtin_bit_cast(f4, load_b128(tr, o + 16u));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                tv[i] += lo[i];
+                tv[4 + i] += hi[i];
+            }
+        }
+        const u4 ta = {pack2<BF>(tv[0], tv[1]), pack2<BF>(tv[2], tv[3]),
+                       pack2<BF>(tv[4], tv[5]), pack2<BF>(tv[6], tv[7])};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int n = n0 + 16 * nb + (lane & 15);
+            const uint32_t bo = (jin && n < N) ? (uint32_t)(n * r + j) * 2u : kOOB;
+            acc[nb] = mfma16x16x32_t<BF>(ta, load_b128(br, bo), acc[nb]);
+        }
+    }
+    // the tile through LDS, so that y is read and written in 16-byte runs
+    __shared__ float tile[16][TN + 4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            tile[4 * (lane >> 4) + i][16 * NB * w + 16 * nb + (lane & 15)] = acc[nb][i];
+    __syncthreads();
+    constexpr int kRuns = TN / 8;                 // 8-column runs per row
+    for (int q = threadIdx.x; q < 16 * kRuns; q += 256) {
+        const int rr = q / kRuns, c = 8 * (q % kRuns);
+        const int m = 16 * mb + rr, n = nt * TN + c;
+        if (m >= M || n >= N) continue;           // N % 8 == 0: runs are whole
+        u4 *p = reinterpret_cast<u4 *>(y + (size_t)m * N + n);
+        const u4 v = *p;
+        u4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = pack2<BF>(act_lo<BF>(v[i]) + scale * tile[rr][c + 2 * i],
+                             act_hi<BF>(v[i]) + scale * tile[rr][c + 2 * i + 1]);
+        *p = o;
+    }
+}
+
+struct LoraPlan {
+    int mblocks, jchunks, chunk_steps, splits, Mp;
+};
+
+LoraPlan lora_plan(int64_t M, int64_t K, int64_t r) {
+    LoraPlan p;
+    p.mblocks = (int)((M + 15) / 16);
+    p.Mp = 16 * p.mblocks;
+    p.jchunks = (int)((r + 63) / 64);
+    const int nsteps = (int)((K + 31) / 32);
+    const int groups = p.mblocks * p.jchunks;
+    int want = (kLoraTargetGroups + groups - 1) / groups;
+    want = want < 1 ? 1 : want > kLoraMaxSplits ? kLoraMaxSplits : want;
+    int per = (nsteps + want - 1) / want;
+    if (per < 4) per = 4 < nsteps ? 4 : nsteps;   // every wave of a chunk gets a step
+    p.chunk_steps = per;
+    p.splits = (nsteps + per - 1) / per;          // every chunk non-empty
+    return p;
+}
+
+}  // namespace
+
+size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r) {
+    if (M <= 0) return 0;
+    const LoraPlan p = lora_plan(M, K, r);
+    return (size_t)p.splits * (size_t)p.Mp * (size_t)r * sizeof(float);
+}
+
+hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace) {
+    const LoraPlan p = lora_plan(a.M, a.K, a.r);
+    const int M = (int)a.M, K = (int)a.K, N = (int)a.N, r = (int)a.r;
+    const auto *x = static_cast<const uint16_t *>(a.x);
+    const auto *A = static_cast<const uint16_t *>(a.A);
+    const auto *B = static_cast<const uint16_t *>(a.B);
+    auto *y = static_cast<uint16_t *>(a.y);
+    auto *tp = static_cast<float *>(workspace);
+    const dim3 sg(p.mblocks, p.splits, p.jchunks);
+    if (a.bf16)
+        lora_shrink_kernel<true><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
+    else
+        lora_shrink_kernel<false><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // decode-sized batches: narrow tiles for more workgroups on a short y
+    const bool narrow = a.M <= 16;
+    const int TN = narrow ? 64 : 256;
+    const dim3 eg((N + TN - 1) / TN, p.mblocks);
+    if (narrow) {
+        if (a.bf16)
+            lora_expand_kernel<true, 1><<<eg, 256, 0, stream>>>(tp, B, y, a.scale, M, N, r, p.Mp,
+                                                                p.splits);
+        else
+            lora_expand_kernel<false, 1><<<eg, 256, 0, stream>>>(tp, B, y, a.scale, M, N, r,
+                                                                 p.Mp, p.splits);
+    } else {
+        if (a.bf16)
+            lora_expand_kernel<true, 4><<<eg, 256, 0, stream>>>(tp, B, y, a.scale, M, N, r, p.Mp,
+                                                                p.splits);
+        else
+            lora_expand_kernel<false, 4><<<eg, 256, 0, stream>>>(tp, B, y, a.scale, M, N, r,
+                                                                 p.Mp, p.splits);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace w4a16

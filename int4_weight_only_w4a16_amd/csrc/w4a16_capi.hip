@@ -204,6 +204,53 @@ extern "C" int w4a16_gate_up_silu_bf16(const void *x, const int32_t *qweight,
                        true, true);
 }
 
+// The linear followed by the LoRA adapter term on the same stream.
+static int lora_call(const void *x, const int32_t *qweight, const void *scales,
+                     const void *lora_a, const void *lora_b, float lora_scale, void *y,
+                     int64_t M, int64_t K, int64_t N, int64_t group_size, int64_t rank,
+                     void *workspace, size_t workspace_bytes, void *stream, bool bf16) {
+    int st = validate(x, qweight, scales, y, M, K, N, group_size);
+    if (st != W4A16_OK) return st;
+    if (rank < 8 || rank > W4A16_LORA_MAX_RANK || rank % 8 != 0) return W4A16_ERR_RANK;
+    if (2 * rank * K >= kMaxBufferBytes || 2 * N * rank >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+    const size_t need = w4a16::lora_workspace_bytes(M, K, rank);
+    if (need >= (size_t)kMaxBufferBytes) return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!lora_a || !lora_b || !workspace) return W4A16_ERR_NULL;
+    if (!aligned16(lora_a) || !aligned16(lora_b) || !aligned16(workspace)) return W4A16_ERR_ALIGN;
+    if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+    st = linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO, bf16);
+    if (st != W4A16_OK) return st;
+    const w4a16::LoraArgs a{x, lora_a, lora_b, y, M, K, N, rank, lora_scale, bf16};
+    const hipError_t e = w4a16::launch_lora(a, reinterpret_cast<hipStream_t>(stream), workspace);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+extern "C" size_t w4a16_lora_workspace_bytes(int64_t M, int64_t K, int64_t rank) {
+    if (M <= 0 || K <= 0 || K % 16 != 0 || rank < 8 || rank > W4A16_LORA_MAX_RANK ||
+        rank % 8 != 0 || M >= kMaxBufferBytes || K >= kMaxBufferBytes)
+        return 0;
+    return w4a16::lora_workspace_bytes(M, K, rank);
+}
+
+extern "C" int w4a16_linear_lora(const void *x, const int32_t *qweight, const void *scales,
+                                 const void *lora_a, const void *lora_b, float lora_scale,
+                                 void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
+                                 int64_t rank, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    return lora_call(x, qweight, scales, lora_a, lora_b, lora_scale, y, M, K, N, group_size, rank,
+                     workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int w4a16_linear_lora_bf16(const void *x, const int32_t *qweight, const void *scales,
+                                      const void *lora_a, const void *lora_b, float lora_scale,
+                                      void *y, int64_t M, int64_t K, int64_t N,
+                                      int64_t group_size, int64_t rank, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    return lora_call(x, qweight, scales, lora_a, lora_b, lora_scale, y, M, K, N, group_size, rank,
+                     workspace, workspace_bytes, stream, true);
+}
+
 extern "C" int pack_gptq_v2(const uint8_t *codes, int32_t *qweight, int64_t K, int64_t N) {
     if (K <= 0 || N <= 0 || K % 8 != 0) return W4A16_ERR_SHAPE;
     if (!codes || !qweight) return W4A16_ERR_NULL;
@@ -260,6 +307,8 @@ extern "C" const char *w4a16_status_string(int status) {
         case W4A16_ERR_DEVICE: return "no usable gfx950 device";
         case W4A16_ERR_LAUNCH: return "kernel launch failed";
         case W4A16_ERR_KERNEL: return "requested kernel cannot take this M";
+        case W4A16_ERR_RANK: return "LoRA rank must be a multiple of 8 in [8, 1024]";
+        case W4A16_ERR_WORKSPACE: return "workspace smaller than w4a16_lora_workspace_bytes";
         default: return "unknown status";
     }
 }

@@ -39,6 +39,20 @@ bool prefill_wants_workspace(const LinearArgs &a, int num_cus);
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                           int num_cus);
 
+// LoRA adapter term, added to a y the linear has already written:
+// y = round(y + scale * (x . A^T) . B^T), A [r, K] and B [N, r] in the
+// activation type (r % 8 == 0).  `workspace` holds lora_workspace_bytes(M, K,
+// r) bytes of fp32 partial sums of x . A^T, no initial contents.
+struct LoraArgs {
+    const void *x, *A, *B;
+    void *y;
+    int64_t M, K, N, r;
+    float scale;
+    bool bf16;
+};
+size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r);
+hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace);
+
 // Streaming-read probe over `bytes` (a multiple of 16) at data.
 hipError_t launch_read_probe(const void *data, int64_t bytes, void *sink, hipStream_t stream,
                              int num_cus);

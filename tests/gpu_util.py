@@ -44,13 +44,15 @@ BF16_U = 2.0 ** -8
 
 
 def check_parity_bf16(y_gpu: np.ndarray, y_ref: np.ndarray, mag: np.ndarray, K: int,
-                      what: str = "", mag0=None) -> dict:
+                      what: str = "", mag0=None, extra=None) -> dict:
     y = y_gpu.astype(np.float64)
     d = np.abs(y - y_ref)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
     bound = BF16_U * np.abs(y_ref) + 1.02 * (BF16_U + K * 2.0 ** -24) * mag + 1e-30
     if mag0 is not None:
         bound = bound + 1.02 * 35 * K * 2.0 ** -24 * mag0
+    if extra is not None:
+        bound = bound + extra
     bad = d > bound
     worst = int(np.argmax(d - bound)) if d.size else 0
     assert not np.any(bad), \
@@ -98,6 +100,17 @@ def check_gate_up(y, ref, lin, mag, mag0, K, bf16, what):
     mean_rel = float(d.sum()) / denom if denom > 0 else float(d.sum())
     assert mean_rel <= mean_bar, f"{what}: mean relative error {mean_rel:.4g}"
 
+
+
+# LoRA adapter term (w4a16_linear_lora): beyond the linear's own bound, the
+# C ABI states, per element (u half an ulp of the activation type, relative):
+#   u |y_lin| + u |y| + u P1 + K 2^-24 P2 + r 2^-24 P1
+# with P1 = |s| sum_j |t_j| |B[n,j]| (t exact) and P2 = |s| sum_j
+# (sum_k |x| |A[j,k]|) |B[n,j]|: y_lin rounded once, t summed in fp32 and
+# rounded to the activation type, the rank-r product in fp32, y rounded once.
+def lora_extra_bound(lin, ref, p1, p2, K, r, u):
+    return 1.02 * (u * np.abs(lin) + u * np.abs(ref) + u * p1 + K * 2.0 ** -24 * p2
+                   + r * 2.0 ** -24 * p1)
 
 
 def bf16_to_float(bits: np.ndarray) -> np.ndarray:

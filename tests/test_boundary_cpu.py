@@ -29,7 +29,7 @@ def declared_functions():
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(?:int|const char \*)\s*\*?\s*(\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(?:int|size_t|const char \*)\s*\*?\s*(\w+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_names():
@@ -112,8 +112,58 @@ def test_gate_up_validation(lib, name):
     assert f(0, 0, 0, 0, 0, 32, 16, 32, None, 0) == w4.W4A16_OK
 
 
+def _lora(lib, x=0x1000, q=0x2000, s=0x3000, a=0x5000, b=0x6000, y=0x4000, M=1, K=32, N=8,
+          g=32, r=8, ws=0x7000, wsb=1 << 20, bf16=False, scale=1.0):
+    f = lib.w4a16_linear_lora_bf16 if bf16 else lib.w4a16_linear_lora
+    return f(x, q, s, a, b, scale, y, M, K, N, g, r, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(r=0), w4.W4A16_ERR_RANK),
+    (dict(r=12), w4.W4A16_ERR_RANK),
+    (dict(r=-8), w4.W4A16_ERR_RANK),
+    (dict(r=1032), w4.W4A16_ERR_RANK),
+    (dict(a=0), w4.W4A16_ERR_NULL),
+    (dict(b=0), w4.W4A16_ERR_NULL),
+    (dict(ws=0), w4.W4A16_ERR_NULL),
+    (dict(a=0x5008), w4.W4A16_ERR_ALIGN),
+    (dict(b=0x6004), w4.W4A16_ERR_ALIGN),
+    (dict(ws=0x7008), w4.W4A16_ERR_ALIGN),
+    (dict(wsb=0), w4.W4A16_ERR_WORKSPACE),
+    (dict(wsb=511), w4.W4A16_ERR_WORKSPACE),
+    (dict(K=40), w4.W4A16_ERR_SHAPE),
+    (dict(N=12), w4.W4A16_ERR_SHAPE),
+    (dict(g=48), w4.W4A16_ERR_GROUP),
+    (dict(x=0), w4.W4A16_ERR_NULL),
+    (dict(K=1 << 20, r=1024), w4.W4A16_ERR_SHAPE),     # A reaches 2^31 bytes
+    (dict(N=1 << 20, r=1024), w4.W4A16_ERR_SHAPE),     # B reaches 2^31 bytes
+])
+def test_lora_invalid_arguments_rejected_before_any_hip_call(lib, kw, status, bf16):
+    assert _lora(lib, bf16=bf16, **kw) == status
+
+
+def test_lora_workspace_size_and_empty_batch(lib):
+    # M=1, K=32, r=8: one 16-row block, one K chunk of 8 fp32 columns
+    assert w4.w4a16_lora_workspace_bytes(1, 32, 8) == 16 * 8 * 4
+    assert _lora(lib, wsb=16 * 8 * 4) != w4.W4A16_ERR_WORKSPACE
+    assert w4.w4a16_lora_workspace_bytes(0, 32, 8) == 0
+    assert w4.w4a16_lora_workspace_bytes(1, 32, 12) == 0
+    assert w4.w4a16_lora_workspace_bytes(1, 40, 8) == 0
+    # at most 16 chunks of K, and never more chunks than 4-step pieces of K
+    for M, K, r in ((1, 5120, 32), (16, 17408, 64), (2048, 5120, 32), (300, 16, 8)):
+        b = w4.w4a16_lora_workspace_bytes(M, K, r)
+        rows = 16 * ((M + 15) // 16)
+        chunks = b // (rows * r * 4)
+        assert b == chunks * rows * r * 4 and 1 <= chunks <= 16
+        assert chunks <= max(1, -(-((K + 31) // 32) // 4))
+    # M == 0 is a no-op whatever the pointers (shapes still checked)
+    assert _lora(lib, x=0, q=0, s=0, a=0, b=0, y=0, ws=0, wsb=0, M=0) == w4.W4A16_OK
+    assert _lora(lib, M=0, r=12) == w4.W4A16_ERR_RANK
+
+
 def test_status_strings(lib):
-    for st in range(0, 9):
+    for st in range(0, 11):
         assert w4.w4a16_status_string(st)
     assert w4.w4a16_status_string(99) == "unknown status"
 
