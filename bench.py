@@ -134,7 +134,7 @@ def rotations_for(weight_bytes: int, minimum: int = 2) -> int:
     return max(minimum, -(-2 * MALL_BYTES // weight_bytes))
 
 
-def bench_case(torch, w4, case, steps, warmup, eager, bf16=False, gate_up=False):
+def bench_case(torch, w4, case, steps, warmup, eager, bf16=False, gate_up=False, lora_rank=0):
     import workloads
     inp = workloads.generate_bf16(case) if bf16 else workloads.generate(case)
     wbytes = case.K * case.N // 2 + 2 * case.G * case.N
@@ -148,6 +148,19 @@ def bench_case(torch, w4, case, steps, warmup, eager, bf16=False, gate_up=False)
 
     def step(i):
         call(x, qs[i % R], ss[i % R], y, case.M, case.K, case.N, case.group_size)
+
+    if lora_rank:
+        # the adapter rotates with the weights: each layer of a model has its own
+        A, B = workloads.lora_adapter(case.K, case.N, lora_rank, case.seed + 500)
+        As = [torch.from_numpy(A).to(x.device) for _ in range(R)]
+        Bs = [torch.from_numpy(B).to(x.device) for _ in range(R)]
+        wsb = w4.w4a16_lora_workspace_bytes(case.M, case.K, lora_rank)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+
+        def step(i):  # noqa: F811
+            w4.w4a16_linear_lora(x, qs[i % R], ss[i % R], As[i % R], Bs[i % R],
+                                 workloads.LORA_SCALE, y, case.M, case.K, case.N,
+                                 case.group_size, lora_rank, ws, wsb)
 
     sec = Timed(torch).run(step, steps, warmup, eager)
     return inp, y, sec, R
@@ -242,6 +255,8 @@ def main():
                     help="skip the streaming-read ceiling measurement")
     ap.add_argument("--no-gate-up", action="store_true",
                     help="skip the merged gate/up (SiLU * mul) decode and prefill lines")
+    ap.add_argument("--no-lora", action="store_true",
+                    help="skip the linear + LoRA adapter lines")
     ap.add_argument("--no-bf16", action="store_true",
                     help="skip the bfloat16-activation variant's decode and prefill lines")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -385,6 +400,38 @@ def main():
                                       "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4)}}
         torch.cuda.empty_cache()
         out["gate_up_silu"] = gu
+
+    if args.only == "all" and not args.no_lora:
+        # the linear with a rank-32 LoRA adapter (the pages' suggested rank):
+        # the linear's kernel, then the adapter's shrink and expand kernels
+        lo, r = {}, 32
+        case = workloads.decode_up()
+        _, _, sec, R = bench_case(torch, w4, case, args.steps, args.warmup, args.eager,
+                                  lora_rank=r)
+        B = algorithmic_bytes(case.M, case.K, case.N, case.G) + 2 * r * (case.K + case.N)
+        gbs = B / sec / 1e9
+        lo["decode"] = {"workload": "decode up-projection GEMV M=1 K=5120 N=17408 g=128 + LoRA r=32",
+                        "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": sec * 1e3,
+                        "linear_alone_ms": out.get("ms_per_step"),
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                     "algorithmic_bytes": B}}
+        torch.cuda.empty_cache()
+        case = workloads.prefill_up()
+        psteps = args.prefill_steps or max(10, args.steps // 4)
+        _, _, sec, R = bench_case(torch, w4, case, psteps, max(1, min(args.warmup, psteps)),
+                                  args.eager, lora_rank=r)
+        flops = 2.0 * case.M * (case.N * case.K + r * (case.K + case.N))
+        tflops = flops / sec / 1e12
+        lo["prefill"] = {"workload": "prefill up-projection GEMM M=2048 K=5120 N=17408 g=128 + LoRA r=32",
+                         "value": round(tflops, 1), "unit": "TFLOP/s", "ms_per_step": sec * 1e3,
+                         "linear_alone_ms": out.get("prefill", {}).get("ms_per_step"),
+                         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4)}}
+        torch.cuda.empty_cache()
+        out["lora"] = lo
 
     out["device"] = dev_name
     out["timing"] = "eager launches" if args.eager else "one HIP graph of K steps"

@@ -59,7 +59,9 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__rest
     const auto ar = make_rsrc(A, (uint32_t)r * (uint32_t)K * 2u);
     const int row = 16 * mb + (lane & 15);
     const int kofs = 8 * (lane >> 4);
+    const int jbn = min(4, (r - 64 * jc + 15) / 16);   // column blocks of t present here
     f4 acc[4] = {};
+#pragma unroll 4
     for (int st = kb + w; st < ke; st += 4) {
         const int k = 32 * st + kofs;             // K % 8 == 0: eight in or eight out
         const bool kin = k < K;
@@ -67,9 +69,11 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__rest
         const u4 xa = load_b128(xr, xo);
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
-            const int j = 64 * jc + 16 * jb + (lane & 15);
-            const uint32_t ao = (j < r && kin) ? (uint32_t)(j * K + k) * 2u : kOOB;
-            acc[jb] = mfma16x16x32_t<BF>(xa, load_b128(ar, ao), acc[jb]);
+            if (jb < jbn) {                       // uniform across the workgroup
+                const int j = 64 * jc + 16 * jb + (lane & 15);
+                const uint32_t ao = (j < r && kin) ? (uint32_t)(j * K + k) * 2u : kOOB;
+                acc[jb] = mfma16x16x32_t<BF>(xa, load_b128(ar, ao), acc[jb]);
+            }
         }
     }
     __shared__ f4 red[4][4][64];
@@ -88,44 +92,90 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__rest
 
 // One workgroup (4 waves) adds the adapter term to a 16-row by 64*NB-column
 // tile of y; wave w owns columns [16*NB*w, 16*NB*(w+1)) of the tile.
+//  1. The tile of y is loaded first (16-byte runs, rows >= M skipped), so its
+//     latency overlaps the rest.
+//  2. The workgroup sums the S partial slabs of its 16 rows of t once, in
+//     chunk order (kSB slabs in flight at a time), in coalesced 16-byte runs
+//     spread over all threads, and
+//     keeps t in LDS in the activation type ([16][r + 8], dynamic LDS).
+//  3. Each wave multiplies t by its rows of B on the matrix cores.
+//  4. The fp32 delta goes through LDS to the layout of the y runs, and each
+//     run is written once: y = round(y + s * delta).
 template <bool BF, int NB>
 __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restrict__ tp,
                                                           const uint16_t *__restrict__ B,
                                                           uint16_t *__restrict__ y, float scale,
                                                           int M, int N, int r, int Mp, int S) {
     constexpr int TN = 64 * NB;
+    constexpr int kRuns = TN / 8;                 // 8-column runs per row of the tile
+    constexpr int kPer = (16 * kRuns + 255) / 256;
+    constexpr int kSB = NB == 1 ? 8 : 4;          // partial slabs loaded per batch
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int nt = blockIdx.x, mb = blockIdx.y;
+
+    u4 yv[kPer];
+    bool yin[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int q = threadIdx.x + 256 * i;
+        const int m = 16 * mb + q / kRuns, n = nt * TN + 8 * (q % kRuns);
+        yin[i] = q < 16 * kRuns && m < M && n < N;   // N % 8 == 0: runs are whole
+        yv[i] = yin[i] ? *reinterpret_cast<const u4 *>(y + (size_t)m * N + n) : u4{0, 0, 0, 0};
+    }
+
+    extern __shared__ u4 tsh[];                   // t of the 16 rows: [16][r + 8] 16-bit
+    const int ld = r + 8;                         // row pitch in elements (16-byte multiple)
+    {
+        const auto tr = make_rsrc(tp, (uint32_t)S * (uint32_t)Mp * (uint32_t)r * 4u);
+        const int runs = 2 * r;                   // 16 rows x r/8 runs of 8 columns
+        for (int q = threadIdx.x; q < runs; q += 256) {
+            const int rr = q / (r / 8), j = 8 * (q % (r / 8));
+            const int m = 16 * mb + rr;
+            float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (m < M) {
+                for (int s0 = 0; s0 < S; s0 += kSB) {
+                    f4 lo[kSB], hi[kSB];
+#pragma unroll
+                    for (int u = 0; u < kSB; ++u) {   // in flight together; past S: zero
+                        const uint32_t o = s0 + u < S
+                                               ? (uint32_t)((((s0 + u) * Mp + m) * r + j) * 4)
+                                               : kOOB;
+                        lo[u] = __builtin_bit_cast(f4, load_b128(tr, o));
+                        hi[u] = __builtin_bit_cast(f4, load_b128(tr, o + 16u));
+                    }
+#pragma unroll
+                    for (int u = 0; u < kSB; ++u)     // chunk order: deterministic
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            tv[i] += lo[u][i];
+                            tv[4 + i] += hi[u][i];
+                        }
+                }
+            }
+            tsh[(rr * ld + j) / 8] = u4{pack2<BF>(tv[0], tv[1]), pack2<BF>(tv[2], tv[3]),
+                                        pack2<BF>(tv[4], tv[5]), pack2<BF>(tv[6], tv[7])};
+        }
+    }
+    __syncthreads();
+
     const int n0 = nt * TN + 16 * NB * w;
     const auto br = make_rsrc(B, (uint32_t)N * (uint32_t)r * 2u);
-    const auto tr = make_rsrc(tp, (uint32_t)S * (uint32_t)Mp * (uint32_t)r * 4u);
-    const int trow = 16 * mb + (lane & 15);       // < Mp always
     const int kofs = 8 * (lane >> 4);
     f4 acc[NB] = {};
     for (int kk = 0; kk < r; kk += 32) {
         const int j = kk + kofs;                  // r % 8 == 0: eight in or eight out
         const bool jin = j < r;
-        float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < S; ++s) {             // fixed order: deterministic
-            const uint32_t o = jin ? (uint32_t)(((s * Mp + trow) * r + j) * 4) : kOOB;
-            const f4 lo = __builtin_bit_cast(f4, load_b128(tr, o));
-            const f4 hi = __builtin_bit_cast(f4, load_b128(tr, o + 16u));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                tv[i] += lo[i];
-                tv[4 + i] += hi[i];
-            }
-        }
-        const u4 ta = {pack2<BF>(tv[0], tv[1]), pack2<BF>(tv[2], tv[3]),
-                       pack2<BF>(tv[4], tv[5]), pack2<BF>(tv[6], tv[7])};
+        u4 bb[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int n = n0 + 16 * nb + (lane & 15);
-            const uint32_t bo = (jin && n < N) ? (uint32_t)(n * r + j) * 2u : kOOB;
-            acc[nb] = mfma16x16x32_t<BF>(ta, load_b128(br, bo), acc[nb]);
+            bb[nb] = load_b128(br, (jin && n < N) ? (uint32_t)(n * r + j) * 2u : kOOB);
         }
+        const u4 ta = jin ? tsh[((lane & 15) * ld + j) / 8] : u4{0, 0, 0, 0};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16x32_t<BF>(ta, bb[nb], acc[nb]);
     }
-    // the tile through LDS, so that y is read and written in 16-byte runs
+    // the delta tile through LDS, from the MFMA layout to 16-byte runs of rows
     __shared__ float tile[16][TN + 4];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -133,19 +183,18 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
         for (int i = 0; i < 4; ++i)
             tile[4 * (lane >> 4) + i][16 * NB * w + 16 * nb + (lane & 15)] = acc[nb][i];
     __syncthreads();
-    constexpr int kRuns = TN / 8;                 // 8-column runs per row
-    for (int q = threadIdx.x; q < 16 * kRuns; q += 256) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        if (!yin[i]) continue;
+        const int q = threadIdx.x + 256 * i;
         const int rr = q / kRuns, c = 8 * (q % kRuns);
         const int m = 16 * mb + rr, n = nt * TN + c;
-        if (m >= M || n >= N) continue;           // N % 8 == 0: runs are whole
-        u4 *p = reinterpret_cast<u4 *>(y + (size_t)m * N + n);
-        const u4 v = *p;
         u4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o[i] = pack2<BF>(act_lo<BF>(v[i]) + scale * tile[rr][c + 2 * i],
-                             act_hi<BF>(v[i]) + scale * tile[rr][c + 2 * i + 1]);
-        *p = o;
+        for (int e = 0; e < 4; ++e)
+            o[e] = pack2<BF>(act_lo<BF>(yv[i][e]) + scale * tile[rr][c + 2 * e],
+                             act_hi<BF>(yv[i][e]) + scale * tile[rr][c + 2 * e + 1]);
+        *reinterpret_cast<u4 *>(y + (size_t)m * N + n) = o;
     }
 }
 
@@ -196,19 +245,20 @@ hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace) {
     const bool narrow = a.M <= 16;
     const int TN = narrow ? 64 : 256;
     const dim3 eg((N + TN - 1) / TN, p.mblocks);
+    const size_t tlds = (size_t)16 * (size_t)(r + 8) * 2;   // t of 16 rows, 16-bit
     if (narrow) {
         if (a.bf16)
-            lora_expand_kernel<true, 1><<<eg, 256, 0, stream>>>(tp, B, y, a.scale, M, N, r, p.Mp,
+            lora_expand_kernel<true, 1><<<eg, 256, tlds, stream>>>(tp, B, y, a.scale, M, N, r, p.Mp,
                                                                 p.splits);
         else
-            lora_expand_kernel<false, 1><<<eg, 256, 0, stream>>>(tp, B, y, a.scale, M, N, r,
+            lora_expand_kernel<false, 1><<<eg, 256, tlds, stream>>>(tp, B, y, a.scale, M, N, r,
                                                                  p.Mp, p.splits);
     } else {
         if (a.bf16)
-            lora_expand_kernel<true, 4><<<eg, 256, 0, stream>>>(tp, B, y, a.scale, M, N, r, p.Mp,
+            lora_expand_kernel<true, 4><<<eg, 256, tlds, stream>>>(tp, B, y, a.scale, M, N, r, p.Mp,
                                                                 p.splits);
         else
-            lora_expand_kernel<false, 4><<<eg, 256, 0, stream>>>(tp, B, y, a.scale, M, N, r,
+            lora_expand_kernel<false, 4><<<eg, 256, tlds, stream>>>(tp, B, y, a.scale, M, N, r,
                                                                  p.Mp, p.splits);
     }
     return hipGetLastError();
