@@ -42,10 +42,16 @@ def algorithmic_bytes(M, K, N, G):
     return K * N // 2 + 2 * G * N + 2 * M * K + 2 * M * N
 
 
-def kernel_sources_sha() -> str:
+# The sources each measured kernel is built and launched from: its own file
+# (kernels and launch logic) and the shared device header.
+KERNEL_SOURCES = {"decode": ("decode_gfx950.hip", "w4a16_device.hpp"),
+                  "prefill": ("prefill_gfx950.hip", "w4a16_device.hpp")}
+
+
+def kernel_sources_sha(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int4_weight_only_w4a16_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -60,7 +66,7 @@ def load_traffic(kernel: str):
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("sources_sha") != kernel_sources_sha():
+    if not rec or rec.get("sources_sha") != kernel_sources_sha(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
