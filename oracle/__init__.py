@@ -86,6 +86,8 @@ class Oracle:
         lib.oracle_lora_expand.argtypes = [p, p, i32, i32, f64, i64, i64, i64, p]
         lib.oracle_lora_expand_at.argtypes = [p, p, i32, i32, f64, i64, i64, i64, p, p, i64, p]
         lib.oracle_linear_lora.argtypes = [p, i32, p, p, p, p, f64, i64, i64, i64, i64, i64, p]
+        lib.oracle_linear_zp.argtypes = [p, i32, i32, p, p, p, i64, i64, i64, i64, p]
+        lib.oracle_linear_zp.restype = ctypes.c_int
         for f in (lib.oracle_unpack, lib.oracle_pack, lib.oracle_dequant,
                   lib.oracle_linear, lib.oracle_linear_at, lib.oracle_linear_ex,
                   lib.oracle_linear_at_ex, lib.oracle_gate_up_silu, lib.oracle_lora_shrink,
@@ -251,6 +253,25 @@ class Oracle:
                "linear_lora")
         return y
 
+    def linear_zp(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+                  qzeros: np.ndarray, group_size: int, act: str = "f16",
+                  absval: bool = False) -> np.ndarray:
+        """y [M, N] float64 = x . W with W[k,n] = (q - z[k/g, n]) * s[k/g, n]; qzeros
+        int32 [G, N/8], nibble j of word c the zero point of column 8c+j."""
+        xb = _act_bits(x, act)
+        qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+        scales = np.ascontiguousarray(scales, dtype=np.float16)
+        qzeros = np.ascontiguousarray(qzeros, dtype=np.int32)
+        M, K = xb.shape
+        N = qweight.shape[1]
+        if qweight.shape[0] * 8 != K or qzeros.shape != (scales.shape[0], N // 8):
+            raise ValueError("qweight must be [K/8, N] and qzeros [G, N/8]")
+        y = np.empty((M, N), dtype=np.float64)
+        _check(self.lib.oracle_linear_zp(_ptr(xb), _ACTS[act], int(absval), _ptr(qweight),
+                                         _ptr(scales.view(np.uint16)), _ptr(qzeros), M, K, N,
+                                         group_size, _ptr(y)), "linear_zp")
+        return y
+
 
 _default: Optional[Oracle] = None
 
@@ -307,3 +328,7 @@ def lora_expand_at(t, B, scale, ms, ns, act="f16", absval=False):
 
 def linear_lora(x, qweight, scales, group_size, A, B, scale, act="f16"):
     return default().linear_lora(x, qweight, scales, group_size, A, B, scale, act)
+
+
+def linear_zp(x, qweight, scales, qzeros, group_size, act="f16", absval=False):
+    return default().linear_zp(x, qweight, scales, qzeros, group_size, act, absval)

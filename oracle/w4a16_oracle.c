@@ -68,6 +68,18 @@
  * weight [r, K], lora_B weight [N, r]) with s given as a number (alpha / r
  * for plain LoRA).  With absval = 1 the functions return the magnitudes
  * sum |x| |A| and |s| sum |t| |B| instead.
+ * Asymmetric weights with stored zero points (oracle_linear_zp): the same
+ * definition with the zero point of (group, column) read from qzeros instead
+ * of the constant 8:
+ *   z[g,n]  = (uint32(qzeros[g][n/8]) >> (4*(n mod 8))) & 0xF
+ *   w[k,n]  = float(q[k,n] - z[gidx(k),n]) * float(scales[gidx(k)][n])   (exact in fp32)
+ * GPTQModel quantises with sym=False and stores per-group zero points, which
+ * the GPTQ-Pro contract leaves out ("GPTQ-Pro" README, "Runtime contract";
+ * "GPT-QModel" README), and its checkpoint formats v1 and v2 store them
+ * differently without saying how.  This file takes qzeros as int32 [G, N/8]
+ * packed along N, nibble j of word c = column 8c+j, low bits first, each
+ * nibble the zero point itself (v1's stored z - 1 becomes z by adding one
+ * before the call).  With every zero point 8 it is the symmetric definition.
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math).  OpenMP only
  * splits rows m and column blocks of n, never the sum over k.
  */
@@ -384,4 +396,42 @@ int oracle_linear_lora(const uint16_t *x, int act, const int32_t *qweight,
     free(t);
     free(d);
     return rc;
+}
+
+/* ---- asymmetric weights: stored zero points ---- */
+
+/* Zero point of (group gi, column n): nibble (n mod 8) of qzeros[gi][n/8]. */
+static inline unsigned zero_at(const int32_t *qzeros, int64_t N, int64_t gi, int64_t n) {
+    uint32_t word;
+    memcpy(&word, &qzeros[gi * (N / 8) + n / 8], sizeof word);
+    return (word >> (4 * (unsigned)(n % 8))) & 0xFu;
+}
+
+/* y[m*N + n] <- sum_k x[m,k] * (q[k,n] - z[gidx(k),n]) * s[gidx(k),n] in fp64,
+ * k ascending, x of type act; absval: sum_k |x| |w| instead. */
+int oracle_linear_zp(const uint16_t *x, int act, int absval, const int32_t *qweight,
+                     const uint16_t *scales, const int32_t *qzeros, int64_t M, int64_t K,
+                     int64_t N, int64_t g, double *y) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || (act != 0 && act != 1)) return OR_ERR_ARG;
+    if (M == 0) return OR_OK;
+    if (!x || !qweight || !scales || !qzeros || !y) return OR_ERR_ARG;
+    float *W = (float *)malloc((size_t)K * (size_t)N * sizeof(float));
+    if (!W) return OR_ERR_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            const int64_t gi = group_of(k, g);
+            const int q = (int)code_at(qweight, N, k, n), z = (int)zero_at(qzeros, N, gi, n);
+            W[k * N + n] = (float)(q - z) * (float)half_to_double(scales[gi * N + n]);
+        }
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += term(act_to_double(x[m * K + k], act), (double)W[k * N + n], absval);
+            y[m * N + n] = acc;
+        }
+    free(W);
+    return OR_OK;
 }

@@ -22,6 +22,10 @@ when it disagrees with:
   - for the LoRA adapter, the merged dense weight W + s A^T B^T through
     numpy's matmul, one-hot closed forms (A picking a channel of x, B = I),
     pure-Python loops on tiny inputs, and exact scaling relations.
+  - for stored zero points, the symmetric definition exactly when every zero
+    point is 8, numpy's matmul on W built from codes and zero points, a
+    hand-derived word 0x76543210 (zero point n at column n), and y == 0
+    exactly when every code equals its zero point.
 ``tests/test_oracle_mutants.py`` plants plausible mistakes in copies of the
 oracle source and checks that every one of them trips at least one pin.
 """
@@ -517,6 +521,76 @@ def pin_lora_magnitudes_and_samples(o):
         assert np.array_equal(o.lora_expand_at(t, B, s, ms, ns, act=act), d[ms, ns])
         assert np.array_equal(o.lora_expand_at(t, B, s, ms, ns, act=act, absval=True),
                               da[ms, ns])
+
+
+# --- stored zero points: qzeros int32 [G, N/8], packed along N ------------------
+
+def _pack_zeros(o, z):
+    """uint8 zero points [G, N] -> int32 [G, N/8]: the K packing applied to z^T."""
+    return np.ascontiguousarray(o.pack(np.ascontiguousarray(z.T)).T)
+
+
+def pin_zp_eight_is_symmetric(o):
+    """Every zero point 8: bit for bit the symmetric linear, both activation types."""
+    rng = np.random.default_rng(41)
+    for M, K, N, g in ((2, 64, 16, 16), (3, 256, 24, -1), (1, 96, 40, 32)):
+        G = 1 if g == -1 else -(-K // g)
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        scales = rng.uniform(1e-2, 8e-2, size=(G, N)).astype(np.float16)
+        q = o.pack(codes)
+        qz = _pack_zeros(o, np.full((G, N), 8, dtype=np.uint8))
+        x = rng.standard_normal((M, K)).astype(np.float16)
+        assert np.array_equal(o.linear_zp(x, q, scales, qz, g), o.linear(x, q, scales, g))
+        xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(o.linear_zp(xb, q, scales, qz, g, act="bf16"),
+                              o.linear(xb, q, scales, g, act="bf16"))
+
+
+def pin_zp_against_numpy(o):
+    """W[k,n] = (q - z[k/g, n]) s[k/g, n] built in numpy from the codes and zero
+    points (never from packed words), products by numpy's matmul in fp64; the
+    magnitude form against |x| |W|."""
+    rng = np.random.default_rng(42)
+    for M, K, N, g in ((1, 16, 8, 16), (4, 128, 40, 32), (3, 96, 24, 64), (2, 64, 16, -1),
+                       (5, 80, 8, 32)):
+        G = 1 if g == -1 else -(-K // g)
+        grp = np.zeros(K, dtype=np.int64) if g == -1 else np.arange(K) // g
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        z = rng.integers(0, 16, size=(G, N), dtype=np.uint8)
+        scales = rng.uniform(1e-2, 8e-2, size=(G, N)).astype(np.float16)
+        W = (codes.astype(np.float64) - z.astype(np.float64)[grp]) * scales.astype(np.float64)[grp]
+        x = rng.standard_normal((M, K)).astype(np.float16)
+        xv = x.astype(np.float64)
+        y = o.linear_zp(x, o.pack(codes), scales, _pack_zeros(o, z), g)
+        ref = xv @ W
+        assert np.abs(y - ref).max() <= 1e-12 * max(1.0, float(np.abs(ref).max())), (M, K, N, g)
+        ya = o.linear_zp(x, o.pack(codes), scales, _pack_zeros(o, z), g, absval=True)
+        refa = np.abs(xv) @ np.abs(W)
+        assert np.abs(ya - refa).max() <= 1e-12 * max(1.0, float(refa.max()))
+
+
+def pin_zp_worked_word_and_zero_output(o):
+    """Zero point n at column n packs to the word 0x76543210; with x = e_0 and
+    code 0 in row 0, y[n] = (0 - n) s[n] exactly.  Codes equal to their zero
+    points give y == 0 exactly."""
+    N, K = 8, 16
+    z = np.arange(N, dtype=np.uint8)[None, :]
+    qz = _pack_zeros(o, z)
+    assert qz.shape == (1, 1) and int(qz.view(np.uint32)[0, 0]) == 0x76543210
+    s = np.array([[0.5, 0.25, 1.0, 2.0, 0.125, 0.75, 1.5, 3.0]], dtype=np.float16)
+    codes = np.full((K, N), 5, dtype=np.uint8)
+    codes[0, :] = 0
+    x = np.zeros((1, K), dtype=np.float16)
+    x[0, 0] = 1.0
+    y = o.linear_zp(x, o.pack(codes), s, qz, -1)
+    assert np.array_equal(y[0], -np.arange(N) * s[0].astype(np.float64))
+    rng = np.random.default_rng(43)
+    K, N, g = 64, 16, 16
+    zz = rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)
+    codes = np.repeat(zz, g, axis=0)
+    xs = rng.standard_normal((3, K)).astype(np.float16)
+    sc = rng.uniform(1e-2, 8e-2, size=(K // g, N)).astype(np.float16)
+    assert np.all(o.linear_zp(xs, o.pack(codes), sc, _pack_zeros(o, zz), g) == 0.0)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -38,6 +38,11 @@ MUTANTS = {
     "lora_scale_dropped": ("return (absval ? fabs(scale) : scale) * acc;", "return acc;"),
     "lora_delta_subtracted": ("out[i] += d[i];", "out[i] -= d[i];"),
     "lora_a_read_as_half": ("act_to_double(A[j * K + k], act)", "act_to_double(A[j * K + k], 0)"),
+    "zp_nibble_order_reversed": ("(4 * (unsigned)(n % 8))) & 0xFu;", "(4 * (unsigned)(7 - n % 8))) & 0xFu;"),
+    "zp_v1_offset": ("return (word >> (4 * (unsigned)(n % 8))) & 0xFu;",
+                     "return ((word >> (4 * (unsigned)(n % 8))) & 0xFu) + 1u;"),
+    "zp_added": ("(float)(q - z)", "(float)(q + z - 16)"),
+    "zp_row_of_k": ("zero_at(qzeros, N, gi, n)", "zero_at(qzeros, N, k / 8 % (gi + 1), n)"),
     "lora_last_rank_dropped": ("for (int64_t j = 0; j < r; ++j)\n        acc +=",
                                "for (int64_t j = 0; j + 1 < r; ++j)\n        acc +="),
 }

@@ -193,6 +193,12 @@ def lora_adapter(K: int, N: int, rank: int, seed: int, act: str = "f16"):
     return A.astype(np.float16), B.astype(np.float16)
 
 
+def zero_points(G: int, N: int, seed: int) -> np.ndarray:
+    """Seeded zero points for asymmetric weights: uint8 [G, N], uniform over
+    0..15 (every code value; 8 is the symmetric one), from their own generator."""
+    return np.random.default_rng(seed).integers(0, 16, size=(G, N), dtype=np.uint8)
+
+
 def sweep() -> List[Case]:
     """Group-size and shape sweep: 6 g x 3 (K,N) x 4 M = 72 cases, 5% zero cells, seed 4."""
     out = []
