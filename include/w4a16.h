@@ -76,7 +76,8 @@ typedef enum {
     W4A16_ERR_LAUNCH = 7,  /* the kernel launch reported an error */
     W4A16_ERR_KERNEL = 8,  /* w4a16_linear_ex: the requested kernel cannot take this M */
     W4A16_ERR_RANK = 9,    /* LoRA rank not a multiple of 8 in [8, W4A16_LORA_MAX_RANK] */
-    W4A16_ERR_WORKSPACE = 10  /* LoRA workspace smaller than w4a16_lora_workspace_bytes */
+    W4A16_ERR_WORKSPACE = 10  /* workspace smaller than w4a16_lora_workspace_bytes or
+                                 w4a16_zp_workspace_bytes gives */
 } w4a16_status;
 
 /* Largest M the small-batch (decode) kernel takes; larger M runs the MFMA
@@ -205,6 +206,43 @@ int w4a16_linear_lora_bf16(const void *x, const int32_t *qweight, const void *sc
  * sums of x . A^T, at most 16 chunks of [M rounded up to 16, rank].  0 for
  * M <= 0 or arguments the linear would reject. */
 size_t w4a16_lora_workspace_bytes(int64_t M, int64_t K, int64_t rank);
+
+/* Asymmetric weights with stored zero points: w[k,n] = (q[k,n] - z[k/g, n]) *
+ * scales[k/g][n] in place of the symmetric (q - 8) * s.  GPTQModel quantises
+ * with sym=False and stores per-group zero points, which the GPTQ-Pro contract
+ * leaves out ("GPTQ-Pro" README, "Runtime contract"); the pages say only that
+ * the v1 and v2 checkpoint formats store them differently.
+ *   qzeros : device int32 [G, N/8], 16-byte aligned: nibble j (bits 4j..4j+3)
+ *     of word [g][c] is the zero point of column 8c + j, read as unsigned and
+ *     used as stored (a v1 checkpoint's z - 1 becomes z by adding one before
+ *     the call).  It is pack_gptq_v2 applied to the transposed [N, G] zero
+ *     points, transposed back.
+ *   workspace : device buffer of at least w4a16_zp_workspace_bytes(M, K,
+ *     group_size) bytes, 16-byte aligned, no initial contents, owned by the
+ *     caller; calls that overlap in time must not share one.
+ *   ceil(G / 8) * 8 <= 1536 (else W4A16_ERR_SHAPE); everything else as for
+ *   w4a16_linear (the _bf16 form: bfloat16 x and y, as w4a16_linear_bf16).
+ * Steps on the stream: since (q - z) s = (q - 8) s + (8 - z) s, the symmetric
+ * linear writes y; a kernel sums x over each group in fp32 (X[m, g]); an
+ * expand kernel forms C[g, n] = (8 - z) s exactly in fp32, rounds X and C to
+ * the activation type, takes X . C in fp32 on the matrix cores and writes
+ * y = round(y + X . C).  Where every zero point is 8, C is 0 and y is the
+ * symmetric result bit for bit.
+ * Hence, per element and beyond the symmetric linear's own bound (u = 2^-11
+ * for fp16, 2^-8 for bfloat16): u |y_sym| + u |y| + (2u + K 2^-24) P, to
+ * first order, with P = sum_k |x[m,k]| |8 - z| s (the magnitude of the
+ * correction).  Deterministic, as w4a16_linear. */
+int w4a16_linear_zp(const void *x, const int32_t *qweight, const void *scales,
+                    const int32_t *qzeros, void *y, int64_t M, int64_t K, int64_t N,
+                    int64_t group_size, void *workspace, size_t workspace_bytes, void *stream);
+int w4a16_linear_zp_bf16(const void *x, const int32_t *qweight, const void *scales,
+                         const int32_t *qzeros, void *y, int64_t M, int64_t K, int64_t N,
+                         int64_t group_size, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Bytes of workspace w4a16_linear_zp needs: fp32 group sums of x, [M rounded
+ * up to 16, G rounded up to 8].  0 for M <= 0 or arguments it rejects. */
+size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t group_size);
 
 /* Host-side packing into the GPTQ_V2 layout (native int32 qweight, "GPTQ-Pro"
  * README, "Runtime contract"):

@@ -8,10 +8,11 @@ not a gfx950, calls raise.
 Names match the C ABI in ``include/w4a16.h``:
   w4a16_linear, w4a16_linear_ex, w4a16_linear_bf16, w4a16_linear_bf16_ex,
   w4a16_gate_up_silu(_ex, _bf16, _bf16_ex), w4a16_linear_lora(_bf16),
-  w4a16_lora_workspace_bytes, pack_gptq_v2, unpack_gptq_v2,
+  w4a16_lora_workspace_bytes, w4a16_linear_zp(_bf16), w4a16_zp_workspace_bytes,
+  pack_gptq_v2, unpack_gptq_v2,
   w4a16_status_string, and the measurement aid w4a16_read_probe
-plus ``linear``, ``gate_up_silu`` and ``linear_lora`` (allocate y, and the
-LoRA workspace, with torch, then call the entry point of x's dtype).
+plus ``linear``, ``gate_up_silu``, ``linear_lora`` and ``linear_zp`` (allocate
+y, and a workspace, with torch, then call the entry point of x's dtype).
 """
 
 from __future__ import annotations
@@ -46,7 +47,8 @@ W4A16_KERNEL_PREFILL = 2
 EXPORTS = ("w4a16_linear", "w4a16_linear_ex", "w4a16_linear_bf16", "w4a16_linear_bf16_ex",
            "w4a16_gate_up_silu", "w4a16_gate_up_silu_ex", "w4a16_gate_up_silu_bf16",
            "w4a16_gate_up_silu_bf16_ex", "w4a16_linear_lora", "w4a16_linear_lora_bf16",
-           "w4a16_lora_workspace_bytes", "pack_gptq_v2", "unpack_gptq_v2", "w4a16_read_probe",
+           "w4a16_lora_workspace_bytes", "w4a16_linear_zp", "w4a16_linear_zp_bf16",
+           "w4a16_zp_workspace_bytes", "pack_gptq_v2", "unpack_gptq_v2", "w4a16_read_probe",
            "w4a16_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -89,6 +91,11 @@ def load_library() -> ctypes.CDLL:
         getattr(lib, name).restype = i32
     lib.w4a16_lora_workspace_bytes.argtypes = [i64, i64, i64]
     lib.w4a16_lora_workspace_bytes.restype = sz
+    for name in ("w4a16_linear_zp", "w4a16_linear_zp_bf16"):
+        getattr(lib, name).argtypes = [p, p, p, p, p, i64, i64, i64, i64, p, sz, p]
+        getattr(lib, name).restype = i32
+    lib.w4a16_zp_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.w4a16_zp_workspace_bytes.restype = sz
     lib.pack_gptq_v2.argtypes = [p, p, i64, i64]
     lib.pack_gptq_v2.restype = i32
     lib.unpack_gptq_v2.argtypes = [p, p, i64, i64]
@@ -265,6 +272,65 @@ def linear_lora(x, qweight, scales, group_size: int, lora_a, lora_b, lora_scale:
     w4a16_linear_lora(x, qweight, scales, lora_a, lora_b, lora_scale, out, M, K, N, group_size,
                       rank, workspace, workspace.numel() * workspace.element_size(), stream,
                       x.dtype == torch.bfloat16)
+    return out
+
+
+def w4a16_zp_workspace_bytes(M: int, K: int, group_size: int) -> int:
+    """Workspace bytes w4a16_linear_zp needs (0 for arguments it rejects)."""
+    return int(load_library().w4a16_zp_workspace_bytes(int(M), int(K), int(group_size)))
+
+
+def w4a16_linear_zp(x, qweight, scales, qzeros, y, M: int, K: int, N: int, group_size: int,
+                    workspace, workspace_bytes: int, stream=None, bf16: bool = False) -> None:
+    """y = x . W with W[k,n] = (q - z[k/g, n]) s[k/g, n], qzeros int32 [G, N/8] (the C
+    w4a16_linear_zp, or its _bf16 form when bf16)."""
+    lib = load_library()
+    f = lib.w4a16_linear_zp_bf16 if bf16 else lib.w4a16_linear_zp
+    st = f(_addr(x), _addr(qweight), _addr(scales), _addr(qzeros), _addr(y), int(M), int(K),
+           int(N), int(group_size), _addr(workspace), int(workspace_bytes), _stream_handle(stream))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_linear_zp")
+
+
+def w4a16_linear_zp_bf16(x, qweight, scales, qzeros, y, M: int, K: int, N: int,
+                         group_size: int, workspace, workspace_bytes: int, stream=None) -> None:
+    """Same as the C ``w4a16_linear_zp_bf16``."""
+    w4a16_linear_zp(x, qweight, scales, qzeros, y, M, K, N, group_size, workspace,
+                    workspace_bytes, stream, bf16=True)
+
+
+def pack_zeros(zeros: np.ndarray) -> np.ndarray:
+    """uint8 zero points [G, N] (values 0..15) -> int32 qzeros [G, N/8] packed along N
+    (pack_gptq_v2 of the transpose, transposed back)."""
+    z = np.ascontiguousarray(np.asarray(zeros, dtype=np.uint8).T)
+    return np.ascontiguousarray(pack_gptq_v2(z).T)
+
+
+def linear_zp(x, qweight, scales, qzeros, group_size: int, out=None, workspace=None,
+              stream=None):
+    """Allocate y (x's dtype, [M, N]) and, unless given, the workspace with torch, then
+    run the linear with stored zero points (qzeros int32 [G, N/8])."""
+    import torch
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be float16 or bfloat16")
+    for name, t, dt in (("x", x, x.dtype), ("qweight", qweight, torch.int32),
+                        ("scales", scales, torch.float16), ("qzeros", qzeros, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    M, K = x.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K or tuple(qzeros.shape) != (scales.shape[0], N // 8):
+        raise ValueError("qweight must be [K/8, N] and qzeros [G, N/8]")
+    need = w4a16_zp_workspace_bytes(M, K, group_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    elif out.dtype != x.dtype:
+        raise ValueError("out must have x's dtype")
+    w4a16_linear_zp(x, qweight, scales, qzeros, out, M, K, N, group_size, workspace,
+                    workspace.numel() * workspace.element_size(), stream,
+                    x.dtype == torch.bfloat16)
     return out
 
 

@@ -20,6 +20,12 @@
 // Both operands of every MFMA are contiguous along the contracted index (x
 // and A rows along K, t rows and B rows along r), so each lane loads its
 // eight values with one 16-byte load.  The result is deterministic.
+//
+// Stored zero points (asymmetric weights, w = (q - z) s) use the same expand:
+// (q - z) s = (q - 8) s + (8 - z) s, so y = y_sym + sum_g X[m,g] C[g,n] with
+// X the sums of x over each group (zp_group_sums_kernel) and C = (8 - z) s,
+// formed in the expand's B fragments straight from qzeros and scales: a
+// rank-G correction of the symmetric linear, exactly zero where z = 8.
 
 #include "w4a16_device.hpp"
 #include "w4a16_launch.h"
@@ -90,6 +96,33 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__rest
     }
 }
 
+// X[m, gi] = sum of x[m, k] over group gi (fp32; K for g = -1), one wave per
+// (group, row): lane l sums the 16-byte runs l, l + 64, ... of the group in
+// order, then a fixed butterfly adds the lanes.  Columns G .. Gp-1 are zero.
+// Written as one slab [M rounded up to 16][Gp] of the expand's layout.
+template <bool BF>
+__global__ void __launch_bounds__(64) zp_group_sums_kernel(const uint16_t *__restrict__ x,
+                                                           float *__restrict__ t, int M, int K,
+                                                           int gsz, int G, int Gp) {
+    const int gi = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
+    float acc = 0.f;
+    if (gi < G) {
+        const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+        const int k0 = gi * gsz, k1 = min(K, k0 + gsz);   // both multiples of 16
+        for (int k = k0 + 8 * lane; k < k1; k += 512) {
+            const u4 v = load_b128(xr, (uint32_t)(m * K + k) * 2u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc += act_lo<BF>(v[e]);
+                acc += act_hi<BF>(v[e]);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    }
+    if (lane == 0) t[(size_t)m * Gp + gi] = acc;
+}
+
 // One workgroup (4 waves) adds the adapter term to a 16-row by 64*NB-column
 // tile of y; wave w owns columns [16*NB*w, 16*NB*(w+1)) of the tile.
 //  1. The tile of y is loaded first (16-byte runs, rows >= M skipped), so its
@@ -101,11 +134,16 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__rest
 //  3. Each wave multiplies t by its rows of B on the matrix cores.
 //  4. The fp32 delta goes through LDS to the layout of the y runs, and each
 //     run is written once: y = round(y + s * delta).
-template <bool BF, int NB>
+// With ZP the "B" rows are C[g, n] = (8 - z[g,n]) s[g,n] for g < G (zero for
+// G <= g < r), formed exactly in fp32 from qzeros and scales and rounded to
+// the activation type like B.
+template <bool BF, int NB, bool ZP>
 __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restrict__ tp,
                                                           const uint16_t *__restrict__ B,
                                                           uint16_t *__restrict__ y, float scale,
-                                                          int M, int N, int r, int Mp, int S) {
+                                                          int M, int N, int r, int Mp, int S,
+                                                          const int32_t *__restrict__ qzeros,
+                                                          int G) {
     constexpr int TN = 64 * NB;
     constexpr int kRuns = TN / 8;                 // 8-column runs per row of the tile
     constexpr int kPer = (16 * kRuns + 255) / 256;
@@ -159,7 +197,7 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
     __syncthreads();
 
     const int n0 = nt * TN + 16 * NB * w;
-    const auto br = make_rsrc(B, (uint32_t)N * (uint32_t)r * 2u);
+    const auto br = make_rsrc(B, ZP ? 0u : (uint32_t)N * (uint32_t)r * 2u);
     const int kofs = 8 * (lane >> 4);
     f4 acc[NB] = {};
     for (int kk = 0; kk < r; kk += 32) {
@@ -169,7 +207,23 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int n = n0 + 16 * nb + (lane & 15);
-            bb[nb] = load_b128(br, (jin && n < N) ? (uint32_t)(n * r + j) * 2u : kOOB);
+            if constexpr (ZP) {                   // B is the scale grid [G, N] here
+                float c[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int g = j + e;
+                    c[e] = 0.f;
+                    if (jin && n < N && g < G) {
+                        const uint32_t zw = (uint32_t)qzeros[(size_t)g * (N / 8) + n / 8];
+                        const int z = (int)((zw >> (4 * (n % 8))) & 0xFu);
+                        c[e] = (float)(8 - z) * (float)half_lo((uint32_t)B[(size_t)g * N + n]);
+                    }
+                }
+                bb[nb] = u4{pack2<BF>(c[0], c[1]), pack2<BF>(c[2], c[3]), pack2<BF>(c[4], c[5]),
+                            pack2<BF>(c[6], c[7])};
+            } else {
+                bb[nb] = load_b128(br, (jin && n < N) ? (uint32_t)(n * r + j) * 2u : kOOB);
+            }
         }
         const u4 ta = jin ? tsh[((lane & 15) * ld + j) / 8] : u4{0, 0, 0, 0};
 #pragma unroll
@@ -226,6 +280,24 @@ size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r) {
     return (size_t)p.splits * (size_t)p.Mp * (size_t)r * sizeof(float);
 }
 
+template <bool BF, bool ZP>
+static hipError_t launch_expand(const float *tp, const uint16_t *B, uint16_t *y, float scale,
+                                int M, int N, int r, int Mp, int S, const int32_t *qzeros, int G,
+                                int mblocks, hipStream_t stream) {
+    // decode-sized batches: narrow tiles for more workgroups on a short y
+    const bool narrow = M <= 16;
+    const int TN = narrow ? 64 : 256;
+    const dim3 eg((N + TN - 1) / TN, mblocks);
+    const size_t tlds = (size_t)16 * (size_t)(r + 8) * 2;   // t of 16 rows, 16-bit
+    if (narrow)
+        lora_expand_kernel<BF, 1, ZP><<<eg, 256, tlds, stream>>>(tp, B, y, scale, M, N, r, Mp, S,
+                                                                 qzeros, G);
+    else
+        lora_expand_kernel<BF, 4, ZP><<<eg, 256, tlds, stream>>>(tp, B, y, scale, M, N, r, Mp, S,
+                                                                 qzeros, G);
+    return hipGetLastError();
+}
+
 hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace) {
     const LoraPlan p = lora_plan(a.M, a.K, a.r);
     const int M = (int)a.M, K = (int)a.K, N = (int)a.N, r = (int)a.r;
@@ -241,27 +313,42 @@ hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace) {
         lora_shrink_kernel<false><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // decode-sized batches: narrow tiles for more workgroups on a short y
-    const bool narrow = a.M <= 16;
-    const int TN = narrow ? 64 : 256;
-    const dim3 eg((N + TN - 1) / TN, p.mblocks);
-    const size_t tlds = (size_t)16 * (size_t)(r + 8) * 2;   // t of 16 rows, 16-bit
-    if (narrow) {
-        if (a.bf16)
-            lora_expand_kernel<true, 1><<<eg, 256, tlds, stream>>>(tp, B, y, a.scale, M, N, r, p.Mp,
-                                                                p.splits);
-        else
-            lora_expand_kernel<false, 1><<<eg, 256, tlds, stream>>>(tp, B, y, a.scale, M, N, r,
-                                                                 p.Mp, p.splits);
-    } else {
-        if (a.bf16)
-            lora_expand_kernel<true, 4><<<eg, 256, tlds, stream>>>(tp, B, y, a.scale, M, N, r, p.Mp,
-                                                                p.splits);
-        else
-            lora_expand_kernel<false, 4><<<eg, 256, tlds, stream>>>(tp, B, y, a.scale, M, N, r,
-                                                                 p.Mp, p.splits);
-    }
-    return hipGetLastError();
+    return a.bf16 ? launch_expand<true, false>(tp, B, y, a.scale, M, N, r, p.Mp, p.splits,
+                                               nullptr, 0, p.mblocks, stream)
+                  : launch_expand<false, false>(tp, B, y, a.scale, M, N, r, p.Mp, p.splits,
+                                                nullptr, 0, p.mblocks, stream);
+}
+
+int zp_groups(int64_t K, int64_t group_size) {
+    return group_size == -1 ? 1 : (int)((K + group_size - 1) / group_size);
+}
+
+size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t group_size) {
+    if (M <= 0) return 0;
+    const int64_t Gp = (zp_groups(K, group_size) + 7) / 8 * 8;
+    return (size_t)((M + 15) / 16 * 16) * (size_t)Gp * sizeof(float);
+}
+
+hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace) {
+    const int M = (int)a.M, K = (int)a.K, N = (int)a.N;
+    const int G = zp_groups(a.K, a.group_size), Gp = (G + 7) / 8 * 8;
+    const int gsz = a.group_size == -1 ? K : (int)a.group_size;
+    const int mblocks = (M + 15) / 16;
+    const auto *x = static_cast<const uint16_t *>(a.x);
+    const auto *sc = static_cast<const uint16_t *>(a.scales);
+    auto *y = static_cast<uint16_t *>(a.y);
+    auto *t = static_cast<float *>(workspace);
+    const dim3 gg(Gp, M);
+    if (a.bf16)
+        zp_group_sums_kernel<true><<<gg, 64, 0, stream>>>(x, t, M, K, gsz, G, Gp);
+    else
+        zp_group_sums_kernel<false><<<gg, 64, 0, stream>>>(x, t, M, K, gsz, G, Gp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return a.bf16 ? launch_expand<true, true>(t, sc, y, 1.0f, M, N, Gp, 16 * mblocks, 1,
+                                              a.qzeros, G, mblocks, stream)
+                  : launch_expand<false, true>(t, sc, y, 1.0f, M, N, Gp, 16 * mblocks, 1,
+                                               a.qzeros, G, mblocks, stream);
 }
 
 }  // namespace w4a16

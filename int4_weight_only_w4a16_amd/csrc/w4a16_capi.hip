@@ -251,6 +251,51 @@ extern "C" int w4a16_linear_lora_bf16(const void *x, const int32_t *qweight, con
                      workspace, workspace_bytes, stream, true);
 }
 
+// The symmetric linear followed by the zero-point correction on the same stream.
+static int zp_call(const void *x, const int32_t *qweight, const void *scales,
+                   const int32_t *qzeros, void *y, int64_t M, int64_t K, int64_t N,
+                   int64_t group_size, void *workspace, size_t workspace_bytes, void *stream,
+                   bool bf16) {
+    int st = validate(x, qweight, scales, y, M, K, N, group_size);
+    if (st != W4A16_OK) return st;
+    if ((w4a16::zp_groups(K, group_size) + 7) / 8 * 8 > w4a16::kZpMaxGroups) return W4A16_ERR_SHAPE;
+    const size_t need = w4a16::zp_workspace_bytes(M, K, group_size);
+    if (need >= (size_t)kMaxBufferBytes) return W4A16_ERR_SHAPE;
+    if (M == 0) return W4A16_OK;
+    if (!qzeros || !workspace) return W4A16_ERR_NULL;
+    if (!aligned16(qzeros) || !aligned16(workspace)) return W4A16_ERR_ALIGN;
+    if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+    st = linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO, bf16);
+    if (st != W4A16_OK) return st;
+    const w4a16::ZpArgs a{x, scales, qzeros, y, M, K, N, group_size, bf16};
+    const hipError_t e = w4a16::launch_zp(a, reinterpret_cast<hipStream_t>(stream), workspace);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+extern "C" size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t group_size) {
+    if (M <= 0 || K <= 0 || K % 16 != 0 || !group_ok(group_size) || M >= kMaxBufferBytes ||
+        K >= kMaxBufferBytes)
+        return 0;
+    if ((w4a16::zp_groups(K, group_size) + 7) / 8 * 8 > w4a16::kZpMaxGroups) return 0;
+    return w4a16::zp_workspace_bytes(M, K, group_size);
+}
+
+extern "C" int w4a16_linear_zp(const void *x, const int32_t *qweight, const void *scales,
+                               const int32_t *qzeros, void *y, int64_t M, int64_t K, int64_t N,
+                               int64_t group_size, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    return zp_call(x, qweight, scales, qzeros, y, M, K, N, group_size, workspace,
+                   workspace_bytes, stream, false);
+}
+
+extern "C" int w4a16_linear_zp_bf16(const void *x, const int32_t *qweight, const void *scales,
+                                    const int32_t *qzeros, void *y, int64_t M, int64_t K,
+                                    int64_t N, int64_t group_size, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    return zp_call(x, qweight, scales, qzeros, y, M, K, N, group_size, workspace,
+                   workspace_bytes, stream, true);
+}
+
 extern "C" int pack_gptq_v2(const uint8_t *codes, int32_t *qweight, int64_t K, int64_t N) {
     if (K <= 0 || N <= 0 || K % 8 != 0) return W4A16_ERR_SHAPE;
     if (!codes || !qweight) return W4A16_ERR_NULL;
@@ -308,7 +353,7 @@ extern "C" const char *w4a16_status_string(int status) {
         case W4A16_ERR_LAUNCH: return "kernel launch failed";
         case W4A16_ERR_KERNEL: return "requested kernel cannot take this M";
         case W4A16_ERR_RANK: return "LoRA rank must be a multiple of 8 in [8, 1024]";
-        case W4A16_ERR_WORKSPACE: return "workspace smaller than w4a16_lora_workspace_bytes";
+        case W4A16_ERR_WORKSPACE: return "workspace smaller than the size its _workspace_bytes call gives";
         default: return "unknown status";
     }
 }

@@ -53,6 +53,22 @@ struct LoraArgs {
 size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r);
 hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace);
 
+// Stored zero points: y (the symmetric linear, already written) += the
+// rank-G correction sum_g X[m,g] (8 - z[g,n]) s[g,n], X the group sums of x.
+// `workspace` holds zp_workspace_bytes(M, K, group_size) bytes (X, fp32), no
+// initial contents; G rounded up to 8 is at most kZpMaxGroups.
+constexpr int kZpMaxGroups = 1536;
+struct ZpArgs {
+    const void *x, *scales;
+    const int32_t *qzeros;
+    void *y;
+    int64_t M, K, N, group_size;
+    bool bf16;
+};
+int zp_groups(int64_t K, int64_t group_size);
+size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t group_size);
+hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace);
+
 // Streaming-read probe over `bytes` (a multiple of 16) at data.
 hipError_t launch_read_probe(const void *data, int64_t bytes, void *sink, hipStream_t stream,
                              int num_cus);

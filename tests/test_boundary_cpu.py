@@ -162,6 +162,46 @@ def test_lora_workspace_size_and_empty_batch(lib):
     assert _lora(lib, M=0, r=12) == w4.W4A16_ERR_RANK
 
 
+def _zp(lib, x=0x1000, q=0x2000, s=0x3000, z=0x5000, y=0x4000, M=1, K=32, N=8, g=16,
+        ws=0x7000, wsb=1 << 20, bf16=False):
+    f = lib.w4a16_linear_zp_bf16 if bf16 else lib.w4a16_linear_zp
+    return f(x, q, s, z, y, M, K, N, g, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=0), w4.W4A16_ERR_NULL),
+    (dict(ws=0), w4.W4A16_ERR_NULL),
+    (dict(z=0x5004), w4.W4A16_ERR_ALIGN),
+    (dict(ws=0x7008), w4.W4A16_ERR_ALIGN),
+    (dict(wsb=16 * 8 * 4 - 1), w4.W4A16_ERR_WORKSPACE),
+    (dict(K=40), w4.W4A16_ERR_SHAPE),
+    (dict(g=48), w4.W4A16_ERR_GROUP),
+    (dict(K=16 * 1544, g=16), w4.W4A16_ERR_SHAPE),      # more than 1536 groups
+    (dict(x=0), w4.W4A16_ERR_NULL),
+])
+def test_zp_invalid_arguments_rejected_before_any_hip_call(lib, kw, status, bf16):
+    assert _zp(lib, bf16=bf16, **kw) == status
+
+
+def test_zp_workspace_size_and_packing(lib):
+    # M=1, K=32, g=16: 2 groups padded to 8, one 16-row block
+    assert w4.w4a16_zp_workspace_bytes(1, 32, 16) == 16 * 8 * 4
+    assert w4.w4a16_zp_workspace_bytes(33, 5120, 128) == 48 * 40 * 4
+    assert w4.w4a16_zp_workspace_bytes(1, 5120, -1) == 16 * 8 * 4
+    assert w4.w4a16_zp_workspace_bytes(0, 32, 16) == 0
+    assert w4.w4a16_zp_workspace_bytes(1, 32, 48) == 0
+    assert w4.w4a16_zp_workspace_bytes(1, 16 * 1544, 16) == 0
+    assert _zp(lib, x=0, q=0, s=0, z=0, y=0, ws=0, wsb=0, M=0) == w4.W4A16_OK
+    # zero points packed along N: the product's packing against the oracle's
+    rng = np.random.default_rng(5)
+    z = rng.integers(0, 16, size=(7, 48), dtype=np.uint8)
+    want = np.ascontiguousarray(oracle.pack(np.ascontiguousarray(z.T)).T)
+    assert np.array_equal(w4.pack_zeros(z), want)
+    z8 = np.arange(8, dtype=np.uint8)[None, :]
+    assert int(w4.pack_zeros(z8).view(np.uint32)[0, 0]) == 0x76543210
+
+
 def test_status_strings(lib):
     for st in range(0, 11):
         assert w4.w4a16_status_string(st)
