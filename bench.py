@@ -140,7 +140,8 @@ def rotations_for(weight_bytes: int, minimum: int = 2) -> int:
     return max(minimum, -(-2 * MALL_BYTES // weight_bytes))
 
 
-def bench_case(torch, w4, case, steps, warmup, eager, bf16=False, gate_up=False, lora_rank=0):
+def bench_case(torch, w4, case, steps, warmup, eager, bf16=False, gate_up=False, lora_rank=0,
+               zero_points=False):
     import workloads
     inp = workloads.generate_bf16(case) if bf16 else workloads.generate(case)
     wbytes = case.K * case.N // 2 + 2 * case.G * case.N
@@ -167,6 +168,17 @@ def bench_case(torch, w4, case, steps, warmup, eager, bf16=False, gate_up=False,
             w4.w4a16_linear_lora(x, qs[i % R], ss[i % R], As[i % R], Bs[i % R],
                                  workloads.LORA_SCALE, y, case.M, case.K, case.N,
                                  case.group_size, lora_rank, ws, wsb)
+
+    if zero_points:
+        # zero points rotate with the weights, like the scales they belong to
+        qz = torch.from_numpy(w4.pack_zeros(workloads.zero_points(case.G, case.N, case.seed + 700)))
+        qzs = [qz.to(x.device) for _ in range(R)]
+        wsb = w4.w4a16_zp_workspace_bytes(case.M, case.K, case.N, case.group_size)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+
+        def step(i):  # noqa: F811
+            w4.w4a16_linear_zp(x, qs[i % R], ss[i % R], qzs[i % R], y, case.M, case.K, case.N,
+                               case.group_size, ws, wsb)
 
     sec = Timed(torch).run(step, steps, warmup, eager)
     return inp, y, sec, R
@@ -263,6 +275,8 @@ def main():
                     help="skip the merged gate/up (SiLU * mul) decode and prefill lines")
     ap.add_argument("--no-lora", action="store_true",
                     help="skip the linear + LoRA adapter lines")
+    ap.add_argument("--no-zero-points", action="store_true",
+                    help="skip the stored-zero-point (asymmetric weight) lines")
     ap.add_argument("--no-bf16", action="store_true",
                     help="skip the bfloat16-activation variant's decode and prefill lines")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -438,6 +452,36 @@ def main():
                                       "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4)}}
         torch.cuda.empty_cache()
         out["lora"] = lo
+
+    if args.only == "all" and not args.no_zero_points:
+        # asymmetric weights: the linear with stored zero points (int32 [G, N/8])
+        zp = {}
+        case = workloads.decode_up()
+        _, _, sec, R = bench_case(torch, w4, case, args.steps, args.warmup, args.eager,
+                                  zero_points=True)
+        B = algorithmic_bytes(case.M, case.K, case.N, case.G) + case.G * case.N // 2
+        gbs = B / sec / 1e9
+        zp["decode"] = {"workload": "decode up-projection GEMV M=1 K=5120 N=17408 g=128, stored zero points",
+                        "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": sec * 1e3,
+                        "linear_alone_ms": out.get("ms_per_step"),
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                     "algorithmic_bytes": B}}
+        torch.cuda.empty_cache()
+        case = workloads.prefill_up()
+        psteps = args.prefill_steps or max(10, args.steps // 4)
+        _, _, sec, R = bench_case(torch, w4, case, psteps, max(1, min(args.warmup, psteps)),
+                                  args.eager, zero_points=True)
+        tflops = 2.0 * case.M * case.N * case.K / sec / 1e12
+        zp["prefill"] = {"workload": "prefill up-projection GEMM M=2048 K=5120 N=17408 g=128, stored zero points",
+                         "value": round(tflops, 1), "unit": "TFLOP/s", "ms_per_step": sec * 1e3,
+                         "linear_alone_ms": out.get("prefill", {}).get("ms_per_step"),
+                         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4)}}
+        torch.cuda.empty_cache()
+        out["zero_points"] = zp
 
     out["device"] = dev_name
     out["timing"] = "eager launches" if args.eager else "one HIP graph of K steps"

@@ -217,16 +217,16 @@ size_t w4a16_lora_workspace_bytes(int64_t M, int64_t K, int64_t rank);
  *     used as stored (a v1 checkpoint's z - 1 becomes z by adding one before
  *     the call).  It is pack_gptq_v2 applied to the transposed [N, G] zero
  *     points, transposed back.
- *   workspace : device buffer of at least w4a16_zp_workspace_bytes(M, K,
+ *   workspace : device buffer of at least w4a16_zp_workspace_bytes(M, K, N,
  *     group_size) bytes, 16-byte aligned, no initial contents, owned by the
  *     caller; calls that overlap in time must not share one.
  *   ceil(G / 8) * 8 <= 1536 (else W4A16_ERR_SHAPE); everything else as for
  *   w4a16_linear (the _bf16 form: bfloat16 x and y, as w4a16_linear_bf16).
  * Steps on the stream: since (q - z) s = (q - 8) s + (8 - z) s, the symmetric
- * linear writes y; a kernel sums x over each group in fp32 (X[m, g]); an
- * expand kernel forms C[g, n] = (8 - z) s exactly in fp32, rounds X and C to
- * the activation type, takes X . C in fp32 on the matrix cores and writes
- * y = round(y + X . C).  Where every zero point is 8, C is 0 and y is the
+ * linear writes y; one kernel sums x over each group in fp32 (X[m, g]) and
+ * forms C[g, n] = (8 - z) s exactly in fp32, rounded to the activation type;
+ * an expand kernel rounds X to the activation type, takes X . C in fp32 on
+ * the matrix cores and writes y = round(y + X . C).  Where every zero point is 8, C is 0 and y is the
  * symmetric result bit for bit.
  * Hence, per element and beyond the symmetric linear's own bound (u = 2^-11
  * for fp16, 2^-8 for bfloat16): u |y_sym| + u |y| + (2u + K 2^-24) P, to
@@ -240,9 +240,10 @@ int w4a16_linear_zp_bf16(const void *x, const int32_t *qweight, const void *scal
                          int64_t group_size, void *workspace, size_t workspace_bytes,
                          void *stream);
 
-/* Bytes of workspace w4a16_linear_zp needs: fp32 group sums of x, [M rounded
- * up to 16, G rounded up to 8].  0 for M <= 0 or arguments it rejects. */
-size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t group_size);
+/* Bytes of workspace w4a16_linear_zp needs: fp32 group sums of x [M rounded
+ * up to 16, Gp] and the correction matrix C^T [N, Gp] in the activation type,
+ * Gp = G rounded up to 8.  0 for M <= 0 or arguments it rejects. */
+size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
 
 /* Host-side packing into the GPTQ_V2 layout (native int32 qweight, "GPTQ-Pro"
  * README, "Runtime contract"):

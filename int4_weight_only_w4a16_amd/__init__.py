@@ -94,7 +94,7 @@ def load_library() -> ctypes.CDLL:
     for name in ("w4a16_linear_zp", "w4a16_linear_zp_bf16"):
         getattr(lib, name).argtypes = [p, p, p, p, p, i64, i64, i64, i64, p, sz, p]
         getattr(lib, name).restype = i32
-    lib.w4a16_zp_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.w4a16_zp_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.w4a16_zp_workspace_bytes.restype = sz
     lib.pack_gptq_v2.argtypes = [p, p, i64, i64]
     lib.pack_gptq_v2.restype = i32
@@ -275,9 +275,9 @@ def linear_lora(x, qweight, scales, group_size: int, lora_a, lora_b, lora_scale:
     return out
 
 
-def w4a16_zp_workspace_bytes(M: int, K: int, group_size: int) -> int:
+def w4a16_zp_workspace_bytes(M: int, K: int, N: int, group_size: int) -> int:
     """Workspace bytes w4a16_linear_zp needs (0 for arguments it rejects)."""
-    return int(load_library().w4a16_zp_workspace_bytes(int(M), int(K), int(group_size)))
+    return int(load_library().w4a16_zp_workspace_bytes(int(M), int(K), int(N), int(group_size)))
 
 
 def w4a16_linear_zp(x, qweight, scales, qzeros, y, M: int, K: int, N: int, group_size: int,
@@ -321,7 +321,7 @@ def linear_zp(x, qweight, scales, qzeros, group_size: int, out=None, workspace=N
     N = qweight.shape[1]
     if qweight.shape[0] * 8 != K or tuple(qzeros.shape) != (scales.shape[0], N // 8):
         raise ValueError("qweight must be [K/8, N] and qzeros [G, N/8]")
-    need = w4a16_zp_workspace_bytes(M, K, group_size)
+    need = w4a16_zp_workspace_bytes(M, K, N, group_size)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     if out is None:

@@ -23,9 +23,10 @@
 //
 // Stored zero points (asymmetric weights, w = (q - z) s) use the same expand:
 // (q - z) s = (q - 8) s + (8 - z) s, so y = y_sym + sum_g X[m,g] C[g,n] with
-// X the sums of x over each group (zp_group_sums_kernel) and C = (8 - z) s,
-// formed in the expand's B fragments straight from qzeros and scales: a
-// rank-G correction of the symmetric linear, exactly zero where z = 8.
+// X the sums of x over each group and C = (8 - z) s, both formed by
+// zp_prepare_kernel (C transposed to [N, Gp] in the activation type, the
+// layout of B): a rank-G correction of the symmetric linear, exactly zero
+// where z = 8.
 
 #include "w4a16_device.hpp"
 #include "w4a16_launch.h"
@@ -96,31 +97,85 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__rest
     }
 }
 
-// X[m, gi] = sum of x[m, k] over group gi (fp32; K for g = -1), one wave per
-// (group, row): lane l sums the 16-byte runs l, l + 64, ... of the group in
-// order, then a fixed butterfly adds the lanes.  Columns G .. Gp-1 are zero.
-// Written as one slab [M rounded up to 16][Gp] of the expand's layout.
+// Two kinds of 64-thread blocks in one launch:
+//  - the first `sum_blocks`: X[m, gi] = sum of x[m, k] over group gi (fp32;
+//    K for g = -1), columns G .. Gp-1 zero, one slab [M rounded up to 16][Gp]
+//    of the expand's layout.  Groups of at most 256 (per_thread): one thread
+//    per (row, group) adds the group's 16-byte runs in order.  Larger groups:
+//    one wave per (group, row), lane l adds the runs l, l + 64, ... in order,
+//    then a fixed butterfly adds the lanes.
+//  - the rest: ct[n][g0 .. g0+7] = (8 - z[g,n]) s[g,n] for eight groups per
+//    thread (zero for g >= G), exact in fp32 and rounded to the activation
+//    type; consecutive threads take consecutive columns, so each load of the
+//    scale grid and of qzeros is coalesced.
 template <bool BF>
-__global__ void __launch_bounds__(64) zp_group_sums_kernel(const uint16_t *__restrict__ x,
-                                                           float *__restrict__ t, int M, int K,
-                                                           int gsz, int G, int Gp) {
-    const int gi = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
-    float acc = 0.f;
-    if (gi < G) {
-        const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-        const int k0 = gi * gsz, k1 = min(K, k0 + gsz);   // both multiples of 16
-        for (int k = k0 + 8 * lane; k < k1; k += 512) {
-            const u4 v = load_b128(xr, (uint32_t)(m * K + k) * 2u);
+__global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ scales,
+                                                        const int32_t *__restrict__ qzeros,
+                                                        float *__restrict__ t,
+                                                        uint16_t *__restrict__ ct, int M, int K,
+                                                        int N, int gsz, int G, int Gp,
+                                                        int per_thread, int sum_blocks) {
+    const int lane = threadIdx.x;
+    const int b = blockIdx.x;
+    if (per_thread && b < sum_blocks) {
+        const int64_t i = (int64_t)b * 64 + lane;
+        if (i >= (int64_t)M * Gp) return;
+        const int gi = (int)(i % Gp), m = (int)(i / Gp);
+        float acc = 0.f;
+        if (gi < G) {
+            const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+            const int k0 = gi * gsz, k1 = min(K, k0 + gsz);   // both multiples of 16
+#pragma unroll 4
+            for (int k = k0; k < k1; k += 8) {
+                const u4 v = load_b128(xr, (uint32_t)(m * K + k) * 2u);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc += act_lo<BF>(v[e]);
-                acc += act_hi<BF>(v[e]);
+                for (int e = 0; e < 4; ++e) {
+                    acc += act_lo<BF>(v[e]);
+                    acc += act_hi<BF>(v[e]);
+                }
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        t[(size_t)m * Gp + gi] = acc;
+        return;
     }
-    if (lane == 0) t[(size_t)m * Gp + gi] = acc;
+    if (b < sum_blocks) {
+        const int gi = b % Gp, m = b / Gp;
+        float acc = 0.f;
+        if (gi < G) {
+            const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+            const int k0 = gi * gsz, k1 = min(K, k0 + gsz);   // both multiples of 16
+            for (int k = k0 + 8 * lane; k < k1; k += 512) {
+                const u4 v = load_b128(xr, (uint32_t)(m * K + k) * 2u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc += act_lo<BF>(v[e]);
+                    acc += act_hi<BF>(v[e]);
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        }
+        if (lane == 0) t[(size_t)m * Gp + gi] = acc;
+        return;
+    }
+    const int64_t tt = (int64_t)(b - sum_blocks) * 64 + lane;
+    if (tt >= (int64_t)N * (Gp / 8)) return;
+    const int n = (int)(tt % N), g0 = 8 * (int)(tt / N);
+    float c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int g = g0 + e;
+        c[e] = 0.f;
+        if (g < G) {
+            const uint32_t zw = (uint32_t)qzeros[(size_t)g * (N / 8) + n / 8];
+            const int z = (int)((zw >> (4 * (n % 8))) & 0xFu);
+            c[e] = (float)(8 - z) * (float)half_lo((uint32_t)scales[(size_t)g * N + n]);
+        }
+    }
+    *reinterpret_cast<u4 *>(ct + (size_t)n * Gp + g0) =
+        u4{pack2<BF>(c[0], c[1]), pack2<BF>(c[2], c[3]), pack2<BF>(c[4], c[5]),
+           pack2<BF>(c[6], c[7])};
 }
 
 // One workgroup (4 waves) adds the adapter term to a 16-row by 64*NB-column
@@ -134,16 +189,11 @@ __global__ void __launch_bounds__(64) zp_group_sums_kernel(const uint16_t *__res
 //  3. Each wave multiplies t by its rows of B on the matrix cores.
 //  4. The fp32 delta goes through LDS to the layout of the y runs, and each
 //     run is written once: y = round(y + s * delta).
-// With ZP the "B" rows are C[g, n] = (8 - z[g,n]) s[g,n] for g < G (zero for
-// G <= g < r), formed exactly in fp32 from qzeros and scales and rounded to
-// the activation type like B.
-template <bool BF, int NB, bool ZP>
+template <bool BF, int NB>
 __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restrict__ tp,
                                                           const uint16_t *__restrict__ B,
                                                           uint16_t *__restrict__ y, float scale,
-                                                          int M, int N, int r, int Mp, int S,
-                                                          const int32_t *__restrict__ qzeros,
-                                                          int G) {
+                                                          int M, int N, int r, int Mp, int S) {
     constexpr int TN = 64 * NB;
     constexpr int kRuns = TN / 8;                 // 8-column runs per row of the tile
     constexpr int kPer = (16 * kRuns + 255) / 256;
@@ -197,7 +247,7 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
     __syncthreads();
 
     const int n0 = nt * TN + 16 * NB * w;
-    const auto br = make_rsrc(B, ZP ? 0u : (uint32_t)N * (uint32_t)r * 2u);
+    const auto br = make_rsrc(B, (uint32_t)N * (uint32_t)r * 2u);
     const int kofs = 8 * (lane >> 4);
     f4 acc[NB] = {};
     for (int kk = 0; kk < r; kk += 32) {
@@ -207,23 +257,7 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int n = n0 + 16 * nb + (lane & 15);
-            if constexpr (ZP) {                   // B is the scale grid [G, N] here
-                float c[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int g = j + e;
-                    c[e] = 0.f;
-                    if (jin && n < N && g < G) {
-                        const uint32_t zw = (uint32_t)qzeros[(size_t)g * (N / 8) + n / 8];
-                        const int z = (int)((zw >> (4 * (n % 8))) & 0xFu);
-                        c[e] = (float)(8 - z) * (float)half_lo((uint32_t)B[(size_t)g * N + n]);
-                    }
-                }
-                bb[nb] = u4{pack2<BF>(c[0], c[1]), pack2<BF>(c[2], c[3]), pack2<BF>(c[4], c[5]),
-                            pack2<BF>(c[6], c[7])};
-            } else {
-                bb[nb] = load_b128(br, (jin && n < N) ? (uint32_t)(n * r + j) * 2u : kOOB);
-            }
+            bb[nb] = load_b128(br, (jin && n < N) ? (uint32_t)(n * r + j) * 2u : kOOB);
         }
         const u4 ta = jin ? tsh[((lane & 15) * ld + j) / 8] : u4{0, 0, 0, 0};
 #pragma unroll
@@ -280,21 +314,19 @@ size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r) {
     return (size_t)p.splits * (size_t)p.Mp * (size_t)r * sizeof(float);
 }
 
-template <bool BF, bool ZP>
+template <bool BF>
 static hipError_t launch_expand(const float *tp, const uint16_t *B, uint16_t *y, float scale,
-                                int M, int N, int r, int Mp, int S, const int32_t *qzeros, int G,
-                                int mblocks, hipStream_t stream) {
+                                int M, int N, int r, int Mp, int S, int mblocks,
+                                hipStream_t stream) {
     // decode-sized batches: narrow tiles for more workgroups on a short y
     const bool narrow = M <= 16;
     const int TN = narrow ? 64 : 256;
     const dim3 eg((N + TN - 1) / TN, mblocks);
     const size_t tlds = (size_t)16 * (size_t)(r + 8) * 2;   // t of 16 rows, 16-bit
     if (narrow)
-        lora_expand_kernel<BF, 1, ZP><<<eg, 256, tlds, stream>>>(tp, B, y, scale, M, N, r, Mp, S,
-                                                                 qzeros, G);
+        lora_expand_kernel<BF, 1><<<eg, 256, tlds, stream>>>(tp, B, y, scale, M, N, r, Mp, S);
     else
-        lora_expand_kernel<BF, 4, ZP><<<eg, 256, tlds, stream>>>(tp, B, y, scale, M, N, r, Mp, S,
-                                                                 qzeros, G);
+        lora_expand_kernel<BF, 4><<<eg, 256, tlds, stream>>>(tp, B, y, scale, M, N, r, Mp, S);
     return hipGetLastError();
 }
 
@@ -313,20 +345,22 @@ hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace) {
         lora_shrink_kernel<false><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return a.bf16 ? launch_expand<true, false>(tp, B, y, a.scale, M, N, r, p.Mp, p.splits,
-                                               nullptr, 0, p.mblocks, stream)
-                  : launch_expand<false, false>(tp, B, y, a.scale, M, N, r, p.Mp, p.splits,
-                                                nullptr, 0, p.mblocks, stream);
+    return a.bf16 ? launch_expand<true>(tp, B, y, a.scale, M, N, r, p.Mp, p.splits, p.mblocks,
+                                        stream)
+                  : launch_expand<false>(tp, B, y, a.scale, M, N, r, p.Mp, p.splits, p.mblocks,
+                                         stream);
 }
 
 int zp_groups(int64_t K, int64_t group_size) {
     return group_size == -1 ? 1 : (int)((K + group_size - 1) / group_size);
 }
 
-size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t group_size) {
+// Workspace: X [M rounded up to 16][Gp] fp32, then C^T [N][Gp] 16-bit.
+size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
     if (M <= 0) return 0;
     const int64_t Gp = (zp_groups(K, group_size) + 7) / 8 * 8;
-    return (size_t)((M + 15) / 16 * 16) * (size_t)Gp * sizeof(float);
+    return (size_t)((M + 15) / 16 * 16) * (size_t)Gp * sizeof(float) +
+           (size_t)N * (size_t)Gp * sizeof(uint16_t);
 }
 
 hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace) {
@@ -338,17 +372,24 @@ hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace) {
     const auto *sc = static_cast<const uint16_t *>(a.scales);
     auto *y = static_cast<uint16_t *>(a.y);
     auto *t = static_cast<float *>(workspace);
-    const dim3 gg(Gp, M);
+    auto *ct = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) +
+                                            (size_t)16 * mblocks * Gp * sizeof(float));
+    const int64_t cthreads = (int64_t)N * (Gp / 8);
+    const int per_thread = a.group_size != -1 && a.group_size <= 256;
+    const int sum_blocks =
+        per_thread ? (int)(((int64_t)M * Gp + 63) / 64) : (int)((int64_t)M * Gp);
+    const unsigned blocks = (unsigned)(sum_blocks + (cthreads + 63) / 64);
     if (a.bf16)
-        zp_group_sums_kernel<true><<<gg, 64, 0, stream>>>(x, t, M, K, gsz, G, Gp);
+        zp_prepare_kernel<true><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, t, ct, M, K, N, gsz, G,
+                                                          Gp, per_thread, sum_blocks);
     else
-        zp_group_sums_kernel<false><<<gg, 64, 0, stream>>>(x, t, M, K, gsz, G, Gp);
+        zp_prepare_kernel<false><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, t, ct, M, K, N, gsz,
+                                                           G, Gp, per_thread, sum_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return a.bf16 ? launch_expand<true, true>(t, sc, y, 1.0f, M, N, Gp, 16 * mblocks, 1,
-                                              a.qzeros, G, mblocks, stream)
-                  : launch_expand<false, true>(t, sc, y, 1.0f, M, N, Gp, 16 * mblocks, 1,
-                                               a.qzeros, G, mblocks, stream);
+    return a.bf16 ? launch_expand<true>(t, ct, y, 1.0f, M, N, Gp, 16 * mblocks, 1, mblocks, stream)
+                  : launch_expand<false>(t, ct, y, 1.0f, M, N, Gp, 16 * mblocks, 1, mblocks,
+                                         stream);
 }
 
 }  // namespace w4a16

@@ -259,7 +259,7 @@ static int zp_call(const void *x, const int32_t *qweight, const void *scales,
     int st = validate(x, qweight, scales, y, M, K, N, group_size);
     if (st != W4A16_OK) return st;
     if ((w4a16::zp_groups(K, group_size) + 7) / 8 * 8 > w4a16::kZpMaxGroups) return W4A16_ERR_SHAPE;
-    const size_t need = w4a16::zp_workspace_bytes(M, K, group_size);
+    const size_t need = w4a16::zp_workspace_bytes(M, K, N, group_size);
     if (need >= (size_t)kMaxBufferBytes) return W4A16_ERR_SHAPE;
     if (M == 0) return W4A16_OK;
     if (!qzeros || !workspace) return W4A16_ERR_NULL;
@@ -272,12 +272,13 @@ static int zp_call(const void *x, const int32_t *qweight, const void *scales,
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
-extern "C" size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t group_size) {
-    if (M <= 0 || K <= 0 || K % 16 != 0 || !group_ok(group_size) || M >= kMaxBufferBytes ||
-        K >= kMaxBufferBytes)
+extern "C" size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t N,
+                                           int64_t group_size) {
+    if (M <= 0 || K <= 0 || K % 16 != 0 || N <= 0 || N % 8 != 0 || !group_ok(group_size) ||
+        M >= kMaxBufferBytes || K >= kMaxBufferBytes || N >= kMaxBufferBytes)
         return 0;
     if ((w4a16::zp_groups(K, group_size) + 7) / 8 * 8 > w4a16::kZpMaxGroups) return 0;
-    return w4a16::zp_workspace_bytes(M, K, group_size);
+    return w4a16::zp_workspace_bytes(M, K, N, group_size);
 }
 
 extern "C" int w4a16_linear_zp(const void *x, const int32_t *qweight, const void *scales,

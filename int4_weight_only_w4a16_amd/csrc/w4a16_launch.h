@@ -55,8 +55,9 @@ hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace);
 
 // Stored zero points: y (the symmetric linear, already written) += the
 // rank-G correction sum_g X[m,g] (8 - z[g,n]) s[g,n], X the group sums of x.
-// `workspace` holds zp_workspace_bytes(M, K, group_size) bytes (X, fp32), no
-// initial contents; G rounded up to 8 is at most kZpMaxGroups.
+// `workspace` holds zp_workspace_bytes(M, K, N, group_size) bytes (X in fp32,
+// then C^T in the activation type), no initial contents; G rounded up to 8 is
+// at most kZpMaxGroups.
 constexpr int kZpMaxGroups = 1536;
 struct ZpArgs {
     const void *x, *scales;
@@ -66,7 +67,7 @@ struct ZpArgs {
     bool bf16;
 };
 int zp_groups(int64_t K, int64_t group_size);
-size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t group_size);
+size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
 hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace);
 
 // Streaming-read probe over `bytes` (a multiple of 16) at data.

@@ -174,7 +174,7 @@ def _zp(lib, x=0x1000, q=0x2000, s=0x3000, z=0x5000, y=0x4000, M=1, K=32, N=8, g
     (dict(ws=0), w4.W4A16_ERR_NULL),
     (dict(z=0x5004), w4.W4A16_ERR_ALIGN),
     (dict(ws=0x7008), w4.W4A16_ERR_ALIGN),
-    (dict(wsb=16 * 8 * 4 - 1), w4.W4A16_ERR_WORKSPACE),
+    (dict(wsb=16 * 8 * 4 + 8 * 8 * 2 - 1), w4.W4A16_ERR_WORKSPACE),
     (dict(K=40), w4.W4A16_ERR_SHAPE),
     (dict(g=48), w4.W4A16_ERR_GROUP),
     (dict(K=16 * 1544, g=16), w4.W4A16_ERR_SHAPE),      # more than 1536 groups
@@ -185,13 +185,14 @@ def test_zp_invalid_arguments_rejected_before_any_hip_call(lib, kw, status, bf16
 
 
 def test_zp_workspace_size_and_packing(lib):
-    # M=1, K=32, g=16: 2 groups padded to 8, one 16-row block
-    assert w4.w4a16_zp_workspace_bytes(1, 32, 16) == 16 * 8 * 4
-    assert w4.w4a16_zp_workspace_bytes(33, 5120, 128) == 48 * 40 * 4
-    assert w4.w4a16_zp_workspace_bytes(1, 5120, -1) == 16 * 8 * 4
-    assert w4.w4a16_zp_workspace_bytes(0, 32, 16) == 0
-    assert w4.w4a16_zp_workspace_bytes(1, 32, 48) == 0
-    assert w4.w4a16_zp_workspace_bytes(1, 16 * 1544, 16) == 0
+    # M=1, K=32, N=8, g=16: 2 groups padded to 8, one 16-row block, C^T [8, 8]
+    assert w4.w4a16_zp_workspace_bytes(1, 32, 8, 16) == 16 * 8 * 4 + 8 * 8 * 2
+    assert w4.w4a16_zp_workspace_bytes(33, 5120, 264, 128) == 48 * 40 * 4 + 264 * 40 * 2
+    assert w4.w4a16_zp_workspace_bytes(1, 5120, 8, -1) == 16 * 8 * 4 + 8 * 8 * 2
+    assert w4.w4a16_zp_workspace_bytes(0, 32, 8, 16) == 0
+    assert w4.w4a16_zp_workspace_bytes(1, 32, 8, 48) == 0
+    assert w4.w4a16_zp_workspace_bytes(1, 32, 12, 16) == 0
+    assert w4.w4a16_zp_workspace_bytes(1, 16 * 1544, 8, 16) == 0
     assert _zp(lib, x=0, q=0, s=0, z=0, y=0, ws=0, wsb=0, M=0) == w4.W4A16_OK
     # zero points packed along N: the product's packing against the oracle's
     rng = np.random.default_rng(5)

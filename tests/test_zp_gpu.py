@@ -132,7 +132,7 @@ def test_zp_deterministic_and_graph_replay(dev):
         q = torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev)
         s = torch.from_numpy(inp.scales).to(dev)
         qz = torch.from_numpy(w4.pack_zeros(z)).to(dev)
-        ws = torch.empty(w4.w4a16_zp_workspace_bytes(M, K, g), dtype=torch.uint8, device=dev)
+        ws = torch.empty(w4.w4a16_zp_workspace_bytes(M, K, N, g), dtype=torch.uint8, device=dev)
         e1 = w4.linear_zp(x, q, s, qz, g, workspace=ws, stream=st)
         e2 = w4.linear_zp(x, q, s, qz, g, workspace=ws, stream=st)
         torch.cuda.synchronize()
