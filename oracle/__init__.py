@@ -88,6 +88,8 @@ class Oracle:
         lib.oracle_linear_lora.argtypes = [p, i32, p, p, p, p, f64, i64, i64, i64, i64, i64, p]
         lib.oracle_linear_zp.argtypes = [p, i32, i32, p, p, p, i64, i64, i64, i64, p]
         lib.oracle_linear_zp.restype = ctypes.c_int
+        lib.oracle_linear_zp_at.argtypes = [p, i32, p, p, p, i64, i64, i64, i64, p, p, i64, p]
+        lib.oracle_linear_zp_at.restype = ctypes.c_int
         for f in (lib.oracle_unpack, lib.oracle_pack, lib.oracle_dequant,
                   lib.oracle_linear, lib.oracle_linear_at, lib.oracle_linear_ex,
                   lib.oracle_linear_at_ex, lib.oracle_gate_up_silu, lib.oracle_lora_shrink,
@@ -272,6 +274,27 @@ class Oracle:
                                          group_size, _ptr(y)), "linear_zp")
         return y
 
+    def linear_zp_at(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+                     qzeros: np.ndarray, group_size: int, ms: np.ndarray, ns: np.ndarray,
+                     act: str = "f16") -> np.ndarray:
+        """y[ms[i], ns[i]] of linear_zp for sampled outputs, each from the definition."""
+        xb = _act_bits(x, act)
+        qweight = np.ascontiguousarray(qweight, dtype=np.int32)
+        scales = np.ascontiguousarray(scales, dtype=np.float16)
+        qzeros = np.ascontiguousarray(qzeros, dtype=np.int32)
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        M, K = xb.shape
+        N = qweight.shape[1]
+        if qzeros.shape != (scales.shape[0], N // 8):
+            raise ValueError("qzeros must be [G, N/8]")
+        out = np.empty(ms.shape[0], dtype=np.float64)
+        _check(self.lib.oracle_linear_zp_at(_ptr(xb), _ACTS[act], _ptr(qweight),
+                                            _ptr(scales.view(np.uint16)), _ptr(qzeros), M, K, N,
+                                            group_size, _ptr(ms), _ptr(ns), ms.shape[0],
+                                            _ptr(out)), "linear_zp_at")
+        return out
+
 
 _default: Optional[Oracle] = None
 
@@ -332,3 +355,7 @@ def linear_lora(x, qweight, scales, group_size, A, B, scale, act="f16"):
 
 def linear_zp(x, qweight, scales, qzeros, group_size, act="f16", absval=False):
     return default().linear_zp(x, qweight, scales, qzeros, group_size, act, absval)
+
+
+def linear_zp_at(x, qweight, scales, qzeros, group_size, ms, ns, act="f16"):
+    return default().linear_zp_at(x, qweight, scales, qzeros, group_size, ms, ns, act)

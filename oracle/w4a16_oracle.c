@@ -435,3 +435,30 @@ int oracle_linear_zp(const uint16_t *x, int act, int absval, const int32_t *qwei
     free(W);
     return OR_OK;
 }
+
+/* out[i] <- y[ms[i], ns[i]] of oracle_linear_zp for sampled outputs, each from
+ * the definition directly (no dequantised matrix). */
+int oracle_linear_zp_at(const uint16_t *x, int act, const int32_t *qweight,
+                        const uint16_t *scales, const int32_t *qzeros, int64_t M, int64_t K,
+                        int64_t N, int64_t g, const int64_t *ms, const int64_t *ns,
+                        int64_t count, double *out) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || count < 0 || (act != 0 && act != 1))
+        return OR_ERR_ARG;
+    if (count == 0) return OR_OK;
+    if (!x || !qweight || !scales || !qzeros || !ms || !ns || !out) return OR_ERR_ARG;
+    for (int64_t i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return OR_ERR_ARG;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t m = ms[i], n = ns[i];
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t gi = group_of(k, g);
+            const int q = (int)code_at(qweight, N, k, n), z = (int)zero_at(qzeros, N, gi, n);
+            const float w = (float)(q - z) * (float)half_to_double(scales[gi * N + n]);
+            acc += act_to_double(x[m * K + k], act) * (double)w;
+        }
+        out[i] = acc;
+    }
+    return OR_OK;
+}

@@ -593,4 +593,22 @@ def pin_zp_worked_word_and_zero_output(o):
     assert np.all(o.linear_zp(xs, o.pack(codes), sc, _pack_zeros(o, zz), g) == 0.0)
 
 
+def pin_zp_sampled_matches_full(o):
+    """Sampled zero-point outputs equal the full ones bit for bit (same fp32
+    weights, k ascending, fp64 sums), both activation types."""
+    rng = np.random.default_rng(44)
+    M, K, N, g = 5, 192, 48, 64
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    z = rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)
+    scales = rng.uniform(1e-2, 8e-2, size=(K // g, N)).astype(np.float16)
+    q, qz = o.pack(codes), _pack_zeros(o, z)
+    ms = rng.integers(0, M, size=60)
+    ns = rng.integers(0, N, size=60)
+    xh = rng.standard_normal((M, K)).astype(np.float16)
+    xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for x, act in ((xh, "f16"), (xb, "bf16")):
+        full = o.linear_zp(x, q, scales, qz, g, act=act)
+        assert np.array_equal(o.linear_zp_at(x, q, scales, qz, g, ms, ns, act=act), full[ms, ns])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -103,6 +103,20 @@ def test_zp_parity(dev, M, K, N, g, act):
     _check(case, inp, z, y, act)
 
 
+def test_zp_prefill_full_shape_sampled(dev):
+    """The prefill up-projection shape (M=2048, K=5120, N=17408, g=128) with stored
+    zero points: sampled outputs plus whole first and last rows, from the oracle."""
+    M, K, N, g = 2048, 5120, 17408, 128
+    case, inp, z = _inputs(M, K, N, g, 3, "f16")
+    y = _run(inp, z, g, dev, False)
+    rng = np.random.default_rng(78)
+    ms = np.concatenate([rng.integers(0, M, 4096), np.zeros(N, np.int64), np.full(N, M - 1, np.int64)])
+    ns = np.concatenate([rng.integers(0, N, 4096), np.arange(N), np.arange(N)])
+    qz_o = np.ascontiguousarray(oracle.pack(np.ascontiguousarray(z.T)).T)
+    ref = oracle.linear_zp_at(inp.x, oracle.pack(inp.codes), inp.scales, qz_o, g, ms, ns)
+    check_parity(y[ms, ns], ref, "zero points prefill_up (sampled)")
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_zp_all_eight_is_the_symmetric_linear_bitwise(dev, bf16):
     """Every zero point 8 makes the correction exactly zero: y equals the
