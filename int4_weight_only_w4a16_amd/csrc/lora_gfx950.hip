@@ -182,6 +182,7 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
 // tile of y; wave w owns columns [16*NB*w, 16*NB*(w+1)) of the tile.
 //  1. The tile of y is loaded first (16-byte runs, rows >= M skipped), so its
 //     latency overlaps the rest.
+//     The first rank step's rows of B are requested next, for the same reason.
 //  2. The workgroup sums the S partial slabs of its 16 rows of t once, in
 //     chunk order (kSB slabs in flight at a time), in coalesced 16-byte runs
 //     spread over all threads, and
@@ -209,6 +210,17 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
         const int m = 16 * mb + q / kRuns, n = nt * TN + 8 * (q % kRuns);
         yin[i] = q < 16 * kRuns && m < M && n < N;   // N % 8 == 0: runs are whole
         yv[i] = yin[i] ? *reinterpret_cast<const u4 *>(y + (size_t)m * N + n) : u4{0, 0, 0, 0};
+    }
+
+    // the first rank step's rows of B, which do not depend on t
+    const int n0 = nt * TN + 16 * NB * w;
+    const auto br = make_rsrc(B, (uint32_t)N * (uint32_t)r * 2u);
+    const int kofs = 8 * (lane >> 4);
+    u4 bb0[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int n = n0 + 16 * nb + (lane & 15);
+        bb0[nb] = load_b128(br, (kofs < r && n < N) ? (uint32_t)(n * r + kofs) * 2u : kOOB);
     }
 
     extern __shared__ u4 tsh[];                   // t of the 16 rows: [16][r + 8] 16-bit
@@ -246,9 +258,6 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
     }
     __syncthreads();
 
-    const int n0 = nt * TN + 16 * NB * w;
-    const auto br = make_rsrc(B, (uint32_t)N * (uint32_t)r * 2u);
-    const int kofs = 8 * (lane >> 4);
     f4 acc[NB] = {};
     for (int kk = 0; kk < r; kk += 32) {
         const int j = kk + kofs;                  // r % 8 == 0: eight in or eight out
@@ -257,7 +266,8 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int n = n0 + 16 * nb + (lane & 15);
-            bb[nb] = load_b128(br, (jin && n < N) ? (uint32_t)(n * r + j) * 2u : kOOB);
+            bb[nb] = kk == 0 ? bb0[nb]
+                             : load_b128(br, (jin && n < N) ? (uint32_t)(n * r + j) * 2u : kOOB);
         }
         const u4 ta = jin ? tsh[((lane & 15) * ld + j) / 8] : u4{0, 0, 0, 0};
 #pragma unroll
