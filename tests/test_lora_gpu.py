@@ -159,7 +159,8 @@ def test_lora_scale_zero_equals_linear_and_is_deterministic(dev, bf16):
         assert np.array_equal(y1, y2), M
 
 
-def test_lora_graph_capture_and_replay(dev):
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_lora_graph_capture_and_replay(dev, act):
     """Linear + adapter captured in a HIP graph on a stream that already holds
     the linear's workspaces, replayed several times with eager work between the
     replays: every replay equals the eager call bit for bit."""
@@ -167,13 +168,21 @@ def test_lora_graph_capture_and_replay(dev):
     runs = []
     for M, K, N, g, r in ((1, 5120, 2048, 128, 32), (64, 1024, 1032, 64, 16),
                           (300, 2048, 1024, 128, 64)):
-        _, inp, A, B = _inputs(M, K, N, g, r, 95, "f16")
-        x = torch.from_numpy(inp.x).to(dev)
+        _, inp, A, B = _inputs(M, K, N, g, r, 95, act)
+        dt = torch.bfloat16 if act == "bf16" else torch.float16
+
+        def up(arr):
+            arr = np.ascontiguousarray(arr)
+            if act == "bf16":
+                return torch.from_numpy(arr.view(np.int16)).view(dt).to(dev)
+            return torch.from_numpy(arr).to(dev)
+
+        x = up(inp.x)
         q = torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev)
         s = torch.from_numpy(inp.scales).to(dev)
-        a, b = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        a, b = up(A), up(B)
         ws = torch.empty(w4.w4a16_lora_workspace_bytes(M, K, r), dtype=torch.uint8, device=dev)
-        eager = torch.empty((M, N), dtype=torch.float16, device=dev)
+        eager = torch.empty((M, N), dtype=dt, device=dev)
         w4.linear_lora(x, q, s, g, a, b, S, out=eager, workspace=ws, stream=st)
         runs.append((x, q, s, a, b, g, ws, eager, torch.empty_like(eager)))
     torch.cuda.synchronize()

@@ -135,14 +135,15 @@ def test_zp_all_eight_is_the_symmetric_linear_bitwise(dev, bf16):
         assert np.array_equal(y, lin), (M, K, N, g)
 
 
-def test_zp_deterministic_and_graph_replay(dev):
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_zp_deterministic_and_graph_replay(dev, act):
     """Two eager calls agree bit for bit; the call captured in a HIP graph on a
     stream that already holds the linear's workspaces replays to the same bits."""
     st = torch.cuda.Stream()
     runs = []
     for M, K, N, g in ((1, 5120, 2048, 128), (64, 1024, 1032, 32), (300, 2048, 1024, 64)):
-        case, inp, z = _inputs(M, K, N, g, 97, "f16")
-        x = torch.from_numpy(inp.x).to(dev)
+        case, inp, z = _inputs(M, K, N, g, 97, act)
+        x = _upload_x(inp.x, act == "bf16", dev)
         q = torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev)
         s = torch.from_numpy(inp.scales).to(dev)
         qz = torch.from_numpy(w4.pack_zeros(z)).to(dev)
