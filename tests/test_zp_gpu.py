@@ -117,6 +117,18 @@ def test_zp_prefill_full_shape_sampled(dev):
     check_parity(y[ms, ns], ref, "zero points prefill_up (sampled)")
 
 
+@pytest.mark.parametrize("M", [2, 20])
+def test_zp_largest_group_count(dev, M):
+    """1536 groups (K = 24576, g = 16), the most the call takes: the expand's t
+    tile in LDS is at its largest (49 KiB, plus the delta tile), for the decode
+    (M <= 16) and the prefill tile widths."""
+    K, N, g = 16 * 1536, 264, 16
+    case, inp, z = _inputs(M, K, N, g, 60 + M, "f16")
+    assert w4.w4a16_zp_workspace_bytes(M, K, N, g) > 0
+    y = _run(inp, z, g, dev, False)
+    _check(case, inp, z, y, "f16")
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_zp_all_eight_is_the_symmetric_linear_bitwise(dev, bf16):
     """Every zero point 8 makes the correction exactly zero: y equals the
