@@ -198,3 +198,26 @@ def test_lora_graph_capture_and_replay(dev, act):
         torch.cuda.synchronize()
         for i, (*_, eager, out) in enumerate(runs):
             assert torch.equal(out, eager), (i, rep)
+
+
+@pytest.mark.parametrize("M", [3, 20])
+def test_lora_and_zero_points_leave_memory_past_y_untouched(dev, M):
+    """y is a prefix of a larger buffer filled with a canary: after the LoRA and
+    the zero-point calls (ragged N = 136) everything past M*N is unchanged."""
+    K, N, g, r = 1040, 136, 16, 24
+    _, inp, A, B = _inputs(M, K, N, g, r, 99, "f16")
+    x = torch.from_numpy(inp.x).to(dev)
+    q = torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev)
+    s = torch.from_numpy(inp.scales).to(dev)
+    qz = torch.from_numpy(w4.pack_zeros(workloads.zero_points(inp.scales.shape[0], N, 5))).to(dev)
+    for call in ("lora", "zp"):
+        buf = torch.full((M * N + 4096,), 1234.0, dtype=torch.float16, device=dev)
+        out = buf[: M * N].view(M, N)
+        if call == "lora":
+            w4.linear_lora(x, q, s, g, torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
+                           S, out=out)
+        else:
+            w4.linear_zp(x, q, s, qz, g, out=out)
+        torch.cuda.synchronize()
+        assert bool((buf[M * N:] == 1234.0).all()), call
+        assert bool(torch.isfinite(out).all()), call
