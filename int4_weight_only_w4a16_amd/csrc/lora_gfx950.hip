@@ -10,7 +10,7 @@
 // storage order: A [r, K] (lora_A weight) and B [N, r] (lora_B weight), both
 // in the activation type, and a scaling s given as a number.
 //
-// Two kernels, both on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
+// The adapter runs two kernels on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
 //   lora_shrink_kernel  t = x . A^T as fp32 partial sums over S chunks of K,
 //                       one [Mp, r] slab per chunk (Mp = M rounded up to 16);
 //   lora_expand_kernel  sums the S slabs of a 16-row block in a fixed order,
