@@ -79,6 +79,8 @@ class Oracle:
         lib.oracle_linear_at.argtypes = [p, p, p, i64, i64, i64, i64, p, p, i64, p]
         i32 = ctypes.c_int
         lib.oracle_linear_ex.argtypes = [p, i32, i32, p, p, i64, i64, i64, i64, p]
+        lib.oracle_decode_act.argtypes = [p, i32, i64, p]
+        lib.oracle_decode_act.restype = ctypes.c_int
         lib.oracle_linear_at_ex.argtypes = [p, i32, i32, p, p, i64, i64, i64, i64, p, p, i64, p]
         lib.oracle_gate_up_silu.argtypes = [p, i32, p, p, i64, i64, i64, i64, p]
         f64 = ctypes.c_double
@@ -127,6 +129,27 @@ class Oracle:
         _check(self.lib.oracle_dequant(_ptr(qweight), _ptr(scales.view(np.uint16)), K, N,
                                        group_size, _ptr(out)), "dequant")
         return out
+
+    def decode_act(self, x: np.ndarray, act: str = "f16") -> np.ndarray:
+        """Activations (fp16 values, or bfloat16 bit patterns as uint16) -> float64,
+        decoded field by field by the oracle."""
+        xb = _act_bits(x, act)
+        out = np.empty(xb.shape, dtype=np.float64)
+        _check(self.lib.oracle_decode_act(_ptr(xb), _ACTS[act], xb.size, _ptr(out)),
+               "decode_act")
+        return out
+
+    def linear_dense(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+                     group_size: int, act: str = "f16") -> np.ndarray:
+        """y [M, N] float64 = x . W through numpy's float64 matmul, with W the
+        oracle's fp32 dequantised weight and x decoded by the oracle: the
+        definition with a library matmul as its product step (any summation
+        order, in fp64), for shapes too large for the triple loop."""
+        xd = self.decode_act(x, act)
+        W = self.dequant(qweight, scales, group_size).astype(np.float64)
+        if xd.shape[1] != W.shape[0]:
+            raise ValueError("oracle linear_dense: x and qweight disagree on K")
+        return np.matmul(xd, W)
 
     def linear(self, x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
                group_size: int, act: str = "f16", absval: bool = False) -> np.ndarray:
@@ -323,6 +346,14 @@ def unpack(qweight):
 
 def dequant(qweight, scales, group_size):
     return default().dequant(qweight, scales, group_size)
+
+
+def decode_act(x, act="f16"):
+    return default().decode_act(x, act)
+
+
+def linear_dense(x, qweight, scales, group_size, act="f16"):
+    return default().linear_dense(x, qweight, scales, group_size, act)
 
 
 def linear(x, qweight, scales, group_size, act="f16", absval=False):

@@ -80,6 +80,11 @@
  * packed along N, nibble j of word c = column 8c+j, low bits first, each
  * nibble the zero point itself (v1's stored z - 1 becomes z by adding one
  * before the call).  With every zero point 8 it is the symmetric definition.
+ * For shapes too large for the triple loop (the 2048-row prefill case in
+ * full), oracle.linear_dense (Python) takes the same fp32 dequantised W and
+ * the activations decoded here (oracle_decode_act) and forms x . W with
+ * numpy's float64 matmul, a library primitive: the same sums up to the order
+ * of fp64 rounding, pinned against the triple loop.
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math).  OpenMP only
  * splits rows m and column blocks of n, never the sum over k.
  */
@@ -211,6 +216,15 @@ int oracle_dequant(const int32_t *qweight, const uint16_t *scales, int64_t K, in
     for (int64_t k = 0; k < K; ++k)
         for (int64_t n = 0; n < N; ++n)
             W[k * N + n] = weight_at(qweight, scales, N, g, k, n);
+    return OR_OK;
+}
+
+/* out[i] <- the value of activation bits x[i] (act 0 fp16, 1 bfloat16), for
+ * callers that take the product with a library matmul (oracle.linear_dense). */
+int oracle_decode_act(const uint16_t *x, int act, int64_t n, double *out) {
+    if (n < 0 || (act != 0 && act != 1) || (n > 0 && (!x || !out))) return OR_ERR_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = act_to_double(x[i], act);
     return OR_OK;
 }
 

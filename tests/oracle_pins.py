@@ -26,6 +26,10 @@ when it disagrees with:
     point is 8, numpy's matmul on W built from codes and zero points, a
     hand-derived word 0x76543210 (zero point n at column n), and y == 0
     exactly when every code equals its zero point.
+  - for the dense form (numpy's float64 matmul as the product step), the
+    oracle's decoding of every fp16 and bfloat16 pattern against numpy's, and
+    agreement with the triple loop within fp64 reordering (bit for bit on
+    exact-arithmetic inputs).
 ``tests/test_oracle_mutants.py`` plants plausible mistakes in copies of the
 oracle source and checks that every one of them trips at least one pin.
 """
@@ -609,6 +613,51 @@ def pin_zp_sampled_matches_full(o):
     for x, act in ((xh, "f16"), (xb, "bf16")):
         full = o.linear_zp(x, q, scales, qz, g, act=act)
         assert np.array_equal(o.linear_zp_at(x, q, scales, qz, g, ms, ns, act=act), full[ms, ns])
+
+
+
+# --- the dense form (a library matmul as the product step) ------------------------
+
+def pin_decode_act_all_patterns(o):
+    """The oracle's field-by-field decoding of every fp16 and every bfloat16
+    pattern against numpy's own (fp16 -> float64; bfloat16 as a float32's top half)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    for act, ref in (("f16", bits.view(np.float16).astype(np.float64)),
+                     ("bf16", _bf16_value(bits))):
+        x = bits.view(np.float16) if act == "f16" else bits
+        got = o.decode_act(x, act)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan), act
+        assert np.array_equal(got[~nan], ref[~nan]), act
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), act
+
+
+def pin_dense_matches_triple_loop(o):
+    """linear_dense (numpy's float64 matmul over the oracle's W and decoded x)
+    agrees with the k-ascending triple loop to within fp64 reordering, K 2^-52
+    of the magnitude sum, for every group size, ragged K and both activation
+    types; and bit for bit where every partial sum is exact (integer x, power-
+    of-two scales)."""
+    rng = np.random.default_rng(45)
+    for M, K, N in ((3, 272, 40), (17, 1040, 64), (2, 4096, 24)):
+        for g in GROUPS:
+            G = 1 if g == -1 else -(-K // g)
+            codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+            scales = rng.uniform(1e-3, 2e-2, size=(G, N)).astype(np.float16)
+            q = o.pack(codes)
+            xh = rng.standard_normal((M, K)).astype(np.float16)
+            xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            for x, act in ((xh, "f16"), (xb, "bf16")):
+                ref = o.linear(x, q, scales, g, act=act)
+                mag = o.linear(x, q, scales, g, act=act, absval=True)
+                d = np.abs(o.linear_dense(x, q, scales, g, act=act) - ref)
+                assert np.all(d <= K * 2.0 ** -52 * mag + 1e-300), (M, K, N, g, act)
+    M, K, N = 4, 2048, 32
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    scales = np.exp2(rng.integers(-4, -1, size=(K // 64, N)).astype(np.float64)).astype(np.float16)
+    x = rng.integers(-4, 5, size=(M, K)).astype(np.float16)
+    q = o.pack(codes)
+    assert np.array_equal(o.linear_dense(x, q, scales, 64), o.linear(x, q, scales, 64))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

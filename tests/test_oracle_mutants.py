@@ -43,6 +43,7 @@ MUTANTS = {
                      "return ((word >> (4 * (unsigned)(n % 8))) & 0xFu) + 1u;"),
     "zp_added": ("(float)(q - z)", "(float)(q + z - 16)"),
     "zp_row_of_k": ("zero_at(qzeros, N, gi, n)", "zero_at(qzeros, N, k / 8 % (gi + 1), n)"),
+    "decode_act_as_half": ("out[i] = act_to_double(x[i], act);", "out[i] = act_to_double(x[i], 0);"),
     "lora_last_rank_dropped": ("for (int64_t j = 0; j < r; ++j)\n        acc +=",
                                "for (int64_t j = 0; j + 1 < r; ++j)\n        acc +="),
 }
