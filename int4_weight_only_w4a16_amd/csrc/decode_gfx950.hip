@@ -335,6 +335,15 @@ __device__ __forceinline__ void decode_units(
 // Dynamic LDS: the staged activations (XLDS) follow the static arrays.
 extern __shared__ __attribute__((aligned(16))) unsigned char decode_dyn_lds[];
 
+// Static LDS of the two kernels (bytes), for the budget check at the launch
+// parameters below: the tiles kernel's wave partials, and the stream-K
+// kernel's partial blocks (two segments per wave plus the -0.0 block) with
+// each wave's tile bounds.
+constexpr size_t tiles_static_lds(int waves) { return (size_t)waves * kNW * 64 * sizeof(f4); }
+constexpr size_t streamk_static_lds(int waves) {
+    return (size_t)(2 * waves + 1) * 256 * sizeof(f4) + (size_t)waves * 2 * sizeof(int);
+}
+
 // Tiles kernel: one workgroup per column tile, its waves split K.
 template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU>
 __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
@@ -342,6 +351,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
     int group_steps) {
     __shared__ f4 red[WAVES][kNW][64];
+    static_assert(sizeof(red) == tiles_static_lds(WAVES), "tiles kernel LDS layout");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -456,6 +466,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     constexpr int kZeroBlock = 2 * WAVES;
     __shared__ f4 red[(2 * WAVES + 1) * 256];
     __shared__ int wtile[WAVES][2];              // each wave's first and last tile
+    static_assert(sizeof(red) + sizeof(wtile) == streamk_static_lds(WAVES),
+                  "stream-K kernel LDS layout");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -680,6 +692,16 @@ int decode_streamk_grid(const LinearArgs &a, int num_cus) {
 
 // Activations are staged in LDS when they fit in this many bytes.
 constexpr size_t kXStageMax = 64 * 1024;
+
+// Every shipped instantiation fits a gfx950 workgroup's 160 KiB of LDS with
+// the largest staging area (plus its zero chunk), so the launch-time check
+// against the device's limit (stage_fits) can never be what keeps a launch
+// valid; a larger wave count or staging area fails here, at compile time.
+constexpr size_t kGfx950LdsPerWorkgroup = 160 * 1024;
+static_assert(streamk_static_lds(kDecWaves) + kXStageMax + 16 <= kGfx950LdsPerWorkgroup,
+              "stream-K decode: static LDS plus staged activations exceed 160 KiB");
+static_assert(tiles_static_lds(kDecWaves) + kXStageMax + 16 <= kGfx950LdsPerWorkgroup,
+              "tiles decode: static LDS plus staged activations exceed 160 KiB");
 
 // Static LDS of a kernel, read once from its attributes.
 static size_t static_lds(const void *kernel) {
