@@ -66,9 +66,11 @@ def check_parity_bf16(y_gpu: np.ndarray, y_ref: np.ndarray, mag: np.ndarray, K: 
 
 # Merged gate/up with SiLU * mul: the kernels form the gate and up sums g, u
 # as the linear does (error at most eps * sum|x||w| per column), take
-# silu(g) * u in fp32 (|silu'| <= 1.1) and round once (half an ulp, r):
-#   |y - y_ref| <= r |y_ref| + 1.02 (1.1 |u| eps A_g + |silu(g)| eps A_u
-#                                    + 1.1 eps^2 A_g A_u) + 4e-7 |y_ref|
+# silu(g) * u in fp32 (|silu'| <= 1.1) and round once (half an ulp: r |y| for
+# normal outputs, and at most h = half the spacing of the output type's
+# subnormals, 2^-25 for fp16 and 2^-134 for bfloat16, below its normal range):
+#   |y - y_ref| <= r |y_ref| + h + 1.02 (1.1 |u| eps A_g + |silu(g)| eps A_u
+#                                        + 1.1 eps^2 A_g A_u) + 4e-7 |y_ref|
 # with A_g, A_u the oracle's magnitude sums of the two columns; plus the mean
 # relative error of the linear's bar.
 def _silu(z):
@@ -84,12 +86,14 @@ def check_gate_up(y, ref, lin, mag, mag0, K, bf16, what):
         eps_g = r + K * 2.0 ** -24 + 35 * K * 2.0 ** -24 * mag0[:, 0::2] / np.maximum(a_g, 1e-300)
         eps_u = r + K * 2.0 ** -24 + 35 * K * 2.0 ** -24 * mag0[:, 1::2] / np.maximum(a_u, 1e-300)
         mean_bar = 2.0 ** -8
+        h = 2.0 ** -134
     else:
         r = 2.0 ** -11
         eps_g = eps_u = 2.0 ** -11 + K * 2.0 ** -24
         mean_bar = 1e-3
+        h = 2.0 ** -25
     dg, du = eps_g * a_g, eps_u * a_u
-    bound = (r * np.abs(ref) + 1.02 * (1.1 * np.abs(u) * dg + np.abs(_silu(g)) * du + 1.1 * dg * du)
+    bound = (r * np.abs(ref) + h + 1.02 * (1.1 * np.abs(u) * dg + np.abs(_silu(g)) * du + 1.1 * dg * du)
              + 4e-7 * np.abs(ref) + 1e-30)
     d = np.abs(y - ref)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"

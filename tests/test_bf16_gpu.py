@@ -113,3 +113,57 @@ def test_bf16_rejects_mixed_dtypes(dev):
     x = torch.zeros((1, K), dtype=torch.bfloat16, device=dev)
     with pytest.raises(ValueError):
         w4.linear(x, q, s, -1, out=torch.empty((1, N), dtype=torch.float16, device=dev))
+
+
+def test_bf16_decode_tiles_kernel_path(dev):
+    """More than 8 column tiles of 64 per CU: the bfloat16 decode runs one
+    workgroup per tile (the tiles kernel), in all three of its weight forms:
+    dequantised before the matrix core (g = 16), offset folded per group with
+    one step per group (g = 32) and over several steps (g = 64)."""
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 8 * 64 * n_cus + 8
+    for M, K, g in ((1, 64, 32), (5, 64, 16), (3, 128, 64)):
+        case = workloads.Case(f"bf16_tiles_{M}_{g}", M, K, N, g, 64 + M, scales="loguniform")
+        inp, q_o, x, q, s = _upload(case, dev)
+        y_ref = oracle.linear(inp.x, q_o, inp.scales, g, act="bf16")
+        mag = oracle.linear(inp.x, q_o, inp.scales, g, act="bf16", absval=True)
+        mag0 = oracle.linear(inp.x, np.zeros_like(q_o), inp.scales, g, act="bf16", absval=True)
+        y = bf16_to_float(_run(x, q, s, g, DEC))
+        check_parity_bf16(y, y_ref, mag, K, f"bf16 tiles path M={M} g={g}", mag0)
+
+
+def test_bf16_graph_capture_on_fresh_stream(dev):
+    """bfloat16 decode and prefill captured on a stream that has no workspace yet
+    (the decode then runs its tiles kernel, the prefill whole tiles), replayed
+    several times with eager work in between; every replay within the bar."""
+    cases = [workloads.Case("bf16_g_dec", 4, 5120, 2048, 128, 66, scales="loguniform"),
+             workloads.Case("bf16_g_dec32", 1, 2048, 1032, 32, 67, scales="loguniform"),
+             workloads.Case("bf16_g_pre", 96, 1024, 1032, 64, 68, scales="loguniform")]
+    prepared = []
+    for c in cases:
+        inp, q_o, x, q, s = _upload(c, dev)
+        ref = oracle.linear(inp.x, q_o, inp.scales, c.group_size, act="bf16")
+        mag = oracle.linear(inp.x, q_o, inp.scales, c.group_size, act="bf16", absval=True)
+        mag0 = oracle.linear(inp.x, np.zeros_like(q_o), inp.scales, c.group_size, act="bf16",
+                             absval=True)
+        prepared.append((c, x, q, s, ref, mag, mag0))
+    st = torch.cuda.Stream()
+    outs = [torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev) for c, *_ in prepared]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        for (c, x, q, s, *_), y in zip(prepared, outs):
+            w4.w4a16_linear_bf16(x, q, s, y, c.M, c.K, c.N, c.group_size, st)
+    first = None
+    for rep in range(3):
+        for y in outs:
+            y.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [y.cpu().view(torch.int16).numpy().copy() for y in outs]
+        for (c, x, q, s, ref, mag, mag0), bits in zip(prepared, got):
+            check_parity_bf16(bf16_to_float(bits), ref, mag, c.K, f"{c.name} replay {rep}", mag0)
+        if first is None:
+            first = got
+        else:
+            assert all(np.array_equal(a, b) for a, b in zip(first, got)), rep

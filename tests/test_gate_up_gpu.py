@@ -104,3 +104,72 @@ def test_gate_up_silu_zero_gate_gives_exact_zero(dev):
         y = w4.gate_up_silu(x, q, s, g, kernel=k)
         torch.cuda.synchronize()
         assert y.shape == (M, N // 2) and torch.count_nonzero(y).item() == 0, (M, k)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp16", "bf16"])
+def test_gate_up_decode_tiles_kernel_path(dev, bf16):
+    """More than 8 column tiles of 64 per CU (merged width N > 8 * 64 * CUs):
+    the SiLU * mul epilogue of the decode tiles kernel, fp16 and bfloat16."""
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 8 * 64 * n_cus + 16
+    act = "bf16" if bf16 else "f16"
+    for M, K, g in ((1, 64, 32), (6, 64, 16), (3, 128, 64)):
+        case, inp = _case(M, K, N, g, 92 + M, bf16)
+        q_o = oracle.pack(inp.codes)
+        q = torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev)
+        s = torch.from_numpy(inp.scales).to(dev)
+        ref = oracle.gate_up_silu(inp.x, q_o, inp.scales, g, act=act)
+        lin = oracle.linear(inp.x, q_o, inp.scales, g, act=act)
+        mag = oracle.linear(inp.x, q_o, inp.scales, g, act=act, absval=True)
+        mag0 = oracle.linear(inp.x, np.zeros_like(q_o), inp.scales, g, act=act, absval=True)
+        y = _run(inp, q, s, g, DEC, bf16, dev)
+        check_gate_up(y, ref, lin, mag, mag0, K, bf16, f"gate_up tiles M={M} g={g} {act}")
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp16", "bf16"])
+def test_gate_up_graph_capture_on_fresh_stream(dev, bf16):
+    """Merged gate/up calls captured on a stream with no workspace yet (decode:
+    the tiles kernel; prefill: whole tiles) and replayed several times; every
+    replay within the bar and equal to the first."""
+    act = "bf16" if bf16 else "f16"
+    prepared = []
+    for M, K, N, g in ((4, 5120, 2048, 128), (1, 2048, 1040, 32), (80, 1024, 1056, 64),
+                       (300, 1024, 1056, 32)):
+        case, inp = _case(M, K, N, g, 95 + M, bf16)
+        q_o = oracle.pack(inp.codes)
+        if bf16:
+            x = torch.from_numpy(inp.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            x = torch.from_numpy(inp.x).to(dev)
+        prepared.append((case, x, torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev),
+                         torch.from_numpy(inp.scales).to(dev),
+                         oracle.gate_up_silu(inp.x, q_o, inp.scales, g, act=act),
+                         oracle.linear(inp.x, q_o, inp.scales, g, act=act),
+                         oracle.linear(inp.x, q_o, inp.scales, g, act=act, absval=True),
+                         oracle.linear(inp.x, np.zeros_like(q_o), inp.scales, g, act=act,
+                                       absval=True)))
+    st = torch.cuda.Stream()
+    dt = torch.bfloat16 if bf16 else torch.float16
+    outs = [torch.empty((c.M, c.N // 2), dtype=dt, device=dev) for c, *_ in prepared]
+    call = w4.w4a16_gate_up_silu_bf16 if bf16 else w4.w4a16_gate_up_silu
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        for (c, x, q, s, *_), y in zip(prepared, outs):
+            call(x, q, s, y, c.M, c.K, c.N, c.group_size, st)
+    first = None
+    for rep in range(3):
+        for y in outs:
+            y.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = []
+        for (c, x, q, s, ref, lin, mag, mag0), y in zip(prepared, outs):
+            h = y.cpu()
+            v = bf16_to_float(h.view(torch.int16).numpy()) if bf16 else h.numpy().astype(np.float64)
+            check_gate_up(v, ref, lin, mag, mag0, c.K, bf16, f"{c.name} {act} replay {rep}")
+            got.append(v)
+        if first is None:
+            first = got
+        else:
+            assert all(np.array_equal(a, b) for a, b in zip(first, got)), rep

@@ -86,7 +86,7 @@ CASES = [
     (4, 1024, 264, 32),
     (16, 2048, 1032, 16),
     (3, 1040, 136, 16),             # K % 32 == 16, a partial rank block
-    (2, 1000 + 24, 72, 512),        # a partial last group (K % g != 0)
+    (2, 1024, 72, 512),             # two whole groups of 512 (one wave per row and group)
     (17, 1024, 520, -1),            # one group: rank 1 padded to 8
     (100, 1024, 264, 64),
     (129, 512, 264, 128),
@@ -99,6 +99,32 @@ CASES = [
 @pytest.mark.parametrize("M,K,N,g", CASES)
 def test_zp_parity(dev, M, K, N, g, act):
     case, inp, z = _inputs(M, K, N, g, 80 + M, act)
+    y = _run(inp, z, g, dev, act == "bf16")
+    _check(case, inp, z, y, act)
+
+
+# A short last group (K % g != 0: G = ceil(K / g), the last group holds K - (G-1) g
+# rows), on both ways the group sums are taken: one thread per row and group
+# (g <= 256) and one wave per row and group (g > 256), at decode and prefill
+# widths (M <= 16, 17..128, > 128).
+PARTIAL_GROUP_CASES = [
+    # M, K, N, g              last group
+    (3, 272, 136, 256),     # 16 of 256, thread per group
+    (20, 400, 264, 64),     # 16 of 64
+    (130, 1040, 264, 128),  # 16 of 128
+    (2, 1040, 72, 1024),    # 16 of 1024, wave per group
+    (40, 1552, 264, 512),   # 16 of 512
+    (200, 2064, 264, 1024), # 16 of 1024
+    (9, 1104, 136, 512),    # 80 of 512
+]
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("M,K,N,g", PARTIAL_GROUP_CASES)
+def test_zp_partial_last_group(dev, M, K, N, g, act):
+    assert K % g != 0
+    case, inp, z = _inputs(M, K, N, g, 180 + M, act)
+    assert case.G == -(-K // g)
     y = _run(inp, z, g, dev, act == "bf16")
     _check(case, inp, z, y, act)
 
