@@ -33,8 +33,12 @@
  *   - The library keeps no copy of the weights (dense, dequantised or
  *     repacked).  Its only state is a per-device cache of the device's
  *     architecture and up to two workspaces per (device, stream), each
- *     allocated and zero-filled on the first call on that stream that needs
- *     it and kept until the process exits:
+ *     allocated (hipMalloc) and zero-filled on the first call on that stream
+ *     that needs it and kept until w4a16_stream_release(stream) frees them
+ *     or the process exits (a caller that creates and destroys streams
+ *     releases each one before destroying it, else its workspaces stay
+ *     held).  They exist because a split-K reduction across workgroups needs
+ *     device scratch for its partial sums:
  *       decode: 3 MiB on a 256-CU device (per CU: 16x32 64-bit exchange
  *         slots, left zeroed by every launch, and two 16x64 fp32 partial
  *         tiles, written before they are read);
@@ -45,7 +49,10 @@
  *     A call on a stream that is being captured into a graph and has no
  *     workspace yet allocates nothing and runs a kernel that needs none.
  *     Calls on one stream share its workspaces in stream order; calls on
- *     different streams never share one.  Thread-safe and reentrant.
+ *     different streams never share one.  A graph captured on a stream keeps
+ *     that stream's workspaces: replay it in that stream's order (on the
+ *     stream itself, or while nothing else uses that stream's workspaces),
+ *     never beside eager calls on that stream.  Thread-safe and reentrant.
  *   - Device calls are asynchronous on the given stream (a hipStream_t; 0 is
  *     the null stream); results are valid once the stream is synchronised.
  *     No call synchronises the device and nothing is printed.
@@ -76,8 +83,9 @@ typedef enum {
     W4A16_ERR_LAUNCH = 7,  /* the kernel launch reported an error */
     W4A16_ERR_KERNEL = 8,  /* w4a16_linear_ex: the requested kernel cannot take this M */
     W4A16_ERR_RANK = 9,    /* LoRA rank not a multiple of 8 in [8, W4A16_LORA_MAX_RANK] */
-    W4A16_ERR_WORKSPACE = 10  /* workspace smaller than w4a16_lora_workspace_bytes or
+    W4A16_ERR_WORKSPACE = 10, /* workspace smaller than w4a16_lora_workspace_bytes or
                                  w4a16_zp_workspace_bytes gives */
+    W4A16_ERR_CAPTURE = 11    /* w4a16_stream_release: the stream is being captured */
 } w4a16_status;
 
 /* Largest M the small-batch (decode) kernel takes; larger M runs the MFMA
@@ -244,6 +252,14 @@ int w4a16_linear_zp_bf16(const void *x, const int32_t *qweight, const void *scal
  * up to 16, Gp] and the correction matrix C^T [N, Gp] in the activation type,
  * Gp = G rounded up to 8.  0 for M <= 0 or arguments it rejects. */
 size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
+/* Frees the workspaces the library holds for `stream` on the current device
+ * (a hipStream_t, 0 = null stream), after waiting for the work queued on it.
+ * The next call on that stream creates them again.  Returns W4A16_OK (also
+ * when none are held), W4A16_ERR_CAPTURE while the stream is being captured
+ * (nothing is freed), W4A16_ERR_DEVICE without a usable device, or
+ * W4A16_ERR_LAUNCH when waiting for the stream fails. */
+int w4a16_stream_release(void *stream);
 
 /* Host-side packing into the GPTQ_V2 layout (native int32 qweight, "GPTQ-Pro"
  * README, "Runtime contract"):

@@ -9,7 +9,7 @@ Names match the C ABI in ``include/w4a16.h``:
   w4a16_linear, w4a16_linear_ex, w4a16_linear_bf16, w4a16_linear_bf16_ex,
   w4a16_gate_up_silu(_ex, _bf16, _bf16_ex), w4a16_linear_lora(_bf16),
   w4a16_lora_workspace_bytes, w4a16_linear_zp(_bf16), w4a16_zp_workspace_bytes,
-  pack_gptq_v2, unpack_gptq_v2,
+  w4a16_stream_release, pack_gptq_v2, unpack_gptq_v2,
   w4a16_status_string, and the measurement aid w4a16_read_probe
 plus ``linear``, ``gate_up_silu``, ``linear_lora`` and ``linear_zp`` (allocate
 y, and a workspace, with torch, then call the entry point of x's dtype).
@@ -37,6 +37,7 @@ W4A16_ERR_LAUNCH = 7
 W4A16_ERR_KERNEL = 8
 W4A16_ERR_RANK = 9
 W4A16_ERR_WORKSPACE = 10
+W4A16_ERR_CAPTURE = 11
 W4A16_LORA_MAX_RANK = 1024
 
 W4A16_DECODE_MAX_M = 16
@@ -48,8 +49,8 @@ EXPORTS = ("w4a16_linear", "w4a16_linear_ex", "w4a16_linear_bf16", "w4a16_linear
            "w4a16_gate_up_silu", "w4a16_gate_up_silu_ex", "w4a16_gate_up_silu_bf16",
            "w4a16_gate_up_silu_bf16_ex", "w4a16_linear_lora", "w4a16_linear_lora_bf16",
            "w4a16_lora_workspace_bytes", "w4a16_linear_zp", "w4a16_linear_zp_bf16",
-           "w4a16_zp_workspace_bytes", "pack_gptq_v2", "unpack_gptq_v2", "w4a16_read_probe",
-           "w4a16_status_string")
+           "w4a16_zp_workspace_bytes", "w4a16_stream_release", "pack_gptq_v2", "unpack_gptq_v2",
+           "w4a16_read_probe", "w4a16_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -96,6 +97,8 @@ def load_library() -> ctypes.CDLL:
         getattr(lib, name).restype = i32
     lib.w4a16_zp_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.w4a16_zp_workspace_bytes.restype = sz
+    lib.w4a16_stream_release.argtypes = [p]
+    lib.w4a16_stream_release.restype = i32
     lib.pack_gptq_v2.argtypes = [p, p, i64, i64]
     lib.pack_gptq_v2.restype = i32
     lib.unpack_gptq_v2.argtypes = [p, p, i64, i64]
@@ -128,6 +131,15 @@ def _stream_handle(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def w4a16_stream_release(stream=None) -> None:
+    """Free the workspaces the library holds for `stream` (torch stream, raw
+    handle, or None for the current stream) on the current device, after the
+    stream's queued work; raises W4A16Error on a nonzero status."""
+    st = load_library().w4a16_stream_release(_stream_handle(stream))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_stream_release")
 
 
 def w4a16_linear_ex(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,

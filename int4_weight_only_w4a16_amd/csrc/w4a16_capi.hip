@@ -78,9 +78,11 @@ int usable_device(int *num_cus, size_t *max_lds) {
 
 // Kernel workspaces, one per (device, stream, kind): calls on one stream run
 // in stream order and calls on different streams use different workspaces,
-// so the kernels never share one concurrently.  Created on the first call on
-// a stream that needs it (not while the stream is being captured into a
-// graph), zero-filled in stream order, kept until the process exits.
+// so eager calls never share one concurrently (a graph captured on a stream
+// keeps using that stream's workspace wherever it is replayed).  Created on
+// the first call on a stream that needs it (not while the stream is being
+// captured into a graph), zero-filled in stream order, kept until
+// w4a16_stream_release or the end of the process.
 //   kind 0: decode stream-K (exchange slots and partial tiles, 3 MiB)
 //   kind 1: prefill split tail (one 256 x 256 fp32 partial per CU, 64 MiB)
 std::mutex g_ws_mu;
@@ -109,7 +111,38 @@ void *stream_workspace(int dev, hipStream_t stream, int kind, size_t bytes) {
     return p;
 }
 
+// Frees the workspaces held for (dev, stream) after the stream has finished
+// the work queued on it.
+int release_stream_workspaces(int dev, hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    const uintptr_t key = reinterpret_cast<uintptr_t>(stream);
+    bool synced = false;
+    for (auto it = g_ws.begin(); it != g_ws.end();) {
+        if (std::get<0>(it->first) != dev || std::get<1>(it->first) != key) {
+            ++it;
+            continue;
+        }
+        if (!synced) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return W4A16_ERR_LAUNCH;
+            synced = true;
+        }
+        (void)hipFree(it->second.first);
+        it = g_ws.erase(it);
+    }
+    return W4A16_OK;
+}
+
 }  // namespace
+
+extern "C" int w4a16_stream_release(void *stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W4A16_ERR_DEVICE;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) return W4A16_ERR_DEVICE;
+    if (cap != hipStreamCaptureStatusNone) return W4A16_ERR_CAPTURE;
+    return release_stream_workspaces(dev, s);
+}
 
 // One linear call, fp16 or bfloat16 (bf16) activations and outputs; silu:
 // the merged gate/up projection (N % 16 == 0, y is [M, N/2]).
@@ -355,6 +388,7 @@ extern "C" const char *w4a16_status_string(int status) {
         case W4A16_ERR_KERNEL: return "requested kernel cannot take this M";
         case W4A16_ERR_RANK: return "LoRA rank must be a multiple of 8 in [8, 1024]";
         case W4A16_ERR_WORKSPACE: return "workspace smaller than the size its _workspace_bytes call gives";
+        case W4A16_ERR_CAPTURE: return "stream is being captured into a graph";
         default: return "unknown status";
     }
 }

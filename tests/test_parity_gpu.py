@@ -99,6 +99,18 @@ def test_down_small_batch_full(dev, M):
     _full_case(workloads.down_small_batch(M), dev, kernels=(AUTO, PRE))
 
 
+def test_prefill_up_full(dev):
+    """The prefill up-projection (M=2048, K=5120, N=17408, g=128) element by element
+    over all 35.65 M outputs, against the oracle's dense form (its dequantised W
+    and decoded x through numpy's float64 matmul; pinned against the triple loop)."""
+    case = workloads.prefill_up()
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    y = _run(inp, q_dev, s_dev, case.group_size, dev)
+    y_ref = oracle.linear_dense(inp.x, q_o, inp.scales, case.group_size)
+    check_parity(y, y_ref, f"{case.name} (every output)")
+
+
 def test_prefill_up_sampled(dev):
     _sampled_case(workloads.prefill_up(), dev)
 
@@ -302,25 +314,81 @@ def test_two_streams_concurrently(dev):
         check_parity(y.cpu().numpy(), y_ref, c.name)
 
 
-def test_no_device_allocation(dev):
+def _free_bytes():
+    torch.cuda.synchronize()
+    return torch.cuda.mem_get_info()[0]
+
+
+def test_workspace_allocation_stated_and_released(dev):
+    """The library's only device allocations, on a stream with none yet: the
+    first decode call that splits tiles across workgroups creates the stream's
+    decode workspace (12 KiB per CU), the first prefill call that splits K its
+    prefill workspace (256 KiB per CU); further calls allocate nothing; and
+    w4a16_stream_release frees both, leaving free memory where it started."""
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
     case = workloads.Case("alloc", 64, 5120, 5120, 128, 23)
     inp = workloads.generate(case)
     q_o, q_dev, s_dev = _weights(case, inp, dev)
     x = torch.from_numpy(inp.x).to(dev)
     x16 = x[:16].contiguous()
     y = torch.empty((64, 5120), dtype=torch.float16, device=dev)
-    # the first decode call on a stream creates that stream's small workspace
-    w4.w4a16_linear_ex(x16, q_dev, s_dev, y, 16, 5120, 5120, 128, None, DEC)
-    for k in (PRE, AUTO):
-        w4.w4a16_linear_ex(x, q_dev, s_dev, y, 64, 5120, 5120, 128, None, k)
-    torch.cuda.synchronize()
-    free0, _ = torch.cuda.mem_get_info()
+    st = torch.cuda.Stream()
+    w4.w4a16_stream_release(st)        # pooled streams may hold workspaces of earlier tests
+    free0 = _free_bytes()
+    w4.w4a16_linear_ex(x16, q_dev, s_dev, y, 16, 5120, 5120, 128, st, DEC)
+    free1 = _free_bytes()
+    assert free0 - free1 >= n_cus * 12 * 1024, (free0, free1)
+    w4.w4a16_linear_ex(x, q_dev, s_dev, y, 64, 5120, 5120, 128, st, PRE)   # split K
+    free2 = _free_bytes()
+    assert free1 - free2 >= n_cus * 256 * 1024, (free1, free2)
     for _ in range(5):
-        w4.w4a16_linear_ex(x16, q_dev, s_dev, y, 16, 5120, 5120, 128, None, DEC)
-        w4.w4a16_linear_ex(x, q_dev, s_dev, y, 64, 5120, 5120, 128, None, PRE)
+        w4.w4a16_linear_ex(x16, q_dev, s_dev, y, 16, 5120, 5120, 128, st, DEC)
+        w4.w4a16_linear_ex(x, q_dev, s_dev, y, 64, 5120, 5120, 128, st, PRE)
+        w4.w4a16_linear_ex(x, q_dev, s_dev, y, 64, 5120, 5120, 128, st, AUTO)
+    assert _free_bytes() == free2
+    w4.w4a16_stream_release(st)
+    assert _free_bytes() == free0
+    y_ref = oracle.linear(inp.x, q_o, inp.scales, 128)
+    w4.w4a16_linear_ex(x, q_dev, s_dev, y, 64, 5120, 5120, 128, st, AUTO)   # recreated
     torch.cuda.synchronize()
-    free1, _ = torch.cuda.mem_get_info()
-    assert free1 == free0
+    check_parity(y.cpu().numpy(), y_ref, "after release")
+    w4.w4a16_stream_release(st)
+
+
+def test_stream_release_cycles_leave_memory_unchanged(dev):
+    """32 cycles of a new stream, decode and prefill calls on it, release and
+    stream destruction leave the device's free memory unchanged."""
+    case = workloads.Case("cycles", 64, 2048, 4096, 64, 24)
+    inp = workloads.generate(case)
+    _, q_dev, s_dev = _weights(case, inp, dev)
+    x = torch.from_numpy(inp.x).to(dev)
+    x4 = x[:4].contiguous()
+    y = torch.empty((64, 4096), dtype=torch.float16, device=dev)
+
+    def cycle():
+        st = torch.cuda.Stream()
+        w4.w4a16_linear(x4, q_dev, s_dev, y, 4, 2048, 4096, 64, st)
+        w4.w4a16_linear(x, q_dev, s_dev, y, 64, 2048, 4096, 64, st)
+        w4.w4a16_stream_release(st)
+        del st
+
+    # torch hands out streams from a pool of 32 per device: one pass over the
+    # pool first releases whatever earlier work left on those streams
+    for _ in range(40):
+        cycle()
+    free0 = _free_bytes()
+    for _ in range(32):
+        cycle()
+    assert _free_bytes() == free0
+
+
+def test_stream_release_refused_under_capture(dev):
+    st = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        with pytest.raises(w4.W4A16Error) as e:
+            w4.w4a16_stream_release(st)
+    assert e.value.status == w4.W4A16_ERR_CAPTURE
 
 
 def test_decode_tiles_kernel_path(dev):
