@@ -85,7 +85,9 @@ typedef enum {
     W4A16_ERR_RANK = 9,    /* LoRA rank not a multiple of 8 in [8, W4A16_LORA_MAX_RANK] */
     W4A16_ERR_WORKSPACE = 10, /* workspace smaller than w4a16_lora_workspace_bytes or
                                  w4a16_zp_workspace_bytes gives */
-    W4A16_ERR_CAPTURE = 11    /* w4a16_stream_release: the stream is being captured */
+    W4A16_ERR_CAPTURE = 11,   /* w4a16_stream_release: the stream is being captured */
+    W4A16_ERR_SCRATCH = 12    /* w4a16_linear_noalloc: the device has more CUs than its
+                                 scratch covers */
 } w4a16_status;
 
 /* Largest M the small-batch (decode) kernel takes; larger M runs the MFMA
@@ -104,6 +106,23 @@ typedef enum {
  * prefill kernel.  Returns a w4a16_status. */
 int w4a16_linear(const void *x, const int32_t *qweight, const void *scales, void *y,
                  int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream);
+
+/* w4a16_linear for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, layouts, kernels and errors as w4a16_linear (fp16), plus
+ * W4A16_ERR_SCRATCH on a device with more than 320 CUs.  It calls no
+ * allocating routine: the split-K scratch lives in one file-scope device
+ * array of 20,709,376 bytes (the decode workspace laid out for 320
+ * workgroups, 3.75 MiB, and 64 prefill partial tiles of 256 KiB), which
+ * every device the library runs on holds until the process ends.  Prefill
+ * plans that would need more than 64 partial tiles split K into fewer chunks
+ * (the result stays within the same bar; its last bits can differ from
+ * w4a16_linear's for such shapes).  Every call on a device shares that
+ * device's array: calls that overlap in time on one device (two streams, or
+ * a graph replayed beside eager calls) race and give wrong results; calls in
+ * one stream's order do not.  Graph-capturable from the first call. */
+int w4a16_linear_noalloc(const void *x, const int32_t *qweight, const void *scales, void *y,
+                         int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream);
 
 /* Kernel selectors for w4a16_linear_ex. */
 #define W4A16_KERNEL_AUTO 0     /* same choice as w4a16_linear */

@@ -6,7 +6,8 @@ streams.  There is no fallback: if the library is missing or the device is
 not a gfx950, calls raise.
 
 Names match the C ABI in ``include/w4a16.h``:
-  w4a16_linear, w4a16_linear_ex, w4a16_linear_bf16, w4a16_linear_bf16_ex,
+  w4a16_linear, w4a16_linear_noalloc, w4a16_linear_ex, w4a16_linear_bf16,
+  w4a16_linear_bf16_ex,
   w4a16_gate_up_silu(_ex, _bf16, _bf16_ex), w4a16_linear_lora(_bf16),
   w4a16_lora_workspace_bytes, w4a16_linear_zp(_bf16), w4a16_zp_workspace_bytes,
   w4a16_stream_release, pack_gptq_v2, unpack_gptq_v2,
@@ -38,6 +39,7 @@ W4A16_ERR_KERNEL = 8
 W4A16_ERR_RANK = 9
 W4A16_ERR_WORKSPACE = 10
 W4A16_ERR_CAPTURE = 11
+W4A16_ERR_SCRATCH = 12
 W4A16_LORA_MAX_RANK = 1024
 
 W4A16_DECODE_MAX_M = 16
@@ -45,7 +47,7 @@ W4A16_KERNEL_AUTO = 0
 W4A16_KERNEL_DECODE = 1
 W4A16_KERNEL_PREFILL = 2
 
-EXPORTS = ("w4a16_linear", "w4a16_linear_ex", "w4a16_linear_bf16", "w4a16_linear_bf16_ex",
+EXPORTS = ("w4a16_linear", "w4a16_linear_noalloc", "w4a16_linear_ex", "w4a16_linear_bf16", "w4a16_linear_bf16_ex",
            "w4a16_gate_up_silu", "w4a16_gate_up_silu_ex", "w4a16_gate_up_silu_bf16",
            "w4a16_gate_up_silu_bf16_ex", "w4a16_linear_lora", "w4a16_linear_lora_bf16",
            "w4a16_lora_workspace_bytes", "w4a16_linear_zp", "w4a16_linear_zp_bf16",
@@ -74,6 +76,8 @@ def load_library() -> ctypes.CDLL:
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.w4a16_linear.argtypes = [p, p, p, p, i64, i64, i64, i64, p]
     lib.w4a16_linear.restype = i32
+    lib.w4a16_linear_noalloc.argtypes = [p, p, p, p, i64, i64, i64, i64, p]
+    lib.w4a16_linear_noalloc.restype = i32
     lib.w4a16_linear_ex.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i32]
     lib.w4a16_linear_ex.restype = i32
     lib.w4a16_linear_bf16.argtypes = [p, p, p, p, i64, i64, i64, i64, p]
@@ -131,6 +135,18 @@ def _stream_handle(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def w4a16_linear_noalloc(x, qweight, scales, y, M: int, K: int, N: int, group_size: int,
+                         stream=None) -> None:
+    """Same as the C ``w4a16_linear_noalloc``: w4a16_linear (fp16) with its split-K
+    scratch in the library's static device array (allocates nothing; calls that
+    overlap in time on one device race)."""
+    st = load_library().w4a16_linear_noalloc(_addr(x), _addr(qweight), _addr(scales), _addr(y),
+                                             int(M), int(K), int(N), int(group_size),
+                                             _stream_handle(stream))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_linear_noalloc")
 
 
 def w4a16_stream_release(stream=None) -> None:

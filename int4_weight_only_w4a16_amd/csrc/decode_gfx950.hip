@@ -646,9 +646,9 @@ constexpr int kDecD = W4A16_DECODE_D;
 
 static size_t slots_bytes(int capacity) { return (size_t)capacity * 16 * (kCols / 2) * sizeof(uint64_t); }
 
-size_t decode_workspace_bytes(int capacity) {
-    return slots_bytes(capacity) + (size_t)capacity * 2 * 16 * kCols * sizeof(float);
-}
+static_assert(kDecodeWorkspacePerCu == 16 * (kCols / 2) * sizeof(uint64_t) + 2 * 16 * kCols * sizeof(float),
+              "decode workspace layout");
+size_t decode_workspace_bytes(int capacity) { return (size_t)capacity * kDecodeWorkspacePerCu; }
 
 // Stream-K launches whose tiles may have more than two contributors (more
 // ranges than 2T) use partial slots and the reduce kernel; so do batches of

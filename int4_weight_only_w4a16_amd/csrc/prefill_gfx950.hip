@@ -258,13 +258,13 @@ static int m128_mt(int64_t M) { return M <= 32 ? 1 : M <= 64 ? 2 : 4; }
 // K chunks for the small-M kernel: with fewer tiles than CUs, split each
 // tile's K into about CUs / tiles chunks of at least 8 stages, as long as the
 // partials fit the prefill workspace (capacity x 256 KiB).
-static int m128_chunks(const LinearArgs &a, int num_cus) {
+static int m128_chunks(const LinearArgs &a, int num_cus, int capacity) {
     if (num_cus <= 0) return 1;
     const int64_t bm = 32 * m128_mt(a.M);
     const int64_t tiles = ((a.N + kPreBN - 1) / kPreBN) * ((a.M + bm - 1) / bm);
     const int64_t nst = (a.K + kPreBK - 1) / kPreBK;
     int64_t chunks = std::min<int64_t>(num_cus / tiles, nst / 8);
-    const int64_t fit = (int64_t)num_cus * 256 * 256 / (a.M * a.N);
+    const int64_t fit = (int64_t)capacity * 256 * 256 / (a.M * a.N);
     chunks = std::min(chunks, fit);
     return chunks < 2 ? 1 : (int)chunks;
 }
@@ -286,7 +286,7 @@ static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream, v
     int K = (int)a.K, N = (int)a.N, M = (int)a.M;
     int gshift = -1;
     if (a.group_size != -1) gshift = __builtin_ctz((unsigned)a.group_size);
-    int chunks = m128_chunks(a, num_cus);
+    int chunks = m128_chunks(a, num_cus, capacity);
     if (chunks > 1 && (!workspace ||
                        (size_t)chunks * M * N * sizeof(float) > (size_t)capacity * 256 * 256 * 4))
         chunks = 1;
@@ -838,12 +838,12 @@ __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
 // Split of the wide kernel's tiles: whole rounds of one tile per workgroup;
 // a last partial round of `tail` tiles (at most half a round) split into
 // `chunks` >= 2 stage ranges of at least 8 stages, so that tail * chunks
-// workgroups fill about one round.
+// workgroups fill about one round, and at most `capacity` partial tiles.
 struct WidePlan {
     int tiles, tiles_dp, tail, chunks;
 };
 
-static WidePlan wide_plan(const LinearArgs &a, int num_cus) {
+static WidePlan wide_plan(const LinearArgs &a, int num_cus, int capacity) {
     WidePlan w;
     w.tiles = (int)(((a.M + kWBM - 1) / kWBM) * ((a.N + kWBN - 1) / kWBN));
     w.tiles_dp = w.tiles;
@@ -853,7 +853,7 @@ static WidePlan wide_plan(const LinearArgs &a, int num_cus) {
     if (num_cus <= 0 || a.silu) return w;     // the SiLU epilogue stores whole tiles only
     const int tail = w.tiles % num_cus;
     if (tail == 0 || 2 * tail > num_cus) return w;
-    const int chunks = std::min(num_cus / tail, nst / 8);
+    const int chunks = std::min(std::min(num_cus / tail, nst / 8), capacity / tail);
     if (chunks < 2) return w;
     w.tail = tail;
     w.chunks = chunks;
@@ -861,11 +861,12 @@ static WidePlan wide_plan(const LinearArgs &a, int num_cus) {
     return w;
 }
 
-size_t prefill_workspace_bytes(int capacity) { return (size_t)capacity * kWSlot * sizeof(float); }
+static_assert(kPrefillPartialTileBytes == (size_t)kWSlot * sizeof(float), "prefill partial tile size");
+size_t prefill_workspace_bytes(int capacity) { return (size_t)capacity * kPrefillPartialTileBytes; }
 
 bool prefill_wants_workspace(const LinearArgs &a, int num_cus) {
-    if (a.M > 128) return wide_plan(a, num_cus).chunks > 1;
-    return m128_chunks(a, num_cus) > 1;
+    if (a.M > 128) return wide_plan(a, num_cus, num_cus).chunks > 1;
+    return m128_chunks(a, num_cus, num_cus) > 1;
 }
 
 static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, void *workspace,
@@ -874,7 +875,7 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
     int gshift = -1;
     if (a.group_size != -1) gshift = __builtin_ctz((unsigned)a.group_size);
     int tiles_m = (M + kWBM - 1) / kWBM;
-    WidePlan w = wide_plan(a, num_cus);
+    WidePlan w = wide_plan(a, num_cus, capacity);
     if (w.chunks > 1 && (!workspace || w.tail * w.chunks > capacity)) w = WidePlan{w.tiles, w.tiles, 0, 1};
     int tiles_dp = w.tiles_dp, chunks = w.chunks, tail = w.tail;
     int per_xcd = (tiles_dp + 7) / 8;

@@ -184,6 +184,59 @@ static int linear_call(const void *x, const int32_t *qweight, const void *scales
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
+// ---- the allocation-free variant: scratch in a file-scope device array ----
+//
+// For callers that cannot allocate (graph capture, tight serving loops,
+// harnesses that forbid hipMalloc).  The array holds the decode workspace
+// laid out for up to kScratchMaxCus workgroups (exchange slots, zero at load
+// time and left zero by every launch; partial tiles) and kScratchPrefillTiles
+// prefill partial tiles.  In host code `scratch` names a host-side stand-in,
+// never the device memory: its device address comes from hipGetSymbolAddress,
+// once per device, and only that address reaches the kernels.
+constexpr int kScratchMaxCus = 320;
+constexpr int kScratchPrefillTiles = 64;
+constexpr size_t kScratchDecodeBytes = (size_t)kScratchMaxCus * w4a16::kDecodeWorkspacePerCu;
+constexpr size_t kScratchBytes =
+    kScratchDecodeBytes + (size_t)kScratchPrefillTiles * w4a16::kPrefillPartialTileBytes;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];    // device address of `scratch`, per device
+
+static void *scratch_address(int dev) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+extern "C" int w4a16_linear_noalloc(const void *x, const int32_t *qweight, const void *scales,
+                                    void *y, int64_t M, int64_t K, int64_t N,
+                                    int64_t group_size, void *stream) {
+    const int st = validate(x, qweight, scales, y, M, K, N, group_size);
+    if (st != W4A16_OK) return st;
+    if (M == 0) return W4A16_OK;
+    int num_cus = 0;
+    size_t max_lds = 0;
+    const int dev = usable_device(&num_cus, &max_lds);
+    if (dev < 0) return W4A16_ERR_DEVICE;
+    if (num_cus > kScratchMaxCus) return W4A16_ERR_SCRATCH;
+    unsigned char *base = static_cast<unsigned char *>(scratch_address(dev));
+    if (!base) return W4A16_ERR_DEVICE;
+    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, false, false};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (M <= W4A16_DECODE_MAX_M)
+        e = w4a16::launch_decode(a, s, base, kScratchMaxCus, w4a16::decode_streamk_grid(a, num_cus),
+                                 max_lds);
+    else
+        e = w4a16::launch_prefill(a, s, base + kScratchDecodeBytes, kScratchPrefillTiles, num_cus);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
 extern "C" int w4a16_linear_ex(const void *x, const int32_t *qweight, const void *scales,
                                void *y, int64_t M, int64_t K, int64_t N, int64_t group_size,
                                void *stream, int kernel) {
@@ -389,6 +442,7 @@ extern "C" const char *w4a16_status_string(int status) {
         case W4A16_ERR_RANK: return "LoRA rank must be a multiple of 8 in [8, 1024]";
         case W4A16_ERR_WORKSPACE: return "workspace smaller than the size its _workspace_bytes call gives";
         case W4A16_ERR_CAPTURE: return "stream is being captured into a graph";
+        case W4A16_ERR_SCRATCH: return "device has more CUs than the allocation-free scratch covers";
         default: return "unknown status";
     }
 }

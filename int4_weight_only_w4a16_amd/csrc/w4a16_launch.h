@@ -24,7 +24,8 @@ struct LinearArgs {
 // its first use and left zeroed by every launch; grid == 0 runs the tiles
 // kernel, which needs no workspace.  max_lds is the device's LDS limit per
 // workgroup in bytes.
-size_t decode_workspace_bytes(int capacity);
+constexpr size_t kDecodeWorkspacePerCu = 12 * 1024;   // exchange slots 4 KiB + partials 8 KiB
+size_t decode_workspace_bytes(int capacity);            // capacity * kDecodeWorkspacePerCu
 int decode_streamk_grid(const LinearArgs &a, int num_cus);   // 0: use the tiles kernel
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                          int grid, size_t max_lds);
@@ -33,8 +34,10 @@ hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspac
 // for M > 128 a last partial round of tiles can be split along K; either
 // needs `workspace` (prefill_workspace_bytes(capacity) bytes of fp32
 // partials, no initial contents) when prefill_wants_workspace(a, num_cus).
-// Without it (or with too small a capacity) every tile runs whole.
-size_t prefill_workspace_bytes(int capacity);
+// A smaller capacity splits into fewer chunks; without a workspace every
+// tile runs whole.
+constexpr size_t kPrefillPartialTileBytes = 256 * 256 * 4;   // one 256 x 256 fp32 tile
+size_t prefill_workspace_bytes(int capacity);                  // capacity partial tiles
 bool prefill_wants_workspace(const LinearArgs &a, int num_cus);
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                           int num_cus);
