@@ -57,13 +57,14 @@ struct Stage {
     u2 s;     // the 4 columns' fp16 scales
 };
 
-// Activations staged in LDS: rows m < M of x, each zero-padded to Kp = 32*S
+// Activations staged in LDS: rows m < M of x over the S steps from step s0
+// (K indices 32 s0 .. 32 (s0 + S) - 1), each row zero-padded to Kp = 32*S
 // halves and already in unpack order (perm_x per 16-byte chunk), followed by
 // one zero chunk that the lanes of rows m >= M read.  Staging is split in
 // two so that the first kXPre chunks of each thread are requested before the
 // weight prologue (they would otherwise queue behind it): stage_x_issue loads
 // them, stage_x_finish stores them and any further chunks and returns this
-// lane's byte address of step 0.
+// lane's byte address of step s0.
 constexpr int kXPre = 2;
 
 struct XPre {
@@ -71,28 +72,28 @@ struct XPre {
 };
 
 __device__ __forceinline__ u4 stage_x_load(const __amdgpu_buffer_rsrc_t xr, int c, int K,
-                                           int chunks_per_row) {
+                                           int chunks_per_row, int k0) {
     const int m = c / chunks_per_row;
-    const int k = 8 * (c - m * chunks_per_row);
+    const int k = k0 + 8 * (c - m * chunks_per_row);
     return load_b128(xr, k < K ? ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 2u : kOOB);
 }
 
 __device__ __forceinline__ XPre stage_x_issue(const __amdgpu_buffer_rsrc_t xr, int M, int K,
-                                              int S) {
+                                              int S, int s0 = 0) {
     const int chunks_per_row = 4 * S;
     const int total = M * chunks_per_row;
     XPre pre;
 #pragma unroll
     for (int r = 0; r < kXPre; ++r) {
         const int c = threadIdx.x + r * blockDim.x;
-        pre.v[r] = stage_x_load(xr, c < total ? c : 0, K, chunks_per_row);
+        pre.v[r] = stage_x_load(xr, c < total ? c : 0, K, chunks_per_row, 32 * s0);
     }
     return pre;
 }
 
 __device__ __forceinline__ uint32_t stage_x_finish(unsigned char *xs,
                                                    const __amdgpu_buffer_rsrc_t xr, int M, int K,
-                                                   int S, const XPre &pre) {
+                                                   int S, const XPre &pre, int s0 = 0) {
     const int Kp = 32 * S;
     const int chunks_per_row = Kp / 8;
     const int total = M * chunks_per_row;
@@ -107,7 +108,7 @@ __device__ __forceinline__ uint32_t stage_x_finish(unsigned char *xs,
         if (c < total) put(c, pre.v[r]);
     }
     for (int c = threadIdx.x + kXPre * blockDim.x; c < total; c += blockDim.x)
-        put(c, stage_x_load(xr, c, K, chunks_per_row));
+        put(c, stage_x_load(xr, c, K, chunks_per_row, 32 * s0));
     if (threadIdx.x == 0) *reinterpret_cast<u4 *>(xs + (size_t)M * Kp * 2) = u4{0u, 0u, 0u, 0u};
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, kb = lane >> 4;
@@ -134,7 +135,8 @@ __device__ __forceinline__ _Float16 scale_at(const u2 &s, int j) {
 //
 // XLDS: activations come from LDS staged by `after_prologue` (called once the
 // first D weight loads are in flight; it returns this lane's LDS byte address
-// of step 0 and ends with a workgroup barrier); otherwise from global.
+// of step xstep0, the first staged step, and ends with a workgroup barrier;
+// ranges that meet two tiles stage from step 0); otherwise from global.
 // SCALE: 0 scales each 8-deep block before the MFMA (g = 16); 1 sums a
 // group's products in fp32 and scales once per group (scale-after); 2 is
 // scale-after with one step per group (g = 32): every MFMA starts from zero
@@ -151,7 +153,8 @@ template <int D, int SCALE, bool XLDS, bool BF, typename Dump, typename AfterPro
 __device__ __forceinline__ void decode_units(
     const __amdgpu_buffer_rsrc_t xr, const __amdgpu_buffer_rsrc_t qr,
     const __amdgpu_buffer_rsrc_t sr, const unsigned char *xs, int M, int K, int N, int S,
-    int group_steps, int w0, int w1, Dump &&dump, AfterPrologue &&after_prologue) {
+    int group_steps, int w0, int w1, Dump &&dump, AfterPrologue &&after_prologue,
+    int xstep0 = 0) {
     constexpr bool SCALE_AFTER = SCALE != 0;
     const int lane = threadIdx.x & 63;
     const int kb = lane >> 4;
@@ -233,7 +236,7 @@ __device__ __forceinline__ void decode_units(
     // on the zero chunk
     const uint32_t xl0 = after_prologue();
     const uint32_t xl_inc = (XLDS && c16 < M) ? 64u : 0u;
-    uint32_t xl = xl0 + xl_inc * (uint32_t)tA0;
+    uint32_t xl = xl0 + xl_inc * (uint32_t)(tA0 - xstep0);   // staged from step xstep0
 
     int i = 0, pos = SCALE_AFTER ? tA0 % group_steps : 0;
     // one unit of math on ring stage st (unit index i of this wave)
@@ -638,7 +641,7 @@ __global__ __launch_bounds__(256) void decode_split_reduce_kernel(
 #define W4A16_DECODE_WAVES 8
 #endif
 #ifndef W4A16_DECODE_D
-#define W4A16_DECODE_D 6
+#define W4A16_DECODE_D 4
 #endif
 
 constexpr int kDecWaves = W4A16_DECODE_WAVES;
