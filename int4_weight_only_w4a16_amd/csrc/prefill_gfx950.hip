@@ -334,6 +334,7 @@ constexpr int kWSOff = 3 * kWA + 3 * kWB;
 constexpr int kWLds = 3 * (kWA + kWB + kWS);
 
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kLgkm0Imm = 15 | (3 << 14) | (7 << 4);     // lgkmcnt(0), no wait on vmcnt
 constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
@@ -702,65 +703,87 @@ __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands 
 
 constexpr int kWSlot = kWBM * kWBN;   // floats per partial tile
 
+// The tile's sums pass through LDS in four passes of 64 rows (two row tiles),
+// as fp32 pairs in rows of 256 floats plus 32 bytes (so that the two rows a
+// wave writes at once, r and r + 4, start in different bank halves).
+constexpr int kWOutRows = 64;
+constexpr int kWOutPitch = kWBN * 4 + 32;
+static_assert(kWOutRows * kWOutPitch <= kWLds, "a 64-row pass of the output fits the stage buffers");
+
 // Stores the tile's sums.  Register i of lane (c32, kb) in wave w holds row
-// m0 + 32 mt + 8 (i/4) + 4 kb + i%4 of column tiles v0 = acc[mt][0] and
-// v1 = acc[mt][1], at columns n0 + 64w + 2 c32 + {0, 1}.  With part_mask == 0
-// the pair is rounded to fp16 and stored to y (rows >= M and columns >= N
-// dropped); with part_mask == ~0 both fp32 values go to the partial tile
-// `pr` instead, at floats ((w*8 + mt)*16 + i)*128 + {0, 64} + lane.  One
-// copy of the code serves both kinds of workgroup: every element issues the
-// same two stores, the ones that do not apply get an out-of-range offset
-// (two copies of the epilogue would not fit the register file).
+// 32 mt + 8 (i/4) + 4 kb + i%4 of the tile in column tiles v0 = acc[mt][0]
+// and v1 = acc[mt][1], at columns 64w + 2 c32 + {0, 1}.  Each pass writes two
+// row tiles into the stage buffers (the caller's LDS area L, no longer read
+// once every wave has passed the first barrier) and reads them back as runs
+// of 8 columns of a row, so that every store instruction moves 16 bytes per
+// lane:
+//  - y (partial == nullptr): the run rounded to the output type, one store
+//    (rows >= M and columns >= N dropped); with SILU the four (gate, up)
+//    pairs of the run become four values silu(gate) * up of y [M, N/2];
+//  - fp32 partial tile (`partial`, row-major 256 x 256): the run as two stores.
+// One body serves both: the stores that do not apply to this workgroup get an
+// out-of-range offset (two bodies do not fit the register file).
 template <bool BF, bool SILU>
-__device__ __forceinline__ void wide_store(const WideOperands &p, int m0, int n0,
-                                           const f16v (&acc)[8][2], float *partial,
-                                           uint32_t part_mask) {
-    if constexpr (SILU) {
-        // merged gate/up: whole tiles only (the host never splits them), one
-        // value silu(gate) * up per column pair
-        const int lane = threadIdx.x & 63;
-        const int n = n0 + 64 * (threadIdx.x >> 6) + 2 * (lane & 31);
-        if (n >= p.N) return;
+__device__ __forceinline__ void wide_store(lds_u8_t *L, const WideOperands &p, int m0, int n0,
+                                           const f16v (&acc)[8][2], float *partial) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int kb = lane >> 5;
+    const int c32 = lane & 31;
+    uint32_t part = (!SILU && partial) ? ~0u : 0u;        // uniform: this workgroup writes a partial
+    part = __builtin_amdgcn_readfirstlane(part);
+    asm volatile("" : "+s"(part));
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(p.ybase, p.ybytes);
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(partial, (uint32_t)kWSlot * 4u & part);
+    const int NY = SILU ? p.N / 2 : p.N;                  // y columns
+    lds_barrier();                                        // no wave reads the stage buffers any more
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+    for (int pass = 0; pass < 4; ++pass) {
+#pragma unroll
+        for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (m < p.M) store_pair<BF, true>(p.ybase, m, p.N, n, acc[mt][0][i], acc[mt][1][i]);
+                const int r = 32 * mh + 8 * (i >> 2) + 4 * kb + (i & 3);
+                typedef float f2 __attribute__((ext_vector_type(2)));
+                *(__attribute__((address_space(3))) f2 *)(L + r * kWOutPitch +
+                                                          (64 * wave + 2 * c32) * 4) =
+                    f2{acc[2 * pass + mh][0][i], acc[2 * pass + mh][1][i]};
             }
-        return;
-    }
-    // keep the mask opaque, so that the compiler does not split the stores
-    // into one copy per kind of workgroup
-    part_mask = __builtin_amdgcn_readfirstlane(part_mask);
-    asm volatile("" : "+s"(part_mask));
-    const uint64_t mask64 = (uint64_t)(int64_t)(int32_t)part_mask;
-    const uint64_t base = ((uint64_t)(uintptr_t)partial & mask64) |
-                          ((uint64_t)(uintptr_t)p.ybase & ~mask64);
-    const uint32_t bytes = ((uint32_t)kWSlot * 4u & part_mask) | (p.ybytes & ~part_mask);
-    const __amdgpu_buffer_rsrc_t r1 = make_rsrc((const void *)(uintptr_t)base, bytes);
-    const __amdgpu_buffer_rsrc_t r2 = make_rsrc(partial, (uint32_t)kWSlot * 4u & part_mask);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int kb = lane >> 5;
-    const int n = n0 + 64 * wave + 2 * (lane & 31);
+        __builtin_amdgcn_s_waitcnt(kLgkm0Imm);            // this wave's LDS writes are done
+        lds_barrier();
+#pragma unroll 2
+        for (int it = 0; it < kWOutRows * (kWBN / 8) / 256; ++it) {
+            const int id = tid + 256 * it;
+            const int r = id >> 5, cc = id & 31;          // row of the pass, run of 8 columns
+            const lds_u8_t *src = L + r * kWOutPitch + cc * 32;
+            const f4 a = *(const __attribute__((address_space(3))) f4 *)src;
+            const f4 b = *(const __attribute__((address_space(3))) f4 *)(src + 16);
+            const int rt = kWOutRows * pass + r;          // row of the tile
+            const int m = m0 + rt, n = n0 + 8 * cc;
+            const bool in = m < p.M && n < p.N;
+            if constexpr (SILU) {
+                const u2 v = {pack2<BF>(silu_f32(a[0]) * a[1], silu_f32(a[2]) * a[3]),
+                              pack2<BF>(silu_f32(b[0]) * b[1], silu_f32(b[2]) * b[3])};
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    v, yr, in ? ((uint32_t)m * (uint32_t)NY + (uint32_t)(n / 2)) * 2u : kOOB, 0, 0);
+            } else {
+                const u4 h = {pack2<BF>(a[0], a[1]), pack2<BF>(a[2], a[3]), pack2<BF>(b[0], b[1]),
+                              pack2<BF>(b[2], b[3])};
+                const u4 fa = __builtin_bit_cast(u4, a), fb = __builtin_bit_cast(u4, b);
+                const uint32_t po = ((uint32_t)rt * kWBN + 8u * (uint32_t)cc) * 4u;
+                const uint32_t yo = in ? ((uint32_t)m * (uint32_t)NY + (uint32_t)n) * 2u : kOOB;
+                u4 v1;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float f0 = acc[mt][0][i], f1 = acc[mt][1][i];
-            const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * kb + (i & 3);
-            const uint32_t v = pack2<BF>(f0, f1);
-            const uint32_t oy =
-                (m < p.M && n < p.N) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOOB;
-            const uint32_t op = ((uint32_t)((wave * 8 + mt) * 16 + i) * 128u + (uint32_t)lane) * 4u;
-            const uint32_t v1 = (__builtin_bit_cast(uint32_t, f0) & part_mask) |
-                                (v & ~part_mask);
-            const uint32_t o1 = (op & part_mask) | (oy & ~part_mask);
-            const uint32_t o2 = ((op + 256u) & part_mask) | (kOOB & ~part_mask);
-            __builtin_amdgcn_raw_buffer_store_b32(v1, r1, o1, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, f1), r2, o2, 0, 0);
+                for (int e = 0; e < 4; ++e) v1[e] = (fa[e] & part) | (h[e] & ~part);
+                const uint32_t o1 = (po & part) | (yo & ~part);
+                const uint32_t o2 = ((po + 16u) & part) | (kOOB & ~part);
+                __builtin_amdgcn_raw_buffer_store_b128(v1, part ? pr : yr, o1, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(fb, pr, o2, 0, 0);
+            }
         }
+        if (pass < 3) lds_barrier();                      // the next pass reuses the area
+    }
 }
 
 // The wide kernel.  Workgroups [0, 8 * per_xcd) take one tile each of the
@@ -803,36 +826,35 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
     }
     f16v acc[8][2];
     wide_tile_range<BF>((lds_u8_t *)lds_raw, p, m0, n0, sb, se, acc);
-    wide_store<BF, SILU>(p, m0, n0, acc, j < 0 ? partials : partials + (size_t)j * kWSlot,
-                         j < 0 ? 0u : ~0u);
+    wide_store<BF, SILU>((lds_u8_t *)lds_raw, p, m0, n0, acc,
+                         j < 0 ? nullptr : partials + (size_t)j * kWSlot);
 }
 
-// Sums the split tiles' partials in chunk order (fixed, so results are
-// bit-reproducible) and stores y.  One thread per (tile, wave, mt, i, lane):
-// register i of row tile mt, both column tiles, as laid out by wide_store.
+// Sums the split tiles' partials (row-major 256 x 256 fp32 tiles, as
+// wide_store writes them) in chunk order (fixed, so results are
+// bit-reproducible) and stores y.  One thread per (tile, row, run of 8
+// columns): 8192 per tile.
 template <bool BF>
 __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
     const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int tiles_m,
     int tiles_dp, int chunks, int tail_tiles) {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int tt = (int)(gid >> 15);                      // 32768 threads per tile
+    const int tt = (int)(gid >> 13);
     if (tt >= tail_tiles) return;
-    const int r = (int)(gid & 32767);
-    const int lane = r & 63, i = (r >> 6) & 15, mt = (r >> 10) & 7, wave = r >> 13;
+    const int r = (int)((gid >> 5) & 255), cc = (int)(gid & 31);
     const int t = tiles_dp + tt;
-    const int m0 = (t % tiles_m) * kWBM;
-    const int n0 = (t / tiles_m) * kWBN;
-    const float *src = partials + (size_t)tt * chunks * kWSlot +
-                       (size_t)((wave * 8 + mt) * 16 + i) * 128 + lane;
-    float a0 = 0.f, a1 = 0.f;
-    for (int c = 0; c < chunks; ++c) {
-        a0 += src[(size_t)c * kWSlot];
-        a1 += src[(size_t)c * kWSlot + 64];
-    }
-    const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    const int n = n0 + 64 * wave + 2 * (lane & 31);
+    const int m = (t % tiles_m) * kWBM + r;
+    const int n = (t / tiles_m) * kWBN + 8 * cc;
     if (m >= M || n >= N) return;
-    *reinterpret_cast<uint32_t *>(y + (size_t)m * N + n) = pack2<BF>(a0, a1);
+    const float *src = partials + (size_t)tt * chunks * kWSlot + (size_t)r * kWBN + 8 * cc;
+    f4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < chunks; ++c) {
+        a += *reinterpret_cast<const f4 *>(src + (size_t)c * kWSlot);
+        b += *reinterpret_cast<const f4 *>(src + (size_t)c * kWSlot + 4);
+    }
+    *reinterpret_cast<u4 *>(y + (size_t)m * N + n) =
+        u4{pack2<BF>(a[0], a[1]), pack2<BF>(a[2], a[3]), pack2<BF>(b[0], b[1]),
+           pack2<BF>(b[2], b[3])};
 }
 
 // Split of the wide kernel's tiles: whole rounds of one tile per workgroup;
@@ -897,7 +919,7 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
     void *rargs[] = {&pc, &yp, &M, &N, &tiles_m, &tiles_dp, &chunks, &tail};
     const void *rk = a.bf16 ? reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<true>)
                             : reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<false>);
-    return hipLaunchKernel(rk, dim3(128 * tail), dim3(256), rargs, 0, stream);
+    return hipLaunchKernel(rk, dim3(32 * tail), dim3(256), rargs, 0, stream);
 }
 
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
