@@ -249,12 +249,20 @@ size_t w4a16_lora_workspace_bytes(int64_t M, int64_t K, int64_t rank);
  *     caller; calls that overlap in time must not share one.
  *   ceil(G / 8) * 8 <= 1536 (else W4A16_ERR_SHAPE); everything else as for
  *   w4a16_linear (the _bf16 form: bfloat16 x and y, as w4a16_linear_bf16).
- * Steps on the stream: since (q - z) s = (q - 8) s + (8 - z) s, the symmetric
- * linear writes y; one kernel sums x over each group in fp32 (X[m, g]) and
- * forms C[g, n] = (8 - z) s exactly in fp32, rounded to the activation type;
- * an expand kernel rounds X to the activation type, takes X . C in fp32 on
- * the matrix cores and writes y = round(y + X . C).  Where every zero point is 8, C is 0 and y is the
- * symmetric result bit for bit.
+ * Steps on the stream: since (q - z) s = (q - 8) s + (8 - z) s,
+ *   - M <= W4A16_DECODE_MAX_M: one launch of the decode kernel, which sums x
+ *     over each group on the matrix cores beside the symmetric sums and adds
+ *     s (8 - z) times that sum per group and column in fp32 (for g = 16 the
+ *     zero point enters the dequantised weight: fp16 (q - z) s rounded once,
+ *     bfloat16 (q - z) s exact in fp32 and rounded once); the workspace is
+ *     not touched;
+ *   - larger M: the symmetric linear writes y; one kernel sums x over each
+ *     group in fp32 (X[m, g]) and forms C[g, n] = (8 - z) s exactly in fp32,
+ *     rounded to the activation type; an expand kernel rounds X to the
+ *     activation type, takes X . C in fp32 on the matrix cores and writes
+ *     y = round(y + X . C).
+ * Where every zero point is 8 the correction is 0 and y is the symmetric
+ * result (bit for bit, up to the sign of a zero).
  * Hence, per element and beyond the symmetric linear's own bound (u = 2^-11
  * for fp16, 2^-8 for bfloat16): u |y_sym| + u |y| + (2u + K 2^-24) P, to
  * first order, with P = sum_k |x[m,k]| |8 - z| s (the magnitude of the

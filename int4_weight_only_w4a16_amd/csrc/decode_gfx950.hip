@@ -52,9 +52,10 @@ constexpr int kCols = 16 * kNW;        // columns per tile
 
 template <bool XLDS>
 struct Stage {
-    u4 w;     // qweight words of the lane's 4 consecutive columns
-    u4 x;     // 8 activations of this lane's A row / K block (unused when staged in LDS)
-    u2 s;     // the 4 columns' fp16 scales
+    u4 w;       // qweight words of the lane's 4 consecutive columns
+    u4 x;       // 8 activations of this lane's A row / K block (unused when staged in LDS)
+    u2 s;       // the 4 columns' fp16 scales
+    uint32_t z; // with stored zero points: the qzeros word holding the 4 columns' nibbles
 };
 
 // Activations staged in LDS: rows m < M of x over the S steps from step s0
@@ -149,10 +150,19 @@ __device__ __forceinline__ _Float16 scale_at(const u2 &s, int j) {
 // steps; at the group's end acc += s * (sum - sum136) in fp32.  Where every
 // code of a group is 8 the two sums are the same operations on the same
 // values, so that group adds exactly zero, as (8 - 8) * s does.
-template <int D, int SCALE, bool XLDS, bool BF, typename Dump, typename AfterPrologue>
+// ZP: stored zero points (qzeros int32 [G, N/8], nibble j of word c = column
+// 8c + j): w = (q - z) s.  Since (q - z) s = (q - 8) s + (8 - z) s, the
+// symmetric sums run unchanged and one more MFMA per unit sums x itself
+// (B = 1) over the group; at the group's end acc += s (8 - z) * (that sum) per
+// column, in fp32.  With every z = 8 the added term is 0.  For SCALE 0 (two
+// groups in a unit) the zero point enters the dequantised weight instead: fp16
+// adds 8 - z to the exact q - 8 before the scale, bfloat16 takes -z s as the
+// offset of its fma.
+template <int D, int SCALE, bool XLDS, bool BF, bool ZP, typename Dump, typename AfterPrologue>
 __device__ __forceinline__ void decode_units(
     const __amdgpu_buffer_rsrc_t xr, const __amdgpu_buffer_rsrc_t qr,
-    const __amdgpu_buffer_rsrc_t sr, const unsigned char *xs, int M, int K, int N, int S,
+    const __amdgpu_buffer_rsrc_t sr, const __amdgpu_buffer_rsrc_t zr, const unsigned char *xs,
+    int M, int K, int N, int S,
     int group_steps, int w0, int w1, Dump &&dump, AfterPrologue &&after_prologue,
     int xstep0 = 0) {
     constexpr bool SCALE_AFTER = SCALE != 0;
@@ -200,6 +210,9 @@ __device__ __forceinline__ void decode_units(
             st.x = load_b128(xr, xo);
         }
         st.s = load_b64(sr, s_off);
+        // the qzeros word of the same group row: byte (row N / 2 + col / 2) rounded
+        // down to a word, i.e. the scale offset / 4 (N % 8 == 0)
+        if constexpr (ZP) st.z = __builtin_amdgcn_raw_buffer_load_b32(zr, (s_off >> 2) & ~3u, 0, 0);
         // advance to unit li + 1 (stay put at the last unit)
         const bool more = li + 1 < n;
         const bool jump = li + 1 == nA;
@@ -216,7 +229,15 @@ __device__ __forceinline__ void decode_units(
         ++li;
     };
 
-    f4 acc[kNW], accg[kNW], accx = f4{0.f, 0.f, 0.f, 0.f};
+    f4 acc[kNW], accg[kNW], accx = f4{0.f, 0.f, 0.f, 0.f}, accz = f4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t zsh = 16u * (uint32_t)(c16 & 1);   // the lane's 4 nibbles in the qzeros word
+    // 1.0 in both halves of each dword, in the activation type (B of the x sums)
+    const u4 ones = BF ? u4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
+                       : u4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+    // zero point of column j of the lane's quad, as 8 - z
+    auto zdiff = [&](const Stage<XLDS> &st, int j) -> int {
+        return 8 - (int)((st.z >> (zsh + 4u * (uint32_t)j)) & 15u);
+    };
 #pragma unroll
     for (int j = 0; j < kNW; ++j) {
         acc[j] = f4{0.f, 0.f, 0.f, 0.f};
@@ -247,18 +268,22 @@ __device__ __forceinline__ void decode_units(
         else
             a = __builtin_bit_cast(h8, perm_x(st.x));
         const bool seg_end = i == nA - 1 || i == n - 1;
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
         if constexpr (BF && SCALE == 0) {
 #pragma unroll
-            for (int j = 0; j < kNW; ++j)
+            for (int j = 0; j < kNW; ++j) {
+                const float sj = (float)scale_at(st.s, j);
+                const float zoff = ZP ? (float)(zdiff(st, j) - 8) * sj : -8.0f * sj;   // -z s
                 acc[j] = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a),
-                                              dequant_bf16<false>(st.w[j], (float)scale_at(st.s, j)),
-                                              acc[j]);
+                                              dequant_bf16<false>(st.w[j], sj, zoff), acc[j]);
+            }
         } else if constexpr (BF && SCALE == 2) {
             // one step per group: both sums start from zero in the MFMA and go
             // straight into acc (no accumulators to reset)
             const u4 b136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};   // bf16 136.0
-            const f4 zero = {0.f, 0.f, 0.f, 0.f};
             const f4 tx = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), b136, zero);
+            f4 tz = zero;
+            if constexpr (ZP) tz = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), ones, zero);
 #pragma unroll
             for (int j = 0; j < kNW; ++j) {
                 const f4 t = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), codes128_bf16(st.w[j], uc),
@@ -266,6 +291,11 @@ __device__ __forceinline__ void decode_units(
                 const float sj = (float)scale_at(st.s, j);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(sj, t[e] - tx[e], acc[j][e]);
+                if constexpr (ZP) {
+                    const float cj = sj * (float)zdiff(st, j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(cj, tz[e], acc[j][e]);
+                }
             }
         } else if constexpr (BF) {
             const u4 b136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};   // bf16 136.0
@@ -274,6 +304,7 @@ __device__ __forceinline__ void decode_units(
                 accg[j] = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), codes128_bf16(st.w[j], uc),
                                                accg[j]);
             accx = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), b136, accx);
+            if constexpr (ZP) accz = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), ones, accz);
             if (pos == group_steps - 1 || seg_end) {
 #pragma unroll
                 for (int j = 0; j < kNW; ++j) {
@@ -281,34 +312,54 @@ __device__ __forceinline__ void decode_units(
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[j][e] = __builtin_fmaf(sj, accg[j][e] - accx[e], acc[j][e]);
-                    accg[j] = f4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (ZP) {
+                        const float cj = sj * (float)zdiff(st, j);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(cj, accz[e], acc[j][e]);
+                    }
+                    accg[j] = zero;
                 }
-                accx = f4{0.f, 0.f, 0.f, 0.f};
+                accx = zero;
+                accz = zero;
             }
             pos = (pos + 1 == group_steps) ? 0 : pos + 1;
         } else if constexpr (SCALE == 2) {
+            f4 tz = zero;
+            if constexpr (ZP) tz = mfma16x16x32_t<false>(__builtin_bit_cast(u4, a), ones, zero);
 #pragma unroll
             for (int j = 0; j < kNW; ++j) {
-                const f4 t = mfma16x16x32(a, unpack_codes(st.w[j], uc), f4{0.f, 0.f, 0.f, 0.f});
-                acc[j] += (float)scale_at(st.s, j) * t;
+                const f4 t = mfma16x16x32(a, unpack_codes(st.w[j], uc), zero);
+                const float sj = (float)scale_at(st.s, j);
+                acc[j] += sj * t;
+                if constexpr (ZP) acc[j] += (sj * (float)zdiff(st, j)) * tz;
             }
         } else if constexpr (SCALE_AFTER) {
 #pragma unroll
             for (int j = 0; j < kNW; ++j)
                 accg[j] = mfma16x16x32(a, unpack_codes(st.w[j], uc), accg[j]);
+            if constexpr (ZP) accz = mfma16x16x32_t<false>(__builtin_bit_cast(u4, a), ones, accz);
             if (pos == group_steps - 1 || seg_end) {
 #pragma unroll
                 for (int j = 0; j < kNW; ++j) {
-                    acc[j] += (float)scale_at(st.s, j) * accg[j];
-                    accg[j] = f4{0.f, 0.f, 0.f, 0.f};
+                    const float sj = (float)scale_at(st.s, j);
+                    acc[j] += sj * accg[j];
+                    if constexpr (ZP) acc[j] += (sj * (float)zdiff(st, j)) * accz;
+                    accg[j] = zero;
                 }
+                accz = zero;
             }
             pos = (pos + 1 == group_steps) ? 0 : pos + 1;
         } else {
 #pragma unroll
-            for (int j = 0; j < kNW; ++j)
-                acc[j] = mfma16x16x32(a, unpack_codes_scaled(st.w[j], uc, scale_at(st.s, j)),
-                                      acc[j]);
+            for (int j = 0; j < kNW; ++j) {
+                h8 wq = unpack_codes(st.w[j], uc);                 // q - 8, exact
+                if constexpr (ZP) {                                // q - z, exact
+                    const _Float16 d = (_Float16)zdiff(st, j);
+                    wq += h8{d, d, d, d, d, d, d, d};
+                }
+                const _Float16 sj = scale_at(st.s, j);
+                acc[j] = mfma16x16x32(a, wq * h8{sj, sj, sj, sj, sj, sj, sj, sj}, acc[j]);
+            }
         }
         if (seg_end) {
             dump(i < nA ? 0 : 1, acc);
@@ -348,10 +399,11 @@ constexpr size_t streamk_static_lds(int waves) {
 }
 
 // Tiles kernel: one workgroup per column tile, its waves split K.
-template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU>
+template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP>
 __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
-    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
+    const uint16_t *__restrict__ scales, const int32_t *__restrict__ qzeros,
+    uint16_t *__restrict__ y, int M, int K, int N,
     int group_steps) {
     __shared__ f4 red[WAVES][kNW][64];
     static_assert(sizeof(red) == tiles_static_lds(WAVES), "tiles kernel LDS layout");
@@ -368,14 +420,15 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
     const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
     const auto sr = make_rsrc(scales, (uint32_t)G * (uint32_t)N * 2u);
+    const auto zr = make_rsrc(qzeros, ZP ? (uint32_t)G * (uint32_t)N / 2u : 0u);
 
 #pragma unroll
     for (int j = 0; j < kNW; ++j) red[wave][j][lane] = f4{0.f, 0.f, 0.f, 0.f};
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
     __builtin_amdgcn_sched_barrier(0);
-    decode_units<D, SCALE, XLDS, BF>(
-        xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
+    decode_units<D, SCALE, XLDS, BF, ZP>(
+        xr, qr, sr, zr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int, const f4(&acc)[kNW]) {
 #pragma unroll
             for (int j = 0; j < kNW; ++j) red[wave][j][lane] = acc[j];
@@ -455,10 +508,11 @@ __host__ __device__ __forceinline__ int wave_share(int n, int w) {
     return nold + (n - nold) * (w - H) / (WAVES - H);
 }
 
-template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU>
+template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
-    const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
+    const uint16_t *__restrict__ scales, const int32_t *__restrict__ qzeros,
+    uint16_t *__restrict__ y, int M, int K, int N,
     int group_steps, uint64_t *__restrict__ slots, float *__restrict__ partials) {
     constexpr int SLOT = 16 * kCols;             // floats per partial slot
     // Wave partials: block s*WAVES + w (256 f4: [lane][i]) holds wave w's
@@ -487,12 +541,13 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
     const auto qr = make_rsrc(qweight, (uint32_t)(K >> 3) * (uint32_t)N * 4u);
     const auto sr = make_rsrc(scales, (uint32_t)Gs * (uint32_t)N * 2u);
+    const auto zr = make_rsrc(qzeros, ZP ? (uint32_t)Gs * (uint32_t)N / 2u : 0u);
 
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
     __builtin_amdgcn_sched_barrier(0);
-    decode_units<D, SCALE, XLDS, BF>(
-        xr, qr, sr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
+    decode_units<D, SCALE, XLDS, BF, ZP>(
+        xr, qr, sr, zr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int slot, const f4(&acc)[kNW]) {
             if (slot > 1) return;   // cannot happen: ranges hold <= S units
 #pragma unroll
@@ -713,7 +768,7 @@ static size_t static_lds(const void *kernel) {
     return attr.sharedSizeBytes;
 }
 
-template <int SCALE, bool XLDS, bool BF, bool SILU>
+template <int SCALE, bool XLDS, bool BF, bool SILU, bool ZP>
 static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *workspace,
                             int capacity, int grid) {
     const int K = (int)a.K, N = (int)a.N, M = (int)a.M;
@@ -723,6 +778,7 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
     const void *xp = a.x;
     const void *qp = a.qweight;
     const void *sp = a.scales;
+    const void *zp = a.qzeros;
     void *yp = a.y;
     const dim3 block(kDecWaves * 64);
     const size_t dyn = XLDS ? (size_t)M * 32 * S * 2 + 16 : 0;
@@ -732,11 +788,11 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
         const int T = (N + kCols - 1) / kCols;
         const bool part = uses_partials(grid, T, M);
         float *partials = part ? reinterpret_cast<float *>(ws + slots_bytes(capacity)) : nullptr;
-        void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N,
+        void *args[] = {&xp, &qp, &sp, &zp, &yp, (void *)&M, (void *)&K, (void *)&N,
                         &group_steps, &slots, &partials};
         hipError_t e = hipLaunchKernel(
             reinterpret_cast<const void *>(
-                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU>),
+                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP>),
             dim3(grid), block, args, dyn, stream);
         if (e != hipSuccess || !part) return e;
         const float *pc = partials;
@@ -745,11 +801,11 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
         return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel<BF, SILU>),
                                dim3((unsigned)T), dim3(256), rargs, 0, stream);
     }
-    void *args[] = {&xp, &qp, &sp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
+    void *args[] = {&xp, &qp, &sp, &zp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
     const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);
     return hipLaunchKernel(
         reinterpret_cast<const void *>(
-            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU>),
+            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP>),
         dim3(tiles), block, args, dyn, stream);
 }
 
@@ -761,9 +817,9 @@ static bool stage_fits(const LinearArgs &a, int grid, size_t max_lds) {
     const size_t dyn = (size_t)a.M * 32 * ((a.K + 31) / 32) * 2 + 16;
     if (dyn > kXStageMax) return false;
     static const size_t sk_static = static_lds(reinterpret_cast<const void *>(
-        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true, BF, false>));
+        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true, BF, false, false>));
     static const size_t tiles_static = static_lds(reinterpret_cast<const void *>(
-        &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true, BF, false>));
+        &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true, BF, false, false>));
     const size_t st = grid > 0 ? sk_static : tiles_static;
     return st != (size_t)-1 && st + dyn <= max_lds;
 }
@@ -772,11 +828,14 @@ template <int SCALE, bool BF>
 static hipError_t launch_scale(const LinearArgs &a, hipStream_t stream, void *workspace,
                                int capacity, int grid, size_t max_lds) {
     const bool xlds = stage_fits<SCALE, BF>(a, grid, max_lds);
+    if (a.qzeros)   // stored zero points (never with the merged gate/up epilogue)
+        return xlds ? launch_sa<SCALE, true, BF, false, true>(a, stream, workspace, capacity, grid)
+                    : launch_sa<SCALE, false, BF, false, true>(a, stream, workspace, capacity, grid);
     if (a.silu)
-        return xlds ? launch_sa<SCALE, true, BF, true>(a, stream, workspace, capacity, grid)
-                    : launch_sa<SCALE, false, BF, true>(a, stream, workspace, capacity, grid);
-    return xlds ? launch_sa<SCALE, true, BF, false>(a, stream, workspace, capacity, grid)
-                : launch_sa<SCALE, false, BF, false>(a, stream, workspace, capacity, grid);
+        return xlds ? launch_sa<SCALE, true, BF, true, false>(a, stream, workspace, capacity, grid)
+                    : launch_sa<SCALE, false, BF, true, false>(a, stream, workspace, capacity, grid);
+    return xlds ? launch_sa<SCALE, true, BF, false, false>(a, stream, workspace, capacity, grid)
+                : launch_sa<SCALE, false, BF, false, false>(a, stream, workspace, capacity, grid);
 }
 
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,

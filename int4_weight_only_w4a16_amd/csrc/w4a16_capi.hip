@@ -148,7 +148,8 @@ extern "C" int w4a16_stream_release(void *stream) {
 // the merged gate/up projection (N % 16 == 0, y is [M, N/2]).
 static int linear_call(const void *x, const int32_t *qweight, const void *scales, void *y,
                        int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
-                       int kernel, bool bf16, bool silu = false) {
+                       int kernel, bool bf16, bool silu = false,
+                       const int32_t *qzeros = nullptr) {
     const int st = validate(x, qweight, scales, y, M, K, N, group_size);
     if (st != W4A16_OK) return st;
     if (silu && N % 16 != 0) return W4A16_ERR_SHAPE;
@@ -164,9 +165,10 @@ static int linear_call(const void *x, const int32_t *qweight, const void *scales
     size_t max_lds = 0;
     const int dev = usable_device(&num_cus, &max_lds);
     if (dev < 0) return W4A16_ERR_DEVICE;
-    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, bf16, silu};
+    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, bf16, silu, qzeros};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
+    if (qzeros && kernel != W4A16_KERNEL_DECODE) return W4A16_ERR_KERNEL;   // not reached
     if (kernel == W4A16_KERNEL_DECODE) {
         int grid = w4a16::decode_streamk_grid(a, num_cus);
         void *ws = nullptr;
@@ -351,6 +353,10 @@ static int zp_call(const void *x, const int32_t *qweight, const void *scales,
     if (!qzeros || !workspace) return W4A16_ERR_NULL;
     if (!aligned16(qzeros) || !aligned16(workspace)) return W4A16_ERR_ALIGN;
     if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+    // decode: the zero points enter the linear's own kernel (one launch)
+    if (M <= W4A16_DECODE_MAX_M)
+        return linear_call(x, qweight, scales, y, M, K, N, group_size, stream,
+                           W4A16_KERNEL_DECODE, bf16, false, qzeros);
     st = linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO, bf16);
     if (st != W4A16_OK) return st;
     const w4a16::ZpArgs a{x, scales, qzeros, y, M, K, N, group_size, bf16};

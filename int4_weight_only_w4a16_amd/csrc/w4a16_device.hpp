@@ -238,9 +238,11 @@ __device__ __forceinline__ u4 codes128_bf16(uint32_t w, const UnpackConsts &c) {
 // the even nibbles in its bytes (q0, q2, q4, q6), hi the odd ones.
 // NATURAL: order (q0, q1, ..., q7), else the fp16 unpack order (q0, q4, q1,
 // q5, q2, q6, q3, q7).
+// With a stored zero point z the offset term is -z s instead of -8 s (exact
+// in fp32 as well): pass zoff = -z s.
 template <bool NATURAL>
-__device__ __forceinline__ u4 dequant_bf16(uint32_t w, float s) {
-    const float m8s = -8.0f * s;
+__device__ __forceinline__ u4 dequant_bf16(uint32_t w, float s, float zoff) {
+    const float m8s = zoff;
     uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
     // opaque, so that each nibble is one v_cvt_f32_ubyte<d> of the masked
     // word rather than a bit-field extract and a convert
@@ -257,6 +259,11 @@ __device__ __forceinline__ u4 dequant_bf16(uint32_t w, float s) {
         r[3] = pack2<true>(wq(hi, 1), wq(hi, 3));
     }
     return r;
+}
+
+template <bool NATURAL>
+__device__ __forceinline__ u4 dequant_bf16(uint32_t w, float s) {
+    return dequant_bf16<NATURAL>(w, s, -8.0f * s);
 }
 
 }  // namespace w4a16

@@ -16,6 +16,7 @@ struct LinearArgs {
     int64_t M, K, N, group_size;
     bool bf16;   // x and y are bfloat16 (else fp16); scales are fp16 either way
     bool silu;   // merged gate/up: columns alternate gate and up; y[M, N/2] = silu(gate) * up
+    const int32_t *qzeros = nullptr;   // stored zero points int32 [G, N/8] (decode only), or none
 };
 
 // Decode (M <= 16).  grid > 0 runs the stream-K kernel on `grid` workgroups
