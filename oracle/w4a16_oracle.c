@@ -34,8 +34,11 @@
  *
  * bfloat16 activations (oracle_linear_ex / oracle_linear_at_ex with act = 1):
  * the same definition with x given as bfloat16 bit patterns (1 sign, 8
- * exponent, 7 fraction bits), decoded field by field below; scales stay
- * fp16.  The pages serve this checkpoint with bfloat16 activations
+ * exponent, 7 fraction bits), decoded field by field below.  The scales are
+ * fp16, or bfloat16 bit patterns with stype = 1 (decoded the same way): a
+ * checkpoint served in bfloat16 carries its scales in that dtype too.  The
+ * weight (q - 8) * s stays exact in fp32 (4 + 8 significant bits).  The
+ * pages serve this checkpoint with bfloat16 activations
  * ("Qwen3.8-27B-GPTQ-Int4" model card, "4. Deployment": the verified serving
  * command runs with the bfloat16 dtype), while the GPTQ-Pro fork keeps native
  * BF16 outside its own kernels ("GPTQ-Pro" README, "Runtime contract").
@@ -78,8 +81,14 @@
  * "GPT-QModel" README), and its checkpoint formats v1 and v2 store them
  * differently without saying how.  This file takes qzeros as int32 [G, N/8]
  * packed along N, nibble j of word c = column 8c+j, low bits first, each
- * nibble the zero point itself (v1's stored z - 1 becomes z by adding one
- * before the call).  With every zero point 8 it is the symmetric definition.
+ * nibble the zero point itself (the v2 form).  The v1 checkpoint form
+ * (zv1 = 1) is named on the pages ("GPT-QModel" README, "Quant Method /
+ * Format / Backend Matrix": FORMAT.GPTQ beside FORMAT.GPTQ_V2; "Norm
+ * tuning": v1 zero points read as they are decode the weights wrongly) but
+ * not defined there; this file takes the published GPTQ convention that v1
+ * stores z - 1 in the nibble, so z = nibble + 1, in [1, 16] (a symmetric
+ * checkpoint in v1 form holds 7 in every nibble).  With every zero point 8
+ * it is the symmetric definition.
  * For shapes too large for the triple loop (the 2048-row prefill case in
  * full), oracle.linear_dense (Python) takes the same fp32 dequantised W and
  * the activations decoded here (oracle_decode_act) and forms x . W with
@@ -138,6 +147,13 @@ static double act_to_double(uint16_t h, int act) {
     return act ? bf16_to_double(h) : half_to_double(h);
 }
 
+/* A scale's bits -> double: stype 0 is fp16, stype 1 bfloat16. */
+static double scale_to_double(uint16_t h, int stype) {
+    return stype == 1 ? bf16_to_double(h) : half_to_double(h);
+}
+
+static int type_ok(int t) { return t == 0 || t == 1; }
+
 /* One product term, or its magnitude. */
 static inline double term(double xk, double w, int absval) {
     return absval ? fabs(xk) * fabs(w) : xk * w;
@@ -174,11 +190,12 @@ static inline int64_t group_of(int64_t k, int64_t g) {
 }
 
 /* Dequantised weight as the pages' symmetric scheme defines it:
- * (q - 8) * s, computed in fp32 (exact: at most 4 + 11 significant bits). */
-static inline float weight_at(const int32_t *qweight, const uint16_t *scales, int64_t N,
-                              int64_t g, int64_t k, int64_t n) {
+ * (q - 8) * s, computed in fp32 (exact: at most 4 + 11 significant bits);
+ * scales of type stype. */
+static inline float weight_at(const int32_t *qweight, const uint16_t *scales, int stype,
+                              int64_t N, int64_t g, int64_t k, int64_t n) {
     int q = (int)code_at(qweight, N, k, n);
-    float s = (float)half_to_double(scales[group_of(k, g) * N + n]);
+    float s = (float)scale_to_double(scales[group_of(k, g) * N + n], stype);
     return (float)(q - 8) * s;
 }
 
@@ -208,15 +225,21 @@ int oracle_pack(const uint8_t *codes, int64_t K, int64_t N, int32_t *qweight) {
     return OR_OK;
 }
 
-/* W[k*N + n] <- w[k, n] in fp32. */
-int oracle_dequant(const int32_t *qweight, const uint16_t *scales, int64_t K, int64_t N,
-                   int64_t g, float *W) {
-    if (!qweight || !scales || !W || !shape_ok(0, K, N) || !group_ok(K, g)) return OR_ERR_ARG;
+/* W[k*N + n] <- w[k, n] in fp32, scales of type stype (0 fp16, 1 bfloat16). */
+int oracle_dequant_ex(const int32_t *qweight, const uint16_t *scales, int stype, int64_t K,
+                      int64_t N, int64_t g, float *W) {
+    if (!qweight || !scales || !W || !shape_ok(0, K, N) || !group_ok(K, g) || !type_ok(stype))
+        return OR_ERR_ARG;
     #pragma omp parallel for schedule(static)
     for (int64_t k = 0; k < K; ++k)
         for (int64_t n = 0; n < N; ++n)
-            W[k * N + n] = weight_at(qweight, scales, N, g, k, n);
+            W[k * N + n] = weight_at(qweight, scales, stype, N, g, k, n);
     return OR_OK;
+}
+
+int oracle_dequant(const int32_t *qweight, const uint16_t *scales, int64_t K, int64_t N,
+                   int64_t g, float *W) {
+    return oracle_dequant_ex(qweight, scales, 0, K, N, g, W);
 }
 
 /* out[i] <- the value of activation bits x[i] (act 0 fp16, 1 bfloat16), for
@@ -233,14 +256,15 @@ int oracle_decode_act(const uint16_t *x, int act, int64_t n, double *out) {
  * for every row; the loop runs m -> k -> n with a row of fp64 accumulators, so
  * every output still adds its K products in ascending k. */
 static int linear_impl(const uint16_t *x, int act, int absval, const int32_t *qweight,
-                       const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
-                       double *y) {
-    if (!shape_ok(M, K, N) || !group_ok(K, g) || (act != 0 && act != 1)) return OR_ERR_ARG;
+                       const uint16_t *scales, int stype, int64_t M, int64_t K, int64_t N,
+                       int64_t g, double *y) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || !type_ok(act) || !type_ok(stype))
+        return OR_ERR_ARG;
     if (M == 0) return OR_OK;
     if (!x || !qweight || !scales || !y) return OR_ERR_ARG;
     float *W = (float *)malloc((size_t)K * (size_t)N * sizeof(float));
     if (!W) return OR_ERR_ARG;
-    oracle_dequant(qweight, scales, K, N, g, W);
+    oracle_dequant_ex(qweight, scales, stype, K, N, g, W);
     const int64_t NB = 256;                      /* column block per task */
     const int64_t nblocks = (N + NB - 1) / NB;
     #pragma omp parallel for collapse(2) schedule(dynamic, 1)
@@ -263,24 +287,26 @@ static int linear_impl(const uint16_t *x, int act, int absval, const int32_t *qw
 
 int oracle_linear(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                   int64_t M, int64_t K, int64_t N, int64_t g, double *y) {
-    return linear_impl(x, 0, 0, qweight, scales, M, K, N, g, y);
+    return linear_impl(x, 0, 0, qweight, scales, 0, M, K, N, g, y);
 }
 
-/* As oracle_linear, with x of type act (0 fp16, 1 bfloat16) and, when absval
- * is 1, sum_k |x| * |w| in place of the sum of products. */
+/* As oracle_linear, with x of type act and scales of type stype (0 fp16, 1
+ * bfloat16) and, when absval is 1, sum_k |x| * |w| in place of the sum of
+ * products. */
 int oracle_linear_ex(const uint16_t *x, int act, int absval, const int32_t *qweight,
-                     const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
-                     double *y) {
-    return linear_impl(x, act, absval ? 1 : 0, qweight, scales, M, K, N, g, y);
+                     const uint16_t *scales, int stype, int64_t M, int64_t K, int64_t N,
+                     int64_t g, double *y) {
+    return linear_impl(x, act, absval ? 1 : 0, qweight, scales, stype, M, K, N, g, y);
 }
 
 /* out[i] <- y[ms[i], ns[i]] for sampled outputs, each from the definition
  * directly (no dequantised matrix): used at sizes where the full product is
  * too slow for a test. */
 static int linear_at_impl(const uint16_t *x, int act, int absval, const int32_t *qweight,
-                          const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
-                          const int64_t *ms, const int64_t *ns, int64_t count, double *out) {
-    if (!shape_ok(M, K, N) || !group_ok(K, g) || count < 0 || (act != 0 && act != 1))
+                          const uint16_t *scales, int stype, int64_t M, int64_t K, int64_t N,
+                          int64_t g, const int64_t *ms, const int64_t *ns, int64_t count,
+                          double *out) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || count < 0 || !type_ok(act) || !type_ok(stype))
         return OR_ERR_ARG;
     if (count == 0) return OR_OK;
     if (!x || !qweight || !scales || !ms || !ns || !out) return OR_ERR_ARG;
@@ -292,7 +318,7 @@ static int linear_at_impl(const uint16_t *x, int act, int absval, const int32_t 
         double acc = 0.0;
         for (int64_t k = 0; k < K; ++k)
             acc += term(act_to_double(x[m * K + k], act),
-                        (double)weight_at(qweight, scales, N, g, k, n), absval);
+                        (double)weight_at(qweight, scales, stype, N, g, k, n), absval);
         out[i] = acc;
     }
     return OR_OK;
@@ -303,14 +329,14 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* out[m*(N/2) + j] <- silu(y[m,2j]) * y[m,2j+1], y the linear of x (type act). */
 int oracle_gate_up_silu(const uint16_t *x, int act, const int32_t *qweight,
-                        const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
-                        double *out) {
+                        const uint16_t *scales, int stype, int64_t M, int64_t K, int64_t N,
+                        int64_t g, double *out) {
     if (!shape_ok(M, K, N) || N % 2 != 0) return OR_ERR_ARG;
     if (M == 0) return OR_OK;
     if (!out) return OR_ERR_ARG;
     double *y = (double *)malloc((size_t)M * (size_t)N * sizeof(double));
     if (!y) return OR_ERR_ARG;
-    int rc = linear_impl(x, act, 0, qweight, scales, M, K, N, g, y);
+    int rc = linear_impl(x, act, 0, qweight, scales, stype, M, K, N, g, y);
     if (rc == OR_OK)
         for (int64_t m = 0; m < M; ++m)
             for (int64_t j = 0; j < N / 2; ++j)
@@ -322,14 +348,15 @@ int oracle_gate_up_silu(const uint16_t *x, int act, const int32_t *qweight,
 int oracle_linear_at(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
                      int64_t M, int64_t K, int64_t N, int64_t g,
                      const int64_t *ms, const int64_t *ns, int64_t count, double *out) {
-    return linear_at_impl(x, 0, 0, qweight, scales, M, K, N, g, ms, ns, count, out);
+    return linear_at_impl(x, 0, 0, qweight, scales, 0, M, K, N, g, ms, ns, count, out);
 }
 
 int oracle_linear_at_ex(const uint16_t *x, int act, int absval, const int32_t *qweight,
-                        const uint16_t *scales, int64_t M, int64_t K, int64_t N, int64_t g,
-                        const int64_t *ms, const int64_t *ns, int64_t count, double *out) {
-    return linear_at_impl(x, act, absval ? 1 : 0, qweight, scales, M, K, N, g, ms, ns, count,
-                          out);
+                        const uint16_t *scales, int stype, int64_t M, int64_t K, int64_t N,
+                        int64_t g, const int64_t *ms, const int64_t *ns, int64_t count,
+                        double *out) {
+    return linear_at_impl(x, act, absval ? 1 : 0, qweight, scales, stype, M, K, N, g, ms, ns,
+                          count, out);
 }
 
 /* ---- LoRA adapter ---- */
@@ -393,7 +420,7 @@ int oracle_lora_expand_at(const double *t, const uint16_t *B, int act, int absva
 
 /* out[m*N + n] <- linear(x)[m,n] + s * sum_j t[m,j] * B[n,j], t = x . A^T. */
 int oracle_linear_lora(const uint16_t *x, int act, const int32_t *qweight,
-                       const uint16_t *scales, const uint16_t *A, const uint16_t *B,
+                       const uint16_t *scales, int stype, const uint16_t *A, const uint16_t *B,
                        double scale, int64_t M, int64_t K, int64_t N, int64_t g, int64_t r,
                        double *out) {
     if (!shape_ok(M, K, N) || !group_ok(K, g) || r <= 0) return OR_ERR_ARG;
@@ -402,7 +429,7 @@ int oracle_linear_lora(const uint16_t *x, int act, const int32_t *qweight,
     double *t = (double *)malloc((size_t)M * (size_t)r * sizeof(double));
     double *d = (double *)malloc((size_t)M * (size_t)N * sizeof(double));
     int rc = (t && d) ? OR_OK : OR_ERR_ARG;
-    if (rc == OR_OK) rc = linear_impl(x, act, 0, qweight, scales, M, K, N, g, out);
+    if (rc == OR_OK) rc = linear_impl(x, act, 0, qweight, scales, stype, M, K, N, g, out);
     if (rc == OR_OK) rc = oracle_lora_shrink(x, A, act, 0, M, K, r, t);
     if (rc == OR_OK) rc = oracle_lora_expand(t, B, act, 0, scale, M, N, r, d);
     if (rc == OR_OK)
@@ -414,19 +441,28 @@ int oracle_linear_lora(const uint16_t *x, int act, const int32_t *qweight,
 
 /* ---- asymmetric weights: stored zero points ---- */
 
-/* Zero point of (group gi, column n): nibble (n mod 8) of qzeros[gi][n/8]. */
+/* Stored nibble of (group gi, column n): nibble (n mod 8) of qzeros[gi][n/8]. */
 static inline unsigned zero_at(const int32_t *qzeros, int64_t N, int64_t gi, int64_t n) {
     uint32_t word;
     memcpy(&word, &qzeros[gi * (N / 8) + n / 8], sizeof word);
     return (word >> (4 * (unsigned)(n % 8))) & 0xFu;
 }
 
+/* Zero point of (group gi, column n): the stored nibble (v2 form), or the
+ * nibble plus one (v1 form, zv1 = 1). */
+static inline int zero_point(const int32_t *qzeros, int zv1, int64_t N, int64_t gi, int64_t n) {
+    return (int)zero_at(qzeros, N, gi, n) + (zv1 ? 1 : 0);
+}
+
 /* y[m*N + n] <- sum_k x[m,k] * (q[k,n] - z[gidx(k),n]) * s[gidx(k),n] in fp64,
- * k ascending, x of type act; absval: sum_k |x| |w| instead. */
+ * k ascending, x of type act, scales of type stype, zero points in the v2
+ * (zv1 = 0) or v1 (zv1 = 1) form; absval: sum_k |x| |w| instead. */
 int oracle_linear_zp(const uint16_t *x, int act, int absval, const int32_t *qweight,
-                     const uint16_t *scales, const int32_t *qzeros, int64_t M, int64_t K,
-                     int64_t N, int64_t g, double *y) {
-    if (!shape_ok(M, K, N) || !group_ok(K, g) || (act != 0 && act != 1)) return OR_ERR_ARG;
+                     const uint16_t *scales, int stype, const int32_t *qzeros, int zv1,
+                     int64_t M, int64_t K, int64_t N, int64_t g, double *y) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || !type_ok(act) || !type_ok(stype) ||
+        !type_ok(zv1))
+        return OR_ERR_ARG;
     if (M == 0) return OR_OK;
     if (!x || !qweight || !scales || !qzeros || !y) return OR_ERR_ARG;
     float *W = (float *)malloc((size_t)K * (size_t)N * sizeof(float));
@@ -435,8 +471,8 @@ int oracle_linear_zp(const uint16_t *x, int act, int absval, const int32_t *qwei
     for (int64_t k = 0; k < K; ++k)
         for (int64_t n = 0; n < N; ++n) {
             const int64_t gi = group_of(k, g);
-            const int q = (int)code_at(qweight, N, k, n), z = (int)zero_at(qzeros, N, gi, n);
-            W[k * N + n] = (float)(q - z) * (float)half_to_double(scales[gi * N + n]);
+            const int q = (int)code_at(qweight, N, k, n), z = zero_point(qzeros, zv1, N, gi, n);
+            W[k * N + n] = (float)(q - z) * (float)scale_to_double(scales[gi * N + n], stype);
         }
     #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m)
@@ -453,10 +489,11 @@ int oracle_linear_zp(const uint16_t *x, int act, int absval, const int32_t *qwei
 /* out[i] <- y[ms[i], ns[i]] of oracle_linear_zp for sampled outputs, each from
  * the definition directly (no dequantised matrix). */
 int oracle_linear_zp_at(const uint16_t *x, int act, const int32_t *qweight,
-                        const uint16_t *scales, const int32_t *qzeros, int64_t M, int64_t K,
-                        int64_t N, int64_t g, const int64_t *ms, const int64_t *ns,
-                        int64_t count, double *out) {
-    if (!shape_ok(M, K, N) || !group_ok(K, g) || count < 0 || (act != 0 && act != 1))
+                        const uint16_t *scales, int stype, const int32_t *qzeros, int zv1,
+                        int64_t M, int64_t K, int64_t N, int64_t g, const int64_t *ms,
+                        const int64_t *ns, int64_t count, double *out) {
+    if (!shape_ok(M, K, N) || !group_ok(K, g) || count < 0 || !type_ok(act) || !type_ok(stype) ||
+        !type_ok(zv1))
         return OR_ERR_ARG;
     if (count == 0) return OR_OK;
     if (!x || !qweight || !scales || !qzeros || !ms || !ns || !out) return OR_ERR_ARG;
@@ -468,8 +505,8 @@ int oracle_linear_zp_at(const uint16_t *x, int act, const int32_t *qweight,
         double acc = 0.0;
         for (int64_t k = 0; k < K; ++k) {
             const int64_t gi = group_of(k, g);
-            const int q = (int)code_at(qweight, N, k, n), z = (int)zero_at(qzeros, N, gi, n);
-            const float w = (float)(q - z) * (float)half_to_double(scales[gi * N + n]);
+            const int q = (int)code_at(qweight, N, k, n), z = zero_point(qzeros, zv1, N, gi, n);
+            const float w = (float)(q - z) * (float)scale_to_double(scales[gi * N + n], stype);
             acc += act_to_double(x[m * K + k], act) * (double)w;
         }
         out[i] = acc;

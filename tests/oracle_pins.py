@@ -26,6 +26,10 @@ when it disagrees with:
     point is 8, numpy's matmul on W built from codes and zero points, a
     hand-derived word 0x76543210 (zero point n at column n), and y == 0
     exactly when every code equals its zero point.
+  - for bfloat16 scales, numpy's own decoding of the scale patterns (values
+    beyond fp16's range both ways) in W built from the codes, and a closed
+    form; for v1 zero points (stored z - 1), W built from codes and nibbles,
+    the all-7 symmetric checkpoint and the z = 16 closed form.
   - for the dense form (numpy's float64 matmul as the product step), the
     oracle's decoding of every fp16 and bfloat16 pattern against numpy's, and
     agreement with the triple loop within fp64 reordering (bit for bit on
@@ -658,6 +662,108 @@ def pin_dense_matches_triple_loop(o):
     x = rng.integers(-4, 5, size=(M, K)).astype(np.float16)
     q = o.pack(codes)
     assert np.array_equal(o.linear_dense(x, q, scales, 64), o.linear(x, q, scales, 64))
+
+
+
+# --- bfloat16 scales and v1 zero points ---------------------------------------------
+
+def _bf16_bits_random(rng, shape, lo_exp, hi_exp):
+    """Random positive bfloat16 bit patterns with exponents in [lo_exp, hi_exp]
+    (values 2^e (1 + f/128)); the range runs past fp16's in both directions."""
+    e = rng.integers(lo_exp, hi_exp + 1, size=shape)
+    f = rng.integers(0, 128, size=shape)
+    return (((e + 127) << 7) | f).astype(np.uint16)
+
+
+def pin_bf16_scales_against_numpy(o):
+    """bfloat16 scales (bit patterns, values from 2^-30 to 2^20, outside fp16's
+    range both ways): W = (q - 8) s built in numpy from the codes and numpy's
+    own decoding of the scales, products by numpy's matmul in fp64, against
+    linear, linear_at, dequant, gate_up_silu, linear_lora and linear_zp (zero
+    points 8) with either activation type; and a closed form: x all ones, every
+    code 9, scale 3 * 2^20 (bits 0x4A40) gives y = 3 * 2^20 * K exactly."""
+    rng = np.random.default_rng(46)
+    for M, K, N, g in ((2, 64, 16, 16), (3, 272, 24, 128), (1, 96, 40, -1), (4, 160, 8, 32)):
+        G = 1 if g == -1 else -(-K // g)
+        grp = np.zeros(K, dtype=np.int64) if g == -1 else np.arange(K) // g
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        sb = _bf16_bits_random(rng, (G, N), -30, 20)
+        sv = _bf16_value(sb)
+        W = (codes.astype(np.float64) - 8.0) * sv[grp]
+        q = o.pack(codes)
+        assert np.array_equal(o.dequant(q, sb, g, scales_type="bf16").astype(np.float64), W)
+        xh = rng.standard_normal((M, K)).astype(np.float16)
+        xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        for x, act, xv in ((xh, "f16", xh.astype(np.float64)), (xb, "bf16", _bf16_value(xb))):
+            ref = xv @ W
+            tol = 1e-12 * (np.abs(xv) @ np.abs(W)) + 1e-300
+            y = o.linear(x, q, sb, g, act=act, scales_type="bf16")
+            assert np.all(np.abs(y - ref) <= tol), (M, K, N, g, act)
+            ms = rng.integers(0, M, size=20)
+            ns = rng.integers(0, N, size=20)
+            assert np.array_equal(o.linear_at(x, q, sb, g, ms, ns, act=act, scales_type="bf16"),
+                                  y[ms, ns])
+            if N % 2 == 0:
+                gu = o.gate_up_silu(x, q, sb, g, act=act, scales_type="bf16")
+                gg, uu = y[:, 0::2], y[:, 1::2]
+                with np.errstate(over="ignore"):
+                    ref_gu = gg / (1.0 + np.exp(-gg)) * uu
+                fin = np.isfinite(ref_gu)
+                assert np.allclose(gu[fin], ref_gu[fin], rtol=1e-12, atol=0.0)
+            qz = _pack_zeros(o, np.full((G, N), 8, dtype=np.uint8))
+            assert np.array_equal(o.linear_zp(x, q, sb, qz, g, act=act, scales_type="bf16"), y)
+        r = 8
+        A = rng.standard_normal((r, K)).astype(np.float16)
+        B = rng.standard_normal((N, r)).astype(np.float16)
+        yl = o.linear_lora(xh, q, sb, g, A, B, 0.5, scales_type="bf16")
+        refl = xh.astype(np.float64) @ (W + 0.5 * A.astype(np.float64).T @ B.astype(np.float64).T)
+        magl = np.abs(xh.astype(np.float64)) @ (np.abs(W) + 0.5 * np.abs(A.astype(np.float64)).T
+                                                @ np.abs(B.astype(np.float64)).T)
+        assert np.all(np.abs(yl - refl) <= 1e-12 * magl + 1e-300)
+    K, N = 48, 8
+    ones = np.ones((1, K), dtype=np.float16)
+    y = o.linear(ones, o.pack(np.full((K, N), 9, dtype=np.uint8)),
+                 np.full((1, N), 0x4A40, dtype=np.uint16), -1, scales_type="bf16")
+    assert np.all(y == 3.0 * 2.0 ** 20 * K)
+
+
+def pin_zp_v1_form(o):
+    """v1 zero points (stored z - 1): W = (q - (nibble + 1)) s built in numpy from
+    the codes and nibbles (15 gives z = 16), products by numpy's matmul, with
+    fp16 and bfloat16 scales; a symmetric checkpoint in v1 form (every nibble
+    7, word 0x77777777) is bit for bit the symmetric linear; code 0 under
+    nibble 15 gives w = -16 s exactly; sampled outputs equal the full ones."""
+    rng = np.random.default_rng(47)
+    for M, K, N, g in ((2, 64, 16, 16), (3, 272, 24, 128), (1, 96, 40, -1)):
+        G = 1 if g == -1 else -(-K // g)
+        grp = np.zeros(K, dtype=np.int64) if g == -1 else np.arange(K) // g
+        codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+        nib = rng.integers(0, 16, size=(G, N), dtype=np.uint8)
+        nib[0, 0] = 15
+        q, qz = o.pack(codes), _pack_zeros(o, nib)
+        sh = rng.uniform(1e-2, 8e-2, size=(G, N)).astype(np.float16)
+        sb = _bf16_bits_random(rng, (G, N), -12, 3)
+        x = rng.standard_normal((M, K)).astype(np.float16)
+        xv = x.astype(np.float64)
+        for sc, st, sv in ((sh, "f16", sh.astype(np.float64)), (sb, "bf16", _bf16_value(sb))):
+            W = (codes.astype(np.float64) - (nib.astype(np.float64) + 1.0)[grp]) * sv[grp]
+            y = o.linear_zp(x, q, sc, qz, g, scales_type=st, zeros="v1")
+            ref = xv @ W
+            assert np.all(np.abs(y - ref) <= 1e-12 * (np.abs(xv) @ np.abs(W)) + 1e-300), (g, st)
+            ms = rng.integers(0, M, size=16)
+            ns = rng.integers(0, N, size=16)
+            assert np.array_equal(o.linear_zp_at(x, q, sc, qz, g, ms, ns, scales_type=st,
+                                                 zeros="v1"), y[ms, ns])
+        q7 = _pack_zeros(o, np.full((G, N), 7, dtype=np.uint8))
+        assert np.all(q7.view(np.uint32) == 0x77777777)
+        assert np.array_equal(o.linear_zp(x, q, sh, q7, g, zeros="v1"), o.linear(x, q, sh, g))
+    K, N = 16, 8
+    e0 = np.zeros((1, K), dtype=np.float16)
+    e0[0, 0] = 1.0
+    s = np.full((1, N), 0.5, dtype=np.float16)
+    y = o.linear_zp(e0, o.pack(np.zeros((K, N), dtype=np.uint8)), s,
+                    _pack_zeros(o, np.full((1, N), 15, dtype=np.uint8)), -1, zeros="v1")
+    assert np.all(y == -8.0)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

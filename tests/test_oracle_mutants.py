@@ -33,6 +33,14 @@ MUTANTS = {
     "half_subnormal_scale": ("ldexp((double)man, -24)", "ldexp((double)man, -23)"),
     "half_sign_dropped": ("return sign ? -v : v;", "return v;"),
     "scale_column_offset": ("scales[group_of(k, g) * N + n]", "scales[group_of(k, g) * N + (n ^ 1)]"),
+    "bf16_scale_read_as_half": ("return stype == 1 ? bf16_to_double(h) : half_to_double(h);",
+                                "return half_to_double(h);"),
+    "zp_v1_ignored": ("return (int)zero_at(qzeros, N, gi, n) + (zv1 ? 1 : 0);",
+                      "return (int)zero_at(qzeros, N, gi, n);"),
+    "zp_v1_subtracts": ("return (int)zero_at(qzeros, N, gi, n) + (zv1 ? 1 : 0);",
+                        "return (int)zero_at(qzeros, N, gi, n) - (zv1 ? 1 : 0);"),
+    "zp_scales_read_as_half": ("(float)scale_to_double(scales[gi * N + n], stype);\n            acc",
+                               "(float)half_to_double(scales[gi * N + n]);\n            acc"),
     "lora_a_transposed": ("act_to_double(A[j * K + k], act)", "act_to_double(A[k * r + j], act)"),
     "lora_b_row_offset": ("act_to_double(B[n * r + j], act)", "act_to_double(B[(n ^ 1) * r + j], act)"),
     "lora_scale_dropped": ("return (absval ? fabs(scale) : scale) * acc;", "return acc;"),
@@ -42,7 +50,8 @@ MUTANTS = {
     "zp_v1_offset": ("return (word >> (4 * (unsigned)(n % 8))) & 0xFu;",
                      "return ((word >> (4 * (unsigned)(n % 8))) & 0xFu) + 1u;"),
     "zp_added": ("(float)(q - z)", "(float)(q + z - 16)"),
-    "zp_row_of_k": ("zero_at(qzeros, N, gi, n)", "zero_at(qzeros, N, k / 8 % (gi + 1), n)"),
+    "zp_row_of_k": ("zero_point(qzeros, zv1, N, gi, n)",
+                    "zero_point(qzeros, zv1, N, k / 8 % (gi + 1), n)"),
     "decode_act_as_half": ("out[i] = act_to_double(x[i], act);", "out[i] = act_to_double(x[i], 0);"),
     "lora_last_rank_dropped": ("for (int64_t j = 0; j < r; ++j)\n        acc +=",
                                "for (int64_t j = 0; j + 1 < r; ++j)\n        acc +="),
