@@ -86,8 +86,10 @@ typedef enum {
     W4A16_ERR_WORKSPACE = 10, /* workspace smaller than w4a16_lora_workspace_bytes or
                                  w4a16_zp_workspace_bytes gives */
     W4A16_ERR_CAPTURE = 11,   /* w4a16_stream_release: the stream is being captured */
-    W4A16_ERR_SCRATCH = 12    /* w4a16_linear_noalloc: the device has more CUs than its
+    W4A16_ERR_SCRATCH = 12,   /* w4a16_linear_noalloc: the device has more CUs than its
                                  scratch covers */
+    W4A16_ERR_FLAGS = 13      /* w4a16_linear_typed: an unknown flag bit, or flags that
+                                 cannot go together */
 } w4a16_status;
 
 /* Largest M the small-batch (decode) kernel takes; larger M runs the MFMA
@@ -241,8 +243,8 @@ size_t w4a16_lora_workspace_bytes(int64_t M, int64_t K, int64_t rank);
  * the v1 and v2 checkpoint formats store them differently.
  *   qzeros : device int32 [G, N/8], 16-byte aligned: nibble j (bits 4j..4j+3)
  *     of word [g][c] is the zero point of column 8c + j, read as unsigned and
- *     used as stored (a v1 checkpoint's z - 1 becomes z by adding one before
- *     the call).  It is pack_gptq_v2 applied to the transposed [N, G] zero
+ *     used as stored (the v2 form; w4a16_linear_typed with W4A16_ZEROS_V1
+ *     takes the v1 form).  It is pack_gptq_v2 applied to the transposed [N, G] zero
  *     points, transposed back.
  *   workspace : device buffer of at least w4a16_zp_workspace_bytes(M, K, N,
  *     group_size) bytes, 16-byte aligned, no initial contents, owned by the
@@ -279,6 +281,47 @@ int w4a16_linear_zp_bf16(const void *x, const int32_t *qweight, const void *scal
  * up to 16, Gp] and the correction matrix C^T [N, Gp] in the activation type,
  * Gp = G rounded up to 8.  0 for M <= 0 or arguments it rejects. */
 size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
+
+/* Flags of w4a16_linear_typed. */
+#define W4A16_X_BF16 0x1u        /* x and y bfloat16, else fp16 */
+#define W4A16_SCALES_BF16 0x2u   /* scales bfloat16, else fp16; needs W4A16_X_BF16 */
+#define W4A16_ZEROS_V1 0x4u      /* qzeros in the v1 checkpoint form; needs qzeros */
+#define W4A16_GATE_UP_SILU 0x8u  /* merged gate/up with SiLU * mul; not with qzeros */
+
+/* Every variant of the linear behind one call, chosen by flags (bitwise OR of
+ * the W4A16_ flags above) and by whether qzeros is null:
+ *   - qzeros null: w4a16_linear_ex (no flags), w4a16_linear_bf16_ex
+ *     (W4A16_X_BF16), w4a16_gate_up_silu_ex / _bf16_ex (W4A16_GATE_UP_SILU);
+ *     workspace is not used and may be null;
+ *   - qzeros given: w4a16_linear_zp / _bf16, steps as there, with `kernel`
+ *     choosing them: W4A16_KERNEL_AUTO as w4a16_linear_zp, W4A16_KERNEL_DECODE
+ *     the one-launch decode path (M <= W4A16_DECODE_MAX_M, else
+ *     W4A16_ERR_KERNEL), W4A16_KERNEL_PREFILL the symmetric prefill linear
+ *     followed by the correction.  The workspace (w4a16_zp_workspace_bytes,
+ *     as for w4a16_linear_zp) is needed only on the correction path and may
+ *     be null on the one-launch path.
+ * W4A16_SCALES_BF16: scales are bfloat16 bit patterns.  A checkpoint served
+ * in bfloat16 carries its scales in that dtype ("Qwen3.8-27B-GPTQ-Int4" model
+ * card, "4. Deployment": the verified serving command uses the bfloat16
+ * dtype).  Each scale enters the arithmetic exactly where an fp16 scale does
+ * on the bfloat16 path (both convert to fp32 exactly), so the error bounds of
+ * the bfloat16 forms hold unchanged.  fp16 activations take fp16 scales only
+ * (W4A16_ERR_FLAGS).
+ * W4A16_ZEROS_V1: the nibble holds z - 1, so z = nibble + 1, in [1, 16].  The
+ * pages name a GPTQ v1 checkpoint form beside v2 ("GPT-QModel" README, "Quant
+ * Method / Format / Backend Matrix"; "Norm tuning": v1 zero points read as
+ * they are decode the weights wrongly) but print no rule; this is the
+ * published GPTQ one, under which a symmetric checkpoint stores 7 in every
+ * nibble.
+ * Everything else (pointers, shapes, group sizes, alignment, determinism,
+ * the bounds) as for the entry point each combination names above.  Returns
+ * W4A16_ERR_FLAGS for an unknown bit, W4A16_SCALES_BF16 without
+ * W4A16_X_BF16, W4A16_ZEROS_V1 without qzeros, or W4A16_GATE_UP_SILU with
+ * qzeros, before any HIP call. */
+int w4a16_linear_typed(const void *x, const int32_t *qweight, const void *scales,
+                       const int32_t *qzeros, void *y, int64_t M, int64_t K, int64_t N,
+                       int64_t group_size, unsigned flags, int kernel, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* Frees the workspaces the library holds for `stream` on the current device
  * (a hipStream_t, 0 = null stream), after waiting for the work queued on it.

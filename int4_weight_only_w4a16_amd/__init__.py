@@ -10,10 +10,11 @@ Names match the C ABI in ``include/w4a16.h``:
   w4a16_linear_bf16_ex,
   w4a16_gate_up_silu(_ex, _bf16, _bf16_ex), w4a16_linear_lora(_bf16),
   w4a16_lora_workspace_bytes, w4a16_linear_zp(_bf16), w4a16_zp_workspace_bytes,
-  w4a16_stream_release, pack_gptq_v2, unpack_gptq_v2,
+  w4a16_linear_typed, w4a16_stream_release, pack_gptq_v2, unpack_gptq_v2,
   w4a16_status_string, and the measurement aid w4a16_read_probe
 plus ``linear``, ``gate_up_silu``, ``linear_lora`` and ``linear_zp`` (allocate
-y, and a workspace, with torch, then call the entry point of x's dtype).
+y, and a workspace, with torch, then call the entry point of x's and the
+scales' dtypes).
 """
 
 from __future__ import annotations
@@ -40,6 +41,7 @@ W4A16_ERR_RANK = 9
 W4A16_ERR_WORKSPACE = 10
 W4A16_ERR_CAPTURE = 11
 W4A16_ERR_SCRATCH = 12
+W4A16_ERR_FLAGS = 13
 W4A16_LORA_MAX_RANK = 1024
 
 W4A16_DECODE_MAX_M = 16
@@ -47,11 +49,17 @@ W4A16_KERNEL_AUTO = 0
 W4A16_KERNEL_DECODE = 1
 W4A16_KERNEL_PREFILL = 2
 
+W4A16_X_BF16 = 0x1
+W4A16_SCALES_BF16 = 0x2
+W4A16_ZEROS_V1 = 0x4
+W4A16_GATE_UP_SILU = 0x8
+
 EXPORTS = ("w4a16_linear", "w4a16_linear_noalloc", "w4a16_linear_ex", "w4a16_linear_bf16", "w4a16_linear_bf16_ex",
            "w4a16_gate_up_silu", "w4a16_gate_up_silu_ex", "w4a16_gate_up_silu_bf16",
            "w4a16_gate_up_silu_bf16_ex", "w4a16_linear_lora", "w4a16_linear_lora_bf16",
            "w4a16_lora_workspace_bytes", "w4a16_linear_zp", "w4a16_linear_zp_bf16",
-           "w4a16_zp_workspace_bytes", "w4a16_stream_release", "pack_gptq_v2", "unpack_gptq_v2",
+           "w4a16_zp_workspace_bytes", "w4a16_linear_typed", "w4a16_stream_release",
+           "pack_gptq_v2", "unpack_gptq_v2",
            "w4a16_read_probe", "w4a16_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -101,6 +109,9 @@ def load_library() -> ctypes.CDLL:
         getattr(lib, name).restype = i32
     lib.w4a16_zp_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.w4a16_zp_workspace_bytes.restype = sz
+    lib.w4a16_linear_typed.argtypes = [p, p, p, p, p, i64, i64, i64, i64, ctypes.c_uint, i32, p,
+                                       sz, p]
+    lib.w4a16_linear_typed.restype = i32
     lib.w4a16_stream_release.argtypes = [p]
     lib.w4a16_stream_release.restype = i32
     lib.pack_gptq_v2.argtypes = [p, p, i64, i64]
@@ -221,14 +232,12 @@ def w4a16_gate_up_silu_bf16(x, qweight, scales, y, M: int, K: int, N: int, group
 def gate_up_silu(x, qweight, scales, group_size: int, out=None, stream=None,
                  kernel: int = W4A16_KERNEL_AUTO):
     """Allocate y ([M, N/2], x's dtype) and run the merged gate/up projection with
-    SiLU * mul (columns of qweight and scales alternate gate and up)."""
+    SiLU * mul (columns of qweight and scales alternate gate and up); scales
+    fp16, or bfloat16 with bfloat16 x."""
     import torch
-    if x.dtype not in (torch.float16, torch.bfloat16):
-        raise ValueError("x must be float16 or bfloat16")
-    for name, t, dt in (("x", x, x.dtype), ("qweight", qweight, torch.int32),
-                        ("scales", scales, torch.float16)):
-        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    flags = _type_flags(x, scales)
+    _check_tensors(("x", x, x.dtype), ("qweight", qweight, torch.int32),
+                   ("scales", scales, scales.dtype))
     M, K = x.shape
     N = qweight.shape[1]
     if qweight.shape[0] * 8 != K:
@@ -237,8 +246,12 @@ def gate_up_silu(x, qweight, scales, group_size: int, out=None, stream=None,
         out = torch.empty((M, N // 2), dtype=x.dtype, device=x.device)
     elif out.dtype != x.dtype:
         raise ValueError("out must have x's dtype")
-    w4a16_gate_up_silu_ex(x, qweight, scales, out, M, K, N, group_size, stream, kernel,
-                          x.dtype == torch.bfloat16)
+    if flags & W4A16_SCALES_BF16:
+        w4a16_linear_typed(x, qweight, scales, None, out, M, K, N, group_size,
+                           flags | W4A16_GATE_UP_SILU, kernel, stream=stream)
+    else:
+        w4a16_gate_up_silu_ex(x, qweight, scales, out, M, K, N, group_size, stream, kernel,
+                              x.dtype == torch.bfloat16)
     return out
 
 
@@ -335,16 +348,17 @@ def pack_zeros(zeros: np.ndarray) -> np.ndarray:
 
 
 def linear_zp(x, qweight, scales, qzeros, group_size: int, out=None, workspace=None,
-              stream=None):
+              stream=None, zeros_format: str = "v2", kernel: int = W4A16_KERNEL_AUTO):
     """Allocate y (x's dtype, [M, N]) and, unless given, the workspace with torch, then
-    run the linear with stored zero points (qzeros int32 [G, N/8])."""
+    run the linear with stored zero points (qzeros int32 [G, N/8]; zeros_format "v2":
+    each nibble is the zero point, "v1": the zero point minus one).  Scales fp16,
+    or bfloat16 with bfloat16 x."""
     import torch
-    if x.dtype not in (torch.float16, torch.bfloat16):
-        raise ValueError("x must be float16 or bfloat16")
-    for name, t, dt in (("x", x, x.dtype), ("qweight", qweight, torch.int32),
-                        ("scales", scales, torch.float16), ("qzeros", qzeros, torch.int32)):
-        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    flags = _type_flags(x, scales)
+    if zeros_format not in ("v1", "v2"):
+        raise ValueError("zeros_format must be 'v1' or 'v2'")
+    _check_tensors(("x", x, x.dtype), ("qweight", qweight, torch.int32),
+                   ("scales", scales, scales.dtype), ("qzeros", qzeros, torch.int32))
     M, K = x.shape
     N = qweight.shape[1]
     if qweight.shape[0] * 8 != K or tuple(qzeros.shape) != (scales.shape[0], N // 8):
@@ -356,10 +370,50 @@ def linear_zp(x, qweight, scales, qzeros, group_size: int, out=None, workspace=N
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     elif out.dtype != x.dtype:
         raise ValueError("out must have x's dtype")
-    w4a16_linear_zp(x, qweight, scales, qzeros, out, M, K, N, group_size, workspace,
-                    workspace.numel() * workspace.element_size(), stream,
-                    x.dtype == torch.bfloat16)
+    if zeros_format == "v1":
+        flags |= W4A16_ZEROS_V1
+    nbytes = workspace.numel() * workspace.element_size()
+    if flags & (W4A16_SCALES_BF16 | W4A16_ZEROS_V1) or kernel != W4A16_KERNEL_AUTO:
+        w4a16_linear_typed(x, qweight, scales, qzeros, out, M, K, N, group_size, flags, kernel,
+                           workspace, nbytes, stream)
+    else:
+        w4a16_linear_zp(x, qweight, scales, qzeros, out, M, K, N, group_size, workspace, nbytes,
+                        stream, x.dtype == torch.bfloat16)
     return out
+
+
+def w4a16_linear_typed(x, qweight, scales, qzeros, y, M: int, K: int, N: int, group_size: int,
+                       flags: int, kernel: int = W4A16_KERNEL_AUTO, workspace=None,
+                       workspace_bytes: int = 0, stream=None) -> None:
+    """Same as the C ``w4a16_linear_typed``: the variant chosen by flags
+    (W4A16_X_BF16, W4A16_SCALES_BF16, W4A16_ZEROS_V1, W4A16_GATE_UP_SILU) and by
+    whether qzeros is None; raises W4A16Error on a nonzero status."""
+    st = load_library().w4a16_linear_typed(_addr(x), _addr(qweight), _addr(scales),
+                                           _addr(qzeros), _addr(y), int(M), int(K), int(N),
+                                           int(group_size), int(flags), int(kernel),
+                                           _addr(workspace), int(workspace_bytes),
+                                           _stream_handle(stream))
+    if st != W4A16_OK:
+        raise W4A16Error(st, "w4a16_linear_typed")
+
+
+def _type_flags(x, scales) -> int:
+    """Flags for x's and the scales' dtypes (fp16 x takes fp16 scales only)."""
+    import torch
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be float16 or bfloat16")
+    if scales.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("scales must be float16 or bfloat16")
+    if scales.dtype == torch.bfloat16 and x.dtype != torch.bfloat16:
+        raise ValueError("bfloat16 scales need bfloat16 x")
+    return ((W4A16_X_BF16 if x.dtype == torch.bfloat16 else 0)
+            | (W4A16_SCALES_BF16 if scales.dtype == torch.bfloat16 else 0))
+
+
+def _check_tensors(*specs) -> None:
+    for name, t, dt in specs:
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
 
 
 def w4a16_read_probe(data, nbytes: int, sink, stream=None) -> None:
@@ -398,14 +452,12 @@ def linear(x, qweight, scales, group_size: int, out=None, stream=None,
     """Allocate y (x's dtype, [M, N]) with torch on x's device and run the linear.
 
     x: fp16 or bfloat16 [M, K] (y has the same dtype); qweight: int32 [K/8, N];
-    scales: fp16 [G, N]; all CUDA (HIP) tensors, contiguous."""
+    scales: fp16 [G, N], or bfloat16 with bfloat16 x; all CUDA (HIP) tensors,
+    contiguous."""
     import torch
-    if x.dtype not in (torch.float16, torch.bfloat16):
-        raise ValueError("x must be float16 or bfloat16")
-    for name, t, dt in (("x", x, x.dtype), ("qweight", qweight, torch.int32),
-                        ("scales", scales, torch.float16)):
-        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    flags = _type_flags(x, scales)
+    _check_tensors(("x", x, x.dtype), ("qweight", qweight, torch.int32),
+                   ("scales", scales, scales.dtype))
     M, K = x.shape
     N = qweight.shape[1]
     if qweight.shape[0] * 8 != K:
@@ -414,6 +466,10 @@ def linear(x, qweight, scales, group_size: int, out=None, stream=None,
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     elif out.dtype != x.dtype:
         raise ValueError("out must have x's dtype")
-    call = w4a16_linear_bf16_ex if x.dtype == torch.bfloat16 else w4a16_linear_ex
-    call(x, qweight, scales, out, M, K, N, group_size, stream, kernel)
+    if flags & W4A16_SCALES_BF16:
+        w4a16_linear_typed(x, qweight, scales, None, out, M, K, N, group_size, flags, kernel,
+                           stream=stream)
+    else:
+        call = w4a16_linear_bf16_ex if x.dtype == torch.bfloat16 else w4a16_linear_ex
+        call(x, qweight, scales, out, M, K, N, group_size, stream, kernel)
     return out

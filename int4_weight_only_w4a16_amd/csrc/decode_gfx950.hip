@@ -121,6 +121,13 @@ __device__ __forceinline__ _Float16 scale_at(const u2 &s, int j) {
     return (j & 1) ? half_hi(d) : half_lo(d);
 }
 
+// Scale j of the lane's quad as fp32 (exact): bfloat16 when SB, else fp16.
+template <bool SB>
+__device__ __forceinline__ float scale_f32(const u2 &s, int j) {
+    const uint32_t d = j < 2 ? s.x : s.y;
+    return (j & 1) ? hi_f32<SB>(d) : lo_f32<SB>(d);
+}
+
 
 // One wave's pass over a contiguous range [w0, w1) of units (tile-major:
 // unit u = tile u / S, step u % S).  The host keeps w1 - w0 <= S, so the
@@ -157,15 +164,21 @@ __device__ __forceinline__ _Float16 scale_at(const u2 &s, int j) {
 // column, in fp32.  With every z = 8 the added term is 0.  For SCALE 0 (two
 // groups in a unit) the zero point enters the dequantised weight instead: fp16
 // adds 8 - z to the exact q - 8 before the scale, bfloat16 takes -z s as the
-// offset of its fma.
-template <int D, int SCALE, bool XLDS, bool BF, bool ZP, typename Dump, typename AfterPrologue>
+// offset of its fma.  z is the stored nibble plus a bias (0 for the v2 form,
+// 1 for the v1 form): z8 = 8 - bias, and 8 - z = z8 - nibble.
+// SB: bfloat16 scales (with BF only), taken to fp32 exactly wherever the
+// bfloat16 paths take an fp16 scale to fp32.
+template <int D, int SCALE, bool XLDS, bool BF, bool ZP, bool SB, typename Dump,
+          typename AfterPrologue>
 __device__ __forceinline__ void decode_units(
     const __amdgpu_buffer_rsrc_t xr, const __amdgpu_buffer_rsrc_t qr,
-    const __amdgpu_buffer_rsrc_t sr, const __amdgpu_buffer_rsrc_t zr, const unsigned char *xs,
+    const __amdgpu_buffer_rsrc_t sr, const __amdgpu_buffer_rsrc_t zr, int z8,
+    const unsigned char *xs,
     int M, int K, int N, int S,
     int group_steps, int w0, int w1, Dump &&dump, AfterPrologue &&after_prologue,
     int xstep0 = 0) {
     constexpr bool SCALE_AFTER = SCALE != 0;
+    static_assert(BF || !SB, "bfloat16 scales come with bfloat16 activations");
     const int lane = threadIdx.x & 63;
     const int kb = lane >> 4;
     const int c16 = lane & 15;
@@ -236,7 +249,7 @@ __device__ __forceinline__ void decode_units(
                        : u4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
     // zero point of column j of the lane's quad, as 8 - z
     auto zdiff = [&](const Stage<XLDS> &st, int j) -> int {
-        return 8 - (int)((st.z >> (zsh + 4u * (uint32_t)j)) & 15u);
+        return z8 - (int)((st.z >> (zsh + 4u * (uint32_t)j)) & 15u);
     };
 #pragma unroll
     for (int j = 0; j < kNW; ++j) {
@@ -272,7 +285,7 @@ __device__ __forceinline__ void decode_units(
         if constexpr (BF && SCALE == 0) {
 #pragma unroll
             for (int j = 0; j < kNW; ++j) {
-                const float sj = (float)scale_at(st.s, j);
+                const float sj = scale_f32<SB>(st.s, j);
                 const float zoff = ZP ? (float)(zdiff(st, j) - 8) * sj : -8.0f * sj;   // -z s
                 acc[j] = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a),
                                               dequant_bf16<false>(st.w[j], sj, zoff), acc[j]);
@@ -288,7 +301,7 @@ __device__ __forceinline__ void decode_units(
             for (int j = 0; j < kNW; ++j) {
                 const f4 t = mfma16x16x32_t<true>(__builtin_bit_cast(u4, a), codes128_bf16(st.w[j], uc),
                                                   zero);
-                const float sj = (float)scale_at(st.s, j);
+                const float sj = scale_f32<SB>(st.s, j);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[j][e] = __builtin_fmaf(sj, t[e] - tx[e], acc[j][e]);
                 if constexpr (ZP) {
@@ -308,7 +321,7 @@ __device__ __forceinline__ void decode_units(
             if (pos == group_steps - 1 || seg_end) {
 #pragma unroll
                 for (int j = 0; j < kNW; ++j) {
-                    const float sj = (float)scale_at(st.s, j);
+                    const float sj = scale_f32<SB>(st.s, j);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[j][e] = __builtin_fmaf(sj, accg[j][e] - accx[e], acc[j][e]);
@@ -329,7 +342,7 @@ __device__ __forceinline__ void decode_units(
 #pragma unroll
             for (int j = 0; j < kNW; ++j) {
                 const f4 t = mfma16x16x32(a, unpack_codes(st.w[j], uc), zero);
-                const float sj = (float)scale_at(st.s, j);
+                const float sj = scale_f32<SB>(st.s, j);
                 acc[j] += sj * t;
                 if constexpr (ZP) acc[j] += (sj * (float)zdiff(st, j)) * tz;
             }
@@ -341,7 +354,7 @@ __device__ __forceinline__ void decode_units(
             if (pos == group_steps - 1 || seg_end) {
 #pragma unroll
                 for (int j = 0; j < kNW; ++j) {
-                    const float sj = (float)scale_at(st.s, j);
+                    const float sj = scale_f32<SB>(st.s, j);
                     acc[j] += sj * accg[j];
                     if constexpr (ZP) acc[j] += (sj * (float)zdiff(st, j)) * accz;
                     accg[j] = zero;
@@ -399,12 +412,12 @@ constexpr size_t streamk_static_lds(int waves) {
 }
 
 // Tiles kernel: one workgroup per column tile, its waves split K.
-template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP>
+template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP, bool SB>
 __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const int32_t *__restrict__ qzeros,
     uint16_t *__restrict__ y, int M, int K, int N,
-    int group_steps) {
+    int group_steps, int z8) {
     __shared__ f4 red[WAVES][kNW][64];
     static_assert(sizeof(red) == tiles_static_lds(WAVES), "tiles kernel LDS layout");
 
@@ -427,8 +440,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
     __builtin_amdgcn_sched_barrier(0);
-    decode_units<D, SCALE, XLDS, BF, ZP>(
-        xr, qr, sr, zr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
+    decode_units<D, SCALE, XLDS, BF, ZP, SB>(
+        xr, qr, sr, zr, z8, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int, const f4(&acc)[kNW]) {
 #pragma unroll
             for (int j = 0; j < kNW; ++j) red[wave][j][lane] = acc[j];
@@ -508,12 +521,12 @@ __host__ __device__ __forceinline__ int wave_share(int n, int w) {
     return nold + (n - nold) * (w - H) / (WAVES - H);
 }
 
-template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP>
+template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP, bool SB>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const int32_t *__restrict__ qzeros,
     uint16_t *__restrict__ y, int M, int K, int N,
-    int group_steps, uint64_t *__restrict__ slots, float *__restrict__ partials) {
+    int group_steps, int z8, uint64_t *__restrict__ slots, float *__restrict__ partials) {
     constexpr int SLOT = 16 * kCols;             // floats per partial slot
     // Wave partials: block s*WAVES + w (256 f4: [lane][i]) holds wave w's
     // sums of its segment s, row i of the lane's quad, its four columns
@@ -546,8 +559,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
     __builtin_amdgcn_sched_barrier(0);
-    decode_units<D, SCALE, XLDS, BF, ZP>(
-        xr, qr, sr, zr, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
+    decode_units<D, SCALE, XLDS, BF, ZP, SB>(
+        xr, qr, sr, zr, z8, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
         [&](int slot, const f4(&acc)[kNW]) {
             if (slot > 1) return;   // cannot happen: ranges hold <= S units
 #pragma unroll
@@ -768,7 +781,7 @@ static size_t static_lds(const void *kernel) {
     return attr.sharedSizeBytes;
 }
 
-template <int SCALE, bool XLDS, bool BF, bool SILU, bool ZP>
+template <int SCALE, bool XLDS, bool BF, bool SILU, bool ZP, bool SB>
 static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *workspace,
                             int capacity, int grid) {
     const int K = (int)a.K, N = (int)a.N, M = (int)a.M;
@@ -779,6 +792,7 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
     const void *qp = a.qweight;
     const void *sp = a.scales;
     const void *zp = a.qzeros;
+    int z8 = 8 - a.zero_bias;
     void *yp = a.y;
     const dim3 block(kDecWaves * 64);
     const size_t dyn = XLDS ? (size_t)M * 32 * S * 2 + 16 : 0;
@@ -789,10 +803,10 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
         const bool part = uses_partials(grid, T, M);
         float *partials = part ? reinterpret_cast<float *>(ws + slots_bytes(capacity)) : nullptr;
         void *args[] = {&xp, &qp, &sp, &zp, &yp, (void *)&M, (void *)&K, (void *)&N,
-                        &group_steps, &slots, &partials};
+                        &group_steps, &z8, &slots, &partials};
         hipError_t e = hipLaunchKernel(
             reinterpret_cast<const void *>(
-                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP>),
+                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP, SB>),
             dim3(grid), block, args, dyn, stream);
         if (e != hipSuccess || !part) return e;
         const float *pc = partials;
@@ -801,11 +815,12 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
         return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel<BF, SILU>),
                                dim3((unsigned)T), dim3(256), rargs, 0, stream);
     }
-    void *args[] = {&xp, &qp, &sp, &zp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps};
+    void *args[] = {&xp, &qp, &sp, &zp, &yp, (void *)&M, (void *)&K, (void *)&N, &group_steps,
+                    &z8};
     const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);
     return hipLaunchKernel(
         reinterpret_cast<const void *>(
-            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP>),
+            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP, SB>),
         dim3(tiles), block, args, dyn, stream);
 }
 
@@ -817,43 +832,47 @@ static bool stage_fits(const LinearArgs &a, int grid, size_t max_lds) {
     const size_t dyn = (size_t)a.M * 32 * ((a.K + 31) / 32) * 2 + 16;
     if (dyn > kXStageMax) return false;
     static const size_t sk_static = static_lds(reinterpret_cast<const void *>(
-        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true, BF, false, false>));
+        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true, BF, false, false, false>));
     static const size_t tiles_static = static_lds(reinterpret_cast<const void *>(
-        &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true, BF, false, false>));
+        &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true, BF, false, false, false>));
     const size_t st = grid > 0 ? sk_static : tiles_static;
     return st != (size_t)-1 && st + dyn <= max_lds;
 }
 
-template <int SCALE, bool BF>
+template <int SCALE, bool BF, bool SB>
 static hipError_t launch_scale(const LinearArgs &a, hipStream_t stream, void *workspace,
                                int capacity, int grid, size_t max_lds) {
     const bool xlds = stage_fits<SCALE, BF>(a, grid, max_lds);
     if (a.qzeros)   // stored zero points (never with the merged gate/up epilogue)
-        return xlds ? launch_sa<SCALE, true, BF, false, true>(a, stream, workspace, capacity, grid)
-                    : launch_sa<SCALE, false, BF, false, true>(a, stream, workspace, capacity, grid);
+        return xlds ? launch_sa<SCALE, true, BF, false, true, SB>(a, stream, workspace, capacity, grid)
+                    : launch_sa<SCALE, false, BF, false, true, SB>(a, stream, workspace, capacity, grid);
     if (a.silu)
-        return xlds ? launch_sa<SCALE, true, BF, true, false>(a, stream, workspace, capacity, grid)
-                    : launch_sa<SCALE, false, BF, true, false>(a, stream, workspace, capacity, grid);
-    return xlds ? launch_sa<SCALE, true, BF, false, false>(a, stream, workspace, capacity, grid)
-                : launch_sa<SCALE, false, BF, false, false>(a, stream, workspace, capacity, grid);
+        return xlds ? launch_sa<SCALE, true, BF, true, false, SB>(a, stream, workspace, capacity, grid)
+                    : launch_sa<SCALE, false, BF, true, false, SB>(a, stream, workspace, capacity, grid);
+    return xlds ? launch_sa<SCALE, true, BF, false, false, SB>(a, stream, workspace, capacity, grid)
+                : launch_sa<SCALE, false, BF, false, false, SB>(a, stream, workspace, capacity, grid);
+}
+
+template <int SCALE>
+static hipError_t launch_types(const LinearArgs &a, hipStream_t stream, void *workspace,
+                               int capacity, int grid, size_t max_lds) {
+    if (!a.bf16)
+        return launch_scale<SCALE, false, false>(a, stream, workspace, capacity, grid, max_lds);
+    if (a.scales_bf16)
+        return launch_scale<SCALE, true, true>(a, stream, workspace, capacity, grid, max_lds);
+    return launch_scale<SCALE, true, false>(a, stream, workspace, capacity, grid, max_lds);
 }
 
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                          int grid, size_t max_lds) {
-    if (grid > capacity) return hipErrorInvalidValue;
-    // bfloat16: SCALE 0 dequantises before the MFMA (g = 16); 1 and 2 sum
-    // 128 + q and fold the offset out per group (2: one step per group)
+    if (grid > capacity || (a.scales_bf16 && !a.bf16)) return hipErrorInvalidValue;
+    // SCALE 0 scales each 8-deep block (g = 16); 1 scales per group; 2 is one
+    // 32-deep step per group: g = 32, or one group over K <= 32
     const int64_t S = (a.K + 31) / 32;
-    // one 32-deep step per group: g = 32, or one group over K <= 32
     const bool one_step = a.group_size == 32 || (a.group_size == -1 && S == 1);
-    if (a.bf16) {
-        if (a.group_size == 16) return launch_scale<0, true>(a, stream, workspace, capacity, grid, max_lds);
-        if (one_step) return launch_scale<2, true>(a, stream, workspace, capacity, grid, max_lds);
-        return launch_scale<1, true>(a, stream, workspace, capacity, grid, max_lds);
-    }
-    if (a.group_size == 16) return launch_scale<0, false>(a, stream, workspace, capacity, grid, max_lds);
-    if (one_step) return launch_scale<2, false>(a, stream, workspace, capacity, grid, max_lds);
-    return launch_scale<1, false>(a, stream, workspace, capacity, grid, max_lds);
+    if (a.group_size == 16) return launch_types<0>(a, stream, workspace, capacity, grid, max_lds);
+    if (one_step) return launch_types<2>(a, stream, workspace, capacity, grid, max_lds);
+    return launch_types<1>(a, stream, workspace, capacity, grid, max_lds);
 }
 
 }  // namespace w4a16

@@ -37,17 +37,6 @@ namespace {
 constexpr int kLoraTargetGroups = 512;   // shrink workgroups aimed for (2 per CU)
 constexpr int kLoraMaxSplits = 16;       // K chunks of the shrink, at most
 
-template <bool BF>
-__device__ __forceinline__ float act_lo(uint32_t v) {
-    if constexpr (BF) return __uint_as_float(v << 16);
-    else return (float)half_lo(v);
-}
-
-template <bool BF>
-__device__ __forceinline__ float act_hi(uint32_t v) {
-    if constexpr (BF) return __uint_as_float(v & 0xFFFF0000u);
-    else return (float)half_hi(v);
-}
 
 // One workgroup (4 waves) computes the partial t of a 16-row block of x over
 // one K chunk, for 64 columns of t (blockIdx.z): the waves take alternate
@@ -107,7 +96,8 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__rest
 //  - the rest: ct[n][g0 .. g0+7] = (8 - z[g,n]) s[g,n] for eight groups per
 //    thread (zero for g >= G), exact in fp32 and rounded to the activation
 //    type; consecutive threads take consecutive columns, so each load of the
-//    scale grid and of qzeros is coalesced.
+//    scale grid and of qzeros is coalesced.  z = stored nibble + zbias; the
+//    scales are bfloat16 when sbf, else fp16.
 template <bool BF>
 __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ scales,
@@ -115,7 +105,8 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
                                                         float *__restrict__ t,
                                                         uint16_t *__restrict__ ct, int M, int K,
                                                         int N, int gsz, int G, int Gp,
-                                                        int per_thread, int sum_blocks) {
+                                                        int per_thread, int sum_blocks, int sbf,
+                                                        int zbias) {
     const int lane = threadIdx.x;
     const int b = blockIdx.x;
     if (per_thread && b < sum_blocks) {
@@ -131,8 +122,8 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
                 const u4 v = load_b128(xr, (uint32_t)(m * K + k) * 2u);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc += act_lo<BF>(v[e]);
-                    acc += act_hi<BF>(v[e]);
+                    acc += lo_f32<BF>(v[e]);
+                    acc += hi_f32<BF>(v[e]);
                 }
             }
         }
@@ -149,8 +140,8 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
                 const u4 v = load_b128(xr, (uint32_t)(m * K + k) * 2u);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc += act_lo<BF>(v[e]);
-                    acc += act_hi<BF>(v[e]);
+                    acc += lo_f32<BF>(v[e]);
+                    acc += hi_f32<BF>(v[e]);
                 }
             }
 #pragma unroll
@@ -169,8 +160,9 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
         c[e] = 0.f;
         if (g < G) {
             const uint32_t zw = (uint32_t)qzeros[(size_t)g * (N / 8) + n / 8];
-            const int z = (int)((zw >> (4 * (n % 8))) & 0xFu);
-            c[e] = (float)(8 - z) * (float)half_lo((uint32_t)scales[(size_t)g * N + n]);
+            const int z = (int)((zw >> (4 * (n % 8))) & 0xFu) + zbias;
+            const uint32_t sv = scales[(size_t)g * N + n];
+            c[e] = (float)(8 - z) * (sbf ? lo_f32<true>(sv) : lo_f32<false>(sv));
         }
     }
     *reinterpret_cast<u4 *>(ct + (size_t)n * Gp + g0) =
@@ -290,8 +282,8 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
         u4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            o[e] = pack2<BF>(act_lo<BF>(yv[i][e]) + scale * tile[rr][c + 2 * e],
-                             act_hi<BF>(yv[i][e]) + scale * tile[rr][c + 2 * e + 1]);
+            o[e] = pack2<BF>(lo_f32<BF>(yv[i][e]) + scale * tile[rr][c + 2 * e],
+                             hi_f32<BF>(yv[i][e]) + scale * tile[rr][c + 2 * e + 1]);
         *reinterpret_cast<u4 *>(y + (size_t)m * N + n) = o;
     }
 }
@@ -389,12 +381,14 @@ hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace) {
     const int sum_blocks =
         per_thread ? (int)(((int64_t)M * Gp + 63) / 64) : (int)((int64_t)M * Gp);
     const unsigned blocks = (unsigned)(sum_blocks + (cthreads + 63) / 64);
+    const int sbf = a.scales_bf16 ? 1 : 0, zbias = a.zero_bias;
     if (a.bf16)
         zp_prepare_kernel<true><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, t, ct, M, K, N, gsz, G,
-                                                          Gp, per_thread, sum_blocks);
+                                                          Gp, per_thread, sum_blocks, sbf, zbias);
     else
         zp_prepare_kernel<false><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, t, ct, M, K, N, gsz,
-                                                           G, Gp, per_thread, sum_blocks);
+                                                           G, Gp, per_thread, sum_blocks, sbf,
+                                                           zbias);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return a.bf16 ? launch_expand<true>(t, ct, y, 1.0f, M, N, Gp, 16 * mblocks, 1, mblocks, stream)

@@ -49,11 +49,12 @@ constexpr int kPreRing = 3;               // LDS stages, register stages per ope
 constexpr int kPreSteps = kPreBK / 16;    // 16-deep MFMA steps per stage
 
 // gshift: log2(group_size), or -1 for a single group over K.  BF: bfloat16
-// activations and output (weights dequantised by dequant_bf16).
+// activations and output (weights dequantised by dequant_bf16); SB: bfloat16
+// scales (with BF only), else fp16.
 // Split K: workgroup z of `chunks` takes the 64-deep stages [sb, se) of its
 // tile; with chunks > 1 it writes its fp32 sums to partials[z][M][N] and
 // prefill_chunk_reduce_kernel adds the chunks, else it stores y.
-template <bool BF, bool SILU, int MT>
+template <bool BF, bool SILU, int MT, bool SB>
 __global__ __launch_bounds__(256) void prefill_m128_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -155,8 +156,8 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
             else read_a(an, next, 0);
             u4 b0, b1;
             if constexpr (BF) {
-                b0 = dequant_bf16<false>(w[h].x, (float)half_lo(s[h]));
-                b1 = dequant_bf16<false>(w[h].y, (float)half_hi(s[h]));
+                b0 = dequant_bf16<false>(w[h].x, lo_f32<SB>(s[h]));
+                b1 = dequant_bf16<false>(w[h].y, hi_f32<SB>(s[h]));
             } else {
                 b0 = __builtin_bit_cast(u4, unpack_codes_scaled(w[h].x, uc, half_lo(s[h])));
                 b1 = __builtin_bit_cast(u4, unpack_codes_scaled(w[h].y, uc, half_hi(s[h])));
@@ -269,16 +270,19 @@ static int m128_chunks(const LinearArgs &a, int num_cus, int capacity) {
     return chunks < 2 ? 1 : (int)chunks;
 }
 
-template <bool BF, bool SILU>
+template <bool BF, bool SILU, bool SB>
 static const void *m128_kernel_mt(int mt) {
-    if (mt == 1) return reinterpret_cast<const void *>(&prefill_m128_kernel<BF, SILU, 1>);
-    if (mt == 2) return reinterpret_cast<const void *>(&prefill_m128_kernel<BF, SILU, 2>);
-    return reinterpret_cast<const void *>(&prefill_m128_kernel<BF, SILU, 4>);
+    if (mt == 1) return reinterpret_cast<const void *>(&prefill_m128_kernel<BF, SILU, 1, SB>);
+    if (mt == 2) return reinterpret_cast<const void *>(&prefill_m128_kernel<BF, SILU, 2, SB>);
+    return reinterpret_cast<const void *>(&prefill_m128_kernel<BF, SILU, 4, SB>);
 }
 
-static const void *m128_kernel(bool bf16, bool silu, int mt) {
-    if (bf16) return silu ? m128_kernel_mt<true, true>(mt) : m128_kernel_mt<true, false>(mt);
-    return silu ? m128_kernel_mt<false, true>(mt) : m128_kernel_mt<false, false>(mt);
+static const void *m128_kernel(bool bf16, bool silu, bool sbf, int mt) {
+    if (bf16 && sbf)
+        return silu ? m128_kernel_mt<true, true, true>(mt) : m128_kernel_mt<true, false, true>(mt);
+    if (bf16)
+        return silu ? m128_kernel_mt<true, true, false>(mt) : m128_kernel_mt<true, false, false>(mt);
+    return silu ? m128_kernel_mt<false, true, false>(mt) : m128_kernel_mt<false, false, false>(mt);
 }
 
 static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream, void *workspace,
@@ -300,7 +304,7 @@ static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream, v
     dim3 grid((unsigned)((N + kPreBN - 1) / kPreBN), (unsigned)((M + 32 * mt - 1) / (32 * mt)),
               (unsigned)chunks);
     dim3 block(256);
-    const void *k = m128_kernel(a.bf16, a.silu, mt);
+    const void *k = m128_kernel(a.bf16, a.silu, a.scales_bf16, mt);
     hipError_t e = hipLaunchKernel(k, grid, block, args, 0, stream);
     if (e != hipSuccess || chunks == 1) return e;
     const float *pc = partials;
@@ -389,7 +393,7 @@ __device__ __forceinline__ WideOperands wide_operands(const uint16_t *x, const i
 // acc = the fp32 products of the 256 x 256 tile at (m0, n0) over the 64-deep
 // stages [sb, se) of K, 0 <= sb < se <= nst.  Uses the whole LDS area L; on
 // return every copy has landed, but other waves may still be reading L.
-template <bool BF>
+template <bool BF, bool SB>
 __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands &p, int m0, int n0,
                                                 int sb, int se, f16v (&acc)[8][2]) {
     const int M = p.M, K = p.K, N = p.N, gshift = p.gshift, nfull = p.nfull;
@@ -565,7 +569,7 @@ __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands 
             const int j = idx / 25, r = idx % 25;
             const uint32_t w = j ? w_nxt.y : w_nxt.x;
             if (r == 0) {
-                bsf = (float)(j ? half_hi(s_nxt) : half_lo(s_nxt));
+                bsf = j ? hi_f32<SB>(s_nxt) : lo_f32<SB>(s_nxt);
                 asm volatile("" : "+v"(bsf));
             } else if (r == 1) {
                 bm8 = -8.0f * bsf;
@@ -673,8 +677,8 @@ __device__ __forceinline__ void wide_tile_range(lds_u8_t *L, const WideOperands 
     read_ws(0, 0);
     read_a(0, 0);
     if constexpr (BF) {
-        b_cur0 = __builtin_bit_cast(h8, dequant_bf16<true>(w_nxt.x, (float)half_lo(s_nxt)));
-        b_cur1 = __builtin_bit_cast(h8, dequant_bf16<true>(w_nxt.y, (float)half_hi(s_nxt)));
+        b_cur0 = __builtin_bit_cast(h8, dequant_bf16<true>(w_nxt.x, lo_f32<SB>(s_nxt)));
+        b_cur1 = __builtin_bit_cast(h8, dequant_bf16<true>(w_nxt.y, hi_f32<SB>(s_nxt)));
     } else {
         b_cur0 = unpack_nat_scaled(w_nxt.x, half_lo(s_nxt), mask, magic, mul, add);
         b_cur1 = unpack_nat_scaled(w_nxt.y, half_hi(s_nxt), mask, magic, mul, add);
@@ -796,7 +800,7 @@ __device__ __forceinline__ void wide_store(lds_u8_t *L, const WideOperands &p, i
 // prefill_tail_reduce_kernel adds them.  Every workgroup streams K from its
 // range start with the others, nothing is exchanged inside the kernel.
 
-template <bool BF, bool SILU>
+template <bool BF, bool SILU, bool SB>
 __global__ __launch_bounds__(256) void prefill_m256_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
@@ -825,7 +829,7 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
         se = (int)((int64_t)p.nst * (c + 1) / chunks);
     }
     f16v acc[8][2];
-    wide_tile_range<BF>((lds_u8_t *)lds_raw, p, m0, n0, sb, se, acc);
+    wide_tile_range<BF, SB>((lds_u8_t *)lds_raw, p, m0, n0, sb, se, acc);
     wide_store<BF, SILU>((lds_u8_t *)lds_raw, p, m0, n0, acc,
                          j < 0 ? nullptr : partials + (size_t)j * kWSlot);
 }
@@ -908,11 +912,16 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
     void *yp = a.y;
     void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &tiles_m, &tiles_dp, &per_xcd,
                     &chunks, &partials};
-    const void *k =
-        a.silu ? (a.bf16 ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, true>)
-                         : reinterpret_cast<const void *>(&prefill_m256_kernel<false, true>))
-               : (a.bf16 ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, false>)
-                         : reinterpret_cast<const void *>(&prefill_m256_kernel<false, false>));
+    const void *k;
+    if (a.bf16 && a.scales_bf16)
+        k = a.silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, true, true>)
+                   : reinterpret_cast<const void *>(&prefill_m256_kernel<true, false, true>);
+    else if (a.bf16)
+        k = a.silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, true, false>)
+                   : reinterpret_cast<const void *>(&prefill_m256_kernel<true, false, false>);
+    else
+        k = a.silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<false, true, false>)
+                   : reinterpret_cast<const void *>(&prefill_m256_kernel<false, false, false>);
     hipError_t e = hipLaunchKernel(k, dim3(8 * per_xcd + tail * chunks), dim3(256), args, 0, stream);
     if (e != hipSuccess || tail == 0) return e;
     const float *pc = partials;
@@ -924,6 +933,7 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
 
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                           int num_cus) {
+    if (a.scales_bf16 && !a.bf16) return hipErrorInvalidValue;
     if (a.M > 128) return launch_prefill_m256(a, stream, workspace, capacity, num_cus);
     return launch_prefill_m128(a, stream, workspace, capacity, num_cus);
 }

@@ -149,7 +149,8 @@ extern "C" int w4a16_stream_release(void *stream) {
 static int linear_call(const void *x, const int32_t *qweight, const void *scales, void *y,
                        int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
                        int kernel, bool bf16, bool silu = false,
-                       const int32_t *qzeros = nullptr) {
+                       const int32_t *qzeros = nullptr, bool scales_bf16 = false,
+                       int zero_bias = 0) {
     const int st = validate(x, qweight, scales, y, M, K, N, group_size);
     if (st != W4A16_OK) return st;
     if (silu && N % 16 != 0) return W4A16_ERR_SHAPE;
@@ -165,7 +166,9 @@ static int linear_call(const void *x, const int32_t *qweight, const void *scales
     size_t max_lds = 0;
     const int dev = usable_device(&num_cus, &max_lds);
     if (dev < 0) return W4A16_ERR_DEVICE;
-    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, bf16, silu, qzeros};
+    if (scales_bf16 && !bf16) return W4A16_ERR_FLAGS;   // not reached
+    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, bf16, silu, qzeros,
+                              scales_bf16, zero_bias};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (qzeros && kernel != W4A16_KERNEL_DECODE) return W4A16_ERR_KERNEL;   // not reached
@@ -339,27 +342,41 @@ extern "C" int w4a16_linear_lora_bf16(const void *x, const int32_t *qweight, con
                      workspace, workspace_bytes, stream, true);
 }
 
-// The symmetric linear followed by the zero-point correction on the same stream.
+// The linear with stored zero points on the stream: for the decode kernel in
+// one launch, else the symmetric linear followed by the correction.
+// workspace_always: the workspace is required even where it is not used (the
+// contract of w4a16_linear_zp).
 static int zp_call(const void *x, const int32_t *qweight, const void *scales,
                    const int32_t *qzeros, void *y, int64_t M, int64_t K, int64_t N,
                    int64_t group_size, void *workspace, size_t workspace_bytes, void *stream,
-                   bool bf16) {
+                   bool bf16, bool scales_bf16 = false, int zero_bias = 0,
+                   int kernel = W4A16_KERNEL_AUTO, bool workspace_always = true) {
     int st = validate(x, qweight, scales, y, M, K, N, group_size);
     if (st != W4A16_OK) return st;
     if ((w4a16::zp_groups(K, group_size) + 7) / 8 * 8 > w4a16::kZpMaxGroups) return W4A16_ERR_SHAPE;
     const size_t need = w4a16::zp_workspace_bytes(M, K, N, group_size);
     if (need >= (size_t)kMaxBufferBytes) return W4A16_ERR_SHAPE;
+    if (kernel == W4A16_KERNEL_AUTO)
+        kernel = M <= W4A16_DECODE_MAX_M ? W4A16_KERNEL_DECODE : W4A16_KERNEL_PREFILL;
+    if (kernel == W4A16_KERNEL_DECODE) {
+        if (M > W4A16_DECODE_MAX_M) return W4A16_ERR_KERNEL;
+    } else if (kernel != W4A16_KERNEL_PREFILL) {
+        return W4A16_ERR_KERNEL;
+    }
     if (M == 0) return W4A16_OK;
-    if (!qzeros || !workspace) return W4A16_ERR_NULL;
-    if (!aligned16(qzeros) || !aligned16(workspace)) return W4A16_ERR_ALIGN;
-    if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+    const bool fused = kernel == W4A16_KERNEL_DECODE;
+    const bool ws_used = !fused || workspace_always;
+    if (!qzeros || (ws_used && !workspace)) return W4A16_ERR_NULL;
+    if (!aligned16(qzeros) || (ws_used && !aligned16(workspace))) return W4A16_ERR_ALIGN;
+    if (ws_used && workspace_bytes < need) return W4A16_ERR_WORKSPACE;
     // decode: the zero points enter the linear's own kernel (one launch)
-    if (M <= W4A16_DECODE_MAX_M)
+    if (fused)
         return linear_call(x, qweight, scales, y, M, K, N, group_size, stream,
-                           W4A16_KERNEL_DECODE, bf16, false, qzeros);
-    st = linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO, bf16);
+                           W4A16_KERNEL_DECODE, bf16, false, qzeros, scales_bf16, zero_bias);
+    st = linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_PREFILL,
+                     bf16, false, nullptr, scales_bf16);
     if (st != W4A16_OK) return st;
-    const w4a16::ZpArgs a{x, scales, qzeros, y, M, K, N, group_size, bf16};
+    const w4a16::ZpArgs a{x, scales, qzeros, y, M, K, N, group_size, bf16, scales_bf16, zero_bias};
     const hipError_t e = w4a16::launch_zp(a, reinterpret_cast<hipStream_t>(stream), workspace);
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
@@ -387,6 +404,25 @@ extern "C" int w4a16_linear_zp_bf16(const void *x, const int32_t *qweight, const
                                     size_t workspace_bytes, void *stream) {
     return zp_call(x, qweight, scales, qzeros, y, M, K, N, group_size, workspace,
                    workspace_bytes, stream, true);
+}
+
+extern "C" int w4a16_linear_typed(const void *x, const int32_t *qweight, const void *scales,
+                                  const int32_t *qzeros, void *y, int64_t M, int64_t K, int64_t N,
+                                  int64_t group_size, unsigned flags, int kernel,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    constexpr unsigned kKnown = W4A16_X_BF16 | W4A16_SCALES_BF16 | W4A16_ZEROS_V1 |
+                                W4A16_GATE_UP_SILU;
+    const bool bf16 = (flags & W4A16_X_BF16) != 0;
+    const bool scales_bf16 = (flags & W4A16_SCALES_BF16) != 0;
+    const bool v1 = (flags & W4A16_ZEROS_V1) != 0;
+    const bool silu = (flags & W4A16_GATE_UP_SILU) != 0;
+    if ((flags & ~kKnown) != 0 || (scales_bf16 && !bf16) || (v1 && !qzeros) || (silu && qzeros))
+        return W4A16_ERR_FLAGS;
+    if (!qzeros)
+        return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, kernel, bf16, silu,
+                           nullptr, scales_bf16);
+    return zp_call(x, qweight, scales, qzeros, y, M, K, N, group_size, workspace, workspace_bytes,
+                   stream, bf16, scales_bf16, v1 ? 1 : 0, kernel, false);
 }
 
 extern "C" int pack_gptq_v2(const uint8_t *codes, int32_t *qweight, int64_t K, int64_t N) {
@@ -449,6 +485,9 @@ extern "C" const char *w4a16_status_string(int status) {
         case W4A16_ERR_WORKSPACE: return "workspace smaller than the size its _workspace_bytes call gives";
         case W4A16_ERR_CAPTURE: return "stream is being captured into a graph";
         case W4A16_ERR_SCRATCH: return "device has more CUs than the allocation-free scratch covers";
+        case W4A16_ERR_FLAGS: return "unknown flag bit, or flags that cannot go together (bfloat16 "
+                                     "scales need bfloat16 x; v1 zero points need qzeros; gate/up "
+                                     "takes no qzeros)";
         default: return "unknown status";
     }
 }

@@ -117,6 +117,19 @@ __device__ __forceinline__ _Float16 half_hi(uint32_t v) {
     return __builtin_bit_cast(h2, v).y;
 }
 
+// The low / high 16-bit value of a dword as fp32: bfloat16 (BF: the top half
+// of an fp32, exact) or fp16 (converted, exact).
+template <bool BF>
+__device__ __forceinline__ float lo_f32(uint32_t v) {
+    if constexpr (BF) return __uint_as_float(v << 16);
+    else return (float)half_lo(v);
+}
+template <bool BF>
+__device__ __forceinline__ float hi_f32(uint32_t v) {
+    if constexpr (BF) return __uint_as_float(v & 0xFFFF0000u);
+    else return (float)half_hi(v);
+}
+
 // D(16x16, fp32) += A(16x32, fp16) * B(32x16, fp16) on the matrix cores.
 // Lane l supplies A row (l % 16) and B column (l % 16), each as 8 values of
 // K-block (l / 16); it receives D rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.

@@ -14,9 +14,11 @@ struct LinearArgs {
     const void *scales;
     void *y;
     int64_t M, K, N, group_size;
-    bool bf16;   // x and y are bfloat16 (else fp16); scales are fp16 either way
+    bool bf16;   // x and y are bfloat16 (else fp16)
     bool silu;   // merged gate/up: columns alternate gate and up; y[M, N/2] = silu(gate) * up
     const int32_t *qzeros = nullptr;   // stored zero points int32 [G, N/8] (decode only), or none
+    bool scales_bf16 = false;          // scales bfloat16 (requires bf16), else fp16
+    int zero_bias = 0;                 // z = stored nibble + zero_bias: 0 (v2 form) or 1 (v1)
 };
 
 // Decode (M <= 16).  grid > 0 runs the stream-K kernel on `grid` workgroups
@@ -58,7 +60,8 @@ size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r);
 hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace);
 
 // Stored zero points: y (the symmetric linear, already written) += the
-// rank-G correction sum_g X[m,g] (8 - z[g,n]) s[g,n], X the group sums of x.
+// rank-G correction sum_g X[m,g] (8 - z[g,n]) s[g,n], X the group sums of x
+// (z = stored nibble + zero_bias).
 // `workspace` holds zp_workspace_bytes(M, K, N, group_size) bytes (X in fp32,
 // then C^T in the activation type), no initial contents; G rounded up to 8 is
 // at most kZpMaxGroups.
@@ -69,6 +72,8 @@ struct ZpArgs {
     void *y;
     int64_t M, K, N, group_size;
     bool bf16;
+    bool scales_bf16;   // scales bfloat16, else fp16
+    int zero_bias;      // z = stored nibble + zero_bias (0 or 1)
 };
 int zp_groups(int64_t K, int64_t group_size);
 size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);

@@ -46,7 +46,7 @@ class Case:
     N: int
     group_size: int
     seed: int
-    scales: str = "uniform"          # "uniform" | "halfnormal" | "loguniform" | "pow2"
+    scales: str = "uniform"          # "uniform" | "halfnormal" | "loguniform" | "pow2" | "wide"
     x_dist: str = "normal"           # "normal" | "normal_half" | "int"
     outlier_frac: float = 0.0        # fraction of K channels of x scaled x20
     zero_cell_frac: float = 0.0      # fraction of (group, column) cells forced to code 8
@@ -59,7 +59,7 @@ class Case:
 @dataclasses.dataclass
 class Inputs:
     codes: np.ndarray     # uint8 [K, N], values 0..15
-    scales: np.ndarray    # float16 [G, N]
+    scales: np.ndarray    # float16 [G, N], or bfloat16 bit patterns (uint16)
     x: np.ndarray         # float16 [M, K]
     zero_cells: Optional[np.ndarray] = None   # bool [G, N] (sweep only)
     outlier_channels: Optional[np.ndarray] = None  # int64 [n_out] (prefill only)
@@ -74,9 +74,11 @@ def _draw_scales(rng: np.random.Generator, kind: str, G: int, N: int) -> np.ndar
         s = np.exp(rng.uniform(math.log(1e-4), math.log(5e-2), size=(G, N)))
     elif kind == "pow2":           # 2^e, e in {-4, -3, -2}: exact-arithmetic inputs
         s = np.exp2(rng.integers(-4, -1, size=(G, N)).astype(np.float64))
+    elif kind == "wide":           # exp(U(ln 2^-30, ln 2^-2)): beyond fp16's range (bfloat16 only)
+        s = np.exp(rng.uniform(-30 * math.log(2.0), -2 * math.log(2.0), size=(G, N)))
     else:
         raise ValueError(f"unknown scale recipe {kind!r}")
-    return s.astype(np.float16)
+    return s
 
 
 def _draw_x(rng: np.random.Generator, kind: str, M: int, K: int) -> np.ndarray:
@@ -103,12 +105,20 @@ def generate_bf16(case: Case) -> Inputs:
     return generate(case, act="bf16")
 
 
-def generate(case: Case, act: str = "f16") -> Inputs:
-    """Draw one case's inputs in the fixed order stated in the module docstring."""
+def generate(case: Case, act: str = "f16", scales_type: str = "f16") -> Inputs:
+    """Draw one case's inputs in the fixed order stated in the module docstring.
+    act / scales_type "bf16": x / the scales as bfloat16 bit patterns of the
+    same draws (rounded to nearest even), else fp16."""
     rng = np.random.default_rng(case.seed)
     K, N, M, G, g = case.K, case.N, case.M, case.G, case.group_size
     codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
-    scales = _draw_scales(rng, case.scales, G, N)
+    s64 = _draw_scales(rng, case.scales, G, N)
+    if scales_type == "bf16":
+        scales = bf16_bits(s64)
+    elif case.scales == "wide":
+        raise ValueError("the wide scale recipe is for bfloat16 scales")
+    else:
+        scales = s64.astype(np.float16)
     zero_cells = None
     if case.zero_cell_frac > 0.0:
         n_cells = int(round(case.zero_cell_frac * G * N))
