@@ -39,9 +39,10 @@
  *     releases each one before destroying it, else its workspaces stay
  *     held).  They exist because a split-K reduction across workgroups needs
  *     device scratch for its partial sums:
- *       decode: 3 MiB on a 256-CU device (per CU: 16x32 64-bit exchange
- *         slots, left zeroed by every launch, and two 16x64 fp32 partial
- *         tiles, written before they are read);
+ *       decode: 3 MiB + 16.25 KiB on a 256-CU device (per CU: 16x32
+ *         64-bit exchange slots, left zeroed by every launch, and two 16x64
+ *         fp32 partial tiles, written before they are read; then the LoRA
+ *         term's exit count and slice words, also left zeroed);
  *       prefill: 64 MiB on a 256-CU device (one 256x256 fp32 partial tile
  *         per CU), used when a last partial round of tiles is split along
  *         K (M > 128) and when fewer tiles than CUs are split along K
@@ -211,15 +212,27 @@ int w4a16_gate_up_silu_bf16_ex(const void *x, const int32_t *qweight, const void
  *   x, qweight, scales, y, shapes, group sizes, stream and the other errors
  *   as for w4a16_linear (the _bf16 form: bfloat16 x, A, B and y, as for
  *   w4a16_linear_bf16).  All checks run before any HIP call.
- * Steps on the stream: the linear writes y (its own kernel choice); a
- * shrink kernel forms t = x . A^T as fp32 partial sums over chunks of K; an
- * expand kernel adds the chunks in a fixed order, rounds t to the
- * activation type, forms delta = t . B^T in fp32 on the matrix cores and
- * writes y = round(y + s * delta).
+ * Steps on the stream:
+ *   - M <= W4A16_DECODE_MAX_M with rank <= 128, M * rank <= 512 and
+ *     ceil(K / 256) * M * rank <= 4096, when the decode runs its stream-K
+ *     launch (a stream that already holds its workspace, or one that may
+ *     create it): one launch.  Its first ceil(K / 256) workgroups also sum
+ *     t = x . A^T over 256-deep slices of K in fp32 on the matrix cores; after
+ *     its main loop every workgroup adds the slices in slice order, rounds
+ *     s * t to the activation type (t') and adds t' . B^T (fp32, matrix
+ *     cores) to its fp32 sums before the one rounding of y.  The slices pass
+ *     through the library's workspace for the stream, which the launch leaves
+ *     as it found it; the caller's workspace holds t' for the split-K reduce.
+ *   - otherwise: the linear writes y (its own kernel choice); a shrink kernel
+ *     forms t = x . A^T as fp32 partial sums over chunks of K; an expand
+ *     kernel adds the chunks in a fixed order, rounds t to the activation
+ *     type, forms delta = t . B^T in fp32 on the matrix cores and writes
+ *     y = round(y + s * delta).
  * Hence, per element and beyond the linear's own bound (u = 2^-11 for fp16,
  * 2^-8 for bfloat16): u |y_lin| + u |y| + |s| sum_j |B[n,j]| (u |t_j|
  * + K 2^-24 sum_k |x[m,k]| |A[j,k]|) + rank 2^-24 |s| sum_j |t_j| |B[n,j]|,
- * to first order; fp16 needs every t_j inside the fp16 range.
+ * to first order (the one-launch form rounds s t_j, and y once: within the
+ * same terms); fp16 needs every t_j inside the fp16 range.
  * Deterministic, as w4a16_linear. */
 #define W4A16_LORA_MAX_RANK 1024
 int w4a16_linear_lora(const void *x, const int32_t *qweight, const void *scales,
@@ -232,8 +245,9 @@ int w4a16_linear_lora_bf16(const void *x, const int32_t *qweight, const void *sc
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace w4a16_linear_lora needs for (M, K, rank): fp32 partial
- * sums of x . A^T, at most 16 chunks of [M rounded up to 16, rank].  0 for
- * M <= 0 or arguments the linear would reject. */
+ * sums of x . A^T, at most 16 chunks of [M rounded up to 16, rank] (and room
+ * for t' of the one-launch form).  0 for M <= 0 or arguments the linear
+ * would reject. */
 size_t w4a16_lora_workspace_bytes(int64_t M, int64_t K, int64_t rank);
 
 /* Asymmetric weights with stored zero points: w[k,n] = (q[k,n] - z[k/g, n]) *

@@ -408,8 +408,298 @@ extern __shared__ __attribute__((aligned(16))) unsigned char decode_dyn_lds[];
 // each wave's tile bounds.
 constexpr size_t tiles_static_lds(int waves) { return (size_t)waves * kNW * 64 * sizeof(f4); }
 constexpr size_t streamk_static_lds(int waves) {
-    return (size_t)(2 * waves + 1) * 256 * sizeof(f4) + (size_t)waves * 2 * sizeof(int);
+    return (size_t)(2 * waves + 1) * 256 * sizeof(f4) + (size_t)waves * 2 * sizeof(int) +
+           4 * sizeof(int);
 }
+
+// ---------------------------------------------------------------------------
+// LoRA adapter term inside the stream-K launch (LoraTerm, LK).
+//
+// Workgroups g < Su also own shrink unit g: each of their waves adds x . A^T
+// over one 32-deep K step on the matrix cores (the loads issued with the
+// first weight loads), and their last wave, which takes a lighter share of
+// the range, adds the eight wave partials in wave order and stores slab g
+// into the slab words of the decode workspace, each value coded so that it
+// is never zero (as the exchange slots code theirs).  After its main loop
+// every workgroup reads all slab words (M r Su of them), waiting until none
+// is zero: the owners of the units are the first workgroups of the grid,
+// which the device starts first, and they wait on nothing, so the words come;
+// the wait is bounded all the same, so every wave ends.  It adds each entry's
+// slabs in slab order, rounds scale * t to the activation type (t' in LDS),
+// and runs t' . B^T on the matrix cores with each tile it stores.  The
+// workgroup that counts itself out last zeroes the words for the next launch.
+// Each XCD has its own L2, so the words and the count move only through
+// system-scope atomic loads and stores, which bypass it.
+constexpr int kLoraStageChunks = 1024;           // 16 KiB: two chunks per thread of 512
+constexpr size_t kLoraStageBytes = (size_t)kLoraStageChunks * 16;
+constexpr int kLoraSpinMax = 1 << 24;            // waits of about 0.2 us: a few seconds
+
+// This wave's shrink step (K step st of unit g, or none): x rows (A operand)
+// and rows j of A (B operand) for the two 64-column passes.
+struct LoraStep {
+    u4 x;
+    u4 a[2][4];
+};
+
+__device__ __forceinline__ LoraStep lora_step_issue(const LoraTerm &L, const __amdgpu_buffer_rsrc_t xr,
+                                                    int M, int K, int st, bool own) {
+    const int lane = threadIdx.x & 63, c16 = lane & 15, kb = lane >> 4;
+    const auto ar = make_rsrc(L.A, (uint32_t)L.r * (uint32_t)K * 2u);
+    const int k = 32 * st + 8 * kb;
+    const bool in = own && k < K;               // K % 16 == 0: eight in or eight out
+    LoraStep o;
+    o.x = load_b128(xr, (in && c16 < M) ? (uint32_t)(c16 * K + k) * 2u : kOOB);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const int j = 64 * p + 16 * jb + c16;
+            o.a[p][jb] = load_b128(ar, (in && j < L.r) ? (uint32_t)(j * K + k) * 2u : kOOB);
+        }
+    return o;
+}
+
+// The step's products, rows m < M of this wave's partial into part[w][m][j]
+// (LDS, fp32, [WAVES][M][r]).
+template <bool BF>
+__device__ __forceinline__ void lora_step_finish(float *part, const LoraTerm &L, const LoraStep &o,
+                                                 int M, int wave) {
+    const int lane = threadIdx.x & 63, c16 = lane & 15, kb = lane >> 4;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        if (64 * p >= L.r) break;
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const f4 d = mfma16x16x32_t<BF>(o.x, o.a[p][jb], zero);
+            const int j = 64 * p + 16 * jb + c16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = 4 * kb + e;
+                if (m < M && j < L.r) part[(wave * M + m) * L.r + j] = d[e];
+            }
+        }
+    }
+}
+
+// One wave, after a barrier that follows every wave's lora_step_finish: slab
+// g = the wave partials added in wave order; publish it; the last unit's
+// wave forms t' and sets the flag.
+template <typename T>
+__device__ __forceinline__ T sys_load(const T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+template <typename T>
+__device__ __forceinline__ void sys_store(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// A slab value as a word that is never zero (NaN made canonical, then XOR
+// with a NaN pattern), and back.
+constexpr uint32_t kLoraKey = 0x7FBADBADu;
+__device__ __forceinline__ uint32_t lora_code(float v) {
+    return (v != v ? 0x7FC00000u : __builtin_bit_cast(uint32_t, v)) ^ kLoraKey;
+}
+__device__ __forceinline__ float lora_decode(uint32_t w) { return __builtin_bit_cast(float, w ^ kLoraKey); }
+
+// One wave, after a barrier that follows every wave's lora_step_finish: slab
+// g = the wave partials added in wave order, stored as coded words.
+template <int WAVES>
+__device__ __forceinline__ void lora_publish(const float *part, const LoraTerm &L, int M, int g) {
+    const int lane = threadIdx.x & 63;
+    const int total = M * L.r;
+    unsigned *words = L.area + 64;
+    for (int idx = lane; idx < total; idx += 64) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) acc += part[w * total + idx];
+        sys_store(words + (size_t)g * total + idx, lora_code(acc));
+    }
+}
+
+// Every slab value into `vals` (LDS, [Su][M r] fp32), once every word is
+// set: thread t reads words t, t + 512, ... (at most eight; lora_words_issue
+// requests them as soon as the thread's main loop ends), then again after a
+// short sleep while any is zero, within a bounded number of rounds.  The
+// values are visible to the workgroup after the next barrier.
+struct LoraWords {
+    uint32_t w[8];
+};
+
+__device__ __forceinline__ LoraWords lora_words_issue(const LoraTerm &L, int M) {
+    const unsigned *words = L.area + 64;
+    const int nw = L.Su * M * L.r;              // <= kLoraMaxSlabReads = 8 * 512
+    LoraWords o;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int v = (int)threadIdx.x + 512 * k;
+        o.w[k] = v < nw ? sys_load(words + v) : 1u;
+    }
+    return o;
+}
+
+__device__ __forceinline__ void lora_gather(float *vals, LoraWords o, const LoraTerm &L, int M) {
+    const int nw = L.Su * M * L.r;
+    for (int it = 0; it < kLoraSpinMax; ++it) {
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) all = all && o.w[k] != 0u;
+        if (all) break;
+        __builtin_amdgcn_s_sleep(8);
+        o = lora_words_issue(L, M);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int v = (int)threadIdx.x + 512 * k;
+        if (v < nw) vals[v] = lora_decode(o.w[k]);
+    }
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete
+// first, its global loads and atomics may stay in flight across it.
+__device__ __forceinline__ void lds_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// t'[e] = round(scale * sum of the Su slabs of entry e, in slab order) into
+// ta (LDS, activation type) and, when tq is given, into tq as well.
+template <bool BF>
+__device__ __forceinline__ void lora_form_t(uint16_t *ta, uint16_t *tq, const float *vals,
+                                            const LoraTerm &L, int M) {
+    const int total = M * L.r;
+    for (int e = threadIdx.x; e < total; e += blockDim.x) {
+        float acc = 0.f;
+        for (int q = 0; q < L.Su; ++q) acc += vals[q * total + e];
+        const uint16_t t = (uint16_t)pack2<BF>(L.scale * acc, 0.f);
+        ta[e] = t;
+        if (tq) tq[e] = t;
+    }
+}
+
+// The workgroup counted out last (exits + 1 == grid, in `last`) zeroes the
+// slab words and the count: by then every workgroup has read every word.
+// After a barrier that makes `last` visible.
+__device__ __forceinline__ void lora_reset(const LoraTerm &L, int M, bool last) {
+    if (!last) return;
+    unsigned *words = L.area + 64;
+    const int nw = L.Su * M * L.r;
+    for (int v = threadIdx.x; v < nw; v += blockDim.x) sys_store(words + v, 0u);
+    if (threadIdx.x == 0) sys_store(L.area, 0u);
+}
+
+// Rows of B for the workgroup's first tiles, staged through registers: two
+// 16-byte chunks per thread (past the staged rows: zero, no memory access),
+// requested with the first weight loads and written to LDS after the main loop.
+struct LoraBStage {
+    u4 v[2];
+    int nb;     // tiles staged, from the range's first tile
+};
+
+__device__ __forceinline__ LoraBStage lora_b_issue(const LoraTerm &L, int N, int b0, int ntiles) {
+    const auto br = make_rsrc(L.B, (uint32_t)N * (uint32_t)L.r * 2u);
+    const int cb = 8 * L.r;                     // chunks per tile: 64 rows of r
+    LoraBStage o;
+    o.nb = min(ntiles, kLoraStageChunks / cb);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = (int)threadIdx.x + 512 * i;
+        const int t = c / cb, w = c - t * cb;
+        const int n = (b0 + t) * kCols + w / (L.r / 8), j0 = 8 * (w % (L.r / 8));
+        o.v[i] = load_b128(br, (t < o.nb && n < N) ? (uint32_t)(n * L.r + j0) * 2u : kOOB);
+    }
+    return o;
+}
+
+// The term for one tile on the matrix cores, in the layout of the wave sums:
+// d[j][e] = sum_j' t'[m][j'] B[n][j'] for row m = 4 (lane / 16) + e and
+// column n = tile * 64 + 4 (lane % 16) + j (MFMA j takes the columns 4 c + j,
+// as the weight sums do).  A: t' rows (zero past M); B: the staged rows of
+// the tile (`bl`, row pitch r) or global.  Every lane of the wave takes part.
+// A fragments of t' (LDS, [M][r]) for the K steps of the term (r <= 128:
+// four): lane (m = lane % 16, block lane / 16) holds t'[m][32 s + 8 (lane /
+// 16) ..+8], zero past M and r.
+struct LoraTFrag {
+    u4 a[kLoraMaxRank / 32];
+};
+
+__device__ __forceinline__ LoraTFrag lora_t_frags(const uint16_t *ta, const LoraTerm &L, int M) {
+    const int lane = threadIdx.x & 63, c16 = lane & 15, kb = lane >> 4;
+    LoraTFrag f;
+#pragma unroll
+    for (int s = 0; s < kLoraMaxRank / 32; ++s) {
+        const int k = 32 * s + 8 * kb;
+        f.a[s] = (c16 < M && k < L.r) ? *reinterpret_cast<const u4 *>(ta + c16 * L.r + k)
+                                      : u4{0u, 0u, 0u, 0u};
+    }
+    return f;
+}
+
+template <bool BF>
+__device__ __forceinline__ void lora_tile_delta(f4 (&d)[kNW], const LoraTFrag &tf,
+                                                const LoraTerm &L, int N, int tile,
+                                                const uint16_t *bl) {
+    const int lane = threadIdx.x & 63, c16 = lane & 15, kb = lane >> 4;
+    const auto br = make_rsrc(L.B, (uint32_t)N * (uint32_t)L.r * 2u);
+    const u4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kNW; ++j) d[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kLoraMaxRank / 32; ++s) {
+        const int j1 = 32 * s;
+        if (j1 >= L.r) break;
+        const int k = j1 + 8 * kb;
+        const bool kin = k < L.r;               // r % 8 == 0: eight in or eight out
+        const u4 a = tf.a[s];
+        u4 b[kNW];
+#pragma unroll
+        for (int j = 0; j < kNW; ++j) {
+            const int col = kNW * c16 + j;
+            const int n = tile * kCols + col;
+            if (bl)
+                b[j] = kin ? *reinterpret_cast<const u4 *>(bl + col * L.r + k) : zero;
+            else
+                b[j] = load_b128(br, (kin && n < N) ? (uint32_t)(n * L.r + k) * 2u : kOOB);
+        }
+#pragma unroll
+        for (int j = 0; j < kNW; ++j) d[j] = mfma16x16x32_t<BF>(a, b[j], d[j]);
+    }
+}
+
+// v[c] += sum_j t'[m][j] B[n + c][j] for the four columns n .. n + 3, j
+// ascending, t' from `tl` (fp32 values of the activation type, [M][r]); for
+// the reduce kernel (one thread per row and four columns).
+template <bool BF>
+__device__ __forceinline__ void lora_add4(float (&v)[kNW], const float *tl, const LoraTerm &L,
+                                          int m, int n, int N) {
+    const auto br = make_rsrc(L.B, (uint32_t)N * (uint32_t)L.r * 2u);
+    const float *trow = tl + m * L.r;
+    for (int j0 = 0; j0 < L.r; j0 += 8) {
+        u4 b[kNW];
+#pragma unroll
+        for (int c = 0; c < kNW; ++c) b[c] = load_b128(br, (uint32_t)((n + c) * L.r + j0) * 2u);
+#pragma unroll
+        for (int c = 0; c < kNW; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[c] = __builtin_fmaf(trow[j0 + 2 * e], lo_f32<BF>(b[c][e]), v[c]);
+                v[c] = __builtin_fmaf(trow[j0 + 2 * e + 1], hi_f32<BF>(b[c][e]), v[c]);
+            }
+    }
+}
+
+// Dynamic LDS of the stream-K kernel: the staged activations, then (LK) a
+// 16 KiB area that holds in turn the wave partials of the shrink step (M r
+// <= kLoraMaxMR floats per wave), the slab values (Su M r <= 4096 floats) and
+// the staged rows of B; then t' (M r <= kLoraMaxMR 16-bit values).
+__host__ __device__ constexpr size_t lora_lds_offset(bool xlds, int M, int S) {
+    return xlds ? (size_t)M * 32 * S * 2 + 16 : 0;
+}
+constexpr size_t kLoraLdsBytes = kLoraStageBytes + 2 * (size_t)kLoraMaxMR;
+static_assert(8 * kLoraMaxMR * 4 <= kLoraStageBytes, "wave partials fit the LoRA LDS area");
+static_assert(4 * kLoraMaxSlabReads <= kLoraStageBytes, "slab values fit the LoRA LDS area");
 
 // Tiles kernel: one workgroup per column tile, its waves split K.
 template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP, bool SB>
@@ -521,12 +811,27 @@ __host__ __device__ __forceinline__ int wave_share(int n, int w) {
     return nold + (n - nold) * (w - H) / (WAVES - H);
 }
 
-template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP, bool SB>
+// As wave_share, with the last wave's weight a quarter of its younger
+// siblings' (it publishes a LoRA shrink unit before its main loop).
+template <int WAVES>
+__host__ __device__ __forceinline__ int wave_share_light(int n, int w) {
+    constexpr int H = WAVES / 2;
+    constexpr int wo = 2 * kOldShare / H;                  // older waves' weight
+    constexpr int wy = 2 * (1000 - kOldShare) / (WAVES - H);
+    constexpr int wl = wy / 4;
+    constexpr int total = wo * H + wy * (WAVES - H - 1) + wl;
+    const int c = w <= H ? wo * w : w < WAVES ? wo * H + wy * (w - H) : total;
+    return (int)((int64_t)n * c / total);
+}
+
+// LK: the LoRA adapter term in the same launch (LoraTerm; SILU and ZP off).
+template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP, bool SB, bool LK>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const int32_t *__restrict__ qzeros,
     uint16_t *__restrict__ y, int M, int K, int N,
-    int group_steps, int z8, uint64_t *__restrict__ slots, float *__restrict__ partials) {
+    int group_steps, int z8, uint64_t *__restrict__ slots, float *__restrict__ partials,
+    LoraTerm lora) {
     constexpr int SLOT = 16 * kCols;             // floats per partial slot
     // Wave partials: block s*WAVES + w (256 f4: [lane][i]) holds wave w's
     // sums of its segment s, row i of the lane's quad, its four columns
@@ -536,19 +841,25 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     constexpr int kZeroBlock = 2 * WAVES;
     __shared__ f4 red[(2 * WAVES + 1) * 256];
     __shared__ int wtile[WAVES][2];              // each wave's first and last tile
-    static_assert(sizeof(red) + sizeof(wtile) == streamk_static_lds(WAVES),
+    __shared__ int lk_last[4];                   // LK: this workgroup counted out last
+    static_assert(sizeof(red) + sizeof(wtile) + sizeof(lk_last) == streamk_static_lds(WAVES),
                   "stream-K kernel LDS layout");
+    static_assert(!LK || (!SILU && !ZP), "the adapter term goes with the plain linear");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = (K + 31) >> 5;
     const int T = (N + kCols - 1) / kCols;
     const StreamK sk{T * S, (int)gridDim.x};
+    // LK: the first Su workgroups also own a shrink unit, whose publication
+    // by their last wave gives that wave a lighter share of the range
     const int g = blockIdx.x;
+    const bool unit = LK && g < lora.Su;
     const int u0 = sk.begin(g), u1 = sk.begin(g + 1);
     // the host keeps every wave's share <= S units: at most two tiles per wave
-    const int w0 = u0 + wave_share<WAVES>(u1 - u0, wave);
-    const int w1 = u0 + wave_share<WAVES>(u1 - u0, wave + 1);
+    const int w0 = u0 + (unit ? wave_share_light<WAVES>(u1 - u0, wave) : wave_share<WAVES>(u1 - u0, wave));
+    const int w1 = u0 + (unit ? wave_share_light<WAVES>(u1 - u0, wave + 1)
+                              : wave_share<WAVES>(u1 - u0, wave + 1));
 
     const int Gs = SCALE != 0 ? (S + group_steps - 1) / group_steps : (K + 15) >> 4;
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
@@ -558,6 +869,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
 
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
+    u4 *img = reinterpret_cast<u4 *>(decode_dyn_lds + lora_lds_offset(XLDS, M, S));
+    LoraStep lstep{};
+    LoraBStage lb{};
     __builtin_amdgcn_sched_barrier(0);
     decode_units<D, SCALE, XLDS, BF, ZP, SB>(
         xr, qr, sr, zr, z8, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
@@ -569,12 +883,24 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
                     f4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
         },
         [&]() -> uint32_t {
-            if constexpr (XLDS) {
-                const uint32_t a = stage_x_finish(decode_dyn_lds, xr, M, K, S, xpre);
-                __syncthreads();
+            uint32_t a = 0u;
+            if constexpr (LK) {
+                // every load below is issued whatever the workgroup's role
+                // (past its data: zero), so the main loop's wait counts stay fixed
+                lstep = lora_step_issue(lora, xr, M, K, g * kLoraUnitSteps + wave, unit);
+                lb = lora_b_issue(lora, N, u0 / S, u1 > u0 ? (u1 - 1) / S - u0 / S + 1 : 0);
+                if constexpr (XLDS) a = stage_x_finish(decode_dyn_lds, xr, M, K, S, xpre);
+                if (unit) lora_step_finish<BF>(reinterpret_cast<float *>(img), lora, lstep, M, wave);
+                if (XLDS || unit) __syncthreads();
+                if (unit && wave == WAVES - 1)
+                    lora_publish<WAVES>(reinterpret_cast<const float *>(img), lora, M, g);
                 return a;
             }
-            return 0u;
+            if constexpr (XLDS) {
+                a = stage_x_finish(decode_dyn_lds, xr, M, K, S, xpre);
+                __syncthreads();
+            }
+            return a;
         });
     // tiles of the range and of this wave's share (last < first: no units),
     // worked out once the wave's loads are done and kept before the barrier
@@ -589,8 +915,31 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     }
     if (threadIdx.x < 256) red[kZeroBlock * 256 + threadIdx.x] = f4{-0.f, -0.f, -0.f, -0.f};
     asm volatile("" : "+s"(b0), "+s"(b1));
-    __syncthreads();
-    if (u0 >= u1) return;
+    LoraTFrag tfr{};
+    unsigned exits = 0;
+    if constexpr (LK) {
+        // the slab words are requested before the barrier, their round trip
+        // overlapping the other waves' last units; the barriers below order
+        // LDS only.  Every wave is then past its main loop (and the shrink's
+        // partials): the area takes the slab values, then the staged rows of B.
+        const LoraWords words = lora_words_issue(lora, M);
+        lds_sync();
+        uint16_t *ta = reinterpret_cast<uint16_t *>(img + kLoraStageChunks);
+        lora_gather(reinterpret_cast<float *>(img), words, lora, M);
+        lds_sync();
+        if (threadIdx.x == 0)       // every word read here; the answer is needed at the end
+            exits = __hip_atomic_fetch_add(lora.area, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        lora_form_t<BF>(ta, (partials && g == 0) ? static_cast<uint16_t *>(lora.tq) : nullptr,
+                        reinterpret_cast<const float *>(img), lora, M);
+        lds_sync();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) img[threadIdx.x + 512 * q] = lb.v[q];
+        tfr = lora_t_frags(ta, lora, M);
+        lds_sync();
+    } else {
+        __syncthreads();
+        if (u0 >= u1) return;
+    }
 
     // thread: (tile phase h, row i of the lane's quad, lane l); the WAVES/4
     // groups of four waves take turns over the tiles of the range, so a
@@ -603,7 +952,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const int h = threadIdx.x >> 8;
     const int m = 4 * (l >> 4) + i;
     const int c = kNW * (l & 15);
-    if (m >= M) return;                             // no barrier follows
+    // no barrier follows, except LK's last one (every lane stays for the
+    // term's MFMAs and the exit)
+    if (!LK && m >= M) return;
 
     // Fixed-order sum over the waves for every tile of this range; whole
     // tiles are stored.  Without `partials`, a split tile has exactly two
@@ -624,7 +975,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         tl[w] = wtile[w][1];
     }
     for (int tau = b0 + h; tau <= b1; tau += kPhases) {
-        const int ta = tau * S, tb = ta + S;
+        const int ta0 = tau * S, tb = ta0 + S;
         // every wave's part of tile tau (its segment tau - tf, or -0.0),
         // added in wave order; the reads are unconditional and issue together
         f4 rw[WAVES];
@@ -640,8 +991,24 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             for (int j = 0; j < kNW; ++j) v[j] += rw[w][j];
         }
         const int n = tau * kCols + c;
-        if (n >= N) continue;
-        if (ta >= u0 && tb <= u1) {                 // the whole tile is here
+        const bool whole = ta0 >= u0 && tb <= u1;   // the whole tile is here
+        // the tile's later contributor: with two contributors, this workgroup
+        // if the tile ends inside its range, else the next one; the adapter
+        // term rides with the later contributor's sums (either arrival order
+        // then adds the same two fp32 values); with `partials` the reduce
+        // kernel adds it
+        const int gl = tb <= u1 ? g : g + 1;
+        if (LK && (whole || (!partials && gl == g))) {   // uniform over the wave
+            f4 d[kNW];
+            lora_tile_delta<BF>(d, tfr, lora, N, tau,
+                                tau - b0 < lb.nb
+                                    ? reinterpret_cast<const uint16_t *>(img + (tau - b0) * 8 * lora.r)
+                                    : nullptr);
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) v[j] += d[j][i];
+        }
+        if (m >= M || n >= N) continue;
+        if (whole) {
             store_quad<BF, SILU>(y, m, N, n, v);
             continue;
         }
@@ -650,9 +1017,6 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             *reinterpret_cast<f4 *>(mine + m * kCols + c) = f4{v[0], v[1], v[2], v[3]};
             continue;
         }
-        // the tile's later contributor: with two contributors, this workgroup
-        // if the tile ends inside its range, else the next one
-        const int gl = tb <= u1 ? g : g + 1;
         uint64_t *slot = slots + ((size_t)gl * 16 + m) * (kCols / 2) + c / 2;
         uint64_t got[kNW / 2];
 #pragma unroll
@@ -673,6 +1037,11 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             store_pair<BF, SILU>(y, m, N, n + 2 * j, r0, r1);
         }
     }
+    if constexpr (LK) {
+        if (threadIdx.x == 0) lk_last[0] = exits + 1 == gridDim.x;
+        lds_sync();
+        lora_reset(lora, M, lk_last[0] != 0);
+    }
 }
 
 // Adds the partials of every split tile of a stream-K launch of G workgroups
@@ -682,13 +1051,21 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
 // inside one range were stored by the stream-K kernel.
 template <bool BF, bool SILU>
 __global__ __launch_bounds__(256) void decode_split_reduce_kernel(
-    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S, int G) {
+    const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int S, int G,
+    LoraTerm lora) {
     constexpr int SLOT = 16 * kCols;
     const int T = (N + kCols - 1) / kCols;
     const StreamK sk{T * S, G};
     const int tau = blockIdx.x;
     const int gf = sk.owner(tau * S), gl = sk.owner(tau * S + S - 1);
     if (gf == gl) return;
+    __shared__ __attribute__((aligned(16))) float tl[kLoraMaxMR];
+    if (lora.A) {                                   // t' from the stream-K launch
+        const uint16_t *tq = static_cast<const uint16_t *>(lora.tq);
+        for (int idx = threadIdx.x; idx < M * lora.r; idx += 256)
+            tl[idx] = lo_f32<BF>((uint32_t)tq[idx]);
+        __syncthreads();
+    }
     const int m = threadIdx.x >> 4, q = threadIdx.x & 15;
     const int n = tau * kCols + kNW * q;
     if (m >= M || n >= N) return;
@@ -700,6 +1077,7 @@ __global__ __launch_bounds__(256) void decode_split_reduce_kernel(
 #pragma unroll
         for (int j = 0; j < kNW; ++j) r[j] += p[j];
     }
+    if (lora.A) lora_add4<BF>(r, tl, lora, m, n, N);
     store_quad<BF, SILU>(y, m, N, n, r);
 }
 
@@ -719,7 +1097,9 @@ static size_t slots_bytes(int capacity) { return (size_t)capacity * 16 * (kCols 
 
 static_assert(kDecodeWorkspacePerCu == 16 * (kCols / 2) * sizeof(uint64_t) + 2 * 16 * kCols * sizeof(float),
               "decode workspace layout");
-size_t decode_workspace_bytes(int capacity) { return (size_t)capacity * kDecodeWorkspacePerCu; }
+size_t decode_workspace_bytes(int capacity) {
+    return (size_t)capacity * kDecodeWorkspacePerCu + kDecodeLoraBytes;
+}
 
 // Stream-K launches whose tiles may have more than two contributors (more
 // ranges than 2T) use partial slots and the reduce kernel; so do batches of
@@ -761,6 +1141,30 @@ int decode_streamk_grid(const LinearArgs &a, int num_cus) {
     return (int)T;
 }
 
+// Whether the LoRA term (a.lora, counters aside) can go inside a stream-K
+// launch of `grid` workgroups: rank and sizes within the LDS areas, one
+// workgroup per shrink unit, and every wave's lighter or heavier share at
+// most S units.
+static bool lora_inkernel_ok(const LinearArgs &a, int grid) {
+    const LoraTerm &L = a.lora;
+    if (L.r < 8 || L.r % 8 != 0 || L.r > kLoraMaxRank || a.M * L.r > kLoraMaxMR) return false;
+    const int64_t S = (a.K + 31) / 32;
+    const int64_t T = (a.N + kCols - 1) / kCols;
+    if (grid <= 0 || L.Su != (S + kLoraUnitSteps - 1) / kLoraUnitSteps || L.Su > grid) return false;
+    if ((int64_t)L.Su * a.M * L.r > kLoraMaxSlabReads) return false;
+    const int nmax = (int)((T * S + grid - 1) / grid);
+    for (int n = nmax - 1; n <= nmax; ++n)
+        for (int w = 0; w < kDecWaves; ++w)
+            if (wave_share_light<kDecWaves>(n, w + 1) - wave_share_light<kDecWaves>(n, w) > S)
+                return false;
+    return true;
+}
+
+bool decode_lora_inkernel_ok(const LinearArgs &a, int num_cus) {
+    if (a.silu || a.qzeros) return false;
+    return lora_inkernel_ok(a, decode_streamk_grid(a, num_cus));
+}
+
 // Activations are staged in LDS when they fit in this many bytes.
 constexpr size_t kXStageMax = 64 * 1024;
 
@@ -769,10 +1173,13 @@ constexpr size_t kXStageMax = 64 * 1024;
 // against the device's limit (stage_fits) can never be what keeps a launch
 // valid; a larger wave count or staging area fails here, at compile time.
 constexpr size_t kGfx950LdsPerWorkgroup = 160 * 1024;
-static_assert(streamk_static_lds(kDecWaves) + kXStageMax + 16 <= kGfx950LdsPerWorkgroup,
-              "stream-K decode: static LDS plus staged activations exceed 160 KiB");
+static_assert(streamk_static_lds(kDecWaves) + kXStageMax + 16 + kLoraLdsBytes <=
+                  kGfx950LdsPerWorkgroup,
+              "stream-K decode: static LDS plus staged activations and LoRA area exceed 160 KiB");
 static_assert(tiles_static_lds(kDecWaves) + kXStageMax + 16 <= kGfx950LdsPerWorkgroup,
               "tiles decode: static LDS plus staged activations exceed 160 KiB");
+static_assert(kDecWaves * 64 == 512, "the LoRA staging takes two chunks per thread of 512");
+static_assert(kDecWaves == kLoraUnitSteps, "a LoRA shrink unit is one K step per wave");
 
 // Static LDS of a kernel, read once from its attributes.
 static size_t static_lds(const void *kernel) {
@@ -795,23 +1202,29 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
     int z8 = 8 - a.zero_bias;
     void *yp = a.y;
     const dim3 block(kDecWaves * 64);
-    const size_t dyn = XLDS ? (size_t)M * 32 * S * 2 + 16 : 0;
+    LoraTerm lora = a.lora;
+    const bool lk = lora.A != nullptr;
+    const size_t dyn = lora_lds_offset(XLDS, M, S) + (lk ? kLoraLdsBytes : 0);
     if (grid > 0) {
         char *ws = static_cast<char *>(workspace);
         uint64_t *slots = reinterpret_cast<uint64_t *>(ws);
         const int T = (N + kCols - 1) / kCols;
         const bool part = uses_partials(grid, T, M);
         float *partials = part ? reinterpret_cast<float *>(ws + slots_bytes(capacity)) : nullptr;
+        if (lk) lora.area = reinterpret_cast<unsigned *>(ws + capacity * kDecodeWorkspacePerCu);
         void *args[] = {&xp, &qp, &sp, &zp, &yp, (void *)&M, (void *)&K, (void *)&N,
-                        &group_steps, &z8, &slots, &partials};
-        hipError_t e = hipLaunchKernel(
-            reinterpret_cast<const void *>(
-                &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP, SB>),
-            dim3(grid), block, args, dyn, stream);
+                        &group_steps, &z8, &slots, &partials, &lora};
+        const void *kern = reinterpret_cast<const void *>(
+            &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP, SB, false>);
+        if constexpr (!SILU && !ZP)
+            if (lk)
+                kern = reinterpret_cast<const void *>(
+                    &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP, SB, true>);
+        hipError_t e = hipLaunchKernel(kern, dim3(grid), block, args, dyn, stream);
         if (e != hipSuccess || !part) return e;
         const float *pc = partials;
         int Sv = S, G = grid;
-        void *rargs[] = {&pc, &yp, (void *)&M, (void *)&N, &Sv, &G};
+        void *rargs[] = {&pc, &yp, (void *)&M, (void *)&N, &Sv, &G, &lora};
         return hipLaunchKernel(reinterpret_cast<const void *>(&decode_split_reduce_kernel<BF, SILU>),
                                dim3((unsigned)T), dim3(256), rargs, 0, stream);
     }
@@ -829,10 +1242,11 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
 // per-workgroup LDS limit (a launch beyond it is rejected by the device).
 template <int SCALE, bool BF>
 static bool stage_fits(const LinearArgs &a, int grid, size_t max_lds) {
-    const size_t dyn = (size_t)a.M * 32 * ((a.K + 31) / 32) * 2 + 16;
-    if (dyn > kXStageMax) return false;
+    const size_t stage = (size_t)a.M * 32 * ((a.K + 31) / 32) * 2 + 16;
+    if (stage > kXStageMax) return false;
+    const size_t dyn = stage + (a.lora.A ? kLoraLdsBytes : 0);
     static const size_t sk_static = static_lds(reinterpret_cast<const void *>(
-        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true, BF, false, false, false>));
+        &decode_streamk_kernel<kDecWaves, kDecD, SCALE, true, BF, false, false, false, false>));
     static const size_t tiles_static = static_lds(reinterpret_cast<const void *>(
         &decode_tiles_kernel<kDecWaves, kDecD, SCALE, true, BF, false, false, false>));
     const size_t st = grid > 0 ? sk_static : tiles_static;
@@ -866,6 +1280,8 @@ static hipError_t launch_types(const LinearArgs &a, hipStream_t stream, void *wo
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                          int grid, size_t max_lds) {
     if (grid > capacity || (a.scales_bf16 && !a.bf16)) return hipErrorInvalidValue;
+    if (a.lora.A && (grid <= 0 || !workspace || a.silu || a.qzeros || !lora_inkernel_ok(a, grid)))
+        return hipErrorInvalidValue;
     // SCALE 0 scales each 8-deep block (g = 16); 1 scales per group; 2 is one
     // 32-deep step per group: g = 32, or one group over K <= 32
     const int64_t S = (a.K + 31) / 32;

@@ -28,6 +28,8 @@
 // layout of B): a rank-G correction of the symmetric linear, exactly zero
 // where z = 8.
 
+#include <algorithm>
+
 #include "w4a16_device.hpp"
 #include "w4a16_launch.h"
 
@@ -292,7 +294,7 @@ struct LoraPlan {
     int mblocks, jchunks, chunk_steps, splits, Mp;
 };
 
-LoraPlan lora_plan(int64_t M, int64_t K, int64_t r) {
+LoraPlan lora_plan(int64_t M, int64_t K, int64_t r, int max_splits = kLoraMaxSplits) {
     LoraPlan p;
     p.mblocks = (int)((M + 15) / 16);
     p.Mp = 16 * p.mblocks;
@@ -300,7 +302,7 @@ LoraPlan lora_plan(int64_t M, int64_t K, int64_t r) {
     const int nsteps = (int)((K + 31) / 32);
     const int groups = p.mblocks * p.jchunks;
     int want = (kLoraTargetGroups + groups - 1) / groups;
-    want = want < 1 ? 1 : want > kLoraMaxSplits ? kLoraMaxSplits : want;
+    want = want < 1 ? 1 : want > max_splits ? max_splits : want;
     int per = (nsteps + want - 1) / want;
     if (per < 4) per = 4 < nsteps ? 4 : nsteps;   // every wave of a chunk gets a step
     p.chunk_steps = per;
@@ -310,10 +312,24 @@ LoraPlan lora_plan(int64_t M, int64_t K, int64_t r) {
 
 }  // namespace
 
+// The term inside the decode launch: Su = ceil(K steps / kLoraUnitSteps)
+// units; the caller's workspace holds only t' [M][r] (activation type).
+static int64_t lora_units(int64_t K) {
+    return ((K + 31) / 32 + kLoraUnitSteps - 1) / kLoraUnitSteps;
+}
+
+size_t lora_inkernel_bytes(int64_t M, int64_t K, int64_t r) {
+    if (M <= 0 || r <= 0 || r > kLoraMaxRank || M * r > kLoraMaxMR ||
+        lora_units(K) * M * r > kLoraMaxSlabReads)
+        return 0;
+    return (size_t)M * (size_t)r * 2;
+}
+
 size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r) {
     if (M <= 0) return 0;
     const LoraPlan p = lora_plan(M, K, r);
-    return (size_t)p.splits * (size_t)p.Mp * (size_t)r * sizeof(float);
+    const size_t standalone = (size_t)p.splits * (size_t)p.Mp * (size_t)r * sizeof(float);
+    return std::max(standalone, lora_inkernel_bytes(M, K, r));
 }
 
 template <bool BF>
@@ -332,20 +348,26 @@ static hipError_t launch_expand(const float *tp, const uint16_t *B, uint16_t *y,
     return hipGetLastError();
 }
 
-hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace) {
-    const LoraPlan p = lora_plan(a.M, a.K, a.r);
-    const int M = (int)a.M, K = (int)a.K, N = (int)a.N, r = (int)a.r;
+static hipError_t run_shrink(const LoraArgs &a, const LoraPlan &p, hipStream_t stream,
+                             float *tp) {
+    const dim3 sg(p.mblocks, p.splits, p.jchunks);
     const auto *x = static_cast<const uint16_t *>(a.x);
     const auto *A = static_cast<const uint16_t *>(a.A);
-    const auto *B = static_cast<const uint16_t *>(a.B);
-    auto *y = static_cast<uint16_t *>(a.y);
-    auto *tp = static_cast<float *>(workspace);
-    const dim3 sg(p.mblocks, p.splits, p.jchunks);
+    const int M = (int)a.M, K = (int)a.K, r = (int)a.r;
     if (a.bf16)
         lora_shrink_kernel<true><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
     else
         lora_shrink_kernel<false><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace) {
+    const LoraPlan p = lora_plan(a.M, a.K, a.r);
+    const int M = (int)a.M, N = (int)a.N, r = (int)a.r;
+    const auto *B = static_cast<const uint16_t *>(a.B);
+    auto *y = static_cast<uint16_t *>(a.y);
+    auto *tp = static_cast<float *>(workspace);
+    hipError_t e = run_shrink(a, p, stream, tp);
     if (e != hipSuccess) return e;
     return a.bf16 ? launch_expand<true>(tp, B, y, a.scale, M, N, r, p.Mp, p.splits, p.mblocks,
                                         stream)

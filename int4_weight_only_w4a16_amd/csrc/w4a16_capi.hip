@@ -144,13 +144,18 @@ extern "C" int w4a16_stream_release(void *stream) {
     return release_stream_workspaces(dev, s);
 }
 
+// linear_call's answer when it leaves a LoRA term to the caller's other path.
+constexpr int kNotTaken = -1;
+
 // One linear call, fp16 or bfloat16 (bf16) activations and outputs; silu:
-// the merged gate/up projection (N % 16 == 0, y is [M, N/2]).
+// the merged gate/up projection (N % 16 == 0, y is [M, N/2]); lora: the
+// adapter term inside the stream-K decode launch, or kNotTaken (nothing
+// launched) when that launch cannot take it.
 static int linear_call(const void *x, const int32_t *qweight, const void *scales, void *y,
                        int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
                        int kernel, bool bf16, bool silu = false,
                        const int32_t *qzeros = nullptr, bool scales_bf16 = false,
-                       int zero_bias = 0) {
+                       int zero_bias = 0, const w4a16::LoraTerm *lora = nullptr) {
     const int st = validate(x, qweight, scales, y, M, K, N, group_size);
     if (st != W4A16_OK) return st;
     if (silu && N % 16 != 0) return W4A16_ERR_SHAPE;
@@ -167,8 +172,12 @@ static int linear_call(const void *x, const int32_t *qweight, const void *scales
     const int dev = usable_device(&num_cus, &max_lds);
     if (dev < 0) return W4A16_ERR_DEVICE;
     if (scales_bf16 && !bf16) return W4A16_ERR_FLAGS;   // not reached
-    const w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, bf16, silu, qzeros,
-                              scales_bf16, zero_bias};
+    w4a16::LinearArgs a{x, qweight, scales, y, M, K, N, group_size, bf16, silu, qzeros,
+                        scales_bf16, zero_bias};
+    if (lora) {
+        if (kernel != W4A16_KERNEL_DECODE) return W4A16_ERR_KERNEL;   // not reached
+        a.lora = *lora;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (qzeros && kernel != W4A16_KERNEL_DECODE) return W4A16_ERR_KERNEL;   // not reached
@@ -179,6 +188,8 @@ static int linear_call(const void *x, const int32_t *qweight, const void *scales
             ws = stream_workspace(dev, s, 0, w4a16::decode_workspace_bytes(num_cus));
             if (!ws) grid = 0;                   // under capture with no workspace yet
         }
+        // the adapter term needs the stream-K launch and its counters
+        if (lora && (grid == 0 || !w4a16::decode_lora_inkernel_ok(a, num_cus))) return kNotTaken;
         e = w4a16::launch_decode(a, s, ws, num_cus, grid, max_lds);
     } else {
         void *ws = nullptr;
@@ -200,6 +211,7 @@ static int linear_call(const void *x, const int32_t *qweight, const void *scales
 // once per device, and only that address reaches the kernels.
 constexpr int kScratchMaxCus = 320;
 constexpr int kScratchPrefillTiles = 64;
+// (the decode part omits the LoRA term's counters: this entry point has no term)
 constexpr size_t kScratchDecodeBytes = (size_t)kScratchMaxCus * w4a16::kDecodeWorkspacePerCu;
 constexpr size_t kScratchBytes =
     kScratchDecodeBytes + (size_t)kScratchPrefillTiles * w4a16::kPrefillPartialTileBytes;
@@ -310,10 +322,24 @@ static int lora_call(const void *x, const int32_t *qweight, const void *scales,
     if (!lora_a || !lora_b || !workspace) return W4A16_ERR_NULL;
     if (!aligned16(lora_a) || !aligned16(lora_b) || !aligned16(workspace)) return W4A16_ERR_ALIGN;
     if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+    const w4a16::LoraArgs a{x, lora_a, lora_b, y, M, K, N, rank, lora_scale, bf16};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (M <= W4A16_DECODE_MAX_M && w4a16::lora_inkernel_bytes(M, K, rank) > 0) {
+        // decode: the term inside the linear's stream-K launch, when it fits
+        w4a16::LoraTerm term;
+        term.A = lora_a;
+        term.B = lora_b;
+        term.tq = workspace;
+        term.scale = lora_scale;
+        term.r = (int)rank;
+        term.Su = (int)(((K + 31) / 32 + w4a16::kLoraUnitSteps - 1) / w4a16::kLoraUnitSteps);
+        st = linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_DECODE,
+                         bf16, false, nullptr, false, 0, &term);
+        if (st != kNotTaken) return st;
+    }
     st = linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO, bf16);
     if (st != W4A16_OK) return st;
-    const w4a16::LoraArgs a{x, lora_a, lora_b, y, M, K, N, rank, lora_scale, bf16};
-    const hipError_t e = w4a16::launch_lora(a, reinterpret_cast<hipStream_t>(stream), workspace);
+    const hipError_t e = w4a16::launch_lora(a, s, workspace);
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 

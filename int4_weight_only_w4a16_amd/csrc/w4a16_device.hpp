@@ -177,6 +177,12 @@ __device__ __forceinline__ u2 pack4(float a, float b, float c, float d) {
     return u2{pack2<BF>(a, b), pack2<BF>(c, d)};
 }
 
+// v rounded to the activation type (nearest even), as fp32.
+template <bool BF>
+__device__ __forceinline__ float round_act(float v) {
+    return lo_f32<BF>(pack2<BF>(v, 0.f));
+}
+
 // ---- final stores: plain, or the merged gate/up projection's SiLU * mul ----
 // With SILU the columns alternate gate (even) and up (odd) and the pair
 // (gate, up) becomes one value silu(gate) * up at column n/2 of a y with N/2

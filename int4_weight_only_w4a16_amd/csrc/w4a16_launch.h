@@ -6,6 +6,28 @@
 
 namespace w4a16 {
 
+// LoRA adapter term inside the stream-K decode launch (one kernel for the
+// linear and the term): y = round(sum + delta), delta[m,n] = sum_j t'[m,j]
+// B[n,j] in fp32 on the matrix cores, t' = round(scale * t) in the
+// activation type, t = x . A^T summed in fp32 as Su partial slabs of
+// kLoraUnitSteps 32-deep K steps each (one step per wave of a workgroup),
+// added in slab order.  A null: no adapter term.
+constexpr int kLoraUnitSteps = 8;        // one K step per wave of a workgroup
+constexpr int kLoraMaxMR = 512;          // M * r at most
+constexpr int kLoraMaxRank = 128;        // r at most (two 64-column passes per step)
+constexpr int64_t kLoraMaxSlabReads = 4096;    // Su * M * r at most (16 KiB of LDS)
+struct LoraTerm {
+    const void *A = nullptr;     // [r, K] in the activation type
+    const void *B = nullptr;     // [N, r] in the activation type
+    void *tq = nullptr;          // t' [M][r] for the split reduce (caller's workspace)
+    unsigned *area = nullptr;    // exit count, then the slab words (the decode workspace)
+    float scale = 0.f;
+    int r = 0, Su = 0;
+};
+// Bytes of the caller's workspace the term uses (t' for the split reduce), or
+// 0 when (M, K, r) does not take this path.
+size_t lora_inkernel_bytes(int64_t M, int64_t K, int64_t r);
+
 // Validated arguments of one linear call (shapes already checked against the
 // contract, every buffer smaller than 2^31 bytes, M > 0).
 struct LinearArgs {
@@ -19,6 +41,7 @@ struct LinearArgs {
     const int32_t *qzeros = nullptr;   // stored zero points int32 [G, N/8] (decode only), or none
     bool scales_bf16 = false;          // scales bfloat16 (requires bf16), else fp16
     int zero_bias = 0;                 // z = stored nibble + zero_bias: 0 (v2 form) or 1 (v1)
+    LoraTerm lora{};                   // adapter term (stream-K decode only), or none
 };
 
 // Decode (M <= 16).  grid > 0 runs the stream-K kernel on `grid` workgroups
@@ -28,8 +51,14 @@ struct LinearArgs {
 // kernel, which needs no workspace.  max_lds is the device's LDS limit per
 // workgroup in bytes.
 constexpr size_t kDecodeWorkspacePerCu = 12 * 1024;   // exchange slots 4 KiB + partials 8 KiB
-size_t decode_workspace_bytes(int capacity);            // capacity * kDecodeWorkspacePerCu
+// the LoRA term's area: its exit count (256 bytes), then the slab words
+constexpr size_t kDecodeLoraBytes = 256 + 4 * (size_t)kLoraMaxSlabReads;
+size_t decode_workspace_bytes(int capacity);  // capacity * kDecodeWorkspacePerCu + LoRA area
 int decode_streamk_grid(const LinearArgs &a, int num_cus);   // 0: use the tiles kernel
+// Whether a.lora (filled but for its counters) can go inside the stream-K
+// launch; launch_decode then takes it with grid = decode_streamk_grid and the
+// workspace (whose counters it uses).
+bool decode_lora_inkernel_ok(const LinearArgs &a, int num_cus);
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                          int grid, size_t max_lds);
 
@@ -58,6 +87,7 @@ struct LoraArgs {
 };
 size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r);
 hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace);
+
 
 // Stored zero points: y (the symmetric linear, already written) += the
 // rank-G correction sum_g X[m,g] (8 - z[g,n]) s[g,n], X the group sums of x

@@ -90,6 +90,13 @@ CASES = [
     (129, 512, 264, 128, 128),      # wide prefill tiles
     (256, 2048, 1024, 128, 256),
     (33, 4096, 264, 32, 1024),      # largest rank
+    # decode with the term inside the stream-K launch, and the cases it leaves
+    # to the separate shrink and expand kernels
+    (8, 5120, 5120, 128, 64),       # in the launch: M r = 512, exchange slots
+    (1, 17408, 5120, 32, 16),       # in the launch: 68 shrink units (long K)
+    (2, 1024, 264, 32, 256),        # rank above 128: separate kernels
+    (16, 1024, 136, 32, 64),        # M r = 1024 above 512: separate kernels
+    (1, 5120, 256, 128, 32),        # 20 shrink units, 8 workgroups: separate kernels
 ]
 
 
@@ -198,6 +205,53 @@ def test_lora_graph_capture_and_replay(dev, act):
         torch.cuda.synchronize()
         for i, (*_, eager, out) in enumerate(runs):
             assert torch.equal(out, eager), (i, rep)
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_lora_decode_repeatable_and_captured_on_fresh_stream(dev, act):
+    """The term inside the decode launch: three calls in a row give the same
+    bits (its counters start from zero every launch), interleaved with plain
+    linears; captured on a fresh stream (no workspace yet: the separate
+    kernels) and replayed, it meets the bar against the oracle."""
+    M, K, N, g, r = 4, 5120, 4096, 128, 32
+    case, inp, A, B = _inputs(M, K, N, g, r, 96, act)
+    bf16 = act == "bf16"
+    dt = torch.bfloat16 if bf16 else torch.float16
+
+    def up(arr):
+        arr = np.ascontiguousarray(arr)
+        if bf16:
+            return torch.from_numpy(arr.view(np.int16)).view(dt).to(dev)
+        return torch.from_numpy(arr).to(dev)
+
+    x, a, b = up(inp.x), up(A), up(B)
+    q = torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev)
+    s = torch.from_numpy(inp.scales).to(dev)
+    ws = torch.empty(w4.w4a16_lora_workspace_bytes(M, K, r), dtype=torch.uint8, device=dev)
+    outs = []
+    for _ in range(3):
+        outs.append(w4.linear_lora(x, q, s, g, a, b, S, workspace=ws))
+        w4.linear(x, q, s, g)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    y0 = outs[0].cpu()
+    _check(case, inp, A, B, bf16_to_float(y0.view(torch.int16).numpy()) if bf16
+           else y0.numpy().astype(np.float64), act)
+    st = torch.cuda.Stream()
+    out = torch.empty((M, N), dtype=dt, device=dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        w4.linear_lora(x, q, s, g, a, b, S, out=out, workspace=ws, stream=st)
+    for _ in range(2):
+        out.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        yc = out.cpu()
+        _check(case, inp, A, B, bf16_to_float(yc.view(torch.int16).numpy()) if bf16
+               else yc.numpy().astype(np.float64), act)
+    w4.w4a16_stream_release(st)
 
 
 @pytest.mark.parametrize("M", [3, 20])
