@@ -223,7 +223,13 @@ int w4a16_gate_up_silu_bf16_ex(const void *x, const int32_t *qweight, const void
  *     cores) to its fp32 sums before the one rounding of y.  The slices pass
  *     through the library's workspace for the stream, which the launch leaves
  *     as it found it; the caller's workspace holds t' for the split-K reduce.
- *   - otherwise: the linear writes y (its own kernel choice); a shrink kernel
+ *   - M > W4A16_DECODE_MAX_M: a shrink kernel forms t = x . A^T as fp32
+ *     partial sums over chunks of K; a second adds the chunks in a fixed
+ *     order and rounds s * t to the activation type (t'); the prefill linear
+ *     adds t' . B^T (fp32, matrix cores) to its fp32 sums before the one
+ *     rounding of y (for a tile split along K, to the first chunk's partial);
+ *   - otherwise (a decode outside the one-launch limits, or captured on a
+ *     stream with no workspace yet): the linear writes y; a shrink kernel
  *     forms t = x . A^T as fp32 partial sums over chunks of K; an expand
  *     kernel adds the chunks in a fixed order, rounds t to the activation
  *     type, forms delta = t . B^T in fp32 on the matrix cores and writes
@@ -272,11 +278,11 @@ size_t w4a16_lora_workspace_bytes(int64_t M, int64_t K, int64_t rank);
  *     zero point enters the dequantised weight: fp16 (q - z) s rounded once,
  *     bfloat16 (q - z) s exact in fp32 and rounded once); the workspace is
  *     not touched;
- *   - larger M: the symmetric linear writes y; one kernel sums x over each
- *     group in fp32 (X[m, g]) and forms C[g, n] = (8 - z) s exactly in fp32,
- *     rounded to the activation type; an expand kernel rounds X to the
- *     activation type, takes X . C in fp32 on the matrix cores and writes
- *     y = round(y + X . C).
+ *   - larger M: one kernel sums x over each group in fp32 (X[m, g], rounded
+ *     to the activation type) and forms C[g, n] = (8 - z) s exactly in
+ *     fp32, rounded to the activation type; the symmetric prefill linear adds
+ *     X . C (fp32, matrix cores) to its fp32 sums before the one rounding of
+ *     y (for a tile split along K, to the first chunk's partial).
  * Where every zero point is 8 the correction is 0 and y is the symmetric
  * result (bit for bit, up to the sign of a zero).
  * Hence, per element and beyond the symmetric linear's own bound (u = 2^-11

@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
                                                         uint16_t *__restrict__ ct, int M, int K,
                                                         int N, int gsz, int G, int Gp,
                                                         int per_thread, int sum_blocks, int sbf,
-                                                        int zbias) {
+                                                        int zbias, int act_out) {
     const int lane = threadIdx.x;
     const int b = blockIdx.x;
     if (per_thread && b < sum_blocks) {
@@ -129,7 +129,11 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
                 }
             }
         }
-        t[(size_t)m * Gp + gi] = acc;
+        if (act_out) {
+            if (m < M) reinterpret_cast<uint16_t *>(t)[(size_t)m * Gp + gi] = (uint16_t)pack2<BF>(acc, 0.f);
+        } else {
+            t[(size_t)m * Gp + gi] = acc;
+        }
         return;
     }
     if (b < sum_blocks) {
@@ -149,7 +153,10 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
         }
-        if (lane == 0) t[(size_t)m * Gp + gi] = acc;
+        if (lane == 0) {
+            if (act_out) reinterpret_cast<uint16_t *>(t)[(size_t)m * Gp + gi] = (uint16_t)pack2<BF>(acc, 0.f);
+            else t[(size_t)m * Gp + gi] = acc;
+        }
         return;
     }
     const int64_t tt = (int64_t)(b - sum_blocks) * 64 + lane;
@@ -325,10 +332,12 @@ size_t lora_inkernel_bytes(int64_t M, int64_t K, int64_t r) {
     return (size_t)M * (size_t)r * 2;
 }
 
+static size_t lora_t_offset(int64_t M, int64_t K, int64_t r);
+
 size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r) {
     if (M <= 0) return 0;
-    const LoraPlan p = lora_plan(M, K, r);
-    const size_t standalone = (size_t)p.splits * (size_t)p.Mp * (size_t)r * sizeof(float);
+    // the slabs and then t' (prefill), or t' alone (inside the decode launch)
+    const size_t standalone = lora_t_offset(M, K, r) + (size_t)M * (size_t)r * sizeof(uint16_t);
     return std::max(standalone, lora_inkernel_bytes(M, K, r));
 }
 
@@ -361,6 +370,46 @@ static hipError_t run_shrink(const LoraArgs &a, const LoraPlan &p, hipStream_t s
     return hipGetLastError();
 }
 
+// t'[m][j] = round(s * sum of the S slabs of (m, j), in slab order), the
+// activation type, one thread per entry.
+template <bool BF>
+__global__ void __launch_bounds__(256) lora_finish_kernel(const float *__restrict__ tp,
+                                                          uint16_t *__restrict__ ta, float scale,
+                                                          int M, int r, int Mp, int S) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= M * r) return;
+    const int m = e / r, j = e - m * r;
+    float acc = 0.f;
+    for (int q = 0; q < S; ++q) acc += tp[((size_t)q * Mp + m) * r + j];
+    ta[e] = (uint16_t)pack2<BF>(scale * acc, 0.f);
+}
+
+// Byte offset of t' in the workspace: after the standalone plan's slabs.
+static size_t lora_t_offset(int64_t M, int64_t K, int64_t r) {
+    const LoraPlan p = lora_plan(M, K, r);
+    return ((size_t)p.splits * (size_t)p.Mp * (size_t)r * sizeof(float) + 15) / 16 * 16;
+}
+
+hipError_t launch_lora_t(const LoraArgs &a, hipStream_t stream, void *workspace,
+                         PrefillTerm *term) {
+    const LoraPlan p = lora_plan(a.M, a.K, a.r);
+    auto *tp = static_cast<float *>(workspace);
+    auto *ta = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) +
+                                            lora_t_offset(a.M, a.K, a.r));
+    hipError_t e = run_shrink(a, p, stream, tp);
+    if (e != hipSuccess) return e;
+    const int M = (int)a.M, r = (int)a.r;
+    const unsigned blocks = (unsigned)(((int64_t)M * r + 255) / 256);
+    if (a.bf16)
+        lora_finish_kernel<true><<<blocks, 256, 0, stream>>>(tp, ta, a.scale, M, r, p.Mp, p.splits);
+    else
+        lora_finish_kernel<false><<<blocks, 256, 0, stream>>>(tp, ta, a.scale, M, r, p.Mp, p.splits);
+    term->ta = ta;
+    term->B = a.B;
+    term->r = r;
+    return hipGetLastError();
+}
+
 hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace) {
     const LoraPlan p = lora_plan(a.M, a.K, a.r);
     const int M = (int)a.M, N = (int)a.N, r = (int)a.r;
@@ -387,17 +436,20 @@ size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
            (size_t)N * (size_t)Gp * sizeof(uint16_t);
 }
 
-hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace) {
+// zp_prepare_kernel into `workspace`: X (fp32 [16 mblocks][Gp], or with
+// act_out the activation type [M][Gp]) at its start, then C^T [N][Gp].
+static hipError_t run_zp_prepare(const ZpArgs &a, hipStream_t stream, void *workspace,
+                                 int act_out, uint16_t **ct_out) {
     const int M = (int)a.M, K = (int)a.K, N = (int)a.N;
     const int G = zp_groups(a.K, a.group_size), Gp = (G + 7) / 8 * 8;
     const int gsz = a.group_size == -1 ? K : (int)a.group_size;
     const int mblocks = (M + 15) / 16;
     const auto *x = static_cast<const uint16_t *>(a.x);
     const auto *sc = static_cast<const uint16_t *>(a.scales);
-    auto *y = static_cast<uint16_t *>(a.y);
     auto *t = static_cast<float *>(workspace);
     auto *ct = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) +
                                             (size_t)16 * mblocks * Gp * sizeof(float));
+    *ct_out = ct;
     const int64_t cthreads = (int64_t)N * (Gp / 8);
     const int per_thread = a.group_size != -1 && a.group_size <= 256;
     const int sum_blocks =
@@ -406,16 +458,36 @@ hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace) {
     const int sbf = a.scales_bf16 ? 1 : 0, zbias = a.zero_bias;
     if (a.bf16)
         zp_prepare_kernel<true><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, t, ct, M, K, N, gsz, G,
-                                                          Gp, per_thread, sum_blocks, sbf, zbias);
+                                                          Gp, per_thread, sum_blocks, sbf, zbias,
+                                                          act_out);
     else
         zp_prepare_kernel<false><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, t, ct, M, K, N, gsz,
                                                            G, Gp, per_thread, sum_blocks, sbf,
-                                                           zbias);
-    hipError_t e = hipGetLastError();
+                                                           zbias, act_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace) {
+    const int M = (int)a.M, N = (int)a.N;
+    const int Gp = (zp_groups(a.K, a.group_size) + 7) / 8 * 8;
+    const int mblocks = (M + 15) / 16;
+    uint16_t *ct = nullptr;
+    hipError_t e = run_zp_prepare(a, stream, workspace, 0, &ct);
     if (e != hipSuccess) return e;
+    auto *t = static_cast<float *>(workspace);
+    auto *y = static_cast<uint16_t *>(a.y);
     return a.bf16 ? launch_expand<true>(t, ct, y, 1.0f, M, N, Gp, 16 * mblocks, 1, mblocks, stream)
                   : launch_expand<false>(t, ct, y, 1.0f, M, N, Gp, 16 * mblocks, 1, mblocks,
                                          stream);
+}
+
+hipError_t launch_zp_t(const ZpArgs &a, hipStream_t stream, void *workspace, PrefillTerm *term) {
+    uint16_t *ct = nullptr;
+    const hipError_t e = run_zp_prepare(a, stream, workspace, 1, &ct);
+    term->ta = workspace;
+    term->B = ct;
+    term->r = (zp_groups(a.K, a.group_size) + 7) / 8 * 8;
+    return e;
 }
 
 }  // namespace w4a16

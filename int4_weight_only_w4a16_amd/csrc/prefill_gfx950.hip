@@ -48,6 +48,40 @@ constexpr int kPreRowBytes = 144;         // 128 B of a row + 16 B pad (bank spr
 constexpr int kPreRing = 3;               // LDS stages, register stages per operand
 constexpr int kPreSteps = kPreBK / 16;    // 16-deep MFMA steps per stage
 
+// The low-rank term (PrefillTerm) added to a wave's fp32 sums on the matrix
+// cores: acc[mt][j] += ta[m] . B[n]^T for row m = m0 + 32 mt + (lane % 32)
+// and column n = ncol + 2 (lane % 32) + j, the layout of the main sums
+// (32 x 32 x 16 MFMA: A rows and B columns by lane % 32, 8-deep K blocks by
+// lane / 32), over r in 16-deep steps (zero past r, M and N).  Every lane of
+// the wave takes part.
+template <bool BF, int MT>
+__device__ __forceinline__ void prefill_term(f16v (&acc)[MT][2], const PrefillTerm &T, int M,
+                                             int N, int m0, int ncol) {
+    const int lane = threadIdx.x & 63;
+    const int kb = lane >> 5, c32 = lane & 31;
+    const auto tr = make_rsrc(T.ta, (uint32_t)M * (uint32_t)T.r * 2u);
+    const auto br = make_rsrc(T.B, (uint32_t)N * (uint32_t)T.r * 2u);
+    for (int s = 0; s < T.r; s += 16) {
+        const int k = s + 8 * kb;
+        const bool kin = k < T.r;               // r % 8 == 0: eight in or eight out
+        u4 b[2], a[MT];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = ncol + 2 * c32 + j;
+            b[j] = load_b128(br, (kin && n < N) ? (uint32_t)(n * T.r + k) * 2u : kOOB);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = m0 + 32 * mt + c32;
+            a[mt] = load_b128(tr, (kin && m < M) ? (uint32_t)(m * T.r + k) * 2u : kOOB);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[mt][j] = mfma32x32x16_t<BF>(a[mt], b[j], acc[mt][j]);
+    }
+}
+
 // gshift: log2(group_size), or -1 for a single group over K.  BF: bfloat16
 // activations and output (weights dequantised by dequant_bf16); SB: bfloat16
 // scales (with BF only), else fp16.
@@ -58,7 +92,7 @@ template <bool BF, bool SILU, int MT, bool SB>
 __global__ __launch_bounds__(256) void prefill_m128_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
-    int gshift, int chunks, float *__restrict__ partials) {
+    int gshift, int chunks, float *__restrict__ partials, PrefillTerm term) {
     constexpr int BM = 32 * MT;                    // rows per tile
     constexpr int kStage = BM * kPreRowBytes;      // LDS bytes per stage
     __shared__ __attribute__((aligned(16))) unsigned char lds[kPreRing * kStage];
@@ -213,6 +247,9 @@ __global__ __launch_bounds__(256) void prefill_m128_kernel(
         }
     }
 
+    // the low-rank term, once per tile: with the first K chunk
+    if (term.ta && cz == 0) prefill_term<BF, MT>(acc, term, M, N, m0, n - 2 * c32);
+
     // ---- epilogue: register i of tile (mt, j) is row m0 + 32 mt + 8 (i/4) +
     // 4 kb + i%4, column n + j; the two columns of a lane go out together ----
     if (n < N) {
@@ -299,7 +336,8 @@ static hipError_t launch_prefill_m128(const LinearArgs &a, hipStream_t stream, v
     const void *qp = a.qweight;
     const void *sp = a.scales;
     void *yp = a.y;
-    void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &chunks, &partials};
+    PrefillTerm term = a.pterm;
+    void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &chunks, &partials, &term};
     const int mt = m128_mt(M);
     dim3 grid((unsigned)((N + kPreBN - 1) / kPreBN), (unsigned)((M + 32 * mt - 1) / (32 * mt)),
               (unsigned)chunks);
@@ -804,7 +842,8 @@ template <bool BF, bool SILU, bool SB>
 __global__ __launch_bounds__(256) void prefill_m256_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ y, int M, int K, int N,
-    int gshift, int tiles_m, int tiles_dp, int per_xcd, int chunks, float *__restrict__ partials) {
+    int gshift, int tiles_m, int tiles_dp, int per_xcd, int chunks, float *__restrict__ partials,
+    PrefillTerm term) {
     __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kWLds];
     const WideOperands p = wide_operands(x, qweight, scales, y, M, K, N, gshift);
     const int id = blockIdx.x;
@@ -830,6 +869,10 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
     }
     f16v acc[8][2];
     wide_tile_range<BF, SB>((lds_u8_t *)lds_raw, p, m0, n0, sb, se, acc);
+    // the low-rank term, once per tile: whole tiles, and the first K chunk of
+    // a split one (its partial carries the term into the reduce)
+    if (term.ta && (j < 0 || j % chunks == 0))
+        prefill_term<BF, 8>(acc, term, M, N, m0, n0 + 64 * (int)(threadIdx.x >> 6));
     wide_store<BF, SILU>((lds_u8_t *)lds_raw, p, m0, n0, acc,
                          j < 0 ? nullptr : partials + (size_t)j * kWSlot);
 }
@@ -910,8 +953,9 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
     const void *qp = a.qweight;
     const void *sp = a.scales;
     void *yp = a.y;
+    PrefillTerm term = a.pterm;
     void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &tiles_m, &tiles_dp, &per_xcd,
-                    &chunks, &partials};
+                    &chunks, &partials, &term};
     const void *k;
     if (a.bf16 && a.scales_bf16)
         k = a.silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, true, true>)
@@ -934,6 +978,7 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
 hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                           int num_cus) {
     if (a.scales_bf16 && !a.bf16) return hipErrorInvalidValue;
+    if (a.pterm.ta && (a.silu || a.pterm.r <= 0 || a.pterm.r % 8 != 0)) return hipErrorInvalidValue;
     if (a.M > 128) return launch_prefill_m256(a, stream, workspace, capacity, num_cus);
     return launch_prefill_m128(a, stream, workspace, capacity, num_cus);
 }

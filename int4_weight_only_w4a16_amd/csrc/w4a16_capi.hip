@@ -155,7 +155,8 @@ static int linear_call(const void *x, const int32_t *qweight, const void *scales
                        int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream,
                        int kernel, bool bf16, bool silu = false,
                        const int32_t *qzeros = nullptr, bool scales_bf16 = false,
-                       int zero_bias = 0, const w4a16::LoraTerm *lora = nullptr) {
+                       int zero_bias = 0, const w4a16::LoraTerm *lora = nullptr,
+                       const w4a16::PrefillTerm *pterm = nullptr) {
     const int st = validate(x, qweight, scales, y, M, K, N, group_size);
     if (st != W4A16_OK) return st;
     if (silu && N % 16 != 0) return W4A16_ERR_SHAPE;
@@ -177,6 +178,10 @@ static int linear_call(const void *x, const int32_t *qweight, const void *scales
     if (lora) {
         if (kernel != W4A16_KERNEL_DECODE) return W4A16_ERR_KERNEL;   // not reached
         a.lora = *lora;
+    }
+    if (pterm) {
+        if (kernel != W4A16_KERNEL_PREFILL || silu) return W4A16_ERR_KERNEL;   // not reached
+        a.pterm = *pterm;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
@@ -337,6 +342,16 @@ static int lora_call(const void *x, const int32_t *qweight, const void *scales,
                          bf16, false, nullptr, false, 0, &term);
         if (st != kNotTaken) return st;
     }
+    if (M > W4A16_DECODE_MAX_M) {
+        // prefill: the shrink and t', then the linear with the term in its epilogue
+        w4a16::PrefillTerm term;
+        int num_cus = 0;
+        size_t max_lds = 0;
+        if (usable_device(&num_cus, &max_lds) < 0) return W4A16_ERR_DEVICE;
+        if (w4a16::launch_lora_t(a, s, workspace, &term) != hipSuccess) return W4A16_ERR_LAUNCH;
+        return linear_call(x, qweight, scales, y, M, K, N, group_size, stream,
+                           W4A16_KERNEL_PREFILL, bf16, false, nullptr, false, 0, nullptr, &term);
+    }
     st = linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_AUTO, bf16);
     if (st != W4A16_OK) return st;
     const hipError_t e = w4a16::launch_lora(a, s, workspace);
@@ -399,12 +414,16 @@ static int zp_call(const void *x, const int32_t *qweight, const void *scales,
     if (fused)
         return linear_call(x, qweight, scales, y, M, K, N, group_size, stream,
                            W4A16_KERNEL_DECODE, bf16, false, qzeros, scales_bf16, zero_bias);
-    st = linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_PREFILL,
-                     bf16, false, nullptr, scales_bf16);
-    if (st != W4A16_OK) return st;
+    // prefill: X and C^T, then the symmetric linear with X . C^T in its epilogue
+    int num_cus = 0;
+    size_t max_lds = 0;
+    if (usable_device(&num_cus, &max_lds) < 0) return W4A16_ERR_DEVICE;
     const w4a16::ZpArgs a{x, scales, qzeros, y, M, K, N, group_size, bf16, scales_bf16, zero_bias};
-    const hipError_t e = w4a16::launch_zp(a, reinterpret_cast<hipStream_t>(stream), workspace);
-    return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+    w4a16::PrefillTerm term;
+    if (w4a16::launch_zp_t(a, reinterpret_cast<hipStream_t>(stream), workspace, &term) != hipSuccess)
+        return W4A16_ERR_LAUNCH;
+    return linear_call(x, qweight, scales, y, M, K, N, group_size, stream, W4A16_KERNEL_PREFILL,
+                       bf16, false, nullptr, scales_bf16, 0, nullptr, &term);
 }
 
 extern "C" size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t N,

@@ -28,6 +28,18 @@ struct LoraTerm {
 // 0 when (M, K, r) does not take this path.
 size_t lora_inkernel_bytes(int64_t M, int64_t K, int64_t r);
 
+// A low-rank term added in the prefill kernels' epilogue, before the one
+// rounding of y (or into the first K chunk's fp32 partial of a split tile):
+// y += ta . B^T, ta [M, r] and B [N, r] in the activation type (r % 8 == 0),
+// on the matrix cores in fp32.  The LoRA adapter (ta = t' = round(s x . A^T))
+// and the zero-point correction (ta = round(X), the group sums of x, and
+// B = C^T = ((8 - z) s)^T) both take this form.  ta null: no term.
+struct PrefillTerm {
+    const void *ta = nullptr;
+    const void *B = nullptr;
+    int r = 0;
+};
+
 // Validated arguments of one linear call (shapes already checked against the
 // contract, every buffer smaller than 2^31 bytes, M > 0).
 struct LinearArgs {
@@ -42,6 +54,7 @@ struct LinearArgs {
     bool scales_bf16 = false;          // scales bfloat16 (requires bf16), else fp16
     int zero_bias = 0;                 // z = stored nibble + zero_bias: 0 (v2 form) or 1 (v1)
     LoraTerm lora{};                   // adapter term (stream-K decode only), or none
+    PrefillTerm pterm{};               // low-rank term (prefill only), or none
 };
 
 // Decode (M <= 16).  grid > 0 runs the stream-K kernel on `grid` workgroups
@@ -87,6 +100,10 @@ struct LoraArgs {
 };
 size_t lora_workspace_bytes(int64_t M, int64_t K, int64_t r);
 hipError_t launch_lora(const LoraArgs &a, hipStream_t stream, void *workspace);
+// For the prefill: the shrink, then t' = round(s t) [M, r] into the
+// workspace (after the partial sums), and the term for the prefill kernels.
+hipError_t launch_lora_t(const LoraArgs &a, hipStream_t stream, void *workspace,
+                         PrefillTerm *term);
 
 
 // Stored zero points: y (the symmetric linear, already written) += the
@@ -108,6 +125,9 @@ struct ZpArgs {
 int zp_groups(int64_t K, int64_t group_size);
 size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
 hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace);
+// For the prefill: X rounded to the activation type [M, Gp] and C^T [N, Gp]
+// into the workspace (no y yet), and the term for the prefill kernels (r = Gp).
+hipError_t launch_zp_t(const ZpArgs &a, hipStream_t stream, void *workspace, PrefillTerm *term);
 
 // Streaming-read probe over `bytes` (a multiple of 16) at data.
 hipError_t launch_read_probe(const void *data, int64_t bytes, void *sink, hipStream_t stream,
