@@ -144,15 +144,17 @@ def test_lora_invalid_arguments_rejected_before_any_hip_call(lib, kw, status, bf
 
 
 def test_lora_workspace_size_and_empty_batch(lib):
-    # M=1, K=32, r=8: one 16-row block, one K chunk of 8 fp32 columns
-    assert w4.w4a16_lora_workspace_bytes(1, 32, 8) == 16 * 8 * 4
-    assert _lora(lib, wsb=16 * 8 * 4) != w4.W4A16_ERR_WORKSPACE
+    # M=1, K=32, r=8: one 16-row block, one K chunk of 8 fp32 columns, then
+    # t' (M x r in the activation type)
+    assert w4.w4a16_lora_workspace_bytes(1, 32, 8) == 16 * 8 * 4 + 1 * 8 * 2
+    assert _lora(lib, wsb=16 * 8 * 4 + 16) != w4.W4A16_ERR_WORKSPACE
+    assert _lora(lib, wsb=16 * 8 * 4) == w4.W4A16_ERR_WORKSPACE
     assert w4.w4a16_lora_workspace_bytes(0, 32, 8) == 0
     assert w4.w4a16_lora_workspace_bytes(1, 32, 12) == 0
     assert w4.w4a16_lora_workspace_bytes(1, 40, 8) == 0
     # at most 16 chunks of K, and never more chunks than 4-step pieces of K
     for M, K, r in ((1, 5120, 32), (16, 17408, 64), (2048, 5120, 32), (300, 16, 8)):
-        b = w4.w4a16_lora_workspace_bytes(M, K, r)
+        b = w4.w4a16_lora_workspace_bytes(M, K, r) - M * r * 2
         rows = 16 * ((M + 15) // 16)
         chunks = b // (rows * r * 4)
         assert b == chunks * rows * r * 4 and 1 <= chunks <= 16
