@@ -169,14 +169,14 @@ __device__ __forceinline__ float scale_f32(const u2 &s, int j) {
 // SB: bfloat16 scales (with BF only), taken to fp32 exactly wherever the
 // bfloat16 paths take an fp16 scale to fp32.
 template <int D, int SCALE, bool XLDS, bool BF, bool ZP, bool SB, typename Dump,
-          typename AfterPrologue>
+          typename AfterPrologue, typename BeforeTail>
 __device__ __forceinline__ void decode_units(
     const __amdgpu_buffer_rsrc_t xr, const __amdgpu_buffer_rsrc_t qr,
     const __amdgpu_buffer_rsrc_t sr, const __amdgpu_buffer_rsrc_t zr, int z8,
     const unsigned char *xs,
     int M, int K, int N, int S,
     int group_steps, int w0, int w1, Dump &&dump, AfterPrologue &&after_prologue,
-    int xstep0 = 0) {
+    BeforeTail &&before_tail, int xstep0 = 0) {
     constexpr bool SCALE_AFTER = SCALE != 0;
     static_assert(BF || !SB, "bfloat16 scales come with bfloat16 activations");
     const int lane = threadIdx.x & 63;
@@ -391,7 +391,9 @@ __device__ __forceinline__ void decode_units(
             issue(ring[u]);
         }
     }
-    // last, partial round
+    // last, partial round (its loads are all in flight: before_tail may add
+    // loads of its own, which the round does not wait for)
+    before_tail();
 #pragma unroll
     for (int u = 0; u < D; ++u) {
         if (i < n) compute(ring[u]);
@@ -572,7 +574,14 @@ __device__ __forceinline__ void lora_form_t(uint16_t *ta, uint16_t *tq, const fl
     const int total = M * L.r;
     for (int e = threadIdx.x; e < total; e += blockDim.x) {
         float acc = 0.f;
-        for (int q = 0; q < L.Su; ++q) acc += vals[q * total + e];
+        for (int q0 = 0; q0 < L.Su; q0 += 8) {      // eight reads in flight
+            float pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) pv[u] = q0 + u < L.Su ? vals[(q0 + u) * total + e] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < L.Su) acc += pv[u];
+        }
         const uint16_t t = (uint16_t)pack2<BF>(L.scale * acc, 0.f);
         ta[e] = t;
         if (tq) tq[e] = t;
@@ -692,12 +701,13 @@ __device__ __forceinline__ void lora_add4(float (&v)[kNW], const float *tl, cons
 
 // Dynamic LDS of the stream-K kernel: the staged activations, then (LK) a
 // 16 KiB area that holds in turn the wave partials of the shrink step (M r
-// <= kLoraMaxMR floats per wave), the slab values (Su M r <= 4096 floats) and
-// the staged rows of B; then t' (M r <= kLoraMaxMR 16-bit values).
+// <= kLoraMaxMR floats per wave) and the slab values (Su M r <= 4096
+// floats), a 16 KiB area for the staged rows of B, and t' (M r <=
+// kLoraMaxMR 16-bit values).
 __host__ __device__ constexpr size_t lora_lds_offset(bool xlds, int M, int S) {
     return xlds ? (size_t)M * 32 * S * 2 + 16 : 0;
 }
-constexpr size_t kLoraLdsBytes = kLoraStageBytes + 2 * (size_t)kLoraMaxMR;
+constexpr size_t kLoraLdsBytes = 2 * kLoraStageBytes + 2 * (size_t)kLoraMaxMR;
 static_assert(8 * kLoraMaxMR * 4 <= kLoraStageBytes, "wave partials fit the LoRA LDS area");
 static_assert(4 * kLoraMaxSlabReads <= kLoraStageBytes, "slab values fit the LoRA LDS area");
 
@@ -743,7 +753,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_tiles_kernel(
                 return a;
             }
             return 0u;
-        });
+        },
+        [] {});
     __syncthreads();
     if (threadIdx.x < 256) {
         const int l = threadIdx.x & 63;
@@ -870,8 +881,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     XPre xpre;
     if constexpr (XLDS) xpre = stage_x_issue(xr, M, K, S);
     u4 *img = reinterpret_cast<u4 *>(decode_dyn_lds + lora_lds_offset(XLDS, M, S));
+    u4 *bst = img + kLoraStageChunks;            // LK: the staged rows of B
     LoraStep lstep{};
     LoraBStage lb{};
+    LoraWords words{};
     __builtin_amdgcn_sched_barrier(0);
     decode_units<D, SCALE, XLDS, BF, ZP, SB>(
         xr, qr, sr, zr, z8, decode_dyn_lds, M, K, N, S, group_steps, w0, w1,
@@ -885,9 +898,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         [&]() -> uint32_t {
             uint32_t a = 0u;
             if constexpr (LK) {
-                // every load below is issued whatever the workgroup's role
-                // (past its data: zero), so the main loop's wait counts stay fixed
-                lstep = lora_step_issue(lora, xr, M, K, g * kLoraUnitSteps + wave, unit);
+                // the shrink step's loads (unit workgroups) and the rows of B
+                if (unit) lstep = lora_step_issue(lora, xr, M, K, g * kLoraUnitSteps + wave, unit);
                 lb = lora_b_issue(lora, N, u0 / S, u1 > u0 ? (u1 - 1) / S - u0 / S + 1 : 0);
                 if constexpr (XLDS) a = stage_x_finish(decode_dyn_lds, xr, M, K, S, xpre);
                 if (unit) lora_step_finish<BF>(reinterpret_cast<float *>(img), lora, lstep, M, wave);
@@ -901,6 +913,11 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
                 __syncthreads();
             }
             return a;
+        },
+        [&] {
+            // LK: the slab words, requested a few units before the end of the
+            // wave's range so that their round trip overlaps its last units
+            if constexpr (LK) words = lora_words_issue(lora, M);
         });
     // tiles of the range and of this wave's share (last < first: no units),
     // worked out once the wave's loads are done and kept before the barrier
@@ -922,20 +939,24 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         // overlapping the other waves' last units; the barriers below order
         // LDS only.  Every wave is then past its main loop (and the shrink's
         // partials): the area takes the slab values, then the staged rows of B.
-        const LoraWords words = lora_words_issue(lora, M);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) bst[threadIdx.x + 512 * q] = lb.v[q];
         lds_sync();
-        uint16_t *ta = reinterpret_cast<uint16_t *>(img + kLoraStageChunks);
+        uint16_t *ta = reinterpret_cast<uint16_t *>(bst + kLoraStageChunks);
         lora_gather(reinterpret_cast<float *>(img), words, lora, M);
         lds_sync();
-        if (threadIdx.x == 0)       // every word read here; the answer is needed at the end
-            exits = __hip_atomic_fetch_add(lora.area, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (threadIdx.x == 0) {     // every word read here; the answer is needed at the end
+            // the address in a vector register: the compiler then issues one
+            // plain atomic and waits for its answer only where it is used
+            __attribute__((address_space(1))) unsigned *cnt =
+                (__attribute__((address_space(1))) unsigned *)lora.area;
+            asm volatile("" : "+v"(cnt));
+            exits = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
         lora_form_t<BF>(ta, (partials && g == 0) ? static_cast<uint16_t *>(lora.tq) : nullptr,
                         reinterpret_cast<const float *>(img), lora, M);
         lds_sync();
-#pragma unroll
-        for (int q = 0; q < 2; ++q) img[threadIdx.x + 512 * q] = lb.v[q];
         tfr = lora_t_frags(ta, lora, M);
-        lds_sync();
     } else {
         __syncthreads();
         if (u0 >= u1) return;
@@ -1002,7 +1023,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
             f4 d[kNW];
             lora_tile_delta<BF>(d, tfr, lora, N, tau,
                                 tau - b0 < lb.nb
-                                    ? reinterpret_cast<const uint16_t *>(img + (tau - b0) * 8 * lora.r)
+                                    ? reinterpret_cast<const uint16_t *>(bst + (tau - b0) * 8 * lora.r)
                                     : nullptr);
 #pragma unroll
             for (int j = 0; j < kNW; ++j) v[j] += d[j][i];
@@ -1038,6 +1059,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         }
     }
     if constexpr (LK) {
+        asm volatile("" : "+v"(exits));   // the count's first use is here, at the end
         if (threadIdx.x == 0) lk_last[0] = exits + 1 == gridDim.x;
         lds_sync();
         lora_reset(lora, M, lk_last[0] != 0);
@@ -1169,13 +1191,15 @@ bool decode_lora_inkernel_ok(const LinearArgs &a, int num_cus) {
 constexpr size_t kXStageMax = 64 * 1024;
 
 // Every shipped instantiation fits a gfx950 workgroup's 160 KiB of LDS with
-// the largest staging area (plus its zero chunk), so the launch-time check
-// against the device's limit (stage_fits) can never be what keeps a launch
-// valid; a larger wave count or staging area fails here, at compile time.
+// the largest staging area (plus its zero chunk), and the LoRA kernels with
+// their areas and no staging, so the launch-time check against the device's
+// limit (stage_fits) only ever turns the LoRA kernels' staging off; a larger
+// wave count or staging area fails here, at compile time.
 constexpr size_t kGfx950LdsPerWorkgroup = 160 * 1024;
-static_assert(streamk_static_lds(kDecWaves) + kXStageMax + 16 + kLoraLdsBytes <=
-                  kGfx950LdsPerWorkgroup,
-              "stream-K decode: static LDS plus staged activations and LoRA area exceed 160 KiB");
+static_assert(streamk_static_lds(kDecWaves) + kXStageMax + 16 <= kGfx950LdsPerWorkgroup,
+              "stream-K decode: static LDS plus staged activations exceed 160 KiB");
+static_assert(streamk_static_lds(kDecWaves) + kLoraLdsBytes <= kGfx950LdsPerWorkgroup,
+              "stream-K decode: static LDS plus the LoRA areas exceed 160 KiB");
 static_assert(tiles_static_lds(kDecWaves) + kXStageMax + 16 <= kGfx950LdsPerWorkgroup,
               "tiles decode: static LDS plus staged activations exceed 160 KiB");
 static_assert(kDecWaves * 64 == 512, "the LoRA staging takes two chunks per thread of 512");
