@@ -4,8 +4,9 @@
 Headline (``value``): HBM GB/s of the decode up-projection GEMV, M=1,
 K=5120, N=17408, g=128 (one step = one w4a16_linear call over one batch).
 The same line carries the prefill up-projection GEMM, M=2048, K=5120,
-N=17408, g=128, in TFLOP/s under ``prefill``, the variants (bfloat16, merged
-gate/up + SiLU*mul, LoRA, stored zero points) at the same two shapes, and
+N=17408, g=128, in TFLOP/s under ``prefill``, the variants (bfloat16 with
+fp16 and with bfloat16 scales, merged gate/up + SiLU*mul, LoRA, stored zero
+points) at the same two shapes, and
 under ``configs`` the other workloads: the tiny linear, the small-batch down
 projection (M = 1, 4, 16) and the 72-case group-size / shape sweep.
 
@@ -184,7 +185,8 @@ def upload_x(torch, x_np, bf16, dev):
 
 
 def time_linear(torch, w4, codes, scales, x_np, M, K, N, g, steps, warmup, eager,
-                bf16=False, gate_up=False, lora_rank=0, zero_points=None, seed=0):
+                bf16=False, gate_up=False, lora_rank=0, zero_points=None, seed=0,
+                scales_bf16=False):
     """Times one workload (the linear or a variant) with R rotating weight sets.
     Returns (y of the last step, seconds per step, per-replay ms, R)."""
     import workloads
@@ -193,6 +195,8 @@ def time_linear(torch, w4, codes, scales, x_np, M, K, N, g, steps, warmup, eager
     R = rotations_for(wbytes)
     q = torch.from_numpy(w4.pack_gptq_v2(codes)).to(dev)
     s = torch.from_numpy(scales).to(dev)
+    if scales_bf16:   # bfloat16 bit patterns -> a bfloat16 tensor
+        s = s.view(torch.bfloat16)
     qs = [q] + [q.clone() for _ in range(R - 1)]
     ss = [s] + [s.clone() for _ in range(R - 1)]
     x = upload_x(torch, x_np, bf16, dev)
@@ -205,6 +209,12 @@ def time_linear(torch, w4, codes, scales, x_np, M, K, N, g, steps, warmup, eager
 
     def step(i):
         call(x, qs[i % R], ss[i % R], y, M, K, N, g)
+
+    if scales_bf16:
+        flags = w4.W4A16_X_BF16 | w4.W4A16_SCALES_BF16
+
+        def step(i):  # noqa: F811
+            w4.w4a16_linear_typed(x, qs[i % R], ss[i % R], None, y, M, K, N, g, flags)
 
     if lora_rank:
         # the adapter rotates with the weights: each layer of a model has its own
@@ -233,13 +243,16 @@ def time_linear(torch, w4, codes, scales, x_np, M, K, N, g, steps, warmup, eager
 
 
 def bench_case(torch, w4, case, steps, warmup, eager, bf16=False, gate_up=False, lora_rank=0,
-               zero_points=False):
+               zero_points=False, scales_bf16=False):
     import workloads
-    inp = workloads.generate_bf16(case) if bf16 else workloads.generate(case)
+    if scales_bf16:
+        inp = workloads.generate(case, act="bf16", scales_type="bf16")
+    else:
+        inp = workloads.generate_bf16(case) if bf16 else workloads.generate(case)
     zp = workloads.zero_points(case.G, case.N, case.seed + 700) if zero_points else None
     y, sec, per, R = time_linear(torch, w4, inp.codes, inp.scales, inp.x, case.M, case.K, case.N,
                                  case.group_size, steps, warmup, eager, bf16, gate_up, lora_rank,
-                                 zp, case.seed)
+                                 zp, case.seed, scales_bf16)
     return y, sec, per, R
 
 
@@ -404,7 +417,8 @@ def main():
     ap.add_argument("--no-zero-points", action="store_true",
                     help="skip the stored-zero-point (asymmetric weight) lines")
     ap.add_argument("--no-bf16", action="store_true",
-                    help="skip the bfloat16-activation variant's decode and prefill lines")
+                    help="skip the bfloat16 variants' decode and prefill lines (bfloat16 x/y "
+                         "with fp16 scales, and with bfloat16 scales)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the tiny, down-projection and sweep workloads")
     ap.add_argument("--no-sweep", action="store_true",
@@ -529,6 +543,8 @@ def main():
     if args.only == "all" and not args.no_bf16:
         out["bf16"] = pair("bfloat16 x/y", workloads.decode_up(), workloads.prefill_up(),
                            bf16=True)
+        out["bf16_scales"] = pair("bfloat16 x/y and scales", workloads.decode_up(),
+                                  workloads.prefill_up(), bf16=True, scales_bf16=True)
     if args.only == "all" and not args.no_gate_up:
         out["gate_up_silu"] = pair("gate_up + SiLU*mul (N = 2x17408)", workloads.gate_up_decode(),
                                    workloads.gate_up_prefill(), gate_up=True)
