@@ -92,8 +92,12 @@ CASES = [
     (33, 4096, 264, 32, 1024),      # largest rank
     # decode with the term inside the stream-K launch, and the cases it leaves
     # to the separate shrink and expand kernels
-    (8, 5120, 5120, 128, 64),       # in the launch: M r = 512, exchange slots
+    (8, 2048, 1032, 64, 64),        # in the launch: M r = 512 and 8 M r = 4096, both limits
+    (1, 8192, 2048, 128, 128),      # in the launch: rank 128, 32 units x M r = 4096
+    (4, 12288, 5120, 128, 16),      # in the launch, wide grid: the reduce kernel adds t'
     (1, 17408, 5120, 32, 16),       # in the launch: 68 shrink units (long K)
+    (8, 5120, 5120, 128, 64),       # 20 units x M r = 10240 slab words: separate kernels
+    (8, 2304, 1032, 64, 64),        # 9 units x M r = 4608, just past the limit: separate kernels
     (2, 1024, 264, 32, 256),        # rank above 128: separate kernels
     (16, 1024, 136, 32, 64),        # M r = 1024 above 512: separate kernels
     (1, 5120, 256, 128, 32),        # 20 shrink units, 8 workgroups: separate kernels
