@@ -297,9 +297,10 @@ int w4a16_linear_zp_bf16(const void *x, const int32_t *qweight, const void *scal
                          int64_t group_size, void *workspace, size_t workspace_bytes,
                          void *stream);
 
-/* Bytes of workspace w4a16_linear_zp needs: fp32 group sums of x [M rounded
- * up to 16, Gp] and the correction matrix C^T [N, Gp] in the activation type,
- * Gp = G rounded up to 8.  0 for M <= 0 or arguments it rejects. */
+/* Bytes of workspace w4a16_linear_zp needs: an area of (M rounded up to 16)
+ * x Gp fp32 values for the group sums of x (stored in the activation type),
+ * then the correction matrix C^T [N, Gp] in the activation type, Gp = G
+ * rounded up to 8.  0 for M <= 0 or arguments it rejects. */
 size_t w4a16_zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
 
 /* Flags of w4a16_linear_typed. */

@@ -1,5 +1,4 @@
-// LoRA adapter term on the quantised linear, gfx950: y += s * (x . A^T) . B^T
-// after the W4A16 linear has written y.
+// LoRA adapter term and zero-point correction kernels, gfx950.
 //
 // The pages list LoRA adapters on the quantised linear path in the runtime
 // contract ("GPTQ-Pro" README, "Runtime contract" table) and keep an adapter
@@ -8,25 +7,32 @@
 // suggested ranks are 32 and 64, with 128 and 256 as larger choices ("EoRA
 // Accuracy Recovery").  The update is the textbook low-rank one in PEFT's
 // storage order: A [r, K] (lora_A weight) and B [N, r] (lora_B weight), both
-// in the activation type, and a scaling s given as a number.
+// in the activation type, and a scaling s given as a number:
+// y = x . W + s * (x . A^T) . B^T.
 //
-// The adapter runs two kernels on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
+// Kernels here (all products on the matrix cores, v_mfma_f32_16x16x32_{f16,bf16}):
 //   lora_shrink_kernel  t = x . A^T as fp32 partial sums over S chunks of K,
 //                       one [Mp, r] slab per chunk (Mp = M rounded up to 16);
-//   lora_expand_kernel  sums the S slabs of a 16-row block in a fixed order,
+//   lora_finish_kernel  adds the slabs in chunk order and rounds t' = s * t
+//                       to the activation type, for the prefill kernels to
+//                       add t' . B^T in their epilogue (PrefillTerm);
+//   lora_expand_kernel  the form after a linear that has already written y:
+//                       sums the slabs of a 16-row block in a fixed order,
 //                       rounds t to the activation type, multiplies by B^T,
-//                       and adds s times the result to y in place:
-//                       y = round(y + s * delta), one rounding of the sum.
+//                       and writes y = round(y + s * delta), one rounding of
+//                       the sum (decode calls outside the one-launch limits,
+//                       and calls captured on a stream with no workspace yet).
+// (Inside the limits the decode kernel runs the whole term in its own launch.)
 // Both operands of every MFMA are contiguous along the contracted index (x
 // and A rows along K, t rows and B rows along r), so each lane loads its
-// eight values with one 16-byte load.  The result is deterministic.
+// eight values with one 16-byte load.  Results are deterministic.
 //
-// Stored zero points (asymmetric weights, w = (q - z) s) use the same expand:
+// Stored zero points (asymmetric weights, w = (q - z) s) at prefill sizes:
 // (q - z) s = (q - 8) s + (8 - z) s, so y = y_sym + sum_g X[m,g] C[g,n] with
 // X the sums of x over each group and C = (8 - z) s, both formed by
-// zp_prepare_kernel (C transposed to [N, Gp] in the activation type, the
-// layout of B): a rank-G correction of the symmetric linear, exactly zero
-// where z = 8.
+// zp_prepare_kernel (X in the activation type [M, Gp], C transposed to
+// [N, Gp], the layout of a low-rank term's B): the prefill kernels add X . C
+// in their epilogue, a correction exactly zero where z = 8.
 
 #include <algorithm>
 
@@ -89,9 +95,9 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__rest
 }
 
 // Two kinds of 64-thread blocks in one launch:
-//  - the first `sum_blocks`: X[m, gi] = sum of x[m, k] over group gi (fp32;
-//    K for g = -1), columns G .. Gp-1 zero, one slab [M rounded up to 16][Gp]
-//    of the expand's layout.  Groups of at most 256 (per_thread): one thread
+//  - the first `sum_blocks`: X[m, gi] = sum of x[m, k] over group gi (in fp32,
+//    K for g = -1), rounded to the activation type into xs [M][Gp], columns
+//    G .. Gp-1 zero.  Groups of at most 256 (per_thread): one thread
 //    per (row, group) adds the group's 16-byte runs in order.  Larger groups:
 //    one wave per (group, row), lane l adds the runs l, l + 64, ... in order,
 //    then a fixed butterfly adds the lanes.
@@ -104,11 +110,11 @@ template <bool BF>
 __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ scales,
                                                         const int32_t *__restrict__ qzeros,
-                                                        float *__restrict__ t,
+                                                        uint16_t *__restrict__ xs,
                                                         uint16_t *__restrict__ ct, int M, int K,
                                                         int N, int gsz, int G, int Gp,
                                                         int per_thread, int sum_blocks, int sbf,
-                                                        int zbias, int act_out) {
+                                                        int zbias) {
     const int lane = threadIdx.x;
     const int b = blockIdx.x;
     if (per_thread && b < sum_blocks) {
@@ -129,11 +135,7 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
                 }
             }
         }
-        if (act_out) {
-            if (m < M) reinterpret_cast<uint16_t *>(t)[(size_t)m * Gp + gi] = (uint16_t)pack2<BF>(acc, 0.f);
-        } else {
-            t[(size_t)m * Gp + gi] = acc;
-        }
+        xs[(size_t)m * Gp + gi] = (uint16_t)pack2<BF>(acc, 0.f);
         return;
     }
     if (b < sum_blocks) {
@@ -153,10 +155,7 @@ __global__ void __launch_bounds__(64) zp_prepare_kernel(const uint16_t *__restri
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
         }
-        if (lane == 0) {
-            if (act_out) reinterpret_cast<uint16_t *>(t)[(size_t)m * Gp + gi] = (uint16_t)pack2<BF>(acc, 0.f);
-            else t[(size_t)m * Gp + gi] = acc;
-        }
+        if (lane == 0) xs[(size_t)m * Gp + gi] = (uint16_t)pack2<BF>(acc, 0.f);
         return;
     }
     const int64_t tt = (int64_t)(b - sum_blocks) * 64 + lane;
@@ -428,7 +427,8 @@ int zp_groups(int64_t K, int64_t group_size) {
     return group_size == -1 ? 1 : (int)((K + group_size - 1) / group_size);
 }
 
-// Workspace: X [M rounded up to 16][Gp] fp32, then C^T [N][Gp] 16-bit.
+// Workspace: X [M][Gp] in the activation type (in an area sized for fp32
+// [M rounded up to 16][Gp]), then C^T [N][Gp] in the activation type.
 size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
     if (M <= 0) return 0;
     const int64_t Gp = (zp_groups(K, group_size) + 7) / 8 * 8;
@@ -436,20 +436,16 @@ size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size) {
            (size_t)N * (size_t)Gp * sizeof(uint16_t);
 }
 
-// zp_prepare_kernel into `workspace`: X (fp32 [16 mblocks][Gp], or with
-// act_out the activation type [M][Gp]) at its start, then C^T [N][Gp].
-static hipError_t run_zp_prepare(const ZpArgs &a, hipStream_t stream, void *workspace,
-                                 int act_out, uint16_t **ct_out) {
+hipError_t launch_zp_t(const ZpArgs &a, hipStream_t stream, void *workspace, PrefillTerm *term) {
     const int M = (int)a.M, K = (int)a.K, N = (int)a.N;
     const int G = zp_groups(a.K, a.group_size), Gp = (G + 7) / 8 * 8;
     const int gsz = a.group_size == -1 ? K : (int)a.group_size;
     const int mblocks = (M + 15) / 16;
     const auto *x = static_cast<const uint16_t *>(a.x);
     const auto *sc = static_cast<const uint16_t *>(a.scales);
-    auto *t = static_cast<float *>(workspace);
+    auto *xs = static_cast<uint16_t *>(workspace);
     auto *ct = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) +
                                             (size_t)16 * mblocks * Gp * sizeof(float));
-    *ct_out = ct;
     const int64_t cthreads = (int64_t)N * (Gp / 8);
     const int per_thread = a.group_size != -1 && a.group_size <= 256;
     const int sum_blocks =
@@ -457,37 +453,15 @@ static hipError_t run_zp_prepare(const ZpArgs &a, hipStream_t stream, void *work
     const unsigned blocks = (unsigned)(sum_blocks + (cthreads + 63) / 64);
     const int sbf = a.scales_bf16 ? 1 : 0, zbias = a.zero_bias;
     if (a.bf16)
-        zp_prepare_kernel<true><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, t, ct, M, K, N, gsz, G,
-                                                          Gp, per_thread, sum_blocks, sbf, zbias,
-                                                          act_out);
+        zp_prepare_kernel<true><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, xs, ct, M, K, N, gsz,
+                                                          G, Gp, per_thread, sum_blocks, sbf, zbias);
     else
-        zp_prepare_kernel<false><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, t, ct, M, K, N, gsz,
-                                                           G, Gp, per_thread, sum_blocks, sbf,
-                                                           zbias, act_out);
-    return hipGetLastError();
-}
-
-hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace) {
-    const int M = (int)a.M, N = (int)a.N;
-    const int Gp = (zp_groups(a.K, a.group_size) + 7) / 8 * 8;
-    const int mblocks = (M + 15) / 16;
-    uint16_t *ct = nullptr;
-    hipError_t e = run_zp_prepare(a, stream, workspace, 0, &ct);
-    if (e != hipSuccess) return e;
-    auto *t = static_cast<float *>(workspace);
-    auto *y = static_cast<uint16_t *>(a.y);
-    return a.bf16 ? launch_expand<true>(t, ct, y, 1.0f, M, N, Gp, 16 * mblocks, 1, mblocks, stream)
-                  : launch_expand<false>(t, ct, y, 1.0f, M, N, Gp, 16 * mblocks, 1, mblocks,
-                                         stream);
-}
-
-hipError_t launch_zp_t(const ZpArgs &a, hipStream_t stream, void *workspace, PrefillTerm *term) {
-    uint16_t *ct = nullptr;
-    const hipError_t e = run_zp_prepare(a, stream, workspace, 1, &ct);
-    term->ta = workspace;
+        zp_prepare_kernel<false><<<blocks, 64, 0, stream>>>(x, sc, a.qzeros, xs, ct, M, K, N, gsz,
+                                                           G, Gp, per_thread, sum_blocks, sbf, zbias);
+    term->ta = xs;
     term->B = ct;
-    term->r = (zp_groups(a.K, a.group_size) + 7) / 8 * 8;
-    return e;
+    term->r = Gp;
+    return hipGetLastError();
 }
 
 }  // namespace w4a16

@@ -83,7 +83,8 @@ int usable_device(int *num_cus, size_t *max_lds) {
 // the first call on a stream that needs it (not while the stream is being
 // captured into a graph), zero-filled in stream order, kept until
 // w4a16_stream_release or the end of the process.
-//   kind 0: decode stream-K (exchange slots and partial tiles, 3 MiB)
+//   kind 0: decode stream-K (exchange slots and partial tiles, 3 MiB, then
+//           the one-launch LoRA term's exit count and slice words, 16.25 KiB)
 //   kind 1: prefill split tail (one 256 x 256 fp32 partial per CU, 64 MiB)
 std::mutex g_ws_mu;
 std::map<std::tuple<int, uintptr_t, int>, std::pair<void *, size_t>> g_ws;

@@ -106,12 +106,12 @@ hipError_t launch_lora_t(const LoraArgs &a, hipStream_t stream, void *workspace,
                          PrefillTerm *term);
 
 
-// Stored zero points: y (the symmetric linear, already written) += the
-// rank-G correction sum_g X[m,g] (8 - z[g,n]) s[g,n], X the group sums of x
-// (z = stored nibble + zero_bias).
-// `workspace` holds zp_workspace_bytes(M, K, N, group_size) bytes (X in fp32,
-// then C^T in the activation type), no initial contents; G rounded up to 8 is
-// at most kZpMaxGroups.
+// Stored zero points at prefill sizes: the correction sum_g X[m,g]
+// (8 - z[g,n]) s[g,n] as a low-rank term of the prefill kernels, X the group
+// sums of x (z = stored nibble + zero_bias).
+// `workspace` holds zp_workspace_bytes(M, K, N, group_size) bytes (X, then
+// C^T, both in the activation type), no initial contents; G rounded up to 8
+// is at most kZpMaxGroups.
 constexpr int kZpMaxGroups = 1536;
 struct ZpArgs {
     const void *x, *scales;
@@ -124,9 +124,8 @@ struct ZpArgs {
 };
 int zp_groups(int64_t K, int64_t group_size);
 size_t zp_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t group_size);
-hipError_t launch_zp(const ZpArgs &a, hipStream_t stream, void *workspace);
-// For the prefill: X rounded to the activation type [M, Gp] and C^T [N, Gp]
-// into the workspace (no y yet), and the term for the prefill kernels (r = Gp).
+// X rounded to the activation type [M, Gp] and C^T [N, Gp] into the
+// workspace (no y yet), and the term for the prefill kernels (r = Gp).
 hipError_t launch_zp_t(const ZpArgs &a, hipStream_t stream, void *workspace, PrefillTerm *term);
 
 // Streaming-read probe over `bytes` (a multiple of 16) at data.
