@@ -181,7 +181,9 @@ int w4a16_linear_bf16_ex(const void *x, const int32_t *qweight, const void *scal
  *   N % 16 == 0 (else W4A16_ERR_SHAPE), everything else as for w4a16_linear.
  * The _bf16 forms take bfloat16 x and write bfloat16 y (arithmetic as in
  * w4a16_linear_bf16); the _ex forms choose the kernel as w4a16_linear_ex.
- * Prefill with M > 128 runs whole tiles only (no split last round). */
+ * Prefill with M > 128 splits a short last round of tiles along K as the
+ * linear does; those tiles' fp32 sums are added in a fixed order and SiLU *
+ * mul is applied to the sums, as above. */
 int w4a16_gate_up_silu(const void *x, const int32_t *qweight, const void *scales, void *y,
                        int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream);
 int w4a16_gate_up_silu_ex(const void *x, const int32_t *qweight, const void *scales, void *y,

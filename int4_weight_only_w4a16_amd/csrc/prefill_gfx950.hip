@@ -773,7 +773,7 @@ __device__ __forceinline__ void wide_store(lds_u8_t *L, const WideOperands &p, i
     const int wave = tid >> 6;
     const int kb = lane >> 5;
     const int c32 = lane & 31;
-    uint32_t part = (!SILU && partial) ? ~0u : 0u;        // uniform: this workgroup writes a partial
+    uint32_t part = partial ? ~0u : 0u;                   // uniform: this workgroup writes a partial
     part = __builtin_amdgcn_readfirstlane(part);
     asm volatile("" : "+s"(part));
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(p.ybase, p.ybytes);
@@ -805,10 +805,16 @@ __device__ __forceinline__ void wide_store(lds_u8_t *L, const WideOperands &p, i
             const int m = m0 + rt, n = n0 + 8 * cc;
             const bool in = m < p.M && n < p.N;
             if constexpr (SILU) {
-                const u2 v = {pack2<BF>(silu_f32(a[0]) * a[1], silu_f32(a[2]) * a[3]),
-                              pack2<BF>(silu_f32(b[0]) * b[1], silu_f32(b[2]) * b[3])};
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    v, yr, in ? ((uint32_t)m * (uint32_t)NY + (uint32_t)(n / 2)) * 2u : kOOB, 0, 0);
+                if (part) {        // a split tile: the plain fp32 sums (the reduce applies SiLU)
+                    const uint32_t po = ((uint32_t)rt * kWBN + 8u * (uint32_t)cc) * 4u;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, a), pr, po, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, b), pr, po + 16u, 0, 0);
+                } else {
+                    const u2 v = {pack2<BF>(silu_f32(a[0]) * a[1], silu_f32(a[2]) * a[3]),
+                                  pack2<BF>(silu_f32(b[0]) * b[1], silu_f32(b[2]) * b[3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        v, yr, in ? ((uint32_t)m * (uint32_t)NY + (uint32_t)(n / 2)) * 2u : kOOB, 0, 0);
+                }
             } else {
                 const u4 h = {pack2<BF>(a[0], a[1]), pack2<BF>(a[2], a[3]), pack2<BF>(b[0], b[1]),
                               pack2<BF>(b[2], b[3])};
@@ -880,8 +886,10 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
 // Sums the split tiles' partials (row-major 256 x 256 fp32 tiles, as
 // wide_store writes them) in chunk order (fixed, so results are
 // bit-reproducible) and stores y.  One thread per (tile, row, run of 8
-// columns): 8192 per tile.
-template <bool BF>
+// columns): 8192 per tile.  SILU: the merged gate/up projection, whose split
+// tiles ran without the SiLU epilogue: each (gate, up) column pair of the
+// sums becomes silu(gate) * up at column n/2 of y [M, N/2].
+template <bool BF, bool SILU>
 __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
     const float *__restrict__ partials, uint16_t *__restrict__ y, int M, int N, int tiles_m,
     int tiles_dp, int chunks, int tail_tiles) {
@@ -899,15 +907,23 @@ __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
         a += *reinterpret_cast<const f4 *>(src + (size_t)c * kWSlot);
         b += *reinterpret_cast<const f4 *>(src + (size_t)c * kWSlot + 4);
     }
-    *reinterpret_cast<u4 *>(y + (size_t)m * N + n) =
-        u4{pack2<BF>(a[0], a[1]), pack2<BF>(a[2], a[3]), pack2<BF>(b[0], b[1]),
-           pack2<BF>(b[2], b[3])};
+    if constexpr (SILU) {
+        *reinterpret_cast<u2 *>(y + (size_t)m * (N / 2) + n / 2) =
+            u2{pack2<BF>(silu_f32(a[0]) * a[1], silu_f32(a[2]) * a[3]),
+               pack2<BF>(silu_f32(b[0]) * b[1], silu_f32(b[2]) * b[3])};
+    } else {
+        *reinterpret_cast<u4 *>(y + (size_t)m * N + n) =
+            u4{pack2<BF>(a[0], a[1]), pack2<BF>(a[2], a[3]), pack2<BF>(b[0], b[1]),
+               pack2<BF>(b[2], b[3])};
+    }
 }
 
 // Split of the wide kernel's tiles: whole rounds of one tile per workgroup;
 // a last partial round of `tail` tiles (at most half a round) split into
 // `chunks` >= 2 stage ranges of at least 8 stages, so that tail * chunks
 // workgroups fill about one round, and at most `capacity` partial tiles.
+// (For the merged gate/up projection the split tiles store plain fp32 sums
+// and the reduce kernel applies SiLU.)
 struct WidePlan {
     int tiles, tiles_dp, tail, chunks;
 };
@@ -919,7 +935,7 @@ static WidePlan wide_plan(const LinearArgs &a, int num_cus, int capacity) {
     w.tail = 0;
     w.chunks = 1;
     const int nst = (int)((a.K + kWBK - 1) / kWBK);
-    if (num_cus <= 0 || a.silu) return w;     // the SiLU epilogue stores whole tiles only
+    if (num_cus <= 0) return w;
     const int tail = w.tiles % num_cus;
     if (tail == 0 || 2 * tail > num_cus) return w;
     const int chunks = std::min(std::min(num_cus / tail, nst / 8), capacity / tail);
@@ -956,22 +972,26 @@ static hipError_t launch_prefill_m256(const LinearArgs &a, hipStream_t stream, v
     PrefillTerm term = a.pterm;
     void *args[] = {&xp, &qp, &sp, &yp, &M, &K, &N, &gshift, &tiles_m, &tiles_dp, &per_xcd,
                     &chunks, &partials, &term};
-    const void *k;
-    if (a.bf16 && a.scales_bf16)
-        k = a.silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, true, true>)
-                   : reinterpret_cast<const void *>(&prefill_m256_kernel<true, false, true>);
-    else if (a.bf16)
-        k = a.silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, true, false>)
-                   : reinterpret_cast<const void *>(&prefill_m256_kernel<true, false, false>);
-    else
-        k = a.silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<false, true, false>)
-                   : reinterpret_cast<const void *>(&prefill_m256_kernel<false, false, false>);
-    hipError_t e = hipLaunchKernel(k, dim3(8 * per_xcd + tail * chunks), dim3(256), args, 0, stream);
+    auto kernel = [&](bool silu) -> const void * {
+        if (a.bf16 && a.scales_bf16)
+            return silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, true, true>)
+                        : reinterpret_cast<const void *>(&prefill_m256_kernel<true, false, true>);
+        if (a.bf16)
+            return silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<true, true, false>)
+                        : reinterpret_cast<const void *>(&prefill_m256_kernel<true, false, false>);
+        return silu ? reinterpret_cast<const void *>(&prefill_m256_kernel<false, true, false>)
+                    : reinterpret_cast<const void *>(&prefill_m256_kernel<false, false, false>);
+    };
+    hipError_t e = hipLaunchKernel(kernel(a.silu), dim3(8 * per_xcd + tail * chunks), dim3(256),
+                                   args, 0, stream);
     if (e != hipSuccess || tail == 0) return e;
     const float *pc = partials;
     void *rargs[] = {&pc, &yp, &M, &N, &tiles_m, &tiles_dp, &chunks, &tail};
-    const void *rk = a.bf16 ? reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<true>)
-                            : reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<false>);
+    const void *rk =
+        a.silu ? (a.bf16 ? reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<true, true>)
+                         : reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<false, true>))
+               : (a.bf16 ? reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<true, false>)
+                         : reinterpret_cast<const void *>(&prefill_tail_reduce_kernel<false, false>));
     return hipLaunchKernel(rk, dim3(32 * tail), dim3(256), rargs, 0, stream);
 }
 

@@ -60,7 +60,8 @@ def _run(inp, q, s, g, kernel, bf16, dev):
     (4, 2064, 1040, 16, (DEC, PRE)),     # g = 16, ragged K, ragged tiles
     (16, 4096, 1024, 64, (DEC,)),        # partial slots and the reduce kernel
     (64, 2048, 4096, -1, (PRE,)),        # 128-row prefill, split K
-    (300, 1024, 1056, 32, (PRE,)),       # 256-row prefill, whole tiles, ragged M
+    (300, 1024, 1056, 32, (PRE,)),       # 256-row prefill, ragged M: all 10 tiles split along K,
+                                         # sums reduced with SiLU applied by the reduce kernel
 ])
 def test_gate_up_silu_parity(dev, bf16, M, K, N, g, kernels):
     case, inp = _case(M, K, N, g, 80 + M, bf16)
@@ -90,6 +91,42 @@ def test_gate_up_silu_model_shape(dev):
     y = _run(inp, q, s, 128, AUTO, False, dev)
     assert y.shape == (1, 17408)
     check_gate_up(y, ref, lin, mag, None, 5120, False, "gate_up model shape")
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp16", "bf16"])
+def test_gate_up_prefill_model_shape_sampled(dev, bf16):
+    """The 27B MLP at M = 2048 (K=5120, N = 2 x 17408): 1024 whole tiles with
+    the SiLU epilogue and a last round of 64 tiles split along K, whose sums
+    the reduce kernel turns into silu(gate) * up.  Checked on 4096 sampled
+    outputs, half of them in the split tiles (outputs 16384 .. 17407), against
+    the oracle's linear at both columns of each pair with SiLU applied to the
+    gate in float64 (the oracle's gate/up definition)."""
+    c = workloads.gate_up_prefill()
+    inp = workloads.generate_bf16(c) if bf16 else workloads.generate(c)
+    act = "bf16" if bf16 else "f16"
+    M, K, N, g = c.M, c.K, c.N, c.group_size
+    q_o = oracle.pack(inp.codes)
+    q = torch.from_numpy(w4.pack_gptq_v2(inp.codes)).to(dev)
+    s = torch.from_numpy(inp.scales).to(dev)
+    y = _run(inp, q, s, g, AUTO, bf16, dev)
+    y2 = _run(inp, q, s, g, AUTO, bf16, dev)
+    assert np.array_equal(y, y2), "results differ between runs"
+    rng = np.random.default_rng(92)
+    ms = rng.integers(0, M, size=4096)
+    js = np.concatenate([rng.integers(0, N // 2, size=2048),
+                         rng.integers(N // 2 - 1024, N // 2, size=2048)])
+    cols = np.stack([2 * js, 2 * js + 1], axis=1).reshape(-1)
+    rows = np.repeat(ms, 2)
+    lin = oracle.linear_at(inp.x, q_o, inp.scales, g, rows, cols, act=act).reshape(1, -1)
+    mag = oracle.linear_at(inp.x, q_o, inp.scales, g, rows, cols, act=act,
+                           absval=True).reshape(1, -1)
+    mag0 = oracle.linear_at(inp.x, np.zeros_like(q_o), inp.scales, g, rows, cols, act=act,
+                            absval=True).reshape(1, -1)
+    gg, uu = lin[:, 0::2], lin[:, 1::2]
+    with np.errstate(over="ignore"):
+        ref = gg / (1.0 + np.exp(-gg)) * uu
+    check_gate_up(y[ms, js].reshape(1, -1), ref, lin, mag, mag0, K, bf16,
+                  f"gate_up prefill model shape {act}")
 
 
 def test_gate_up_silu_zero_gate_gives_exact_zero(dev):
