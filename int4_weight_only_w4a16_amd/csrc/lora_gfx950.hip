@@ -46,51 +46,65 @@ constexpr int kLoraTargetGroups = 512;   // shrink workgroups aimed for (2 per C
 constexpr int kLoraMaxSplits = 16;       // K chunks of the shrink, at most
 
 
-// One workgroup (4 waves) computes the partial t of a 16-row block of x over
-// one K chunk, for 64 columns of t (blockIdx.z): the waves take alternate
-// 32-wide K steps of the chunk and their sums are added in LDS in wave order.
-template <bool BF>
+// One workgroup (4 waves) computes the partial t of RB 16-row blocks of x
+// over one K chunk, for 64 columns of t (blockIdx.z): the waves take
+// alternate 32-wide K steps of the chunk (each A fragment loaded once for the
+// RB blocks) and their sums are added in LDS in wave order.  Row blocks past
+// the last (mblocks) are not written.
+template <bool BF, int RB>
 __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__restrict__ x,
                                                           const uint16_t *__restrict__ A,
                                                           float *__restrict__ tp, int M, int K,
                                                           int r, int Mp, int chunk_steps) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int mb = blockIdx.x, s = blockIdx.y, jc = blockIdx.z;
+    const int mg = blockIdx.x, s = blockIdx.y, jc = blockIdx.z;
     const int nsteps = (K + 31) / 32;
     const int kb = s * chunk_steps;
     const int ke = min(kb + chunk_steps, nsteps);
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
     const auto ar = make_rsrc(A, (uint32_t)r * (uint32_t)K * 2u);
-    const int row = 16 * mb + (lane & 15);
     const int kofs = 8 * (lane >> 4);
     const int jbn = min(4, (r - 64 * jc + 15) / 16);   // column blocks of t present here
-    f4 acc[4] = {};
+    f4 acc[RB][4] = {};
 #pragma unroll 4
     for (int st = kb + w; st < ke; st += 4) {
         const int k = 32 * st + kofs;             // K % 8 == 0: eight in or eight out
         const bool kin = k < K;
-        const uint32_t xo = (row < M && kin) ? (uint32_t)(row * K + k) * 2u : kOOB;
-        const u4 xa = load_b128(xr, xo);
+        u4 xa[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row = 16 * (RB * mg + rb) + (lane & 15);
+            xa[rb] = load_b128(xr, (row < M && kin) ? (uint32_t)(row * K + k) * 2u : kOOB);
+        }
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             if (jb < jbn) {                       // uniform across the workgroup
                 const int j = 64 * jc + 16 * jb + (lane & 15);
                 const uint32_t ao = (j < r && kin) ? (uint32_t)(j * K + k) * 2u : kOOB;
-                acc[jb] = mfma16x16x32_t<BF>(xa, load_b128(ar, ao), acc[jb]);
+                const u4 av = load_b128(ar, ao);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) acc[rb][jb] = mfma16x16x32_t<BF>(xa[rb], av, acc[rb][jb]);
             }
         }
     }
-    __shared__ f4 red[4][4][64];
+    __shared__ f4 red[4][RB][4][64];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) red[w][jb][lane] = acc[jb];
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) red[w][rb][jb][lane] = acc[rb][jb];
     __syncthreads();
-    // thread (w, lane) finishes column block w of the four
-    const f4 v = ((red[0][w][lane] + red[1][w][lane]) + red[2][w][lane]) + red[3][w][lane];
+    // thread (w, lane) finishes column block w of the four, for every row block
     const int j = 64 * jc + 16 * w + (lane & 15);
-    if (j < r) {
-        float *dst = tp + ((size_t)s * Mp + 16 * mb + 4 * (lane >> 4)) * r + j;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(size_t)i * r] = v[i];
+    for (int rb = 0; rb < RB; ++rb) {
+        const int mb = RB * mg + rb;
+        const f4 v = ((red[0][rb][w][lane] + red[1][rb][w][lane]) + red[2][rb][w][lane]) +
+                     red[3][rb][w][lane];
+        if (j < r && 16 * mb < Mp) {
+            float *dst = tp + ((size_t)s * Mp + 16 * mb + 4 * (lane >> 4)) * r + j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(size_t)i * r] = v[i];
+        }
     }
 }
 
@@ -296,8 +310,12 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const float *__restric
     }
 }
 
+// rb: 16-row blocks per shrink workgroup: 4 from 64 blocks on (M > 1008),
+// each A fragment then serving four blocks (M=2048, rank 32: 336 -> 334 us
+// for the whole LoRA prefill step); 1 below (at M=512, four measured 2-4 us
+// slower: too few workgroups).
 struct LoraPlan {
-    int mblocks, jchunks, chunk_steps, splits, Mp;
+    int mblocks, jchunks, chunk_steps, splits, Mp, rb;
 };
 
 LoraPlan lora_plan(int64_t M, int64_t K, int64_t r, int max_splits = kLoraMaxSplits) {
@@ -305,8 +323,9 @@ LoraPlan lora_plan(int64_t M, int64_t K, int64_t r, int max_splits = kLoraMaxSpl
     p.mblocks = (int)((M + 15) / 16);
     p.Mp = 16 * p.mblocks;
     p.jchunks = (int)((r + 63) / 64);
+    p.rb = p.mblocks >= 64 ? 4 : 1;
     const int nsteps = (int)((K + 31) / 32);
-    const int groups = p.mblocks * p.jchunks;
+    const int groups = (p.mblocks + p.rb - 1) / p.rb * p.jchunks;
     int want = (kLoraTargetGroups + groups - 1) / groups;
     want = want < 1 ? 1 : want > max_splits ? max_splits : want;
     int per = (nsteps + want - 1) / want;
@@ -358,14 +377,21 @@ static hipError_t launch_expand(const float *tp, const uint16_t *B, uint16_t *y,
 
 static hipError_t run_shrink(const LoraArgs &a, const LoraPlan &p, hipStream_t stream,
                              float *tp) {
-    const dim3 sg(p.mblocks, p.splits, p.jchunks);
+    const dim3 sg((p.mblocks + p.rb - 1) / p.rb, p.splits, p.jchunks);
     const auto *x = static_cast<const uint16_t *>(a.x);
     const auto *A = static_cast<const uint16_t *>(a.A);
     const int M = (int)a.M, K = (int)a.K, r = (int)a.r;
-    if (a.bf16)
-        lora_shrink_kernel<true><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
-    else
-        lora_shrink_kernel<false><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
+    if (p.rb == 4) {
+        if (a.bf16)
+            lora_shrink_kernel<true, 4><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
+        else
+            lora_shrink_kernel<false, 4><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
+    } else {
+        if (a.bf16)
+            lora_shrink_kernel<true, 1><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
+        else
+            lora_shrink_kernel<false, 1><<<sg, 256, 0, stream>>>(x, A, tp, M, K, r, p.Mp, p.chunk_steps);
+    }
     return hipGetLastError();
 }
 
