@@ -862,6 +862,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const int S = (K + 31) >> 5;
     const int T = (N + kCols - 1) / kCols;
     const StreamK sk{T * S, (int)gridDim.x};
+    // three contributors per tile (each range a third of one tile)
+    const bool three = partials == nullptr && (int)gridDim.x == 3 * T;
     // LK: the first Su workgroups also own a shrink unit, whose publication
     // by their last wave gives that wave a lighter share of the range
     const int g = blockIdx.x;
@@ -980,7 +982,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     // Fixed-order sum over the waves for every tile of this range; whole
     // tiles are stored.  Without `partials`, a split tile has exactly two
     // contributors (the host keeps every range at least one tile long, or
-    // makes each tile exactly two ranges), and they meet per output element
+    // makes each tile exactly two ranges; a grid of 3T, three, is finished in
+    // two such meetings, below), and they meet per output element
     // in the tile's exchange slots with one system-scope compare-and-swap per
     // column pair: the first deposits its partials, the second gets them
     // back, adds its own (one fp32 add each, so the result does not depend on
@@ -1019,7 +1022,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         // then adds the same two fp32 values); with `partials` the reduce
         // kernel adds it
         const int gl = tb <= u1 ? g : g + 1;
-        if (LK && (whole || (!partials && gl == g))) {   // uniform over the wave
+        // (with three contributors, the last one carries the term)
+        if (LK && (whole || (!partials && (three ? g - 3 * tau == 2 : gl == g)))) {   // uniform
             f4 d[kNW];
             lora_tile_delta<BF>(d, tfr, lora, N, tau,
                                 tau - b0 < lb.nb
@@ -1036,6 +1040,58 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         if (partials) {
             float *mine = partials + ((size_t)g * 2 + (tau == b0 ? 0 : 1)) * SLOT;
             *reinterpret_cast<f4 *>(mine + m * kCols + c) = f4{v[0], v[1], v[2], v[3]};
+            continue;
+        }
+        if (three) {
+            // three contributors i = g - 3 tau: 0 and 1 meet at the slot of
+            // workgroup 3 tau + 1; whichever comes second carries p0 + p1 to
+            // the slot of 3 tau + 2 and meets contributor 2 there.  Each
+            // meeting adds two fp32 values, so y = (p0 + p1) + p2 whatever the
+            // arrival order.
+            const int i3 = g - 3 * tau;
+            float w[kNW];
+            bool live[kNW / 2];
+#pragma unroll
+            for (int j = 0; j < kNW; ++j) w[j] = v[j];
+#pragma unroll
+            for (int j = 0; j < kNW / 2; ++j) live[j] = true;
+            if (i3 < 2) {
+                uint64_t *s1 = slots + ((size_t)(3 * tau + 1) * 16 + m) * (kCols / 2) + c / 2;
+                uint64_t got1[kNW / 2];
+#pragma unroll
+                for (int j = 0; j < kNW / 2; ++j) {
+                    got1[j] = 0;
+                    const uint64_t mine = (uint64_t)slot_code(w[2 * j]) | ((uint64_t)slot_code(w[2 * j + 1]) << 32);
+                    __hip_atomic_compare_exchange_strong(s1 + j, &got1[j], mine, __ATOMIC_RELAXED,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                }
+#pragma unroll
+                for (int j = 0; j < kNW / 2; ++j) {
+                    live[j] = got1[j] != 0;
+                    if (!live[j]) continue;
+                    w[2 * j] = __builtin_bit_cast(float, (uint32_t)got1[j] ^ kSlotKey) + w[2 * j];
+                    w[2 * j + 1] = __builtin_bit_cast(float, (uint32_t)(got1[j] >> 32) ^ kSlotKey) + w[2 * j + 1];
+                    __hip_atomic_store(s1 + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                }
+            }
+            uint64_t *s2 = slots + ((size_t)(3 * tau + 2) * 16 + m) * (kCols / 2) + c / 2;
+            uint64_t got2[kNW / 2];
+#pragma unroll
+            for (int j = 0; j < kNW / 2; ++j) {
+                got2[j] = 0;
+                if (!live[j]) continue;
+                const uint64_t mine = (uint64_t)slot_code(w[2 * j]) | ((uint64_t)slot_code(w[2 * j + 1]) << 32);
+                __hip_atomic_compare_exchange_strong(s2 + j, &got2[j], mine, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+#pragma unroll
+            for (int j = 0; j < kNW / 2; ++j) {
+                if (got2[j] == 0) continue;
+                const float r0 = __builtin_bit_cast(float, (uint32_t)got2[j] ^ kSlotKey) + w[2 * j];
+                const float r1 = __builtin_bit_cast(float, (uint32_t)(got2[j] >> 32) ^ kSlotKey) + w[2 * j + 1];
+                __hip_atomic_store(s2 + j, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                store_pair<BF, SILU>(y, m, N, n + 2 * j, r0, r1);
+            }
             continue;
         }
         uint64_t *slot = slots + ((size_t)gl * 16 + m) * (kCols / 2) + c / 2;
@@ -1130,7 +1186,9 @@ size_t decode_workspace_bytes(int capacity) {
 // us on K = 5120, N = 17408 and -1.5 us on N = 27648; at M = 12 +0.25 us).
 // The other launches use the exchange slots.
 constexpr int kPartialsMinM = 15;
-static bool uses_partials(int grid, int T, int M) { return grid > 2 * T || M >= kPartialsMinM; }
+static bool uses_partials(int grid, int T, int M) {
+    return (grid > 2 * T && grid != 3 * T) || M >= kPartialsMinM;
+}
 
 // With fewer than half as many tiles as CUs, batches above two rows spread
 // over every CU (a tile then has several contributors) when K is long: the
@@ -1139,9 +1197,10 @@ static bool uses_partials(int grid, int T, int M) { return grid > 2 * T || M >= 
 // from S = 256 at M = 16, a loss at S = 256, M = 4 and none at S = 128.
 static bool spread_wide(int64_t M, int64_t S) { return M > 2 && (S >= 384 || (M >= 8 && S >= 256)); }
 
-// Stream-K grid, or 0 for the tiles kernel.  Every tile must have at most two
-// contributors: either every range holds at least one tile (G <= T), or
-// G = 2T and each tile is exactly two ranges.
+// Stream-K grid, or 0 for the tiles kernel.  With the exchange, every tile
+// has at most two contributors (every range holds at least one tile, G <= T,
+// or G = 2T and each tile is exactly two ranges) or exactly three (G = 3T);
+// wider grids use the partial slots.
 int decode_streamk_grid(const LinearArgs &a, int num_cus) {
     const int64_t S = (a.K + 31) / 32;
     const int64_t T = (a.N + kCols - 1) / kCols;
@@ -1159,6 +1218,13 @@ int decode_streamk_grid(const LinearArgs &a, int num_cus) {
     }
     // G > 2T: partial slots (a tile may have more than two contributors)
     if (2 * T < num_cus && spread_wide(a.M, S)) return num_cus;
+    // G = 3T: each tile exactly three ranges, finished by the two-level
+    // exchange; its second round trip pays off with long ranges (K >= 8192)
+    // or heavier units (M >= 4): down projection K=17408, M=1 15.5 -> 13.7 us,
+    // M=2 16.6 -> 14.0 us, K=N=5120 M=8 9.7 -> 9.3 us; at K=5120 and M=1,
+    // 0.2 us slower
+    if (3 * T <= num_cus && S >= 24 && a.M < kPartialsMinM && (S >= 256 || a.M >= 4))
+        return (int)(3 * T);
     if (2 * T <= num_cus && S >= 2) return (int)(2 * T);
     return (int)T;
 }
