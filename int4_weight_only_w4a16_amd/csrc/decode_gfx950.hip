@@ -1216,15 +1216,17 @@ int decode_streamk_grid(const LinearArgs &a, int num_cus) {
                 if (wave_share<kDecWaves>(n, w + 1) - wave_share<kDecWaves>(n, w) > S) return 0;
         return num_cus;
     }
-    // G > 2T: partial slots (a tile may have more than two contributors)
-    if (2 * T < num_cus && spread_wide(a.M, S)) return num_cus;
     // G = 3T: each tile exactly three ranges, finished by the two-level
     // exchange; its second round trip pays off with long ranges (K >= 8192)
     // or heavier units (M >= 4): down projection K=17408, M=1 15.5 -> 13.7 us,
     // M=2 16.6 -> 14.0 us, K=N=5120 M=8 9.7 -> 9.3 us; at K=5120 and M=1,
-    // 0.2 us slower
+    // 0.2 us slower.  Where the wide grid below would also apply, three is
+    // faster: K=17408 M = 3 / 4 / 8 / 12 / 14: 15.2 / 15.2 / 16.1 / 17.6 /
+    // 18.4 -> 14.0 / 14.4 / 15.1 / 16.8 / 18.0 us.
     if (3 * T <= num_cus && S >= 24 && a.M < kPartialsMinM && (S >= 256 || a.M >= 4))
         return (int)(3 * T);
+    // G > 2T: partial slots (a tile may have more than two contributors)
+    if (2 * T < num_cus && spread_wide(a.M, S)) return num_cus;
     if (2 * T <= num_cus && S >= 2) return (int)(2 * T);
     return (int)T;
 }
