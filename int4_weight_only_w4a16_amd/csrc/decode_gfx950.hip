@@ -1187,7 +1187,8 @@ size_t decode_workspace_bytes(int capacity) {
 // The other launches use the exchange slots.
 constexpr int kPartialsMinM = 15;
 static bool uses_partials(int grid, int T, int M) {
-    return (grid > 2 * T && grid != 3 * T) || M >= kPartialsMinM;
+    if (grid == 3 * T) return false;   // the two-level exchange, for every M
+    return grid > 2 * T || M >= kPartialsMinM;
 }
 
 // With fewer than half as many tiles as CUs, batches above two rows spread
@@ -1222,9 +1223,9 @@ int decode_streamk_grid(const LinearArgs &a, int num_cus) {
     // M=2 16.6 -> 14.0 us, K=N=5120 M=8 9.7 -> 9.3 us; at K=5120 and M=1,
     // 0.2 us slower.  Where the wide grid below would also apply, three is
     // faster: K=17408 M = 3 / 4 / 8 / 12 / 14: 15.2 / 15.2 / 16.1 / 17.6 /
-    // 18.4 -> 14.0 / 14.4 / 15.1 / 16.8 / 18.0 us.
-    if (3 * T <= num_cus && S >= 24 && a.M < kPartialsMinM && (S >= 256 || a.M >= 4))
-        return (int)(3 * T);
+    // 18.4 -> 14.0 / 14.4 / 15.1 / 16.8 / 18.0 us; and at M = 15-16 than the
+    // partial slots: K=17408 M=16 19.4 -> 18.9 us, K=N=5120 M=16 12.1 -> 11.1 us.
+    if (3 * T <= num_cus && S >= 24 && (S >= 256 || a.M >= 4)) return (int)(3 * T);
     // G > 2T: partial slots (a tile may have more than two contributors)
     if (2 * T < num_cus && spread_wide(a.M, S)) return num_cus;
     if (2 * T <= num_cus && S >= 2) return (int)(2 * T);
