@@ -56,7 +56,8 @@ def _run(x, q, s, g, kernel):
     (3, 2064, 520, 16, (DEC, PRE)),     # g = 16 scale rows, ragged K (K % 32 = 16)
     (8, 1024, 2048, 64, (DEC, PRE)),
     (16, 4096, 1024, 256, (DEC, PRE)),
-    (15, 5120, 5120, 128, (DEC,)),      # partial slots and the reduce kernel
+    (15, 5120, 5120, 128, (DEC,)),      # three ranges per tile, the two-level exchange
+    (15, 2048, 17408, 128, (DEC,)),     # one range per CU: partial slots and the reduce kernel
     (64, 1040, 776, -1, (PRE,)),        # 128-row prefill kernel, ragged K and N
     (300, 1536, 1032, 512, (PRE,)),     # 256-row prefill kernel, ragged M and N
     (2, 2048, 4096, 1024, (DEC,)),

@@ -58,7 +58,8 @@ def _run(inp, q, s, g, kernel, bf16, dev):
 @pytest.mark.parametrize("M,K,N,g,kernels", [
     (1, 5120, 2048, 128, (DEC, PRE)),    # stream-K decode: exchange slots
     (4, 2064, 1040, 16, (DEC, PRE)),     # g = 16, ragged K, ragged tiles
-    (16, 4096, 1024, 64, (DEC,)),        # partial slots and the reduce kernel
+    (16, 4096, 1024, 64, (DEC,)),        # three ranges per tile, the two-level exchange
+    (16, 1024, 17408, 64, (DEC,)),       # one range per CU: partial slots and the reduce kernel
     (64, 2048, 4096, -1, (PRE,)),        # 128-row prefill, split K
     (300, 1024, 1056, 32, (PRE,)),       # 256-row prefill, ragged M: all 10 tiles split along K,
                                          # sums reduced with SiLU applied by the reduce kernel

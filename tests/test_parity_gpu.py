@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import check_parity, sample_indices
+from gpu_util import bf16_to_float, check_parity, check_parity_bf16, sample_indices
 
 pytestmark = pytest.mark.gpu
 
@@ -505,9 +505,11 @@ def test_decode_after_other_launches(dev):
 
 @pytest.mark.parametrize("M", [1, 2, 3, 8, 14, 15, 16])
 def test_decode_split_tiles_exchange(dev, M):
-    """Bench-like widths: most tiles are split between two workgroups, which
-    meet per output column pair in an exchange slot (M <= 14), or leave
-    partial tiles that a second kernel adds (M = 15, 16)."""
+    """Bench-like widths.  K=5120, N=17408 (272 tiles, one range per CU): most
+    tiles are split between two workgroups, which meet per output column pair
+    in an exchange slot (M <= 14), or leave partial tiles that a second kernel
+    adds (M = 15, 16).  K=17408, N=5120 (80 tiles): three ranges per tile,
+    finished by the two-level exchange, for every M."""
     for K, N, g in ((5120, 17408, 128), (17408, 5120, 32)):
         case = workloads.Case(f"split_{M}_{K}_{N}", M, K, N, g, 41, scales="loguniform")
         inp = workloads.generate(case)
@@ -521,10 +523,11 @@ def test_decode_split_tiles_exchange(dev, M):
 
 @pytest.mark.parametrize("M", [3, 5, 16])
 def test_decode_wide_partials_ragged(dev, M):
-    """Few tiles and long K with M > 2: every CU takes a range, a tile has up
-    to many contributors, and a second kernel adds their partials; ragged K
-    (the last 32-deep step half inside K) and ragged N."""
-    case = workloads.Case(f"wide_{M}", M, 16400, 1032, 16, 45, scales="loguniform")
+    """Between a third and a half as many tiles as CUs (6136 columns: 96 tiles)
+    and long K with M > 2: every CU takes a range, a tile has up to three
+    contributors, and a second kernel adds their partials; ragged K (the last
+    32-deep step half inside K) and ragged N."""
+    case = workloads.Case(f"wide_{M}", M, 16400, 6136, 16, 45, scales="loguniform")
     inp = workloads.generate(case)
     q_o, q_dev, s_dev = _weights(case, inp, dev)
     y_ref = oracle.linear(inp.x, q_o, inp.scales, 16)
@@ -532,6 +535,39 @@ def test_decode_wide_partials_ragged(dev, M):
     check_parity(runs[0], y_ref, f"wide M={M}")
     for r in runs[1:]:
         assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N,g", [
+    (1, 8192, 1032, 64),       # 17 tiles, three ranges each (long K)
+    (4, 1040, 264, 16),        # 5 tiles x 3 (M >= 4), ragged K and N
+    (7, 2064, 5432, -1),       # 85 tiles x 3 = 255 workgroups, the most that fit
+    (16, 4096, 2056, 128),     # 33 tiles x 3 at M = 16
+])
+def test_decode_three_contributors(dev, M, K, N, g):
+    """Tiles split into exactly three ranges: contributors 0 and 1 meet first,
+    whichever comes second meets contributor 2, so y = (p0 + p1) + p2 in any
+    arrival order; checked against the oracle and bit for bit across runs,
+    bf16 as well, and a second shape on the same stream reuses the slots."""
+    case = workloads.Case(f"three_{M}_{K}_{N}", M, K, N, g, 47, scales="loguniform")
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    y_ref = oracle.linear(inp.x, q_o, inp.scales, g)
+    runs = [_run(inp, q_dev, s_dev, g, dev, DEC) for _ in range(4)]
+    check_parity(runs[0], y_ref, f"three M={M} K={K} N={N}")
+    for r in runs[1:]:
+        assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
+    cb = workloads.Case(f"three_bf16_{M}_{K}_{N}", M, K, N, g, 48, scales="loguniform")
+    ib = workloads.generate_bf16(cb)
+    qb_o, qb_dev, sb_dev = _weights(cb, ib, dev)
+    xb = torch.from_numpy(ib.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    yb = w4.linear(xb, qb_dev, sb_dev, g, kernel=DEC)
+    torch.cuda.synchronize()
+    yb = bf16_to_float(yb.cpu().view(torch.int16).numpy())
+    check_parity_bf16(yb, oracle.linear(ib.x, qb_o, ib.scales, g, act="bf16"),
+                      oracle.linear(ib.x, qb_o, ib.scales, g, act="bf16", absval=True), K,
+                      f"three bf16 M={M}",
+                      mag0=oracle.linear(ib.x, np.zeros_like(qb_o), ib.scales, g, act="bf16",
+                                         absval=True))
 
 
 @pytest.mark.parametrize("M,K,N,g,full", [

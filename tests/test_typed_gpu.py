@@ -74,7 +74,8 @@ def _zp_workspace(M, K, N, g, dev):
     (1, 256, 256, 32, "wide", (DEC, PRE)),           # one step per group
     (3, 2064, 520, 16, "wide", (DEC, PRE)),          # g = 16 (scale per 8-deep block), ragged K
     (8, 1024, 2048, 64, "loguniform", (DEC, PRE)),   # scale per group
-    (15, 5120, 5120, 128, "loguniform", (DEC,)),     # partial slots and the reduce kernel
+    (15, 5120, 5120, 128, "loguniform", (DEC,)),     # three ranges per tile, the two-level exchange
+    (16, 2048, 17408, 128, "loguniform", (DEC,)),    # one range per CU: partial slots, reduce kernel
     (7, 8192, 1032, -1, "wide", (DEC,)),             # one group over K
     (64, 1040, 776, -1, "wide", (PRE,)),             # 128-row prefill, ragged K and N
     (300, 1536, 1032, 512, "loguniform", (PRE,)),    # 256-row prefill, ragged M and N

@@ -3,7 +3,7 @@ scratch is the library's file-scope device array) against w4a16_linear and the
 oracle, through the C ABI on cuda:0.
 
 Two calls in a row, the second with a smaller input, on the decode kernel
-(stream-K with the exchange slots, and with partial slots and the reduce
+(stream-K with the exchange slots, the two-level exchange, and with partial slots and the reduce
 kernel), the small-M prefill kernel (split K) and the wide prefill kernel
 (split last round); free device memory unchanged across the calls; and a call
 captured on a stream with nothing allocated for it replays to the eager bits.
@@ -46,7 +46,8 @@ def _prepare(M, K, N, g, seed, dev):
 # pairs of calls: the second smaller than the first
 PAIRS = [
     ((1, 5120, 17408, 128), (1, 2048, 4096, 32)),      # decode: exchange slots
-    ((16, 5120, 5120, 64), (15, 1024, 2048, 128)),     # decode: partial slots + reduce kernel
+    ((16, 5120, 5120, 64), (4, 1024, 2048, 128)),      # decode: three ranges per tile
+    ((16, 2048, 17408, 64), (15, 2048, 8192, 128)),    # decode: partial slots + reduce kernel
     ((64, 5120, 5120, 128), (40, 2048, 1024, 32)),     # prefill M <= 128: split K
     ((2048, 5120, 17408, 128), (300, 2048, 2048, 64)), # prefill M > 128: split last round
 ]
