@@ -356,19 +356,23 @@ def test_workspace_allocation_stated_and_released(dev):
 
 
 def test_stream_release_cycles_leave_memory_unchanged(dev):
-    """32 cycles of a new stream, decode and prefill calls on it, release and
-    stream destruction leave the device's free memory unchanged."""
-    case = workloads.Case("cycles", 64, 2048, 4096, 64, 24)
+    """32 cycles of a new stream, decode and prefill calls on it (the 128-row
+    kernel and the 256-row kernel with a split last round, both of which take
+    the stream's workspace), release and stream destruction leave the device's
+    free memory unchanged."""
+    case = workloads.Case("cycles", 300, 2048, 4096, 64, 24)
     inp = workloads.generate(case)
     _, q_dev, s_dev = _weights(case, inp, dev)
     x = torch.from_numpy(inp.x).to(dev)
     x4 = x[:4].contiguous()
-    y = torch.empty((64, 4096), dtype=torch.float16, device=dev)
+    x64 = x[:64].contiguous()
+    y = torch.empty((300, 4096), dtype=torch.float16, device=dev)
 
     def cycle():
         st = torch.cuda.Stream()
         w4.w4a16_linear(x4, q_dev, s_dev, y, 4, 2048, 4096, 64, st)
-        w4.w4a16_linear(x, q_dev, s_dev, y, 64, 2048, 4096, 64, st)
+        w4.w4a16_linear(x64, q_dev, s_dev, y, 64, 2048, 4096, 64, st)
+        w4.w4a16_linear(x, q_dev, s_dev, y, 300, 2048, 4096, 64, st)
         w4.w4a16_stream_release(st)
         del st
 
