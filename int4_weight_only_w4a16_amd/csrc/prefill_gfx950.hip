@@ -834,11 +834,31 @@ __device__ __forceinline__ void wide_store(lds_u8_t *L, const WideOperands &p, i
     }
 }
 
+// Tile order of the wide kernel: bands of kWideBandRows row blocks, each band
+// taken strip by strip (row blocks fastest).  The workgroups that run at the
+// same time on one XCD take consecutive tiles of this order, so they share a
+// few row blocks of activations and a few strips of codes in that XCD's L2,
+// each fetched about once per round: 4 row blocks x 8 strips for the 32
+// workgroups of an XCD, where all 8 row blocks of 4 strips (plain column-
+// major order) fetched every activation row on every XCD.
+#ifndef W4A16_PREFILL_BAND
+#define W4A16_PREFILL_BAND 4
+#endif
+constexpr int kWideBandRows = W4A16_PREFILL_BAND;
+
+__device__ __forceinline__ void wide_tile(int t, int tiles_m, int tiles_n, int &m0, int &n0) {
+    const int band = t / (kWideBandRows * tiles_n);
+    const int first = band * kWideBandRows;
+    const int rows = min(tiles_m - first, kWideBandRows);    // the last band may be lower
+    const int r = t - band * kWideBandRows * tiles_n;
+    m0 = (first + r % rows) * kWBM;
+    n0 = (r / rows) * kWBN;
+}
+
 // The wide kernel.  Workgroups [0, 8 * per_xcd) take one tile each of the
 // first tiles_dp tiles (whole rounds), in XCD-blocked order: workgroup id % 8
-// is taken as its XCD, and XCD x takes tiles x*per_xcd .. in column-major
-// order (row blocks fastest), so the workgroups of one XCD share activation
-// rows.  The remaining tiles (a last, partial round) are split along K into
+// is taken as its XCD, and XCD x takes tiles x*per_xcd .. of the order
+// above.  The remaining tiles (a last, partial round) are split along K into
 // `chunks` equal stage ranges, one workgroup each, run in the same launch;
 // each writes its fp32 partial tile to partials[item] (wide_store) and
 // prefill_tail_reduce_kernel adds them.  Every workgroup streams K from its
@@ -860,16 +880,14 @@ __global__ __launch_bounds__(256) void prefill_m256_kernel(
     if (id < ndp) {
         const int tl = (id & 7) * per_xcd + (id >> 3);
         if (tl >= tiles_dp) return;
-        m0 = (tl % tiles_m) * kWBM;
-        n0 = (tl / tiles_m) * kWBN;
+        wide_tile(tl, tiles_m, (N + kWBN - 1) / kWBN, m0, n0);
         sb = 0;
         se = p.nst;
     } else {
         // split tail: item j = tile tiles_dp + j / chunks, K chunk j % chunks
         j = id - ndp;
         const int t = tiles_dp + j / chunks, c = j % chunks;
-        m0 = (t % tiles_m) * kWBM;
-        n0 = (t / tiles_m) * kWBN;
+        wide_tile(t, tiles_m, (N + kWBN - 1) / kWBN, m0, n0);
         sb = (int)((int64_t)p.nst * c / chunks);
         se = (int)((int64_t)p.nst * (c + 1) / chunks);
     }
@@ -897,9 +915,10 @@ __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
     const int tt = (int)(gid >> 13);
     if (tt >= tail_tiles) return;
     const int r = (int)((gid >> 5) & 255), cc = (int)(gid & 31);
-    const int t = tiles_dp + tt;
-    const int m = (t % tiles_m) * kWBM + r;
-    const int n = (t / tiles_m) * kWBN + 8 * cc;
+    int m0, n0;
+    wide_tile(tiles_dp + tt, tiles_m, (N + kWBN - 1) / kWBN, m0, n0);
+    const int m = m0 + r;
+    const int n = n0 + 8 * cc;
     if (m >= M || n >= N) return;
     const float *src = partials + (size_t)tt * chunks * kWSlot + (size_t)r * kWBN + 8 * cc;
     f4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
