@@ -44,9 +44,11 @@
  *         fp32 partial tiles, written before they are read; then the LoRA
  *         term's exit count and slice words, also left zeroed);
  *       prefill: 64 MiB on a 256-CU device (one 256x256 fp32 partial tile
- *         per CU), used when a last partial round of tiles is split along
- *         K (M > 128) and when fewer tiles than CUs are split along K
- *         (M <= 128: fp32 partials of y, one per K chunk).
+ *         per CU), used when a last partial round of 256-row tiles is split
+ *         along K and when fewer 128-row tiles than CUs are split along K
+ *         (fp32 partials of y, one per K chunk).  The 128-row kernel takes
+ *         M <= 128, the 256-row kernel M > 1024; in between the library
+ *         prices both and takes the cheaper.
  *     A call on a stream that is being captured into a graph and has no
  *     workspace yet allocates nothing and runs a kernel that needs none.
  *     Calls on one stream share its workspaces in stream order; calls on
@@ -181,9 +183,8 @@ int w4a16_linear_bf16_ex(const void *x, const int32_t *qweight, const void *scal
  *   N % 16 == 0 (else W4A16_ERR_SHAPE), everything else as for w4a16_linear.
  * The _bf16 forms take bfloat16 x and write bfloat16 y (arithmetic as in
  * w4a16_linear_bf16); the _ex forms choose the kernel as w4a16_linear_ex.
- * Prefill with M > 128 splits a short last round of tiles along K as the
- * linear does; those tiles' fp32 sums are added in a fixed order and SiLU *
- * mul is applied to the sums, as above. */
+ * Prefill splits K as the linear does; split tiles' fp32 sums are added in
+ * a fixed order and SiLU * mul is applied to the sums, as above. */
 int w4a16_gate_up_silu(const void *x, const int32_t *qweight, const void *scales, void *y,
                        int64_t M, int64_t K, int64_t N, int64_t group_size, void *stream);
 int w4a16_gate_up_silu_ex(const void *x, const int32_t *qweight, const void *scales, void *y,

@@ -8,7 +8,8 @@
 // own lane's: each qweight word is exactly one lane's 8-deep B fragment,
 // dequantised in registers to (q-8)*s in fp16 (one rounding).
 //
-// prefill_m256_kernel (M > 128): 256 x 256 output tile per workgroup.
+// prefill_m256_kernel (M > 1024, and 128 < M <= 1024 where use_m256 prices it
+// cheaper than the 128-row kernel): 256 x 256 output tile per workgroup.
 //  * Wave w owns columns 64w .. 64w+63 of all 256 rows: 8 x 2 MFMA tiles,
 //    256 fp32 accumulators per lane.  Eight row tiles share every unpacked B
 //    fragment, which halves the unpack work per MFMA against 128-row tiles.
@@ -26,7 +27,8 @@
 //    main loop has no branches.  One barrier per stage.
 //  * Tiles go to XCDs in blocks (workgroup id % 8 taken as the XCD).
 //
-// prefill_m128_kernel (M <= 128): 128 x 256 tile, 4 x 2 MFMA tiles per wave;
+// prefill_m128_kernel (M <= 128, and mid-sized M where it is priced cheaper):
+//  128 x 256 tile, 4 x 2 MFMA tiles per wave, row blocks of 128 in grid y;
 //  activations go global -> registers -> LDS (reordered to the nibble unpack
 //  order on the way in), weights are loaded into registers three stages
 //  ahead, A fragments read one step ahead.
@@ -35,6 +37,7 @@
 // per-lane checks; stores are masked per row and per column pair (N % 8 == 0).
 
 #include <algorithm>
+#include <cmath>
 
 #include "w4a16_device.hpp"
 #include "w4a16_launch.h"
@@ -968,8 +971,41 @@ static WidePlan wide_plan(const LinearArgs &a, int num_cus, int capacity) {
 static_assert(kPrefillPartialTileBytes == (size_t)kWSlot * sizeof(float), "prefill partial tile size");
 size_t prefill_workspace_bytes(int capacity) { return (size_t)capacity * kPrefillPartialTileBytes; }
 
+// Which kernel takes 128 < M <= 1024.  Both are priced with a model fitted to
+// their measured times on MI355X (about microseconds): a 64-deep stage costs
+// 1.15 in the 256-row kernel and 0.95 in the 128-row one, per round of
+// workgroups; a K split adds its fp32 partials written and read back at
+// about 4 TB/s and 3 for the reduce launch.  The 128-row kernel wins where
+// the 256-row tiles leave most CUs idle or are half padding (M = 384 on the
+// up-projection: 80 against 92 us; M = 192-768 at K = N = 5120: 5-7 us less)
+// and loses badly where its tiles need a second round (M = 512 on the
+// up-projection: 155 against 98 us).  Above 1024 rows the 256-row kernel
+// always wins; at 128 rows and below only the 128-row kernel runs.
+static bool use_m256(const LinearArgs &a, int num_cus) {
+    if (a.M <= 128) return false;
+    if (a.M > 1024 || num_cus <= 0) return true;
+    const double nst = (double)((a.K + kWBK - 1) / kWBK);
+    const double c256 = 1.15, c128 = 0.95, bytes_per_us = 4e6, reduce = 3.0;
+    double t256;
+    const WidePlan w = wide_plan(a, num_cus, num_cus);
+    if (w.chunks < 2)
+        t256 = (double)((w.tiles + num_cus - 1) / num_cus) * nst * c256;
+    else
+        t256 = (double)(w.tiles_dp / num_cus) * nst * c256 + std::ceil(nst / w.chunks) * c256 +
+               (double)w.tail * w.chunks * kPrefillPartialTileBytes * 2.0 / bytes_per_us + reduce;
+    double t128;
+    const int64_t tiles = ((a.N + kPreBN - 1) / kPreBN) * ((a.M + kPreBM - 1) / kPreBM);
+    const int chunks = m128_chunks(a, num_cus, num_cus);
+    if (chunks < 2)
+        t128 = (double)((tiles + num_cus - 1) / num_cus) * nst * c128;
+    else
+        t128 = std::ceil(nst / chunks) * c128 +
+               (double)chunks * a.M * a.N * sizeof(float) * 2.0 / bytes_per_us + reduce;
+    return t256 <= t128;
+}
+
 bool prefill_wants_workspace(const LinearArgs &a, int num_cus) {
-    if (a.M > 128) return wide_plan(a, num_cus, num_cus).chunks > 1;
+    if (use_m256(a, num_cus)) return wide_plan(a, num_cus, num_cus).chunks > 1;
     return m128_chunks(a, num_cus, num_cus) > 1;
 }
 
@@ -1018,7 +1054,7 @@ hipError_t launch_prefill(const LinearArgs &a, hipStream_t stream, void *workspa
                           int num_cus) {
     if (a.scales_bf16 && !a.bf16) return hipErrorInvalidValue;
     if (a.pterm.ta && (a.silu || a.pterm.r <= 0 || a.pterm.r % 8 != 0)) return hipErrorInvalidValue;
-    if (a.M > 128) return launch_prefill_m256(a, stream, workspace, capacity, num_cus);
+    if (use_m256(a, num_cus)) return launch_prefill_m256(a, stream, workspace, capacity, num_cus);
     return launch_prefill_m128(a, stream, workspace, capacity, num_cus);
 }
 

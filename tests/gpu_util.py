@@ -155,3 +155,68 @@ def sample_indices(M: int, N: int, count: int, seed: int):
 
 def oracle_sampled(inp, qweight_o, group_size, ms, ns):
     return oracle.linear_at(inp.x, qweight_o, inp.scales, group_size, ms, ns)
+
+
+# ---------------------------------------------------------------------------
+# Which prefill kernel a shape takes and which tiles a split last round holds,
+# mirrored from the library's host-side planning (for a 256-CU device) so the
+# tests can pick shapes that reach each path; the results are checked against
+# the oracle whichever kernel runs.
+
+def _ceil(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def _wide_plan(M: int, K: int, N: int, cus: int):
+    tiles = _ceil(M, 256) * _ceil(N, 256)
+    nst = _ceil(K, 64)
+    tail = tiles % cus
+    if tail == 0 or 2 * tail > cus:
+        return tiles, 0, 1
+    chunks = min(cus // tail, nst // 8, cus // tail)
+    return (tiles, 0, 1) if chunks < 2 else (tiles, tail, chunks)
+
+
+def _m128_chunks(M: int, K: int, N: int, cus: int) -> int:
+    mt_rows = 32 if M <= 32 else 64 if M <= 64 else 128
+    tiles = _ceil(N, 256) * _ceil(M, mt_rows)
+    chunks = min(cus // tiles, _ceil(K, 64) // 8, cus * 256 * 256 // (M * N))
+    return 1 if chunks < 2 else chunks
+
+
+def prefill_rows(M: int, K: int, N: int, cus: int = 256) -> int:
+    """Rows per tile of the prefill kernel the library picks: 128 or 256."""
+    if M <= 128:
+        return 128
+    if M > 1024:
+        return 256
+    nst = _ceil(K, 64)
+    tiles, tail, chunks = _wide_plan(M, K, N, cus)
+    if chunks < 2:
+        t256 = _ceil(tiles, cus) * nst * 1.15
+    else:
+        t256 = ((tiles - tail) // cus) * nst * 1.15 + _ceil(nst, chunks) * 1.15 \
+            + tail * chunks * 256 * 256 * 4 * 2.0 / 4e6 + 3.0
+    tiles128 = _ceil(N, 256) * _ceil(M, 128)
+    c = _m128_chunks(M, K, N, cus)
+    if c < 2:
+        t128 = _ceil(tiles128, cus) * nst * 0.95
+    else:
+        t128 = _ceil(nst, c) * 0.95 + c * M * N * 4 * 2.0 / 4e6 + 3.0
+    return 256 if t256 <= t128 else 128
+
+
+def wide_tail_tiles(M: int, K: int, N: int, cus: int = 256):
+    """(row, column) origins of the 256 x 256 tiles of a split last round,
+    in the library's banded tile order (bands of 4 row blocks, each walked
+    strip by strip with its row blocks fastest)."""
+    tiles, tail, _ = _wide_plan(M, K, N, cus)
+    tm, tn = _ceil(M, 256), _ceil(N, 256)
+    out = []
+    for t in range(tiles - tail, tiles):
+        band = t // (4 * tn)
+        first = band * 4
+        rows = min(tm - first, 4)
+        r = t - band * 4 * tn
+        out.append(((first + r % rows) * 256, (r // rows) * 256))
+    return out

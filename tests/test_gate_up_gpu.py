@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import bf16_to_float, check_gate_up
+from gpu_util import bf16_to_float, check_gate_up, prefill_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -61,10 +61,13 @@ def _run(inp, q, s, g, kernel, bf16, dev):
     (16, 4096, 1024, 64, (DEC,)),        # three ranges per tile, the two-level exchange
     (16, 1024, 17408, 64, (DEC,)),       # one range per CU: partial slots and the reduce kernel
     (64, 2048, 4096, -1, (PRE,)),        # 128-row prefill, split K
-    (300, 1024, 1056, 32, (PRE,)),       # 256-row prefill, ragged M: all 10 tiles split along K,
+    (300, 1024, 1056, 32, (PRE,)),       # 128-row prefill, three row blocks, split K
+    (1100, 1024, 528, 32, (PRE,)),       # 256-row prefill, ragged M: all 15 tiles split along K,
                                          # sums reduced with SiLU applied by the reduce kernel
 ])
 def test_gate_up_silu_parity(dev, bf16, M, K, N, g, kernels):
+    if M > 128:
+        assert prefill_rows(M, K, N) == (256 if M > 1024 else 128)
     case, inp = _case(M, K, N, g, 80 + M, bf16)
     act = "bf16" if bf16 else "f16"
     q_o = oracle.pack(inp.codes)

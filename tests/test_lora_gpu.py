@@ -87,8 +87,10 @@ CASES = [
     (3, 1040, 136, 16, 40),         # K % 32 == 16, rank not a multiple of 16
     (17, 1024, 520, -1, 64),        # small-M prefill
     (100, 1024, 264, 16, 24),
-    (129, 512, 264, 128, 128),      # wide prefill tiles
+    (129, 512, 264, 128, 128),      # 128-row prefill, two row blocks
     (256, 2048, 1024, 128, 256),
+    (300, 1024, 264, 128, 32),      # 128-row prefill, three row blocks, split K
+    (1100, 1024, 520, 64, 32),      # 256-row prefill, split last round: the first chunk adds the term
     (33, 4096, 264, 32, 1024),      # largest rank
     # decode with the term inside the stream-K launch, and the cases it leaves
     # to the separate shrink and expand kernels

@@ -16,7 +16,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import bf16_to_float, check_parity, check_parity_bf16, sample_indices
+from gpu_util import (bf16_to_float, check_parity, check_parity_bf16, prefill_rows, sample_indices,
+                      wide_tail_tiles)
 
 pytestmark = pytest.mark.gpu
 
@@ -241,7 +242,7 @@ def test_dispatch_edges(dev, M):
     (1, 1040, 8, 1024), (19, 1040, 8, 1024),
     (16, 5120, 5128, 16), (96, 5120, 5128, 16),
     (200, 48, 24, 32), (257, 272, 5128, 256), (300, 1040, 8, 1024), (129, 5120, 5128, 16),
-    (520, 336, 264, -1),
+    (520, 336, 264, -1), (1100, 272, 5128, 256), (1030, 48, 24, 32),
 ])
 def test_tails(dev, M, K, N, g):
     case = workloads.Case(f"tail_{M}_{K}_{N}_{g}", M, K, N, g, 13, scales="loguniform")
@@ -360,19 +361,20 @@ def test_stream_release_cycles_leave_memory_unchanged(dev):
     kernel and the 256-row kernel with a split last round, both of which take
     the stream's workspace), release and stream destruction leave the device's
     free memory unchanged."""
-    case = workloads.Case("cycles", 300, 2048, 4096, 64, 24)
+    case = workloads.Case("cycles", 1100, 2048, 4096, 64, 24)
+    assert prefill_rows(1100, 2048, 4096) == 256 and wide_tail_tiles(1100, 2048, 4096)
     inp = workloads.generate(case)
     _, q_dev, s_dev = _weights(case, inp, dev)
     x = torch.from_numpy(inp.x).to(dev)
     x4 = x[:4].contiguous()
     x64 = x[:64].contiguous()
-    y = torch.empty((300, 4096), dtype=torch.float16, device=dev)
+    y = torch.empty((1100, 4096), dtype=torch.float16, device=dev)
 
     def cycle():
         st = torch.cuda.Stream()
         w4.w4a16_linear(x4, q_dev, s_dev, y, 4, 2048, 4096, 64, st)
         w4.w4a16_linear(x64, q_dev, s_dev, y, 64, 2048, 4096, 64, st)
-        w4.w4a16_linear(x, q_dev, s_dev, y, 300, 2048, 4096, 64, st)
+        w4.w4a16_linear(x, q_dev, s_dev, y, 1100, 2048, 4096, 64, st)
         w4.w4a16_stream_release(st)
         del st
 
@@ -599,18 +601,51 @@ def test_prefill_m128_split_k(dev, M, K, N, g, full):
         assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16))
 
 
+@pytest.mark.parametrize("M,K,N,g,rows,full", [
+    (384, 5120, 17408, 128, 128, False),   # 204 tiles of 128 rows, one round
+    (512, 5120, 5120, 128, 128, False),    # 80 tiles of 128 rows x 3 K chunks
+    (640, 1024, 2056, 32, 128, True),      # 5 row blocks, ragged N, 2 K chunks
+    (1000, 1024, 2056, 32, 128, True),     # 8 row blocks, the last ragged
+    (512, 5120, 17408, 128, 256, False),   # 136 tiles of 256 rows, one round
+    (256, 5120, 17408, 128, 256, False),   # 68 tiles of 256 rows x 3 K chunks
+    (1024, 5120, 5120, 128, 256, False),   # 80 tiles of 256 rows x 3 K chunks
+])
+def test_prefill_mid_m_kernels(dev, M, K, N, g, rows, full):
+    """128 < M <= 1024: the dispatcher prices both prefill kernels and takes
+    the cheaper; cases on either side (the 128-row kernel with several row
+    blocks, split K or not; the 256-row kernel), bitwise equal runs."""
+    assert prefill_rows(M, K, N) == rows
+    case = workloads.Case(f"midm_{M}_{K}_{N}", M, K, N, g, 48, scales="loguniform")
+    inp = workloads.generate(case)
+    q_o, q_dev, s_dev = _weights(case, inp, dev)
+    runs = [_run(inp, q_dev, s_dev, g, dev, AUTO) for _ in range(2)]
+    if full:
+        check_parity(runs[0], oracle.linear(inp.x, q_o, inp.scales, g), case.name)
+    else:
+        ms, ns = sample_indices(M, N, 4096, seed=49)
+        y_ref = oracle.linear_at(inp.x, q_o, inp.scales, g, ms, ns)
+        check_parity(runs[0][ms, ns], y_ref, f"{case.name} (sampled)")
+    assert np.array_equal(runs[0].view(np.uint16), runs[1].view(np.uint16))
+
+
 def test_prefill_split_tail_ragged(dev):
     """A last partial round of 256 x 256 tiles split along K (on a 256-CU
-    device: 272 tiles, the last 16 split in two, the second chunk ending in a
-    K tail), ragged M and N: every output of the tail tiles' columns, a
-    sample of the rest, and bitwise equal runs."""
+    device: 272 tiles, the last 16 of the banded tile order split in two, the
+    second chunk ending in a K tail), ragged M and N: every output of the tail
+    tiles, a sample of the rest, and bitwise equal runs."""
     M, K, N, g = 2000, 1040, 8456, 16
     case = workloads.Case("split_tail", M, K, N, g, 43, scales="loguniform")
     inp = workloads.generate(case)
     q_o, q_dev, s_dev = _weights(case, inp, dev)
-    tail_cols = np.arange(8192, N)
-    ms = np.repeat(np.arange(M), tail_cols.size)
-    ns = np.tile(tail_cols, M)
+    tail = wide_tail_tiles(M, K, N)
+    assert len(tail) == 16 and any(n0 + 256 > N for _, n0 in tail) and any(m0 + 256 > M for m0, _ in tail)
+    ms, ns = [], []
+    for m0, n0 in tail:
+        rows = np.arange(m0, min(m0 + 256, M))
+        cols = np.arange(n0, min(n0 + 256, N))
+        ms.append(np.repeat(rows, cols.size))
+        ns.append(np.tile(cols, rows.size))
+    ms, ns = np.concatenate(ms), np.concatenate(ns)
     sm, sn = sample_indices(M, N, 4096, seed=44)
     ms = np.concatenate([ms, sm]).astype(np.int64)
     ns = np.concatenate([ns, sn]).astype(np.int64)

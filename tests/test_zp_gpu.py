@@ -92,6 +92,8 @@ CASES = [
     (129, 512, 264, 128),
     (256, 2048, 1024, 256),
     (33, 4096, 264, 1024),
+    (300, 1024, 264, 64),           # 128-row prefill, three row blocks, split K
+    (1100, 1024, 264, 128),         # 256-row prefill, split last round
 ]
 
 

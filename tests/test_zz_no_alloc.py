@@ -48,8 +48,8 @@ PAIRS = [
     ((1, 5120, 17408, 128), (1, 2048, 4096, 32)),      # decode: exchange slots
     ((16, 5120, 5120, 64), (4, 1024, 2048, 128)),      # decode: three ranges per tile
     ((16, 2048, 17408, 64), (15, 2048, 8192, 128)),    # decode: partial slots + reduce kernel
-    ((64, 5120, 5120, 128), (40, 2048, 1024, 32)),     # prefill M <= 128: split K
-    ((2048, 5120, 17408, 128), (300, 2048, 2048, 64)), # prefill M > 128: split last round
+    ((64, 5120, 5120, 128), (40, 2048, 1024, 32)),     # 128-row prefill: split K
+    ((2048, 5120, 17408, 128), (1100, 1024, 1024, 64)),  # 256-row prefill: split last round (20 tiles x 2)
 ]
 
 
