@@ -66,25 +66,38 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const uint16_t *__rest
     const int kofs = 8 * (lane >> 4);
     const int jbn = min(4, (r - 64 * jc + 15) / 16);   // column blocks of t present here
     f4 acc[RB][4] = {};
-#pragma unroll 4
-    for (int st = kb + w; st < ke; st += 4) {
-        const int k = 32 * st + kofs;             // K % 8 == 0: eight in or eight out
-        const bool kin = k < K;
-        u4 xa[RB];
+    // the wave's steps kb + w, kb + w + 4, ... in groups of three: the loads of
+    // a group are issued together, then its products run in step order (the
+    // chunks are short, so one group is usually the wave's whole share)
+    constexpr int kGroup = 3;
+    for (int st0 = kb + w; st0 < ke; st0 += 4 * kGroup) {
+        u4 xa[kGroup][RB], av[kGroup][4];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int row = 16 * (RB * mg + rb) + (lane & 15);
-            xa[rb] = load_b128(xr, (row < M && kin) ? (uint32_t)(row * K + k) * 2u : kOOB);
+        for (int i = 0; i < kGroup; ++i) {
+            const int k = 32 * (st0 + 4 * i) + kofs;   // K % 8 == 0: eight in or eight out
+            const bool kin = st0 + 4 * i < ke && k < K;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int row = 16 * (RB * mg + rb) + (lane & 15);
+                xa[i][rb] = load_b128(xr, (row < M && kin) ? (uint32_t)(row * K + k) * 2u : kOOB);
+            }
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                if (jb < jbn) {                   // uniform across the workgroup
+                    const int j = 64 * jc + 16 * jb + (lane & 15);
+                    av[i][jb] = load_b128(ar, (j < r && kin) ? (uint32_t)(j * K + k) * 2u : kOOB);
+                }
+            }
         }
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            if (jb < jbn) {                       // uniform across the workgroup
-                const int j = 64 * jc + 16 * jb + (lane & 15);
-                const uint32_t ao = (j < r && kin) ? (uint32_t)(j * K + k) * 2u : kOOB;
-                const u4 av = load_b128(ar, ao);
+        for (int i = 0; i < kGroup; ++i) {
+            if (st0 + 4 * i >= ke) break;         // uniform: steps past the chunk add nothing
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) acc[rb][jb] = mfma16x16x32_t<BF>(xa[rb], av, acc[rb][jb]);
-            }
+            for (int jb = 0; jb < 4; ++jb)
+                if (jb < jbn)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        acc[rb][jb] = mfma16x16x32_t<BF>(xa[i][rb], av[i][jb], acc[rb][jb]);
         }
     }
     __shared__ f4 red[4][RB][4][64];
@@ -404,8 +417,19 @@ __global__ void __launch_bounds__(256) lora_finish_kernel(const float *__restric
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e >= M * r) return;
     const int m = e / r, j = e - m * r;
+    const float *src = tp + (size_t)m * r + j;
+    const size_t slab = (size_t)Mp * r;
+    // eight slabs' loads in flight at a time, added in slab order
     float acc = 0.f;
-    for (int q = 0; q < S; ++q) acc += tp[((size_t)q * Mp + m) * r + j];
+    int q = 0;
+    for (; q + 8 <= S; q += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(q + u) * slab];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; q < S; ++q) acc += src[(size_t)q * slab];
     ta[e] = (uint16_t)pack2<BF>(scale * acc, 0.f);
 }
 
