@@ -283,7 +283,18 @@ __global__ __launch_bounds__(256) void prefill_chunk_reduce_kernel(
     const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= total) return;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < chunks; ++c) {
+    // eight chunks' loads in flight at a time, added in chunk order
+    int c = 0;
+    for (; c + 8 <= chunks; c += 8) {
+        f4 p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) p[u] = *reinterpret_cast<const f4 *>(partials + (size_t)(c + u) * total + e);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] += p[u][j];
+    }
+    for (; c < chunks; ++c) {
         const f4 p = *reinterpret_cast<const f4 *>(partials + (size_t)c * total + e);
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] += p[j];
