@@ -75,8 +75,9 @@ bool decode_lora_inkernel_ok(const LinearArgs &a, int num_cus);
 hipError_t launch_decode(const LinearArgs &a, hipStream_t stream, void *workspace, int capacity,
                          int grid, size_t max_lds);
 
-// Prefill (any M).  For M <= 128 the K range can be split into chunks, and
-// for M > 128 a last partial round of tiles can be split along K; either
+// Prefill (any M).  The 128-row kernel (M <= 128, and mid-sized M where it
+// is priced cheaper) can split the K range into chunks, and the 256-row
+// kernel a last partial round of tiles along K; either
 // needs `workspace` (prefill_workspace_bytes(capacity) bytes of fp32
 // partials, no initial contents) when prefill_wants_workspace(a, num_cus).
 // A smaller capacity splits into fewer chunks; without a workspace every
