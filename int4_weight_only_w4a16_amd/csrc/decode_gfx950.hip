@@ -418,9 +418,9 @@ constexpr size_t streamk_static_lds(int waves) {
 // LoRA adapter term inside the stream-K launch (LoraTerm, LK).
 //
 // Workgroups g < Su also own shrink unit g: each of their waves adds x . A^T
-// over one 32-deep K step on the matrix cores (the loads issued with the
-// first weight loads), and their last wave, which takes a lighter share of
-// the range, adds the eight wave partials in wave order and stores slab g
+// over one 32-deep K step on the matrix cores (the loads issued ahead of the
+// weight prologue, so the step waits for them only), and their last wave
+// adds the eight wave partials in wave order and stores slab g
 // into the slab words of the decode workspace, each value coded so that it
 // is never zero (as the exchange slots code theirs).  After its main loop
 // every workgroup reads all slab words (M r Su of them), waiting until none
@@ -822,19 +822,6 @@ __host__ __device__ __forceinline__ int wave_share(int n, int w) {
     return nold + (n - nold) * (w - H) / (WAVES - H);
 }
 
-// As wave_share, with the last wave's weight a quarter of its younger
-// siblings' (it publishes a LoRA shrink unit before its main loop).
-template <int WAVES>
-__host__ __device__ __forceinline__ int wave_share_light(int n, int w) {
-    constexpr int H = WAVES / 2;
-    constexpr int wo = 2 * kOldShare / H;                  // older waves' weight
-    constexpr int wy = 2 * (1000 - kOldShare) / (WAVES - H);
-    constexpr int wl = wy / 4;
-    constexpr int total = wo * H + wy * (WAVES - H - 1) + wl;
-    const int c = w <= H ? wo * w : w < WAVES ? wo * H + wy * (w - H) : total;
-    return (int)((int64_t)n * c / total);
-}
-
 // LK: the LoRA adapter term in the same launch (LoraTerm; SILU and ZP off).
 template <int WAVES, int D, int SCALE, bool XLDS, bool BF, bool SILU, bool ZP, bool SB, bool LK>
 __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
@@ -864,15 +851,13 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     const StreamK sk{T * S, (int)gridDim.x};
     // three contributors per tile (each range a third of one tile)
     const bool three = partials == nullptr && (int)gridDim.x == 3 * T;
-    // LK: the first Su workgroups also own a shrink unit, whose publication
-    // by their last wave gives that wave a lighter share of the range
+    // LK: the first Su workgroups also own a shrink unit
     const int g = blockIdx.x;
     const bool unit = LK && g < lora.Su;
     const int u0 = sk.begin(g), u1 = sk.begin(g + 1);
     // the host keeps every wave's share <= S units: at most two tiles per wave
-    const int w0 = u0 + (unit ? wave_share_light<WAVES>(u1 - u0, wave) : wave_share<WAVES>(u1 - u0, wave));
-    const int w1 = u0 + (unit ? wave_share_light<WAVES>(u1 - u0, wave + 1)
-                              : wave_share<WAVES>(u1 - u0, wave + 1));
+    const int w0 = u0 + wave_share<WAVES>(u1 - u0, wave);
+    const int w1 = u0 + wave_share<WAVES>(u1 - u0, wave + 1);
 
     const int Gs = SCALE != 0 ? (S + group_steps - 1) / group_steps : (K + 15) >> 4;
     const auto xr = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
@@ -885,6 +870,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
     u4 *img = reinterpret_cast<u4 *>(decode_dyn_lds + lora_lds_offset(XLDS, M, S));
     u4 *bst = img + kLoraStageChunks;            // LK: the staged rows of B
     LoraStep lstep{};
+    // LK, unit workgroups: the shrink step's loads go ahead of the weight
+    // prologue, so the step waits for them and not for the weight ring
+    if constexpr (LK)
+        if (unit) lstep = lora_step_issue(lora, xr, M, K, g * kLoraUnitSteps + wave, unit);
     LoraBStage lb{};
     LoraWords words{};
     __builtin_amdgcn_sched_barrier(0);
@@ -900,8 +889,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_streamk_kernel(
         [&]() -> uint32_t {
             uint32_t a = 0u;
             if constexpr (LK) {
-                // the shrink step's loads (unit workgroups) and the rows of B
-                if (unit) lstep = lora_step_issue(lora, xr, M, K, g * kLoraUnitSteps + wave, unit);
+                // the rows of B; the shrink step (unit workgroups)
                 lb = lora_b_issue(lora, N, u0 / S, u1 > u0 ? (u1 - 1) / S - u0 / S + 1 : 0);
                 if constexpr (XLDS) a = stage_x_finish(decode_dyn_lds, xr, M, K, S, xpre);
                 if (unit) lora_step_finish<BF>(reinterpret_cast<float *>(img), lora, lstep, M, wave);
@@ -1234,20 +1222,14 @@ int decode_streamk_grid(const LinearArgs &a, int num_cus) {
 
 // Whether the LoRA term (a.lora, counters aside) can go inside a stream-K
 // launch of `grid` workgroups: rank and sizes within the LDS areas, one
-// workgroup per shrink unit, and every wave's lighter or heavier share at
-// most S units.
+// workgroup per shrink unit (the waves' shares are those of every stream-K
+// launch, at most S units each).
 static bool lora_inkernel_ok(const LinearArgs &a, int grid) {
     const LoraTerm &L = a.lora;
     if (L.r < 8 || L.r % 8 != 0 || L.r > kLoraMaxRank || a.M * L.r > kLoraMaxMR) return false;
     const int64_t S = (a.K + 31) / 32;
-    const int64_t T = (a.N + kCols - 1) / kCols;
     if (grid <= 0 || L.Su != (S + kLoraUnitSteps - 1) / kLoraUnitSteps || L.Su > grid) return false;
     if ((int64_t)L.Su * a.M * L.r > kLoraMaxSlabReads) return false;
-    const int nmax = (int)((T * S + grid - 1) / grid);
-    for (int n = nmax - 1; n <= nmax; ++n)
-        for (int w = 0; w < kDecWaves; ++w)
-            if (wave_share_light<kDecWaves>(n, w + 1) - wave_share_light<kDecWaves>(n, w) > S)
-                return false;
     return true;
 }
 
