@@ -1315,11 +1315,16 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
         dim3(tiles), block, args, dyn, stream);
 }
 
-// Whether the activations can be staged in LDS: at most kXStageMax bytes,
-// and the kernel's static LDS plus the staging area within the device's
-// per-workgroup LDS limit (a launch beyond it is rejected by the device).
+// Whether the activations are staged in LDS: one or two rows (from three
+// rows on, loading them per unit is faster: K=5120, N=17408, M = 3 / 4 / 6:
+// 12.7 / 13.3 / 14.3 -> 12.6 / 12.9 / 13.6 us; K=N=5120: 9.2 / 9.5 / 10.1 ->
+// 8.7 / 8.7 / 9.0 us; at M = 2 staging is 0.4 us faster), at most kXStageMax
+// bytes, and the kernel's static LDS plus the staging area within the
+// device's per-workgroup LDS limit (a launch beyond it is rejected by the
+// device).
 template <int SCALE, bool BF>
 static bool stage_fits(const LinearArgs &a, int grid, size_t max_lds) {
+    if (a.M > 2) return false;
     const size_t stage = (size_t)a.M * 32 * ((a.K + 31) / 32) * 2 + 16;
     if (stage > kXStageMax) return false;
     const size_t dyn = stage + (a.lora.A ? kLoraLdsBytes : 0);
