@@ -1155,9 +1155,19 @@ __global__ __launch_bounds__(256) void decode_split_reduce_kernel(
 #ifndef W4A16_DECODE_D
 #define W4A16_DECODE_D 4
 #endif
+#ifndef W4A16_DECODE_DX
+#define W4A16_DECODE_DX 3
+#endif
 
 constexpr int kDecWaves = W4A16_DECODE_WAVES;
+// Load ring depth: with staged activations (a unit's loads are its weight
+// words and scales), and with activations loaded per unit (one more 16-byte
+// load per stage), where a ring of 3 measured faster than 4 at M = 4-16 on
+// K = 5120 (N=17408 M = 8 / 16: 14.5 / 19.0 -> 14.4 / 18.7 us; K=N=5120 M = 4 /
+// 8 / 16: 8.75 / 9.27 / 11.05 -> 8.55 / 9.03 / 10.75 us) and the same within
+// 0.1 us at K = 17408; 6 was slower everywhere.
 constexpr int kDecD = W4A16_DECODE_D;
+constexpr int kDecDx = W4A16_DECODE_DX;
 
 static size_t slots_bytes(int capacity) { return (size_t)capacity * 16 * (kCols / 2) * sizeof(uint64_t); }
 
@@ -1293,11 +1303,12 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
         void *args[] = {&xp, &qp, &sp, &zp, &yp, (void *)&M, (void *)&K, (void *)&N,
                         &group_steps, &z8, &slots, &partials, &lora};
         const void *kern = reinterpret_cast<const void *>(
-            &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP, SB, false>);
+            &decode_streamk_kernel<kDecWaves, XLDS ? kDecD : kDecDx, SCALE, XLDS, BF, SILU, ZP, SB, false>);
         if constexpr (!SILU && !ZP)
             if (lk)
                 kern = reinterpret_cast<const void *>(
-                    &decode_streamk_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP, SB, true>);
+                    &decode_streamk_kernel<kDecWaves, XLDS ? kDecD : kDecDx, SCALE, XLDS, BF, SILU, ZP, SB,
+                                           true>);
         hipError_t e = hipLaunchKernel(kern, dim3(grid), block, args, dyn, stream);
         if (e != hipSuccess || !part) return e;
         const float *pc = partials;
@@ -1311,7 +1322,7 @@ static hipError_t launch_sa(const LinearArgs &a, hipStream_t stream, void *works
     const unsigned tiles = (unsigned)((N + kCols - 1) / kCols);
     return hipLaunchKernel(
         reinterpret_cast<const void *>(
-            &decode_tiles_kernel<kDecWaves, kDecD, SCALE, XLDS, BF, SILU, ZP, SB>),
+            &decode_tiles_kernel<kDecWaves, XLDS ? kDecD : kDecDx, SCALE, XLDS, BF, SILU, ZP, SB>),
         dim3(tiles), block, args, dyn, stream);
 }
 
