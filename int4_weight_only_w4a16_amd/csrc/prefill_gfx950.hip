@@ -954,12 +954,18 @@ __global__ __launch_bounds__(256) void prefill_tail_reduce_kernel(
 // Split of the wide kernel's tiles: whole rounds of one tile per workgroup;
 // a last partial round of `tail` tiles (at most half a round) split into
 // `chunks` >= 2 stage ranges of at least 8 stages, so that tail * chunks
-// workgroups fill about one round, and at most `capacity` partial tiles.
+// workgroups fill up to one round, and at most `capacity` partial tiles.
 // (For the merged gate/up projection the split tiles store plain fp32 sums
 // and the reduce kernel applies SiLU.)
 struct WidePlan {
     int tiles, tiles_dp, tail, chunks;
 };
+
+// At most six chunks per split tile: on the up-projection (M=2048, K=5120,
+// N=17408: 32 tail tiles) six chunks of 13-14 stages took the step from
+// 317.4 to 314.8 us against eight of 10 (four: 315.9), with 48 MiB of fp32
+// partials written and read back instead of 64.
+constexpr int kWideTailMaxChunks = 6;
 
 static WidePlan wide_plan(const LinearArgs &a, int num_cus, int capacity) {
     WidePlan w;
@@ -971,7 +977,8 @@ static WidePlan wide_plan(const LinearArgs &a, int num_cus, int capacity) {
     if (num_cus <= 0) return w;
     const int tail = w.tiles % num_cus;
     if (tail == 0 || 2 * tail > num_cus) return w;
-    const int chunks = std::min(std::min(num_cus / tail, nst / 8), capacity / tail);
+    const int chunks = std::min(std::min(std::min(num_cus / tail, nst / 8), capacity / tail),
+                                kWideTailMaxChunks);
     if (chunks < 2) return w;
     w.tail = tail;
     w.chunks = chunks;
